@@ -1,0 +1,169 @@
+"""Plain fp64 attention: the definition written out, one (batch, head) at a time.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+What is computed (all in float64, all N x N matrices materialised):
+
+Forward -- page 1 section 五 (standard attention: S = Q K^T, P = softmax(S),
+O = P V), with the 1/sqrt(d) scale that page 2 4.3.2 and page 4 下篇 3.3 write
+into S; the scale is a parameter whose default is 1/sqrt(d):
+
+    S_ij   = scale * <q_i, k_j>
+    S_ij   = -inf  where key j is hidden from query i (mask below)
+    m_i    = max_j S_ij                         (page 1 section 六, safe softmax)
+    e_ij   = exp(S_ij - m_i), exactly 0.0 where hidden
+    l_i    = sum_j e_ij
+    P_ij   = e_ij / l_i
+    O_i    = sum_j P_ij v_j
+    LSE_i  = m_i + ln l_i                       (page 2 4.3.2, "L_i = m_i + log l_i")
+
+Mask: key j is hidden from query i when (causal and j > i) -- the upper-right
+triangle of page 3 第八部分 -- or when j >= kv_len[b] (key padding; the pages
+only name an attention-mask argument, so the reading is: padded keys are hidden
+from every query row, and every query row, padded or not, is computed).
+A row with no visible key (impossible for kv_len >= 1 in these workloads) gives
+O_i = 0, LSE_i = -inf and zero gradients.
+
+Backward -- page 1 section 八 and page 2 4.3.4 say only that P is rebuilt from
+the saved row statistics (P_ij = exp(S_ij - L_i)) and that dS, dQ, dK, dV are
+computed; they print no gradient formula. The reading is ordinary calculus of
+f = sum(O * dO) for softmax attention:
+
+    dV = P^T dO
+    dP = dO V^T
+    D_i = sum_j P_ij dP_ij
+    dS = P * (dP - D 1^T)
+    dQ = scale * dS K
+    dK = scale * dS^T Q
+
+Hidden entries have P = 0, hence dS = 0, so dK/dV rows of padded keys are 0.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d), the default softmax scale (page 4 下篇 section 六, the
+    ``softmax_scale=None`` argument of the flash-attn call)."""
+    return 1.0 / math.sqrt(d)
+
+
+def visible_mask(n: int, causal: bool, kv_len_b: int | None = None,
+                 rows=None) -> np.ndarray:
+    """Boolean [len(rows), n]: True where key j is visible to query i.
+
+    Causal hides j > i (page 3 第八部分, upper-right triangle); key padding
+    hides j >= kv_len_b for every query row.
+    """
+    i = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    j = np.arange(n)
+    vis = np.ones((i.shape[0], n), dtype=bool)
+    if kv_len_b is not None:
+        vis &= (j[None, :] < int(kv_len_b))
+    if causal:
+        vis &= (j[None, :] <= i[:, None])
+    return vis
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def head_forward(q, k, v, scale: float, causal: bool,
+                 kv_len_b: int | None = None, rows=None,
+                 want_p: bool = False) -> dict:
+    """Forward of one head. q, k, v: [n, d] (any real dtype, upcast exactly).
+
+    ``rows`` selects query rows (each output row depends on its own query row
+    and all keys only, so a subset is the same definition evaluated on fewer
+    rows). Returns dict(o=[r, d], lse=[r], and p=[r, n] if ``want_p``).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n = k.shape[0]
+    qr = q if rows is None else q[np.asarray(rows, dtype=np.int64)]
+    vis = visible_mask(n, causal, kv_len_b, rows)
+
+    s = scale * (qr @ k.T)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    has_key = np.isfinite(m)
+    m_ref = np.where(has_key, m, 0.0)
+    e = np.where(vis, np.exp(s - m_ref[:, None]), 0.0)
+    l = e.sum(axis=1)
+    l_safe = np.where(has_key, l, 1.0)
+    p = e / l_safe[:, None]
+    o = p @ v
+    lse = np.where(has_key, m_ref + np.log(l_safe), -np.inf)
+    out = {"o": o, "lse": lse}
+    if want_p:
+        out["p"] = p
+    return out
+
+
+def head_backward(q, k, v, do, scale: float, causal: bool,
+                  kv_len_b: int | None = None) -> dict:
+    """Gradients of f = sum(O * dO) for one head; q, k, v, do: [n, d].
+
+    Returns dict(dq, dk, dv, d=D vector, o, lse).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    fw = head_forward(q, k, v, scale, causal, kv_len_b, want_p=True)
+    p = fw.pop("p")
+    dv = p.T @ do
+    dp = do @ v.T
+    dvec = (p * dp).sum(axis=1)
+    ds = p * (dp - dvec[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return {"dq": dq, "dk": dk, "dv": dv, "d": dvec,
+            "o": fw["o"], "lse": fw["lse"]}
+
+
+def _kv_len_of(kv_len, b: int):
+    return None if kv_len is None else int(np.asarray(kv_len).reshape(-1)[b])
+
+
+def attention_fwd(q, k, v, causal: bool = False, scale: float | None = None,
+                  kv_len=None):
+    """Forward over [B, H, N, d] inputs, one head at a time.
+
+    Returns (o [B,H,N,d] float64, lse [B,H,N] float64, natural log).
+    """
+    q = _f64(q)
+    bsz, heads, n, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    o = np.empty_like(q)
+    lse = np.empty((bsz, heads, n))
+    for b in range(bsz):
+        kvl = _kv_len_of(kv_len, b)
+        for h in range(heads):
+            r = head_forward(q[b, h], k[b, h], v[b, h], scale, causal, kvl)
+            o[b, h] = r["o"]
+            lse[b, h] = r["lse"]
+    return o, lse
+
+
+def attention_bwd(q, k, v, do, causal: bool = False,
+                  scale: float | None = None, kv_len=None):
+    """Backward over [B, H, N, d] inputs, one head at a time.
+
+    Returns (dq, dk, dv), each [B,H,N,d] float64.
+    """
+    q = _f64(q)
+    bsz, heads, n, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = np.empty_like(q)
+    dk = np.empty_like(q)
+    dv = np.empty_like(q)
+    for b in range(bsz):
+        kvl = _kv_len_of(kv_len, b)
+        for h in range(heads):
+            r = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale,
+                              causal, kvl)
+            dq[b, h], dk[b, h], dv[b, h] = r["dq"], r["dk"], r["dv"]
+    return dq, dk, dv
