@@ -1,0 +1,25 @@
+"""MI355X-native fused exact attention (gfx950 HIP kernels behind a C ABI).
+
+Python surface:
+
+* ``binding``   -- ctypes view of include/fa.h (fa_fwd, fa_bwd,
+                   fa_bwd_workspace_bytes, fa_status_str, fa_abi_version).
+* ``attention`` -- torch wrappers: ``flash_attn_fwd``, ``flash_attn_bwd`` and
+                   the autograd-enabled ``flash_attention``.
+* ``inputs``    -- seeded synthetic workloads.
+* ``build``     -- hipcc build of libexact_fa.so (in-tree).
+"""
+
+from .binding import (  # noqa: F401
+    FA_BF16, FA_FP32, fa_abi_version, fa_bwd, fa_bwd_workspace_bytes, fa_fwd,
+    fa_status_str)
+
+
+def __getattr__(name):
+    # torch-facing helpers are imported on first use so that importing the
+    # package (e.g. to build it) does not require torch.
+    if name in ("flash_attention", "flash_attn_fwd", "flash_attn_bwd",
+                "FlashAttentionFunction"):
+        from . import attention
+        return getattr(attention, name)
+    raise AttributeError(name)

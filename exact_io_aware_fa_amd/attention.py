@@ -1,0 +1,108 @@
+"""PyTorch-facing calls: allocate outputs and workspace with torch, pass raw
+pointers and torch's current HIP stream to the C ABI.
+
+PyTorch supplies device memory and streams only; every step of the forward
+and backward runs in the library's HIP kernels. There is no CPU or eager
+fallback: a CPU tensor or a missing library is an error.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as _b
+
+_DTYPES = {torch.bfloat16: _b.FA_BF16, torch.float32: _b.FA_FP32}
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [batch, heads, n, d]")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [batch, heads, n, d] shape")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+
+
+def _kv_len_arg(kv_len, batch, n, device):
+    """int32 device tensor of key lengths (checked to lie in [1, n]), or None."""
+    if kv_len is None:
+        return None
+    t = torch.as_tensor(kv_len)
+    if t.numel() != batch:
+        raise ValueError(f"kv_len must have {batch} entries")
+    host = t.detach().to("cpu", torch.int64).reshape(-1)
+    if int(host.min()) < 1 or int(host.max()) > n:
+        raise ValueError(f"kv_len entries must lie in [1, {n}]")
+    return host.to(torch.int32).to(device)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def flash_attn_fwd(q, k, v, causal=False, softmax_scale=None, kv_len=None):
+    """Forward: returns (o, lse); o like q, lse float32 [batch, heads, n]."""
+    _check_qkv(q, k, v)
+    b, h, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    kvl = _kv_len_arg(kv_len, b, n, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    _b.check(_b.fa_fwd(b, h, n, d, causal, scale, _DTYPES[q.dtype],
+                       q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                       None if kvl is None else kvl.data_ptr(),
+                       o.data_ptr(), lse.data_ptr(), _stream()))
+    return o, lse
+
+
+def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
+                   kv_len=None):
+    """Backward from the saved LSE: returns (dq, dk, dv)."""
+    _check_qkv(q, k, v)
+    if o.shape != q.shape or do.shape != q.shape or o.dtype != q.dtype or do.dtype != q.dtype:
+        raise ValueError("o and do must match q in shape and dtype")
+    o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
+    b, h, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    kvl = _kv_len_arg(kv_len, b, n, q.device)
+    dt = _DTYPES[q.dtype]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = _b.fa_bwd_workspace_bytes(b, h, n, d, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _b.check(_b.fa_bwd(b, h, n, d, causal, scale, dt,
+                       q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       do.data_ptr(), lse.data_ptr(),
+                       None if kvl is None else kvl.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       ws.data_ptr(), ws_bytes, _stream()))
+    return dq, dk, dv
+
+
+class FlashAttentionFunction(torch.autograd.Function):
+    """Autograd wrapper: saves q, k, v, o and the LSE; recomputes P in the
+    backward kernel."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, softmax_scale, kv_len):
+        o, lse = flash_attn_fwd(q, k, v, causal, softmax_scale, kv_len)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale, ctx.kv_len = causal, softmax_scale, kv_len
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = flash_attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.causal,
+                                    ctx.scale, ctx.kv_len)
+        return dq, dk, dv, None, None, None
+
+
+def flash_attention(q, k, v, causal=False, softmax_scale=None, kv_len=None):
+    """O = softmax(scale * Q K^T + mask) V with autograd support."""
+    return FlashAttentionFunction.apply(q, k, v, causal, softmax_scale, kv_len)

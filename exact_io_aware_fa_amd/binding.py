@@ -1,0 +1,97 @@
+"""ctypes binding of the C ABI in include/fa.h -- argument marshalling only.
+
+Every function here has the name and argument order of the C entry point it
+wraps; tensors are passed as raw device addresses (ints). Nothing is
+computed on the host. If the shared library has not been built the loader
+raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("FA_LIB", os.path.join(PKG, "libexact_fa.so"))
+
+FA_BF16 = 0
+FA_FP32 = 1
+
+FA_OK = 0
+FA_E_NULLPTR = 1
+FA_E_SHAPE = 2
+FA_E_UNSUPPORTED = 3
+FA_E_WORKSPACE = 4
+FA_E_ALIAS = 5
+FA_E_LAUNCH = 6
+FA_E_ALIGN = 7
+
+# Every symbol include/fa.h declares.
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str",
+            "fa_abi_version")
+
+_lock = threading.Lock()
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libexact_fa.so once (raises if it is missing)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m exact_io_aware_fa_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fa_fwd.restype = ctypes.c_int
+        L.fa_fwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                             ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                             ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+        L.fa_status_str.restype = ctypes.c_char_p
+        L.fa_status_str.argtypes = [ctypes.c_int]
+        L.fa_abi_version.restype = ctypes.c_int
+        L.fa_abi_version.argtypes = []
+        _lib = L
+        return L
+
+
+def fa_fwd(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, kv_len,
+           o, lse, stream) -> int:
+    return lib().fa_fwd(batch, heads, n, d, int(causal), float(softmax_scale),
+                        int(dtype), q, k, v, kv_len, o, lse, stream)
+
+
+def fa_bwd(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o, d_o,
+           lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream) -> int:
+    return lib().fa_bwd(batch, heads, n, d, int(causal), float(softmax_scale),
+                        int(dtype), q, k, v, o, d_o, lse, kv_len, dq, dk, dv,
+                        workspace, int(workspace_bytes), stream)
+
+
+def fa_bwd_workspace_bytes(batch, heads, n, d, dtype) -> int:
+    return int(lib().fa_bwd_workspace_bytes(batch, heads, n, d, int(dtype)))
+
+
+def fa_status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def fa_abi_version() -> int:
+    return int(lib().fa_abi_version())
+
+
+def check(status: int) -> None:
+    """Raise RuntimeError carrying the library's message for a non-OK status."""
+    if status != FA_OK:
+        raise RuntimeError(fa_status_str(status))

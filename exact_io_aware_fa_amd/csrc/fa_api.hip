@@ -1,0 +1,186 @@
+// C-ABI entry points (include/fa.h): argument validation, workspace layout,
+// kernel dispatch. Host code only; the kernels live in kernels/*.hip.
+//
+// Validation runs on the host before anything is enqueued and touches no HIP
+// state, so every error path is reachable without a GPU.
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 22;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status check_common(int64_t batch, int64_t heads, int64_t n, int64_t d,
+                       float scale, fa_dtype dtype) {
+  if (batch < 1 || heads < 1 || n < 1 || n > kMaxN) return FA_E_SHAPE;
+  if (batch > INT32_MAX || heads > INT32_MAX) return FA_E_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_E_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_FP32) return FA_E_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_E_UNSUPPORTED;
+  // Per-head element offsets are 32-bit; workgroup counts must fit a grid.
+  if (n * d >= (int64_t(1) << 31)) return FA_E_SHAPE;
+  const int64_t tiles = (n + 63) / 64;
+  if (tiles * batch * heads >= (int64_t(1) << 31)) return FA_E_SHAPE;
+  return FA_OK;
+}
+
+size_t elem_size(fa_dtype t) { return t == FA_BF16 ? 2 : 4; }
+
+size_t dvec_bytes(int64_t batch, int64_t heads, int64_t n) {
+  const size_t b = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
+  return (b + 255) & ~size_t(255);
+}
+
+fa::Params base_params(int64_t batch, int64_t heads, int64_t n, int causal,
+                       float scale) {
+  fa::Params p{};
+  p.batch = int(batch);
+  p.heads = int(heads);
+  p.n = int(n);
+  p.causal = causal ? 1 : 0;
+  float c = fabsf(scale) * 1.4426950408889634f;
+  p.c = c < FLT_MIN ? FLT_MIN : c;
+  p.scale = scale;
+  p.q_neg = scale < 0.f ? 1 : 0;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_E_NULLPTR: return "FA_E_NULLPTR: a required pointer is NULL";
+    case FA_E_SHAPE: return "FA_E_SHAPE: batch, heads or n out of range";
+    case FA_E_UNSUPPORTED: return "FA_E_UNSUPPORTED: unsupported d, dtype or scale";
+    case FA_E_WORKSPACE: return "FA_E_WORKSPACE: workspace missing or too small";
+    case FA_E_ALIAS: return "FA_E_ALIAS: an output overlaps an input or another output";
+    case FA_E_LAUNCH: return "FA_E_LAUNCH: kernel launch failed";
+    case FA_E_ALIGN: return "FA_E_ALIGN: pointer not 16-byte aligned";
+  }
+  return "FA_E_UNKNOWN";
+}
+
+size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n, int64_t d,
+                              fa_dtype dtype) {
+  if (check_common(batch, heads, n, d, 1.f, dtype) != FA_OK) return 0;
+  size_t bytes = dvec_bytes(batch, heads, n);
+  if (dtype == FA_BF16)
+    bytes += size_t(batch) * size_t(heads) * size_t(n) * size_t(d) * sizeof(float);
+  return bytes;
+}
+
+fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
+                 float softmax_scale, fa_dtype dtype, const void* q, const void* k,
+                 const void* v, const int32_t* kv_len, void* o, float* lse,
+                 void* stream) {
+  fa_status st = check_common(batch, heads, n, d, softmax_scale, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_E_ALIGN;
+  if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u)) return FA_E_ALIGN;
+  const size_t tb = size_t(batch) * size_t(heads) * size_t(n) * size_t(d) * elem_size(dtype);
+  const size_t lb = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
+  const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range ro = range_of(o, tb), rl = range_of(lse, lb);
+  if (overlaps(ro, rl)) return FA_E_ALIAS;
+  for (const Range& r : ins)
+    if (overlaps(r, ro) || overlaps(r, rl)) return FA_E_ALIAS;
+  if (kv_len) {
+    const Range rk = range_of(kv_len, size_t(batch) * sizeof(int32_t));
+    if (overlaps(rk, ro) || overlaps(rk, rl)) return FA_E_ALIAS;
+  }
+
+  fa::Params p = base_params(batch, heads, n, causal, softmax_scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.kv_len = kv_len;
+  p.o = o;
+  p.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, int(d), s)
+                                          : fa::launch_fwd_fp32(p, int(d), s);
+  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
+}
+
+fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
+                 float softmax_scale, fa_dtype dtype, const void* q, const void* k,
+                 const void* v, const void* o, const void* d_o, const float* lse,
+                 const int32_t* kv_len, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(batch, heads, n, d, softmax_scale, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return FA_E_NULLPTR;
+  if (!workspace) return FA_E_WORKSPACE;
+  const size_t need = fa_bwd_workspace_bytes(batch, heads, n, d, dtype);
+  if (workspace_bytes < need) return FA_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_E_ALIGN;
+  if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u)) return FA_E_ALIGN;
+
+  const size_t tb = size_t(batch) * size_t(heads) * size_t(n) * size_t(d) * elem_size(dtype);
+  const size_t lb = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
+  Range ins[7] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
+                  range_of(d_o, tb), range_of(lse, lb), Range{0, 0}};
+  int nin = 6;
+  if (kv_len) ins[nin++] = range_of(kv_len, size_t(batch) * sizeof(int32_t));
+  const Range outs[4] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
+                         range_of(workspace, need)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j])) return FA_E_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return FA_E_ALIAS;
+  }
+
+  fa::Params p = base_params(batch, heads, n, causal, softmax_scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_in = o;
+  p.d_o = d_o;
+  p.lse = const_cast<float*>(lse);
+  p.kv_len = kv_len;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dvec = static_cast<float*>(workspace);
+  p.dq_acc = (dtype == FA_BF16)
+                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            dvec_bytes(batch, heads, n))
+                 : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = dtype == FA_BF16;
+  hipError_t e = fa::launch_bwd_prep(p, int(d), bf, s);
+  if (e == hipSuccess)
+    e = bf ? fa::launch_bwd_bf16(p, int(d), s) : fa::launch_bwd_fp32(p, int(d), s);
+  if (e == hipSuccess && bf) e = fa::launch_dq_convert(p, int(d), s);
+  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI layer (fa_api.hip) and the kernel
+// translation units. Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a kernel needs about one call; passed by value as a kernel
+// argument. Element offsets inside one (batch, head) slice fit in 32 bits
+// (n * d < 2^31 is enforced by validation); slice bases are 64-bit.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o_in;     // backward: forward output
+  const void* d_o;      // backward: upstream gradient
+  const int32_t* kv_len;  // nullable, device int32[batch]
+  void* o;              // forward output
+  float* lse;           // forward output / backward input, [B,H,N] fp32
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;          // backward workspace: D_i = <dO_i, O_i>, [B,H,N]
+  float* dq_acc;        // backward workspace: fp32 dQ accumulator (bf16 path)
+  int batch;
+  int heads;
+  int n;
+  int causal;
+  // Scores enter exp2 as s * c where c = |scale| * log2(e), raised to at
+  // least FLT_MIN so that c > 0 and hidden entries (-inf) stay -inf; a
+  // negative scale is applied by negating Q (exact), flagged by q_neg.
+  float c;
+  float scale;          // signed softmax scale (backward gradient factor)
+  int q_neg;
+};
+
+hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s);
+hipError_t launch_fwd_fp32(const Params& p, int d, hipStream_t s);
+hipError_t launch_bwd_prep(const Params& p, int d, bool bf16, hipStream_t s);
+hipError_t launch_bwd_bf16(const Params& p, int d, hipStream_t s);
+hipError_t launch_bwd_fp32(const Params& p, int d, hipStream_t s);
+hipError_t launch_dq_convert(const Params& p, int d, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,331 @@
+// Fused attention backward, bf16 in/out, fp32 accumulate, for gfx950.
+//
+// Method: recomputation from the saved row statistic (page 1, "注意力为什么
+// 受限于显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 八; page 2,
+// "4. FlashAttention 深度剖析", 4.3.4): P_ij = exp(scale q_i.k_j - L_i) is
+// rebuilt tile by tile and never stored. The gradient formulas are the
+// ordinary calculus of softmax attention (the pages name dS, dQ, dK, dV but
+// print no formula):
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = <dO_i, O_i>,
+//     dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Mapping onto CDNA4:
+// * A workgroup is 4 wave64s and owns BKV = 128 keys (32 per wave) and their
+//   dK, dV accumulators (fp32, in VGPRs/AGPRs) for the whole query sweep; it
+//   loops over query tiles of BQ rows (key/value-outer order, so dK and dV
+//   need no atomics).
+// * Each wave keeps its 32 K and V rows in VGPRs as the B operands of
+//   S = Q K^T and dP = dO V^T; the results hold one key per lane and 16
+//   queries, which is exactly the B-operand layout of dV^T += dO^T P and
+//   dK^T += Q^T dS, so P and dS go to the matrix cores without leaving
+//   registers.
+// * Q and dO tiles are staged in LDS twice: row-major (A operand of S and
+//   dP) and transposed (A operand of dV^T and dK^T).
+// * dQ needs dS with queries on lanes, so dS is written to LDS as bf16 and
+//   each wave computes a 32x32 block of dQ = dS K over all 128 keys, added
+//   into an fp32 accumulator with float atomics.
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
+
+template <int D, int BQ, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
+  constexpr int ND = D / 16;
+  constexpr int NMB = D / 32;
+  constexpr int NQB = BQ / 32;
+  constexpr int QSTR = D + 8;      // row-major Q / dO tiles
+  constexpr int TSTR = BQ + 4;     // transposed tiles [d][q]
+  constexpr int KTSTR = kBKV + 8;  // K^T [d][key]
+  constexpr int DSSTR = kBKV + 8;  // dS [q][key]
+  constexpr int UPT = (BQ / 4) * (D / 8);  // 4x8 units per tensor tile
+  constexpr int UNITS = 2 * UPT;           // Q and dO
+  constexpr int UPTH = (UNITS + kThreads - 1) / kThreads;
+  constexpr int KUN = (kBKV / 4) * (D / 8);
+  constexpr int KUPT = KUN / kThreads;
+  static_assert(UNITS % kThreads == 0 && KUN % kThreads == 0, "unit split");
+
+  __shared__ __attribute__((aligned(16))) bf16 sKt[D * KTSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sQ[BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sQt[D * TSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * TSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdS[BQ * DSSTR];
+  __shared__ __attribute__((aligned(16))) float sL[BQ];
+  __shared__ __attribute__((aligned(16))) float sDv[BQ];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+  const int n = p.n;
+
+  const int t_c = (n + kBKV - 1) / kBKV;
+  int bh, kt;
+  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, bh, kt);
+  const int b = bh / p.heads;
+  const size_t base = (size_t)bh * (size_t)n * D;
+  const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
+  const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
+  const float* __restrict__ lse = p.lse + (size_t)bh * n;
+  const float* __restrict__ dvec = p.dvec + (size_t)bh * n;
+  float* __restrict__ dQa = p.dq_acc + base;
+  bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + base;
+  bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + base;
+
+  const int kv_lim = kv_limit(p, b);
+  const int k0 = kt * kBKV;
+  const int kw0 = k0 + w * 32;
+  const int mykey = kw0 + c;
+  const float cs = p.c;
+  const uint32_t qflip = p.q_neg ? 0x80008000u : 0u;
+
+  f32x16 dk[NMB], dv[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    dk[mb] = f32x16{};
+    dv[mb] = f32x16{};
+  }
+
+  if (k0 < kv_lim) {
+    // K and V rows of this wave as B fragments: [mykey][kd*16 + h*8 + e].
+    bf16x8 kf[ND], vf[ND];
+#pragma unroll
+    for (int kd = 0; kd < ND; ++kd) {
+      u32x4 a = {0u, 0u, 0u, 0u}, bb = {0u, 0u, 0u, 0u};
+      if (mykey < kv_lim) {
+        a = ld16(K + (size_t)mykey * D + kd * 16 + h * 8);
+        bb = ld16(V + (size_t)mykey * D + kd * 16 + h * 8);
+      }
+      kf[kd] = as_bf16x8(a);
+      vf[kd] = as_bf16x8(bb);
+    }
+    // K^T of the whole workgroup into LDS (B operand of dQ = dS K).
+#pragma unroll
+    for (int i = 0; i < KUPT; ++i) {
+      const int u = tid + i * kThreads;
+      const int kg = (u >> 2) % (kBKV / 4);
+      const int dg = (u & 3) + 4 * (u / kBKV);
+      u32x4 r[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int key = k0 + kg * 4 + t;
+        r[t] = (key < kv_lim) ? ld16(K + (size_t)key * D + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<u32x2*>(&sKt[(dg * 8 + e) * KTSTR + kg * 4]) = column4(r, e);
+    }
+
+    const int n_qt = (n + BQ - 1) / BQ;
+    const int it0 = CAUSAL ? (k0 / BQ) : 0;
+
+    // Register staging of the next Q / dO tile: unit u < UPT is a Q unit,
+    // else a dO unit; a unit is 4 rows x 8 dims.
+    u32x4 ureg[UPTH][4];
+    auto gload = [&](int it) {
+      const int q0 = it * BQ;
+#pragma unroll
+      for (int i = 0; i < UPTH; ++i) {
+        const int u0 = tid + i * kThreads;
+        const bool isq = u0 < UPT;
+        const int u = isq ? u0 : u0 - UPT;
+        const int qg = (u >> 2) % (BQ / 4);
+        const int dg = (u & 3) + 4 * (u / BQ);
+        const bf16* src = isq ? Q : dO;
+        const uint32_t flip = isq ? qflip : 0u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int q = q0 + qg * 4 + t;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (q < n) v = ld16(src + (size_t)q * D + dg * 8) ^ flip;
+          ureg[i][t] = v;
+        }
+      }
+    };
+    auto swrite = [&](int it) {
+      const int q0 = it * BQ;
+#pragma unroll
+      for (int i = 0; i < UPTH; ++i) {
+        const int u0 = tid + i * kThreads;
+        const bool isq = u0 < UPT;
+        const int u = isq ? u0 : u0 - UPT;
+        const int qg = (u >> 2) % (BQ / 4);
+        const int dg = (u & 3) + 4 * (u / BQ);
+        bf16* rm = isq ? sQ : sdO;
+        bf16* tr = isq ? sQt : sdOt;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<u32x4*>(&rm[(qg * 4 + t) * QSTR + dg * 8]) = ureg[i][t];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<u32x2*>(&tr[(dg * 8 + e) * TSTR + qg * 4]) = column4(ureg[i], e);
+      }
+      if (tid < BQ) {
+        const int q = q0 + tid;
+        sL[tid] = (q < n) ? lse[q] * kLog2e : 0.f;
+        sDv[tid] = (q < n) ? dvec[q] : 0.f;
+      }
+    };
+
+    if (it0 < n_qt) gload(it0);
+    for (int it = it0; it < n_qt; ++it) {
+      __syncthreads();  // previous tile's LDS contents are no longer read
+      swrite(it);
+      __syncthreads();
+      if (it + 1 < n_qt) gload(it + 1);
+
+      const int q0 = it * BQ;
+      const bool active = !(CAUSAL && kw0 > q0 + BQ - 1);
+      if (active) {
+        f32x16 sv[NQB], dp[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          sv[qb] = f32x16{};
+          dp[qb] = f32x16{};
+#pragma unroll
+          for (int kd = 0; kd < ND; ++kd) {
+            const bf16x8 a = as_bf16x8(ld16(&sQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+            sv[qb] = mma32(a, kf[kd], sv[qb]);
+            const bf16x8 g = as_bf16x8(ld16(&sdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+            dp[qb] = mma32(g, vf[kd], dp[qb]);
+          }
+        }
+        const bool need_mask = (q0 + BQ > n) || (k0 + kBKV > kv_lim) ||
+                               (CAUSAL && kw0 + 31 > q0);
+        // P (probabilities) into sv, dS into dp; lane owns key `mykey` and
+        // queries q0 + qb*32 + g*8 + h*4 + i.
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[qb * 32 + g * 8 + h * 4]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDv[qb * 32 + g * 8 + h * 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = g * 4 + i;
+              float pr = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], cs, -l4[i]));
+              if (need_mask) {
+                const int q = q0 + qb * 32 + g * 8 + h * 4 + i;
+                const bool hidden = q >= n || mykey >= kv_lim || (CAUSAL && mykey > q);
+                pr = hidden ? 0.f : pr;
+              }
+              sv[qb][r] = pr;
+              dp[qb][r] = pr * (dp[qb][r] - d4[i]);
+            }
+          }
+        // dV^T += dO^T P and dK^T += Q^T dS (queries are the reduction).
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int qc = 0; qc < 2; ++qc) {
+            u32x4 pu, su;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              pu[t] = pack_bf16x2(sv[qb][qc * 8 + 2 * t], sv[qb][qc * 8 + 2 * t + 1]);
+              su[t] = pack_bf16x2(dp[qb][qc * 8 + 2 * t], dp[qb][qc * 8 + 2 * t + 1]);
+            }
+            const bf16x8 pfr = as_bf16x8(pu);
+            const bf16x8 sfr = as_bf16x8(su);
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+              const int off = (mb * 32 + c) * TSTR + qb * 32 + qc * 16 + h * 4;
+              const u32x2 olo = ld8(&sdOt[off]);
+              const u32x2 ohi = ld8(&sdOt[off + 8]);
+              const u32x4 oa = {olo[0], olo[1], ohi[0], ohi[1]};
+              dv[mb] = mma32(as_bf16x8(oa), pfr, dv[mb]);
+              const u32x2 qlo = ld8(&sQt[off]);
+              const u32x2 qhi = ld8(&sQt[off + 8]);
+              const u32x4 qa = {qlo[0], qlo[1], qhi[0], qhi[1]};
+              dk[mb] = mma32(as_bf16x8(qa), sfr, dk[mb]);
+            }
+            // dS (bf16) to LDS as [q][key] for the dQ product.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int qa0 = qb * 32 + qc * 16 + (t >> 1) * 8 + h * 4 + (t & 1) * 2;
+              sdS[qa0 * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] & 0xffffu));
+              sdS[(qa0 + 1) * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] >> 16));
+            }
+          }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sdS[(qb * 32 + (r >> 2) * 8 + h * 4 + (r & 3)) * DSSTR + w * 32 + c] =
+                __builtin_bit_cast(bf16, (uint16_t)0);
+      }
+      __syncthreads();  // dS tile complete
+
+      // dQ[q][d] += scale * sum_key dS[q][key] K[key][d], one 32x32 block
+      // per wave and step.
+#pragma unroll
+      for (int blk = w; blk < NQB * NMB; blk += 4) {
+        const int qb = blk / NMB;
+        const int mb = blk % NMB;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < kBKV / 16; ++kc) {
+          const bf16x8 a = as_bf16x8(ld16(&sdS[(qb * 32 + c) * DSSTR + kc * 16 + h * 8]));
+          const bf16x8 bk = as_bf16x8(ld16(&sKt[(mb * 32 + c) * KTSTR + kc * 16 + h * 8]));
+          acc = mma32(a, bk, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + qb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          if (q < n) unsafeAtomicAdd(&dQa[(size_t)q * D + mb * 32 + c], p.scale * acc[r]);
+        }
+      }
+    }
+  }
+
+  // dK = |scale| * (dS^T Q') with Q' = sign(scale) Q, dV as accumulated.
+  if (mykey < n) {
+    const float ks = fabsf(p.scale);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const size_t off = (size_t)mykey * D + mb * 32 + g * 8 + h * 4;
+        u32x2 uk, uv;
+        uk[0] = pack_bf16x2(dk[mb][g * 4 + 0] * ks, dk[mb][g * 4 + 1] * ks);
+        uk[1] = pack_bf16x2(dk[mb][g * 4 + 2] * ks, dk[mb][g * 4 + 3] * ks);
+        uv[0] = pack_bf16x2(dv[mb][g * 4 + 0], dv[mb][g * 4 + 1]);
+        uv[1] = pack_bf16x2(dv[mb][g * 4 + 2], dv[mb][g * 4 + 3]);
+        *reinterpret_cast<u32x2*>(dK + off) = uk;
+        *reinterpret_cast<u32x2*>(dV + off) = uv;
+      }
+  }
+}
+
+template <int D, int BQ>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  const int t_c = (p.n + kBKV - 1) / kBKV;
+  const long long total = (long long)t_c * p.batch * p.heads;
+  dim3 grid((unsigned)total), block(kThreads);
+  if (p.causal)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, BQ, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, BQ, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const Params& p, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_d<64, 64>(p, s);
+    case 128: return launch_d<128, 32>(p, s);
+    case 256: return launch_d<256, 32>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

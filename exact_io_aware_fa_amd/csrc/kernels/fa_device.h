@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// the bf16 matrix-core product, bf16 packing, and the workgroup-id remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
+// acc[32x32] += A[32x16] * B[16x32] on the bf16 matrix cores, fp32 accumulate.
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, each with the
+// same 8 reduction indices, so any bijection between (l / 32, element) and
+// the 16 reduction indices gives the same product as long as A and B use
+// it alike. The result holds column (l % 32) and rows
+// 8 * (r / 4) + 4 * (l / 32) + (r % 4), r = 0..15.
+__device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x2 ld8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// Round to nearest even, two floats -> one dword of two bf16 (low = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Column e (0..7) of four 8-element bf16 rows, packed as 4 bf16 (row 0 in
+// the lowest half-word): one 8-byte group of a transposed tile.
+__device__ __forceinline__ u32x2 column4(const u32x4 r[4], int e) {
+  const int w = e >> 1;
+  u32x2 out;
+  if (e & 1) {
+    out[0] = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+    out[1] = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
+  } else {
+    out[0] = (r[0][w] & 0xffffu) | (r[1][w] << 16);
+    out[1] = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+  }
+  return out;
+}
+
+// Workgroup remap. The dispatcher places consecutive workgroup ids on the
+// eight XCDs in turn (id % 8), each XCD with its own L2. Hand each XCD a
+// contiguous range of the work list so that workgroups of the same
+// (batch, head) share one L2, and order the list head-major. Within a head,
+// `tile` runs from the most expensive tile down when `heavy_last_index` is
+// set (causal forward: the last query tile sees the most keys), else up from
+// tile 0 (causal backward: the first key tile sees the most queries).
+__device__ __forceinline__ void remap_workgroup(int wg, int total, int tiles,
+                                                bool heavy_last_index,
+                                                int& bh, int& tile) {
+  const int xcd = wg & 7;
+  const int slot = wg >> 3;
+  const int per = total >> 3;
+  const int rem = total & 7;
+  const int idx = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  bh = idx / tiles;
+  const int t = idx - bh * tiles;
+  tile = heavy_last_index ? (tiles - 1 - t) : t;
+}
+
+// Keys j >= kv_limit are hidden for this batch entry (clamped to [0, n]).
+__device__ __forceinline__ int kv_limit(const Params& p, int b) {
+  if (p.kv_len == nullptr) return p.n;
+  int v = p.kv_len[b];
+  v = v < 0 ? 0 : v;
+  return v > p.n ? p.n : v;
+}
+
+}  // namespace fa

@@ -1,0 +1,282 @@
+// Fused attention forward, bf16 in/out, fp32 accumulate, for gfx950.
+//
+// Method: the tiled forward of page 2 ("4. FlashAttention 深度剖析", 4.3.2)
+// with the per-block (m, l, O) update of page 1 ("注意力为什么受限于显存带宽：
+// 用算术强度与分块把 FlashAttention 推导清楚", section 六): query tiles outer,
+// key/value tiles inner, normalisation deferred to the end, and the row
+// statistic L = m + ln l stored for the backward pass. Causal key tiles that
+// lie wholly above the diagonal are never visited (page 2 4.3.2's note; page 3
+// "深入浅出 FlashAttention" 第八部分).
+//
+// Mapping onto CDNA4:
+// * A workgroup is 4 wave64s and owns BR = 128 query rows; each wave owns 32
+//   of them for the whole key sweep (split over queries, so no cross-wave
+//   reduction of m or l is ever needed).
+// * Each wave keeps its Q rows in VGPRs as the B operand of the 32x32x16
+//   bf16 MFMA and computes S^T = K Q^T, so a lane owns one query row and 16
+//   keys of every 32-key block: the row max and row sum are in-lane, plus one
+//   exchange between the two 32-lane halves (the max only; the sums are
+//   combined once at the end).
+// * The probabilities, rounded to bf16, are already laid out as the B
+//   operand of O^T += V^T P^T, so P never leaves registers.
+// * K tiles are stored row-major in LDS (rows padded by 16 bytes); V tiles
+//   are stored transposed ([d][key], rows padded by 8 bytes) so the V^T
+//   operand is two 8-byte LDS reads per lane. Both layouts give each bank the
+//   minimum number of accesses for the wave's reads.
+// * The next K/V tile is fetched from HBM into registers (coalesced 16-byte
+//   loads) while the current tile is being computed.
+// * exp2 with the log2(e) factor folded into the score scale; the max-shift
+//   and scale are one FMA per score.
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
+
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
+  constexpr int KSTR = D + 8;    // K row stride in LDS (bf16 elements)
+  constexpr int VSTR = BC + 4;   // V^T row stride in LDS (bf16 elements)
+  constexpr int ND = D / 16;     // reduction steps of S^T = K Q^T
+  constexpr int NMB = D / 32;    // 32-row blocks of O^T
+  constexpr int NKB = BC / 32;   // 32-key blocks of S^T
+  constexpr int KCH = BC * D / 8 / kThreads;  // 16-byte K chunks per thread
+  constexpr int VUN = (BC / 4) * (D / 8);     // V units: 4 keys x 8 dims
+  constexpr int VUPT = (VUN + kThreads - 1) / kThreads;
+  static_assert(KCH * kThreads * 8 == BC * D, "K tile split");
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+  const int n = p.n;
+
+  const int t_r = (n + kBR - 1) / kBR;
+  int bh, qb;
+  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
+  const int b = bh / p.heads;
+  const size_t base = (size_t)bh * (size_t)n * D;
+  const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
+  bf16* __restrict__ O = static_cast<bf16*>(p.o) + base;
+
+  const int kv_lim = kv_limit(p, b);
+  const int q0 = qb * kBR;
+  const int qw0 = q0 + w * 32;
+  const int qi = qw0 + c;
+  const float cs = p.c;
+
+  // Q rows of this wave as B fragments: Q[qi][kd*16 + h*8 + e].
+  bf16x8 qf[ND];
+  {
+    const uint32_t flip = p.q_neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kd = 0; kd < ND; ++kd) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qi < n) v = ld16(Q + (size_t)qi * D + kd * 16 + h * 8);
+      v ^= flip;
+      qf[kd] = as_bf16x8(v);
+    }
+  }
+
+  int kend = kv_lim;
+  if (CAUSAL) kend = min(kend, q0 + kBR);
+  const int ntiles = (kend + BC - 1) / BC;
+
+  f32x16 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+  float m2 = kNegInf;   // running max in scaled base-2 units (s * cs)
+  float lpart = 0.f;    // this half-wave's share of the running row sum
+
+  u32x4 kreg[KCH];
+  u32x4 vreg[VUPT][4];
+
+  auto gload = [&](int j) {
+    const int kb0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      const int key = ch / (D / 8);
+      const int dc = ch % (D / 8);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (kb0 + key < kv_lim) v = ld16(K + (size_t)(kb0 + key) * D + dc * 8);
+      kreg[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < VUPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (VUN % kThreads == 0 || u < VUN) {
+        const int kg = (u >> 2) % (BC / 4);
+        const int dg = (u & 3) + 4 * (u / BC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb0 + kg * 4 + r;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (key < kv_lim) v = ld16(V + (size_t)key * D + dg * 8);
+          vreg[i][r] = v;
+        }
+      }
+    }
+  };
+
+  auto swrite = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      const int key = ch / (D / 8);
+      const int dc = ch % (D / 8);
+      *reinterpret_cast<u32x4*>(&sK[key * KSTR + dc * 8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VUPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (VUN % kThreads == 0 || u < VUN) {
+        const int kg = (u >> 2) % (BC / 4);
+        const int dg = (u & 3) + 4 * (u / BC);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<u32x2*>(&sVt[(dg * 8 + e) * VSTR + kg * 4]) =
+              column4(vreg[i], e);
+      }
+    }
+  };
+
+  if (ntiles > 0) gload(0);
+  for (int j = 0; j < ntiles; ++j) {
+    __syncthreads();  // every wave is done reading the previous tile
+    swrite();
+    __syncthreads();  // tile j is in LDS
+    if (j + 1 < ntiles) gload(j + 1);
+
+    const int kb0 = j * BC;
+    if (CAUSAL && kb0 > qw0 + 31) continue;  // whole tile above this wave's diagonal
+
+    // S^T (keys x queries) = K Q^T, raw dot products.
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int kd = 0; kd < ND; ++kd) {
+        const bf16x8 a = as_bf16x8(ld16(&sK[(kb * 32 + c) * KSTR + kd * 16 + h * 8]));
+        s[kb] = mma32(a, qf[kd], s[kb]);
+      }
+    }
+
+    const bool need_mask = (kb0 + BC > kv_lim) || (CAUSAL && kb0 + BC - 1 > qw0);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+          s[kb][r] = hidden ? kNegInf : s[kb][r];
+        }
+    }
+
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mt2 = (mt == kNegInf) ? kNegInf : mt * cs;
+    const float m2n = fmaxf(m2, mt2);
+    const float mref = (m2n == kNegInf) ? 0.f : m2n;
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);  // 0 while empty
+    m2 = m2n;
+
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cs, -mref));
+        s[kb][r] = e;
+        rs += e;
+      }
+    lpart = fmaf(lpart, alpha, rs);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+
+    // P^T as bf16 B fragments: chunk (kb, kc) holds keys kb*32 + kc*16 +
+    // {h*4 + 0..3, 8 + h*4 + 0..3}.
+    bf16x8 pf[NKB * 2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4 u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          u[t] = pack_bf16x2(s[kb][kc * 8 + 2 * t], s[kb][kc * 8 + 2 * t + 1]);
+        pf[kb * 2 + kc] = as_bf16x8(u);
+      }
+
+    // O^T (d x queries) += V^T P^T.
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int kk = 0; kk < NKB * 2; ++kk) {
+        const bf16* row = &sVt[(mb * 32 + c) * VSTR + kk * 16 + h * 4];
+        const u32x2 lo = ld8(row);
+        const u32x2 hi = ld8(row + 8);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        acc[mb] = mma32(as_bf16x8(a), pf[kk], acc[mb]);
+      }
+  }
+
+  // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
+  const float l = lpart + __shfl_xor(lpart, 32);
+  if (qi < n) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* orow = O + (size_t)qi * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 u;
+        u[0] = pack_bf16x2(acc[mb][g * 4 + 0] * inv, acc[mb][g * 4 + 1] * inv);
+        u[1] = pack_bf16x2(acc[mb][g * 4 + 2] * inv, acc[mb][g * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + mb * 32 + g * 8 + h * 4) = u;
+      }
+    if (h == 0)
+      p.lse[(size_t)bh * n + qi] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, int BC>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  const int t_r = (p.n + kBR - 1) / kBR;
+  const long long total = (long long)t_r * p.batch * p.heads;
+  dim3 grid((unsigned)total), block(kThreads);
+  if (p.causal)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_d<64, 64>(p, s);
+    case 128: return launch_d<128, 64>(p, s);
+    case 256: return launch_d<256, 32>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,107 @@
+"""Seeded synthetic workloads and their inputs.
+
+This module holds no attention arithmetic: it only names the workloads
+(shapes, dtypes, masks, value distributions, seeds) and draws their inputs.
+Both the HIP path and the CPU oracle are fed from it, so they see identical
+values. Draw order per workload: Q, K, V, dO as float32 standard normals
+(Q and K multiplied by ``qk_sigma``), each rounded to the workload dtype
+(bf16: round to nearest even), then the per-batch key lengths.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    n: int
+    d: int
+    dtype: str              # "bf16" or "fp32"
+    causal: bool
+    seed: int
+    qk_sigma: float = 1.0   # std of Q and K entries (V and dO are unit)
+    padded: bool = False    # per-batch key lengths, uniform in [n/2, n]
+    backward: bool = True
+    scale: float | None = None  # default 1/sqrt(d)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def flops_fwd(self) -> float:
+        """Attention FLOPs of the forward: 4 B H N^2 d, halved when causal."""
+        f = 4.0 * self.batch * self.heads * self.n * self.n * self.d
+        return f / 2 if self.causal else f
+
+    def flops_bwd(self) -> float:
+        """Backward FLOPs: 2.5x the forward (five N^2 d products vs two)."""
+        return 2.5 * self.flops_fwd()
+
+
+def _sweep():
+    out = []
+    idx = 0
+    for n in (2048, 4096, 8192):
+        for d in (64, 128, 256):
+            for causal in (False, True):
+                out.append(Workload(
+                    name=f"sweep_b2_h16_n{n}_d{d}_{'causal' if causal else 'full'}",
+                    batch=2, heads=16, n=n, d=d, dtype="bf16", causal=causal,
+                    seed=500 + idx))
+                idx += 1
+    return out
+
+
+WORKLOADS = {w.name: w for w in [
+    # single head, fp32, forward parity case the oracle finishes instantly
+    Workload("single_head_n128_d64_fp32", 1, 1, 128, 64, "fp32", False, seed=1,
+             backward=False),
+    # BERT-large-shaped encoder attention with key padding
+    Workload("bert_large_b8_h16_n512_d64_padded", 8, 16, 512, 64, "bf16", False,
+             seed=2, padded=True),
+    # GPT-2-shaped causal decoder attention
+    Workload("gpt2_b8_h12_n1024_d64_causal", 8, 12, 1024, 64, "bf16", True, seed=3),
+    # long-sequence causal attention with peaky rows (Q, K ~ N(0, 3^2))
+    Workload("long_causal_b1_h32_n16384_d128", 1, 32, 16384, 128, "bf16", True,
+             seed=4, qk_sigma=3.0),
+    *_sweep(),
+]}
+
+HEADLINE = "long_causal_b1_h32_n16384_d128"
+
+
+def make_inputs(w: Workload, with_grad_out: bool = True) -> dict:
+    """CPU tensors q, k, v (and do), plus kv_len (int32 [batch]) or None."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    shape = (w.batch, w.heads, w.n, w.d)
+    dt = w.torch_dtype
+
+    def draw(sigma):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        return x.to(dt)
+
+    out = {"q": draw(w.qk_sigma), "k": draw(w.qk_sigma), "v": draw(1.0)}
+    out["do"] = draw(1.0) if with_grad_out else None
+    out["kv_len"] = (torch.randint(w.n // 2, w.n + 1, (w.batch,), generator=g,
+                                   dtype=torch.int32) if w.padded else None)
+    return out
+
+
+def custom(name, batch, heads, n, d, dtype="bf16", causal=False, seed=0,
+           qk_sigma=1.0, padded=False, scale=None) -> Workload:
+    """An ad-hoc workload (tests of edge cases: ragged n, tiny shapes...)."""
+    return Workload(name, batch, heads, n, d, dtype, causal, seed, qk_sigma,
+                    padded, True, scale)

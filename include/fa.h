@@ -1,0 +1,149 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact-attention library.
+ *
+ * The library computes exact scaled-dot-product attention
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * without writing the N x N score or probability matrices to device memory:
+ * K/V are streamed through on-chip tiles and per-row (m, l, O~) states are
+ * merged with the online-softmax rescaling rule (page 1, "注意力为什么受限于
+ * 显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 六; page 2,
+ * "4. FlashAttention 深度剖析", 4.2.3-4.2.4 and the tiled forward of 4.3.2).
+ * The backward pass recomputes the probabilities from the saved per-row
+ * logsumexp, P_ij = exp(S_ij - L_i) (page 1 section 八; page 2 4.3.4).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout:    every tensor Q, K, V, O, dO, dQ, dK, dV is a contiguous
+ *            [batch, heads, n, d] array (d fastest); LSE is a contiguous
+ *            [batch, heads, n] float32 array. Queries and keys have the same
+ *            length n (self-attention).
+ * Pointers:  device pointers (memory from hipMalloc or an allocator on top of
+ *            it), at least 16-byte aligned. The caller owns every buffer;
+ *            the library only borrows pointers until the work it enqueued on
+ *            `stream` has finished. The library never allocates, frees or
+ *            synchronises the host.
+ * dtype:     FA_BF16 -- Q, K, V, O, dO, dQ, dK, dV are bfloat16; products on
+ *            bf16 matrix cores with float32 accumulation; the probabilities
+ *            are rounded to bf16 before the P V product; outputs rounded to
+ *            nearest-even. FA_FP32 -- every tensor is float32 and every step
+ *            computes in float32 (no bf16 rounding anywhere).
+ * d:         64, 128 or 256 (bf16 and fp32).
+ * Masks:     causal != 0 hides key j from query i when j > i (the upper-right
+ *            triangle). kv_len, when not NULL, is a device int32[batch]; key
+ *            j of batch b is hidden from every query row when
+ *            j >= kv_len[b]. Every query row is computed, padded or not.
+ *            Hidden probabilities are exactly 0; a row with no visible key
+ *            gets O = 0, LSE = -inf and zero gradients.
+ * Scale:     softmax_scale is any finite float (0 gives uniform weights over
+ *            the visible keys). The usual choice is 1/sqrt(d).
+ * LSE:       LSE_i = ln sum_j exp(scale * q_i . k_j) over the visible keys,
+ *            natural logarithm, float32 (page 2, 4.3.2: L = m + log l).
+ * Streams:   `stream` is a hipStream_t (NULL = the null stream). All work is
+ *            enqueued asynchronously on it; nothing is enqueued elsewhere.
+ * Errors:    arguments are validated synchronously, before anything is
+ *            enqueued; on a validation error nothing is written and a
+ *            FA_E_* code is returned. A failed kernel launch returns
+ *            FA_E_LAUNCH. Faults during execution surface at the caller's
+ *            next synchronisation, as with any HIP kernel.
+ * Threads:   entry points are reentrant; concurrent calls on different
+ *            streams may share inputs but must not share outputs.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_E_NULLPTR = 1,     /* a required pointer is NULL                        */
+  FA_E_SHAPE = 2,       /* batch, heads or n < 1, or n too large             */
+  FA_E_UNSUPPORTED = 3, /* d not in {64,128,256}, unknown dtype, bad scale   */
+  FA_E_WORKSPACE = 4,   /* workspace NULL or smaller than required           */
+  FA_E_ALIAS = 5,       /* an output overlaps an input or another output     */
+  FA_E_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch          */
+  FA_E_ALIGN = 7        /* a pointer is not 16-byte aligned                  */
+} fa_status;
+
+/*
+ * fa_fwd -- forward pass (page 2, 4.3.2: tiled forward with deferred
+ * normalisation, storing L_i = m_i + log l_i).
+ *
+ *   q, k, v : inputs, [batch, heads, n, d] of `dtype`.
+ *   kv_len  : device int32[batch] key lengths, each in [1, n], or NULL
+ *             (no key padding). Values are trusted: the kernels clamp them
+ *             to [0, n], so an out-of-range value cannot cause an
+ *             out-of-bounds access.
+ *   o       : output, [batch, heads, n, d] of `dtype`, overwritten.
+ *   lse     : output, float32 [batch, heads, n], overwritten.
+ *
+ * o and lse must not overlap each other or any input.
+ */
+fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
+                 int causal, float softmax_scale, fa_dtype dtype,
+                 const void* q, const void* k, const void* v,
+                 const int32_t* kv_len,
+                 void* o, float* lse,
+                 void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: one
+ * float32 per query row for D_i = sum_k dO_ik O_ik, plus (bf16 only) a
+ * float32 dQ accumulator of batch*heads*n*d elements. Returns 0 for invalid
+ * sizes.
+ */
+size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n,
+                              int64_t d, fa_dtype dtype);
+
+/*
+ * fa_bwd -- backward pass: the gradients of f = sum(O * dO) with respect to
+ * Q, K and V, recomputing P_ij = exp(scale q_i.k_j - L_i) tile by tile from
+ * the saved LSE (page 1 section 八; page 2 4.3.4). With dS = P * (dP - D),
+ * dP = dO V^T and D_i = sum_k dO_ik O_ik:
+ *     dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+ *
+ *   q, k, v, o, d_o : inputs, [batch, heads, n, d] of `dtype`; o is the
+ *                     forward output for the same arguments.
+ *   lse             : input, float32 [batch, heads, n], from fa_fwd.
+ *   kv_len          : as for fa_fwd (must match the forward call).
+ *   dq, dk, dv      : outputs, [batch, heads, n, d] of `dtype`; overwritten,
+ *                     not accumulated into.
+ *   workspace       : device scratch of at least
+ *                     fa_bwd_workspace_bytes(batch, heads, n, d, dtype)
+ *                     bytes, 256-byte aligned; contents on entry are
+ *                     ignored and undefined on exit.
+ *
+ * Outputs and the workspace must not overlap each other or any input.
+ * dQ is accumulated with float32 atomics, so its last bits may differ from
+ * run to run; dK and dV are deterministic.
+ */
+fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
+                 int causal, float softmax_scale, fa_dtype dtype,
+                 const void* q, const void* k, const void* v,
+                 const void* o, const void* d_o, const float* lse,
+                 const int32_t* kv_len,
+                 void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* FA_ABI_VERSION of the library that was loaded. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,131 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol include/fa.h
+declares, and validates arguments on the host (every call here fails
+validation before anything would be enqueued; no compute runs without a
+GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_io_aware_fa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from exact_io_aware_fa_amd.build import build
+        build()
+    return B.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*?\**\s*\b(fa_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_binding_surface():
+    assert _declared() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (fa_\w+)$", out, flags=re.M))
+    assert set(_declared()) <= exported
+
+
+def test_abi_version_and_status_strings(lib):
+    assert B.fa_abi_version() == 1
+    for code, tag in ((0, "FA_OK"), (1, "FA_E_NULLPTR"), (2, "FA_E_SHAPE"),
+                      (3, "FA_E_UNSUPPORTED"), (4, "FA_E_WORKSPACE"), (5, "FA_E_ALIAS"),
+                      (6, "FA_E_LAUNCH"), (7, "FA_E_ALIGN")):
+        assert B.fa_status_str(code).startswith(tag)
+    assert B.fa_status_str(99) == "FA_E_UNKNOWN"
+
+
+# Fake, well-separated, 256-byte-aligned device addresses; never dereferenced
+# because every call below is rejected by validation.
+Q, K, V, O, L, DO, DQ, DK, DV, WS, KVL = (0x1000_0000 * (i + 1) for i in range(11))
+SHAPE = dict(batch=2, heads=3, n=64, d=64)
+
+
+def fwd(**kw):
+    a = dict(SHAPE, causal=0, softmax_scale=0.125, dtype=B.FA_BF16, q=Q, k=K, v=V,
+             kv_len=None, o=O, lse=L, stream=None)
+    a.update(kw)
+    return B.fa_fwd(a["batch"], a["heads"], a["n"], a["d"], a["causal"], a["softmax_scale"],
+                    a["dtype"], a["q"], a["k"], a["v"], a["kv_len"], a["o"], a["lse"],
+                    a["stream"])
+
+
+def ws_bytes(dtype=B.FA_BF16, **shape):
+    s = dict(SHAPE, **shape)
+    return B.fa_bwd_workspace_bytes(s["batch"], s["heads"], s["n"], s["d"], dtype)
+
+
+def bwd(**kw):
+    a = dict(SHAPE, causal=1, softmax_scale=0.125, dtype=B.FA_BF16, q=Q, k=K, v=V, o=O,
+             d_o=DO, lse=L, kv_len=None, dq=DQ, dk=DK, dv=DV, workspace=WS,
+             workspace_bytes=None, stream=None)
+    a.update(kw)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = ws_bytes(a["dtype"])
+    return B.fa_bwd(a["batch"], a["heads"], a["n"], a["d"], a["causal"], a["softmax_scale"],
+                    a["dtype"], a["q"], a["k"], a["v"], a["o"], a["d_o"], a["lse"],
+                    a["kv_len"], a["dq"], a["dk"], a["dv"], a["workspace"],
+                    a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), B.FA_E_UNSUPPORTED), (dict(d=32), B.FA_E_UNSUPPORTED),
+    (dict(dtype=5), B.FA_E_UNSUPPORTED),
+    (dict(softmax_scale=float("nan")), B.FA_E_UNSUPPORTED),
+    (dict(softmax_scale=float("inf")), B.FA_E_UNSUPPORTED),
+    (dict(batch=0), B.FA_E_SHAPE), (dict(heads=0), B.FA_E_SHAPE), (dict(n=0), B.FA_E_SHAPE),
+    (dict(n=(1 << 22) + 1), B.FA_E_SHAPE), (dict(batch=1 << 16, heads=1 << 16), B.FA_E_SHAPE),
+    (dict(q=None), B.FA_E_NULLPTR), (dict(o=None), B.FA_E_NULLPTR), (dict(lse=None), B.FA_E_NULLPTR),
+    (dict(k=K + 8), B.FA_E_ALIGN), (dict(lse=L + 4), B.FA_E_ALIGN), (dict(kv_len=KVL + 2), B.FA_E_ALIGN),
+    (dict(o=Q + 4096), B.FA_E_ALIAS), (dict(lse=O + 64), B.FA_E_ALIAS), (dict(o=V), B.FA_E_ALIAS),
+    (dict(kv_len=O + 16), B.FA_E_ALIAS),
+])
+def test_fwd_validation(lib, kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=100), B.FA_E_UNSUPPORTED), (dict(batch=-1), B.FA_E_SHAPE),
+    (dict(d_o=None), B.FA_E_NULLPTR), (dict(dk=None), B.FA_E_NULLPTR),
+    (dict(workspace=None), B.FA_E_WORKSPACE),
+    (dict(workspace_bytes=1024), B.FA_E_WORKSPACE),
+    (dict(workspace=WS + 16), B.FA_E_ALIGN), (dict(dv=DV + 2), B.FA_E_ALIGN),
+    (dict(dq=DK), B.FA_E_ALIAS), (dict(dk=L), B.FA_E_ALIAS), (dict(workspace=DQ), B.FA_E_ALIAS),
+    (dict(dv=Q + 256), B.FA_E_ALIAS), (dict(kv_len=DQ + 4), B.FA_E_ALIAS),
+])
+def test_bwd_validation(lib, kw, code):
+    assert bwd(**kw) == code
+
+
+def test_workspace_size_closed_form(lib):
+    b, h, n, d = 2, 3, 100, 128
+    rows = b * h * n * 4
+    dvec = (rows + 255) // 256 * 256
+    assert ws_bytes(B.FA_FP32, batch=b, heads=h, n=n, d=d) == dvec
+    assert ws_bytes(B.FA_BF16, batch=b, heads=h, n=n, d=d) == dvec + b * h * n * d * 4
+    assert ws_bytes(B.FA_BF16, d=48) == 0
+    assert ws_bytes(B.FA_BF16, n=0) == 0
+
+
+def test_loader_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

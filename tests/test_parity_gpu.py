@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+identical seeded inputs, for every named workload and a set of edge shapes.
+
+Small workloads are compared head by head in full. At the full long-sequence
+size (B=1, H=32, N=16384, d=128, causal, in the launch configuration the
+bench times) one head is compared in full, forward and backward, and seeded
+query rows of other heads are compared one by one; every head is also checked
+for properties that hold at any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_fa_amd.inputs import WORKLOADS, custom, make_inputs
+from parity_utils import (check_backward_head, check_forward_head, f64, run_gpu,
+                          workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def _all_heads(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.heads)]
+
+
+def test_single_head_fp32_forward():
+    w = WORKLOADS["single_head_n128_d64_fp32"]
+    inp = workload_inputs(w)
+    gpu = run_gpu(w, inp, backward=False)
+    check_forward_head(w, inp, gpu, 0, 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_head_fp32_backward(causal):
+    w = custom("fp32_n128_d64", 1, 1, 128, 64, "fp32", causal, seed=11)
+    inp = make_inputs(w)
+    gpu = run_gpu(w, inp)
+    check_forward_head(w, inp, gpu, 0, 0)
+    check_backward_head(w, inp, gpu, 0, 0)
+
+
+@pytest.mark.parametrize("name", ["bert_large_b8_h16_n512_d64_padded",
+                                  "gpt2_b8_h12_n1024_d64_causal"])
+def test_encoder_decoder_workloads_every_head(name):
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    print(f"[parity] {name}", flush=True)
+    gpu = run_gpu(w, inp)
+    for b, h in _all_heads(w):
+        check_forward_head(w, inp, gpu, b, h)
+        check_backward_head(w, inp, gpu, b, h)
+
+
+def test_long_causal_full_size():
+    w = WORKLOADS["long_causal_b1_h32_n16384_d128"]
+    print(f"[parity] {w.name}: GPU fwd+bwd at full size", flush=True)
+    inp = workload_inputs(w)
+    gpu = run_gpu(w, inp)
+    # Properties of every head: finite outputs, causal row 0 returns V row 0.
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.isfinite(gpu[name]).all(), name
+    assert torch.equal(gpu["o"][:, :, 0].cpu(), inp["v"][:, :, 0])
+    # Seeded rows of four heads, one by one.
+    rng = np.random.default_rng(4)
+    for h in (1, 9, 22, 31):
+        rows = np.sort(rng.choice(w.n, size=24, replace=False))
+        rows[0] = w.n - 1
+        check_forward_head(w, inp, gpu, 0, h, rows=rows, peaky=True)
+    # One head in full, forward and backward.
+    print("[parity] full-head oracle (fp64, N=16384)", flush=True)
+    check_forward_head(w, inp, gpu, 0, 5, peaky=True)
+    check_backward_head(w, inp, gpu, 0, 5)
+
+
+SWEEP_FULL = [n for n in WORKLOADS if n.startswith("sweep_b2_h16_n2048")]
+SWEEP_ROWS = [n for n in WORKLOADS if n.startswith("sweep_") and n not in SWEEP_FULL]
+
+
+@pytest.mark.parametrize("name", SWEEP_FULL)
+def test_sweep_n2048_two_heads_in_full(name):
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    print(f"[parity] {name}", flush=True)
+    gpu = run_gpu(w, inp)
+    for b, h in ((0, 3), (1, 14)):
+        check_forward_head(w, inp, gpu, b, h)
+        check_backward_head(w, inp, gpu, b, h)
+
+
+@pytest.mark.parametrize("name", SWEEP_ROWS)
+def test_sweep_longer_sampled_rows(name):
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    print(f"[parity] {name}", flush=True)
+    gpu = run_gpu(w, inp)
+    rng = np.random.default_rng(w.seed)
+    for b, h in ((0, 0), (1, 11)):
+        rows = np.sort(rng.choice(w.n, size=16, replace=False))
+        check_forward_head(w, inp, gpu, b, h, rows=rows)
+    for name_ in ("dq", "dk", "dv"):
+        assert torch.isfinite(gpu[name_]).all()
+
+
+EDGE = [
+    # (n, d, causal, dtype, padded)
+    (1, 64, False, "bf16", False), (1, 128, True, "bf16", False),
+    (7, 64, True, "bf16", False), (100, 128, False, "bf16", True),
+    (129, 64, True, "bf16", False), (257, 128, True, "bf16", True),
+    (300, 256, False, "bf16", False), (383, 256, True, "bf16", True),
+    (1000, 64, False, "bf16", True), (65, 128, True, "fp32", False),
+    (200, 256, False, "fp32", True), (31, 64, True, "fp32", True),
+]
+
+
+@pytest.mark.parametrize("n,d,causal,dtype,padded", EDGE)
+def test_edge_shapes(n, d, causal, dtype, padded):
+    w = custom(f"edge_n{n}_d{d}", 2, 3, n, d, dtype, causal, seed=n * 7 + d, padded=padded)
+    inp = make_inputs(w)
+    print(f"[parity] edge n={n} d={d} causal={causal} {dtype} padded={padded}", flush=True)
+    gpu = run_gpu(w, inp)
+    for b, h in ((0, 0), (1, 2)):
+        check_forward_head(w, inp, gpu, b, h)
+        check_backward_head(w, inp, gpu, b, h)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.9])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_nondefault_scales(scale, dtype):
+    w = custom("scale", 1, 2, 150, 64, dtype, True, seed=77, scale=scale)
+    inp = make_inputs(w)
+    gpu = run_gpu(w, inp)
+    for h in range(2):
+        check_forward_head(w, inp, gpu, 0, h)
+        check_backward_head(w, inp, gpu, 0, h)
+
+
+def test_autograd_wrapper_matches_direct_calls():
+    from exact_io_aware_fa_amd.attention import flash_attention, flash_attn_bwd, flash_attn_fwd
+    w = custom("autograd", 2, 2, 96, 64, "bf16", True, seed=5)
+    inp = make_inputs(w)
+    q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
+    qr, kr, vr = (x.clone().requires_grad_(True) for x in (q, k, v))
+    o = flash_attention(qr, kr, vr, causal=True)
+    o.backward(do)
+    o2, lse = flash_attn_fwd(q, k, v, True)
+    dq, dk, dv = flash_attn_bwd(q, k, v, o2, lse, do, True)
+    assert torch.equal(o, o2)
+    assert torch.equal(kr.grad, dk) and torch.equal(vr.grad, dv)
+    torch.testing.assert_close(qr.grad.float(), dq.float(), atol=1e-2, rtol=0)
+
+
+def test_wrapper_rejects_bad_arguments():
+    from exact_io_aware_fa_amd.attention import flash_attn_fwd
+    x = torch.randn(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        flash_attn_fwd(x, x, x)  # CPU tensors: no host fallback
+    g = x.cuda()
+    with pytest.raises(ValueError):
+        flash_attn_fwd(g, g, g.float())
+    with pytest.raises(ValueError):
+        flash_attn_fwd(g, g, g, kv_len=[0])
+    y = torch.randn(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="FA_E_UNSUPPORTED"):
+        flash_attn_fwd(y, y, y)
