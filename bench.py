@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Attention throughput on one MI355X: forward + backward, bf16.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+fa_fwd (O and LSE) followed by fa_bwd (D_i and dQ zeroing, the recompute
+backward, dQ conversion), all on torch's current stream, with the inputs
+already resident in device memory. W untimed steps, then exactly K timed steps
+between two device synchronisations. One JSON line is printed.
+
+FLOPs follow the attention convention: 4 B H N^2 d for the forward (two
+N x N x d products), 2.5x that for the backward (five products), halved when
+causal. ``value`` is fwd+bwd TFLOP/s over the wall time of the timed steps.
+
+The ``roofline`` object is for the dominant kernel, the main backward
+kernel: its algorithmic FLOPs per launch divided by its average duration,
+measured with HIP events recorded on the launch stream immediately before and
+after it (fa_bwd_timed), against the bf16 dense matrix-core peak. ``traffic``
+is read from the committed rocprofv3 counter summary for this kernel and
+workload when that summary was taken from the current kernel source, else
+null.
+
+``cpu_baseline`` times the fp64 CPU oracle (materialised S and P, NumPy/BLAS)
+on a bounded sample of the same workload -- whole heads, fwd+bwd, until about
+10 s of CPU work -- and scales it to the same TFLOP/s convention.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
+KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
+                  "exact_io_aware_fa_amd/csrc/kernels/fa_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_bf16_long_causal_b1_h32_n16384_d128_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw HIP events through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.rt.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def record(self, ev: int, stream: int) -> None:
+        rc = self.rt.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self.rt.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, ev: int) -> None:
+        self.rt.hipEventDestroy(ev)
+
+
+def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
+    """Time the fp64 oracle on whole heads (fwd+bwd) until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    kv = inp["kv_len"]
+    spent, done = 0.0, 0
+    for b, h in heads:
+        args = [inp[x][b, h].float().double().numpy() for x in ("q", "k", "v", "do")]
+        t0 = time.perf_counter()
+        oracle.head_backward(*args, w.softmax_scale, w.causal,
+                             None if kv is None else int(kv[b]))
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    per_head = spent / done
+    flops_per_head = (w.flops_fwd() + w.flops_bwd()) / (w.batch * w.heads)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {
+        "value": flops_per_head / per_head / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} of {w.batch * w.heads} heads, fwd+bwd, fp64 NumPy "
+                   f"(materialised S, P, dP, dS; no causal skipping), "
+                   f"{per_head:.2f} s per head; FLOPs counted as for the GPU"),
+    }
+
+
+def load_traffic(src_hash: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device three times (a plain copy "
+                         "kernel of known size, to scale HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work shards by (batch, head) with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_io_aware_fa_amd import binding as B
+    from exact_io_aware_fa_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    B.lib()  # fail loudly if the library is missing
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    inp = make_inputs(w)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)
+    bsz, hh, n, d = q.shape
+    dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
+    o = torch.empty_like(q)
+    lse = torch.empty((bsz, hh, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws_bytes = B.fa_bwd_workspace_bytes(bsz, hh, n, d, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    kv_ptr = None if kvl is None else kvl.data_ptr()
+    scale = w.softmax_scale
+
+    hip = HipEvents()
+    nev = args.steps
+    ev_f0 = [hip.create() for _ in range(nev)]
+    ev_f1 = [hip.create() for _ in range(nev)]
+    ev_b = [[hip.create() for _ in range(4)] for _ in range(nev)]
+
+    def step(i=None):
+        if i is not None:
+            hip.record(ev_f0[i], stream)
+        B.check(B.fa_fwd(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
+                         v.data_ptr(), kv_ptr, o.data_ptr(), lse.data_ptr(), stream))
+        if i is not None:
+            hip.record(ev_f1[i], stream)
+        B.check(B.fa_bwd_timed(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                               kv_ptr, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               ws.data_ptr(), ws_bytes, stream,
+                               None if i is None else ev_b[i]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [hip.elapsed_ms(ev_f0[i], ev_f1[i]) for i in range(nev)]
+    main_ms = [hip.elapsed_ms(ev_b[i][1], ev_b[i][2]) for i in range(nev)]
+    bwd_ms = [hip.elapsed_ms(ev_b[i][0], ev_b[i][3]) for i in range(nev)]
+    for e in ev_f0 + ev_f1 + [x for r in ev_b for x in r]:
+        hip.destroy(e)
+
+    ff, fb = w.flops_fwd(), w.flops_bwd()
+    ms_step = wall / args.steps * 1e3
+    value = (ff + fb) / (ms_step / 1e3) / 1e12
+    avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    fwd_tf = ff / (avg(fwd_ms) / 1e3) / 1e12
+    bwd_tf = fb / (avg(bwd_ms) / 1e3) / 1e12
+    main_tf = fb / (avg(main_ms) / 1e3) / 1e12
+    src_hash = kernel_source_hash()
+
+    out = {
+        "metric": "attention TFLOP/s fwd+bwd (bf16) and % of MI355X MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == B.FA_BF16 else "fp32",
+        "data": "synthetic (seeded normal inputs; Q,K std %g, V,dO std 1)" % w.qk_sigma,
+        "config": {"workload": w.name, "batch": bsz, "heads": hh, "seq_len": n,
+                   "head_dim": d, "causal": w.causal, "key_padding": w.padded,
+                   "softmax_scale": scale},
+        "frac_of_peak_fwd_bwd": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(avg(fwd_ms), 4), "tflops": round(fwd_tf, 2),
+                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(avg(bwd_ms), 4), "tflops": round(bwd_tf, 2),
+                "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                "main_kernel_ms": round(avg(main_ms), 4)},
+        "roofline": {
+            "kernel": "bwd_bf16_kernel (recompute backward, d=%d)" % d,
+            "bound": "mfma",
+            "achieved": round(main_tf, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(src_hash),
+            "kernel_source_hash": src_hash,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -131,6 +131,16 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                  const void* v, const void* o, const void* d_o, const float* lse,
                  const int32_t* kv_len, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, void* stream) {
+  return fa_bwd_timed(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o, d_o,
+                      lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream, nullptr);
+}
+
+fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
+                       float softmax_scale, fa_dtype dtype, const void* q, const void* k,
+                       const void* v, const void* o, const void* d_o, const float* lse,
+                       const int32_t* kv_len, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* const events[4]) {
   fa_status st = check_common(batch, heads, n, d, softmax_scale, dtype);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return FA_E_NULLPTR;
@@ -175,11 +185,19 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                                             dvec_bytes(batch, heads, n))
                  : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    if (events == nullptr || events[i] == nullptr) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  };
   const bool bf = dtype == FA_BF16;
-  hipError_t e = fa::launch_bwd_prep(p, int(d), bf, s);
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = fa::launch_bwd_prep(p, int(d), bf, s);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = bf ? fa::launch_bwd_bf16(p, int(d), s) : fa::launch_bwd_fp32(p, int(d), s);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess && bf) e = fa::launch_dq_convert(p, int(d), s);
+  if (e == hipSuccess) e = mark(3);
   return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
 }
 

@@ -136,6 +136,26 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
                  void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * fa_bwd_timed -- fa_bwd, additionally recording caller-owned HIP events on
+ * `stream` between its three kernels, for measurement harnesses that time
+ * each kernel with events. events[0] is recorded before the D_i / dQ-zeroing
+ * kernel, events[1] before the main backward kernel, events[2] after it and
+ * events[3] after the dQ conversion (bf16) -- i.e. at the end. Any entry may
+ * be NULL (not recorded); `events` itself may be NULL, which makes the call
+ * identical to fa_bwd. The events must have been created on the device that
+ * owns `stream` (hipEventCreate); the library records them and nothing else.
+ * A failed hipEventRecord returns FA_E_LAUNCH.
+ */
+fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d,
+                       int causal, float softmax_scale, fa_dtype dtype,
+                       const void* q, const void* k, const void* v,
+                       const void* o, const void* d_o, const float* lse,
+                       const int32_t* kv_len,
+                       void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream, void* const events[4]);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_str(fa_status s);
 
