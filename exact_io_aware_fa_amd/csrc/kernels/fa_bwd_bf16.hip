@@ -24,6 +24,8 @@
 // * dQ needs dS with queries on lanes, so dS is written to LDS as bf16 and
 //   each wave computes a 32x32 block of dQ = dS K over all 128 keys, added
 //   into an fp32 accumulator with float atomics.
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -85,7 +87,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
   const int kw0 = k0 + w * 32;
   const int mykey = kw0 + c;
   const float cs = p.c;
-  const uint32_t qflip = p.q_neg ? 0x80008000u : 0u;
+  const float dqs = fabsf(p.scale);
+  // A negative scale is applied by negating K (exact in bf16): the scores
+  // use K' = -K with |scale|, dQ = |scale| dS K' and dK = scale dS^T Q.
+  const uint32_t kflip = p.q_neg ? 0x80008000u : 0u;
 
   f32x16 dk[NMB], dv[NMB];
 #pragma unroll
@@ -96,16 +101,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
 
   if (k0 < kv_lim) {
     // K and V rows of this wave as B fragments: [mykey][kd*16 + h*8 + e].
+    // Rows past the key limit are read clamped and replaced by zeros.
     bf16x8 kf[ND], vf[ND];
+    {
+      const bool kok = mykey < kv_lim;
+      const int kr = kok ? mykey : kv_lim - 1;
 #pragma unroll
-    for (int kd = 0; kd < ND; ++kd) {
-      u32x4 a = {0u, 0u, 0u, 0u}, bb = {0u, 0u, 0u, 0u};
-      if (mykey < kv_lim) {
-        a = ld16(K + (size_t)mykey * D + kd * 16 + h * 8);
-        bb = ld16(V + (size_t)mykey * D + kd * 16 + h * 8);
+      for (int kd = 0; kd < ND; ++kd) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 a = ld16(K + (size_t)kr * D + kd * 16 + h * 8);
+        const u32x4 bb = ld16(V + (size_t)kr * D + kd * 16 + h * 8);
+        kf[kd] = as_bf16x8(kok ? (a ^ kflip) : z);
+        vf[kd] = as_bf16x8(kok ? bb : z);
       }
-      kf[kd] = as_bf16x8(a);
-      vf[kd] = as_bf16x8(bb);
     }
     // K^T of the whole workgroup into LDS (B operand of dQ = dS K).
 #pragma unroll
@@ -117,7 +125,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int key = k0 + kg * 4 + t;
-        r[t] = (key < kv_lim) ? ld16(K + (size_t)key * D + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v = ld16(K + (size_t)min(key, kv_lim - 1) * D + dg * 8) ^ kflip;
+        r[t] = (key < kv_lim) ? v : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -126,9 +135,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
 
     const int n_qt = (n + BQ - 1) / BQ;
     const int it0 = CAUSAL ? (k0 / BQ) : 0;
+    // Tiles that need masking: the causal diagonal band (some key of this
+    // workgroup lies above some query of the tile), every tile when the
+    // workgroup straddles the key limit, and a partial last tile.
+    int a_end = it0;
+    if (k0 + kBKV > kv_lim) a_end = n_qt;
+    else if (CAUSAL) a_end = min(n_qt, (k0 + kBKV - 2) / BQ + 1);
+    const int b_end = max(a_end, (n % BQ) ? n_qt - 1 : n_qt);
 
     // Register staging of the next Q / dO tile: unit u < UPT is a Q unit,
-    // else a dO unit; a unit is 4 rows x 8 dims.
+    // else a dO unit; a unit is 4 rows x 8 dims. Rows past n are read
+    // clamped to row n-1; every product involving them is masked (P = 0,
+    // dS = 0) and their dQ rows are not written.
     u32x4 ureg[UPTH][4];
     auto gload = [&](int it) {
       const int q0 = it * BQ;
@@ -139,19 +157,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
         const int u = isq ? u0 : u0 - UPT;
         const int qg = (u >> 2) % (BQ / 4);
         const int dg = (u & 3) + 4 * (u / BQ);
-        const bf16* src = isq ? Q : dO;
-        const uint32_t flip = isq ? qflip : 0u;
+        const bf16* src = (isq ? Q : dO) + dg * 8;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int q = q0 + qg * 4 + t;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (q < n) v = ld16(src + (size_t)q * D + dg * 8) ^ flip;
-          ureg[i][t] = v;
-        }
+        for (int t = 0; t < 4; ++t)
+          ureg[i][t] = ld16(src + (size_t)min(q0 + qg * 4 + t, n - 1) * D);
       }
     };
     auto swrite = [&](int it) {
-      const int q0 = it * BQ;
 #pragma unroll
       for (int i = 0; i < UPTH; ++i) {
         const int u0 = tid + i * kThreads;
@@ -169,99 +181,87 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
           *reinterpret_cast<u32x2*>(&tr[(dg * 8 + e) * TSTR + qg * 4]) = column4(ureg[i], e);
       }
       if (tid < BQ) {
-        const int q = q0 + tid;
-        sL[tid] = (q < n) ? lse[q] * kLog2e : 0.f;
-        sDv[tid] = (q < n) ? dvec[q] : 0.f;
+        const int q = min(it * BQ + tid, n - 1);
+        sL[tid] = lse[q] * kLog2e;
+        sDv[tid] = dvec[q];
       }
     };
 
-    if (it0 < n_qt) gload(it0);
-    for (int it = it0; it < n_qt; ++it) {
+    // One query tile: S = Q K^T and dP = dO V^T (lane = key, 16 queries per
+    // 32-query block), P = exp2(S c - L log2 e), dS = P (dP - D), then
+    // dV^T += dO^T P, dK^T += Q^T dS, dS to LDS, and dQ += scale dS K.
+    auto step = [&](int it, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       __syncthreads();  // previous tile's LDS contents are no longer read
       swrite(it);
       __syncthreads();
-      if (it + 1 < n_qt) gload(it + 1);
-
+      gload(min(it + 1, n_qt - 1));
       const int q0 = it * BQ;
-      const bool active = !(CAUSAL && kw0 > q0 + BQ - 1);
-      if (active) {
-        f32x16 sv[NQB], dp[NQB];
+
+      f32x16 sv[NQB], dp[NQB];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          sv[qb] = f32x16{};
-          dp[qb] = f32x16{};
+      for (int qb = 0; qb < NQB; ++qb) {
+        sv[qb] = f32x16{};
+        dp[qb] = f32x16{};
 #pragma unroll
-          for (int kd = 0; kd < ND; ++kd) {
-            const bf16x8 a = as_bf16x8(ld16(&sQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-            sv[qb] = mma32(a, kf[kd], sv[qb]);
-            const bf16x8 g = as_bf16x8(ld16(&sdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-            dp[qb] = mma32(g, vf[kd], dp[qb]);
+        for (int kd = 0; kd < ND; ++kd) {
+          const bf16x8 a = as_bf16x8(ld16(&sQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+          sv[qb] = mma32(a, kf[kd], sv[qb]);
+          const bf16x8 g = as_bf16x8(ld16(&sdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+          dp[qb] = mma32(g, vf[kd], dp[qb]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[qb * 32 + g * 8 + h * 4]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDv[qb * 32 + g * 8 + h * 4]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = g * 4 + i;
+            float pr = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], cs, -l4[i]));
+            if (MASK) {
+              const int q = q0 + qb * 32 + g * 8 + h * 4 + i;
+              const bool hidden = q >= n || mykey >= kv_lim || (CAUSAL && mykey > q);
+              pr = hidden ? 0.f : pr;
+            }
+            sv[qb][r] = pr;
+            dp[qb][r] = pr * (dp[qb][r] - d4[i]);
           }
         }
-        const bool need_mask = (q0 + BQ > n) || (k0 + kBKV > kv_lim) ||
-                               (CAUSAL && kw0 + 31 > q0);
-        // P (probabilities) into sv, dS into dp; lane owns key `mykey` and
-        // queries q0 + qb*32 + g*8 + h*4 + i.
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[qb * 32 + g * 8 + h * 4]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDv[qb * 32 + g * 8 + h * 4]);
+        for (int qc = 0; qc < 2; ++qc) {
+          u32x4 pu, su;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = g * 4 + i;
-              float pr = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], cs, -l4[i]));
-              if (need_mask) {
-                const int q = q0 + qb * 32 + g * 8 + h * 4 + i;
-                const bool hidden = q >= n || mykey >= kv_lim || (CAUSAL && mykey > q);
-                pr = hidden ? 0.f : pr;
-              }
-              sv[qb][r] = pr;
-              dp[qb][r] = pr * (dp[qb][r] - d4[i]);
-            }
+          for (int t = 0; t < 4; ++t) {
+            pu[t] = pack_bf16x2(sv[qb][qc * 8 + 2 * t], sv[qb][qc * 8 + 2 * t + 1]);
+            su[t] = pack_bf16x2(dp[qb][qc * 8 + 2 * t], dp[qb][qc * 8 + 2 * t + 1]);
           }
-        // dV^T += dO^T P and dK^T += Q^T dS (queries are the reduction).
+          const bf16x8 pfr = as_bf16x8(pu);
+          const bf16x8 sfr = as_bf16x8(su);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int qc = 0; qc < 2; ++qc) {
-            u32x4 pu, su;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              pu[t] = pack_bf16x2(sv[qb][qc * 8 + 2 * t], sv[qb][qc * 8 + 2 * t + 1]);
-              su[t] = pack_bf16x2(dp[qb][qc * 8 + 2 * t], dp[qb][qc * 8 + 2 * t + 1]);
-            }
-            const bf16x8 pfr = as_bf16x8(pu);
-            const bf16x8 sfr = as_bf16x8(su);
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-              const int off = (mb * 32 + c) * TSTR + qb * 32 + qc * 16 + h * 4;
-              const u32x2 olo = ld8(&sdOt[off]);
-              const u32x2 ohi = ld8(&sdOt[off + 8]);
-              const u32x4 oa = {olo[0], olo[1], ohi[0], ohi[1]};
-              dv[mb] = mma32(as_bf16x8(oa), pfr, dv[mb]);
-              const u32x2 qlo = ld8(&sQt[off]);
-              const u32x2 qhi = ld8(&sQt[off + 8]);
-              const u32x4 qa = {qlo[0], qlo[1], qhi[0], qhi[1]};
-              dk[mb] = mma32(as_bf16x8(qa), sfr, dk[mb]);
-            }
-            // dS (bf16) to LDS as [q][key] for the dQ product.
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int qa0 = qb * 32 + qc * 16 + (t >> 1) * 8 + h * 4 + (t & 1) * 2;
-              sdS[qa0 * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] & 0xffffu));
-              sdS[(qa0 + 1) * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] >> 16));
-            }
+          for (int mb = 0; mb < NMB; ++mb) {
+            const int off = (mb * 32 + c) * TSTR + qb * 32 + qc * 16 + h * 4;
+            const u32x2 olo = ld8(&sdOt[off]);
+            const u32x2 ohi = ld8(&sdOt[off + 8]);
+            const u32x4 oa = {olo[0], olo[1], ohi[0], ohi[1]};
+            dv[mb] = mma32(as_bf16x8(oa), pfr, dv[mb]);
+            const u32x2 qlo = ld8(&sQt[off]);
+            const u32x2 qhi = ld8(&sQt[off + 8]);
+            const u32x4 qa = {qlo[0], qlo[1], qhi[0], qhi[1]};
+            dk[mb] = mma32(as_bf16x8(qa), sfr, dk[mb]);
           }
-      } else {
+          // dS (bf16) to LDS as [q][key] for the dQ product.
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sdS[(qb * 32 + (r >> 2) * 8 + h * 4 + (r & 3)) * DSSTR + w * 32 + c] =
-                __builtin_bit_cast(bf16, (uint16_t)0);
-      }
+          for (int t = 0; t < 4; ++t) {
+            const int qa0 = qb * 32 + qc * 16 + (t >> 1) * 8 + h * 4 + (t & 1) * 2;
+            sdS[qa0 * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] & 0xffffu));
+            sdS[(qa0 + 1) * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] >> 16));
+          }
+        }
       __syncthreads();  // dS tile complete
 
       // dQ[q][d] += scale * sum_key dS[q][key] K[key][d], one 32x32 block
@@ -277,18 +277,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
           const bf16x8 bk = as_bf16x8(ld16(&sKt[(mb * 32 + c) * KTSTR + kc * 16 + h * 8]));
           acc = mma32(a, bk, acc);
         }
+        float* dst = dQa + (size_t)(q0 + qb * 32 + h * 4) * D + mb * 32 + c;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int q = q0 + qb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (q < n) unsafeAtomicAdd(&dQa[(size_t)q * D + mb * 32 + c], p.scale * acc[r]);
+          const int qo = (r >> 2) * 8 + (r & 3);
+          if (!MASK || q0 + qb * 32 + h * 4 + qo < n)
+            unsafeAtomicAdd(dst + (size_t)qo * D, dqs * acc[r]);
         }
       }
-    }
+    };
+
+    gload(it0);
+    int it = it0;
+    for (; it < a_end; ++it) step(it, std::true_type{});
+    for (; it < b_end; ++it) step(it, std::false_type{});
+    for (; it < n_qt; ++it) step(it, std::true_type{});
   }
 
-  // dK = |scale| * (dS^T Q') with Q' = sign(scale) Q, dV as accumulated.
+  // dK = scale * (dS^T Q), dV as accumulated.
   if (mykey < n) {
-    const float ks = fabsf(p.scale);
+    const float ks = p.scale;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll

@@ -53,17 +53,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Column e (0..7) of four 8-element bf16 rows, packed as 4 bf16 (row 0 in
-// the lowest half-word): one 8-byte group of a transposed tile.
+// the lowest half-word): one 8-byte group of a transposed tile. One byte
+// permute per output dword: selector 0x05040100 takes the low half-words of
+// (src1, src0), 0x07060302 the high ones.
 __device__ __forceinline__ u32x2 column4(const u32x4 r[4], int e) {
   const int w = e >> 1;
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
   u32x2 out;
-  if (e & 1) {
-    out[0] = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-    out[1] = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-  } else {
-    out[0] = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-    out[1] = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-  }
+  out[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
+  out[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
   return out;
 }
 

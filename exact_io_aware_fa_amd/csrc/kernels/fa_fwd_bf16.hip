@@ -27,6 +27,8 @@
 //   loads) while the current tile is being computed.
 // * exp2 with the log2(e) factor folded into the score scale; the max-shift
 //   and scale are one FMA per score.
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -75,42 +77,48 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int qi = qw0 + c;
   const float cs = p.c;
 
-  // Q rows of this wave as B fragments: Q[qi][kd*16 + h*8 + e].
+  // Q rows of this wave as B fragments: Q[qi][kd*16 + h*8 + e]. A negative
+  // scale is applied by negating Q (exact); rows past n are zero.
   bf16x8 qf[ND];
   {
     const uint32_t flip = p.q_neg ? 0x80008000u : 0u;
+    const int qr = min(qi, n - 1);
 #pragma unroll
     for (int kd = 0; kd < ND; ++kd) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qi < n) v = ld16(Q + (size_t)qi * D + kd * 16 + h * 8);
-      v ^= flip;
-      qf[kd] = as_bf16x8(v);
+      const u32x4 v = ld16(Q + (size_t)qr * D + kd * 16 + h * 8) ^ flip;
+      qf[kd] = as_bf16x8(qi < n ? v : u32x4{0u, 0u, 0u, 0u});
     }
   }
 
   int kend = kv_lim;
   if (CAUSAL) kend = min(kend, q0 + kBR);
   const int ntiles = (kend + BC - 1) / BC;
+  // Tiles [0, j_unmasked) have every key visible to every query of the
+  // workgroup: wholly below the key limit and, if causal, at or below the
+  // workgroup's first query. The rest go through the masked path.
+  int j_unmasked = kv_lim / BC;
+  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
+  j_unmasked = min(j_unmasked, ntiles);
 
   f32x16 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
-  float m2 = kNegInf;   // running max in scaled base-2 units (s * cs)
+  float m2 = kNegInf;   // reference max in scaled base-2 units (s * cs)
   float lpart = 0.f;    // this half-wave's share of the running row sum
 
   u32x4 kreg[KCH];
   u32x4 vreg[VUPT][4];
 
+  // Fetch key/value tile j into registers. Rows at or past the key limit are
+  // read clamped to the last visible row: their scores are masked to -inf,
+  // so they contribute exactly 0, and padded rows are never read.
   auto gload = [&](int j) {
     const int kb0 = j * BC;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + i * kThreads;
-      const int key = ch / (D / 8);
-      const int dc = ch % (D / 8);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (kb0 + key < kv_lim) v = ld16(K + (size_t)(kb0 + key) * D + dc * 8);
-      kreg[i] = v;
+      const int key = min(kb0 + ch / (D / 8), kv_lim - 1);
+      kreg[i] = ld16(K + (size_t)key * D + (ch % (D / 8)) * 8);
     }
 #pragma unroll
     for (int i = 0; i < VUPT; ++i) {
@@ -120,10 +128,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         const int dg = (u & 3) + 4 * (u / BC);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = kb0 + kg * 4 + r;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (key < kv_lim) v = ld16(V + (size_t)key * D + dg * 8);
-          vreg[i][r] = v;
+          const int key = min(kb0 + kg * 4 + r, kv_lim - 1);
+          vreg[i][r] = ld16(V + (size_t)key * D + dg * 8);
         }
       }
     }
@@ -151,15 +157,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     }
   };
 
-  if (ntiles > 0) gload(0);
-  for (int j = 0; j < ntiles; ++j) {
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     __syncthreads();  // every wave is done reading the previous tile
     swrite();
     __syncthreads();  // tile j is in LDS
-    if (j + 1 < ntiles) gload(j + 1);
+    gload(min(j + 1, ntiles - 1));
 
     const int kb0 = j * BC;
-    if (CAUSAL && kb0 > qw0 + 31) continue;  // whole tile above this wave's diagonal
+    if (MASK && CAUSAL && kb0 > qw0 + 31) return;  // tile above this wave's diagonal
 
     // S^T (keys x queries) = K Q^T, raw dot products.
     f32x16 s[NKB];
@@ -172,9 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         s[kb] = mma32(a, qf[kd], s[kb]);
       }
     }
-
-    const bool need_mask = (kb0 + BC > kv_lim) || (CAUSAL && kb0 + BC - 1 > qw0);
-    if (need_mask) {
+    if (MASK) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -191,10 +195,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // The reference is the exact running max, so the row's largest
+    // probability is exactly 1 before its bf16 rounding. The rescale of O~
+    // is skipped (wave-uniform branch) when no row's max changed.
     const float mt2 = (mt == kNegInf) ? kNegInf : mt * cs;
     const float m2n = fmaxf(m2, mt2);
     const float mref = (m2n == kNegInf) ? 0.f : m2n;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);  // 0 while empty
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);  // 1 if unchanged, 0 while empty
     m2 = m2n;
 
     float rs = 0.f;
@@ -207,8 +214,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         rs += e;
       }
     lpart = fmaf(lpart, alpha, rs);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    }
 
     // P^T as bf16 B fragments: chunk (kb, kc) holds keys kb*32 + kc*16 +
     // {h*4 + 0..3, 8 + h*4 + 0..3}.
@@ -235,7 +244,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         acc[mb] = mma32(as_bf16x8(a), pf[kk], acc[mb]);
       }
-  }
+  };
+
+  if (ntiles > 0) gload(0);
+  int j = 0;
+  for (; j < j_unmasked; ++j) step(j, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{});
 
   // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
   const float l = lpart + __shfl_xor(lpart, 32);
