@@ -135,7 +135,79 @@ def load_traffic(src_hash: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def _short(name: str) -> str:
+    for key in ("fwd_bf16_kernel", "bwd_bf16_kernel", "bwd_prep_kernel", "dq_convert_kernel",
+                "fwd_fp32_kernel", "bwd_fp32_kernel", "copyBuffer"):
+        if key in name:
+            return name if key == "copyBuffer" else key + name[name.find(key) + len(key):].split("(")[0]
+    return name[:60]
+
+
+def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, out_json):
+    """Summarise rocprofv3 databases (kernel trace + FETCH_SIZE + WRITE_SIZE
+    passes) into a short markdown file and the traffic JSON this bench reads."""
+    import sqlite3
+
+    rows = sqlite3.connect(trace_db).execute(
+        "select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+        "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[5] for r in rows)
+    lines = ["# rocprofv3 summary: %s" % os.path.basename(out_md).rsplit(".", 1)[0], "",
+             "Commands (run from the repository root on one MI355X):", "", "```", command, "```", "",
+             "## Kernel trace (`--kernel-trace --stats`)", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, tot in rows:
+        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (_short(name), calls, avg / 1e3,
+                                                                   mn / 1e3, mx / 1e3, 100 * tot / total))
+    per = {}
+    for db, ctr in ((fetch_db, "FETCH_SIZE"), (write_db, "WRITE_SIZE")):
+        for kn, val in sqlite3.connect(db).execute(
+                "select kernel_name, value from counters_collection where counter_name = ?", (ctr,)):
+            per.setdefault(_short(kn), {}).setdefault(ctr, []).append(val)
+    copy = per.get("__amd_rocclr_copyBuffer", {})
+    copy_kib = copy_mib * 1024.0
+    f_fac = copy_kib / (sum(copy["FETCH_SIZE"]) / len(copy["FETCH_SIZE"]))
+    w_fac = copy_kib / (sum(copy["WRITE_SIZE"]) / len(copy["WRITE_SIZE"]))
+    lines += ["", "## HBM bytes per dispatch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)", "",
+              "Calibration: a %d MiB device-to-device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE "
+              "%.0f KiB per dispatch, so FETCH_SIZE is scaled by %.3f and WRITE_SIZE by %.3f." % (
+                  copy_mib, copy_kib / f_fac, copy_kib / w_fac, f_fac, w_fac), "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB (scaled) | write GB (scaled) |",
+              "|---|---|---|---|---|---|"]
+    traffic = {}
+    for k, v in per.items():
+        if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v or k.startswith("__amd") or k.startswith("void at::"):
+            continue
+        fk = sum(v["FETCH_SIZE"]) / len(v["FETCH_SIZE"])
+        wk = sum(v["WRITE_SIZE"]) / len(v["WRITE_SIZE"])
+        rd, wr = fk * 1024 * f_fac, wk * 1024 * w_fac
+        traffic[k] = {"read_bytes": rd, "write_bytes": wr}
+        lines.append("| `%s` | %d | %.0f | %.0f | %.3f | %.3f |" % (k, len(v["FETCH_SIZE"]), fk, wk,
+                                                                   rd / 1e9, wr / 1e9))
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    bwd = [k for k in traffic if k.startswith("bwd_bf16_kernel")]
+    if bwd and out_json:
+        t = traffic[bwd[0]]
+        json.dump({"kernel": bwd[0], "kernel_source_hash": kernel_source_hash(),
+                   "hbm_bytes_per_launch": round(t["read_bytes"] + t["write_bytes"]),
+                   "read_bytes": round(t["read_bytes"]), "write_bytes": round(t["write_bytes"]),
+                   "calibration": {"copy_mib": copy_mib, "fetch_factor": f_fac, "write_factor": w_fac},
+                   "summary": os.path.basename(out_md)}, open(out_json, "w"), indent=1)
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize":
+        sp = argparse.ArgumentParser(prog="bench.py summarize")
+        sp.add_argument("trace_db")
+        sp.add_argument("fetch_db")
+        sp.add_argument("write_db")
+        sp.add_argument("--copy-mib", type=int, default=1024)
+        sp.add_argument("--command", required=True)
+        sp.add_argument("--out-md", required=True)
+        sp.add_argument("--out-json", default=None)
+        a = sp.parse_args(sys.argv[2:])
+        summarize_rocprof(a.trace_db, a.fetch_db, a.write_db, a.copy_mib, a.command, a.out_md, a.out_json)
+        return 0
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
