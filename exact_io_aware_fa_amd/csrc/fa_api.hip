@@ -85,10 +85,7 @@ const char* fa_status_str(fa_status s) {
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n, int64_t d,
                               fa_dtype dtype) {
   if (check_common(batch, heads, n, d, 1.f, dtype) != FA_OK) return 0;
-  size_t bytes = dvec_bytes(batch, heads, n);
-  if (dtype == FA_BF16)
-    bytes += size_t(batch) * size_t(heads) * size_t(n) * size_t(d) * sizeof(float);
-  return bytes;
+  return dvec_bytes(batch, heads, n);
 }
 
 fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
@@ -180,10 +177,8 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d, int c
   p.dk = dk;
   p.dv = dv;
   p.dvec = static_cast<float*>(workspace);
-  p.dq_acc = (dtype == FA_BF16)
-                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                            dvec_bytes(batch, heads, n))
-                 : nullptr;
+  // fp32: the backward adds dQ into the caller's (zeroed) dq with atomics.
+  p.dq_acc = (dtype == FA_FP32) ? static_cast<float*>(dq) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> hipError_t {
     if (events == nullptr || events[i] == nullptr) return hipSuccess;
@@ -194,9 +189,9 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d, int c
   if (e == hipSuccess) e = fa::launch_bwd_prep(p, int(d), bf, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
-    e = bf ? fa::launch_bwd_bf16(p, int(d), s) : fa::launch_bwd_fp32(p, int(d), s);
+    e = bf ? fa::launch_bwd_dkdv_bf16(p, int(d), s) : fa::launch_bwd_fp32(p, int(d), s);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess && bf) e = fa::launch_dq_convert(p, int(d), s);
+  if (e == hipSuccess && bf) e = fa::launch_bwd_dq_bf16(p, int(d), s);
   if (e == hipSuccess) e = mark(3);
   return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
 }

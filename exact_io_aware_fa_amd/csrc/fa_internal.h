@@ -23,7 +23,7 @@ struct Params {
   void* dk;
   void* dv;
   float* dvec;          // backward workspace: D_i = <dO_i, O_i>, [B,H,N]
-  float* dq_acc;        // backward workspace: fp32 dQ accumulator (bf16 path)
+  float* dq_acc;        // fp32 dQ accumulator to zero (fp32 path: dq itself)
   int batch;
   int heads;
   int n;
@@ -39,8 +39,8 @@ struct Params {
 hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s);
 hipError_t launch_fwd_fp32(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_prep(const Params& p, int d, bool bf16, hipStream_t s);
-hipError_t launch_bwd_bf16(const Params& p, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const Params& p, int d, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_fp32(const Params& p, int d, hipStream_t s);
-hipError_t launch_dq_convert(const Params& p, int d, hipStream_t s);
 
 }  // namespace fa

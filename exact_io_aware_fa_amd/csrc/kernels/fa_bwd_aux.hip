@@ -2,12 +2,10 @@
 //
 // bwd_prep: D_i = sum_k dO_ik O_ik in fp32 for every query row -- the row
 // term of dS = P * (dP - D) (ordinary softmax calculus: sum_j P_ij dP_ij =
-// <dO_i, O_i>; the pages name the backward's dS but print no formula) -- and
-// zero the fp32 dQ accumulator that the main kernel adds into. D/8 lanes
-// share a row, each reading 8 elements (16 bytes for bf16) of O and dO.
-//
-// dq_convert: the fp32 dQ accumulator to the caller's bf16 dQ, rounded to
-// nearest even, 8 elements per lane.
+// <dO_i, O_i>; the pages name the backward's dS but print no formula) -- and,
+// when an accumulator is given (fp32 path), zero the dQ rows that the
+// backward kernel adds into. D/8 lanes share a row, each reading 8 elements
+// (16 bytes for bf16) of O and dO.
 #include "fa_device.h"
 
 namespace fa {
@@ -52,24 +50,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Params p, long long 
 #pragma unroll
   for (int m = 1; m < G; m <<= 1) s += __shfl_xor(s, m);
   if (sub == 0) p.dvec[row] = s;
-  float* acc = (p.dq_acc != nullptr) ? p.dq_acc : static_cast<float*>(p.dq);
-  *reinterpret_cast<f32x4*>(acc + off) = f32x4{};
-  *reinterpret_cast<f32x4*>(acc + off + 4) = f32x4{};
-}
-
-__global__ __launch_bounds__(kThreads) void dq_convert_kernel(const float* __restrict__ src,
-                                                              bf16* __restrict__ dst,
-                                                              long long n8) {
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(src + i * 8);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(src + i * 8 + 4);
-  u32x4 u;
-  u[0] = pack_bf16x2(a[0], a[1]);
-  u[1] = pack_bf16x2(a[2], a[3]);
-  u[2] = pack_bf16x2(b[0], b[1]);
-  u[3] = pack_bf16x2(b[2], b[3]);
-  *reinterpret_cast<u32x4*>(dst + i * 8) = u;
+  if (p.dq_acc != nullptr) {
+    *reinterpret_cast<f32x4*>(p.dq_acc + off) = f32x4{};
+    *reinterpret_cast<f32x4*>(p.dq_acc + off + 4) = f32x4{};
+  }
 }
 
 template <int D>
@@ -93,14 +77,6 @@ hipError_t launch_bwd_prep(const Params& p, int d, bool is_bf16, hipStream_t s) 
     case 256: return launch_prep_d<256>(p, is_bf16, s);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_dq_convert(const Params& p, int d, hipStream_t s) {
-  const long long n8 = (long long)p.batch * p.heads * p.n * d / 8;
-  dim3 grid((unsigned)((n8 + kThreads - 1) / kThreads)), block(kThreads);
-  hipLaunchKernelGGL(dq_convert_kernel, grid, block, 0, s, p.dq_acc,
-                     static_cast<bf16*>(p.dq), n8);
-  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -1,4 +1,4 @@
-// Fused attention backward, bf16 in/out, fp32 accumulate, for gfx950.
+// Attention backward, dK/dV part: bf16 in/out, fp32 accumulate, for gfx950.
 //
 // Method: recomputation from the saved row statistic (page 1, "注意力为什么
 // 受限于显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 八; page 2,
@@ -7,23 +7,23 @@
 // ordinary calculus of softmax attention (the pages name dS, dQ, dK, dV but
 // print no formula):
 //     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = <dO_i, O_i>,
-//     dK = scale dS^T Q,  dQ = scale dS K.
+//     dK = scale dS^T Q.
+// dQ = scale dS K is computed by the query-outer kernel in
+// fa_bwd_dq_bf16.hip.
 //
 // Mapping onto CDNA4:
 // * A workgroup is 4 wave64s and owns BKV = 128 keys (32 per wave) and their
-//   dK, dV accumulators (fp32, in VGPRs/AGPRs) for the whole query sweep; it
-//   loops over query tiles of BQ rows (key/value-outer order, so dK and dV
-//   need no atomics).
+//   dK, dV accumulators (fp32, in AGPRs) for the whole query sweep; it loops
+//   over query tiles of BQ rows (key/value-outer order: dK and dV are each
+//   written once, no atomics).
 // * Each wave keeps its 32 K and V rows in VGPRs as the B operands of
 //   S = Q K^T and dP = dO V^T; the results hold one key per lane and 16
 //   queries, which is exactly the B-operand layout of dV^T += dO^T P and
 //   dK^T += Q^T dS, so P and dS go to the matrix cores without leaving
 //   registers.
 // * Q and dO tiles are staged in LDS twice: row-major (A operand of S and
-//   dP) and transposed (A operand of dV^T and dK^T).
-// * dQ needs dS with queries on lanes, so dS is written to LDS as bf16 and
-//   each wave computes a 32x32 block of dQ = dS K over all 128 keys, added
-//   into an fp32 accumulator with float atomics.
+//   dP) and transposed (A operand of dV^T and dK^T), double buffered so one
+//   barrier per query tile suffices.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -35,30 +35,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
 
-template <int D, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
+template <int D, int BQ, int NBUF, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
   constexpr int ND = D / 16;
   constexpr int NMB = D / 32;
   constexpr int NQB = BQ / 32;
   constexpr int QSTR = D + 8;      // row-major Q / dO tiles
   constexpr int TSTR = BQ + 4;     // transposed tiles [d][q]
-  constexpr int KTSTR = kBKV + 8;  // K^T [d][key]
-  constexpr int DSSTR = kBKV + 8;  // dS [q][key]
   constexpr int UPT = (BQ / 4) * (D / 8);  // 4x8 units per tensor tile
   constexpr int UNITS = 2 * UPT;           // Q and dO
   constexpr int UPTH = (UNITS + kThreads - 1) / kThreads;
-  constexpr int KUN = (kBKV / 4) * (D / 8);
-  constexpr int KUPT = KUN / kThreads;
-  static_assert(UNITS % kThreads == 0 && KUN % kThreads == 0, "unit split");
+  static_assert(UNITS % kThreads == 0, "unit split");
 
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * KTSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BQ * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[BQ * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * TSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * TSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdS[BQ * DSSTR];
-  __shared__ __attribute__((aligned(16))) float sL[BQ];
-  __shared__ __attribute__((aligned(16))) float sDv[BQ];
+  // NBUF = 2: the Q/dO tiles, their transposes and L/D are double
+  // buffered, so one barrier per query tile suffices (see the loop below).
+  __shared__ __attribute__((aligned(16))) bf16 sQ[NBUF][BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[NBUF][BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sQt[NBUF][D * TSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdOt[NBUF][D * TSTR];
+  __shared__ __attribute__((aligned(16))) float sL[NBUF][BQ];
+  __shared__ __attribute__((aligned(16))) float sDv[NBUF][BQ];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -78,7 +74,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
   const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
   const float* __restrict__ lse = p.lse + (size_t)bh * n;
   const float* __restrict__ dvec = p.dvec + (size_t)bh * n;
-  float* __restrict__ dQa = p.dq_acc + base;
   bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + base;
   bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + base;
 
@@ -87,9 +82,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
   const int kw0 = k0 + w * 32;
   const int mykey = kw0 + c;
   const float cs = p.c;
-  const float dqs = fabsf(p.scale);
   // A negative scale is applied by negating K (exact in bf16): the scores
-  // use K' = -K with |scale|, dQ = |scale| dS K' and dK = scale dS^T Q.
+  // use K' = -K with |scale|, and dK = scale dS^T Q with the true Q.
   const uint32_t kflip = p.q_neg ? 0x80008000u : 0u;
 
   f32x16 dk[NMB], dv[NMB];
@@ -115,24 +109,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
         vf[kd] = as_bf16x8(kok ? bb : z);
       }
     }
-    // K^T of the whole workgroup into LDS (B operand of dQ = dS K).
-#pragma unroll
-    for (int i = 0; i < KUPT; ++i) {
-      const int u = tid + i * kThreads;
-      const int kg = (u >> 2) % (kBKV / 4);
-      const int dg = (u & 3) + 4 * (u / kBKV);
-      u32x4 r[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int key = k0 + kg * 4 + t;
-        const u32x4 v = ld16(K + (size_t)min(key, kv_lim - 1) * D + dg * 8) ^ kflip;
-        r[t] = (key < kv_lim) ? v : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<u32x2*>(&sKt[(dg * 8 + e) * KTSTR + kg * 4]) = column4(r, e);
-    }
-
     const int n_qt = (n + BQ - 1) / BQ;
     const int it0 = CAUSAL ? (k0 / BQ) : 0;
     // Tiles that need masking: the causal diagonal band (some key of this
@@ -163,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
           ureg[i][t] = ld16(src + (size_t)min(q0 + qg * 4 + t, n - 1) * D);
       }
     };
-    auto swrite = [&](int it) {
+    auto swrite = [&](int it, int buf) {
 #pragma unroll
       for (int i = 0; i < UPTH; ++i) {
         const int u0 = tid + i * kThreads;
@@ -171,8 +147,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
         const int u = isq ? u0 : u0 - UPT;
         const int qg = (u >> 2) % (BQ / 4);
         const int dg = (u & 3) + 4 * (u / BQ);
-        bf16* rm = isq ? sQ : sdO;
-        bf16* tr = isq ? sQt : sdOt;
+        bf16* rm = isq ? sQ[buf] : sdO[buf];
+        bf16* tr = isq ? sQt[buf] : sdOt[buf];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           *reinterpret_cast<u32x4*>(&rm[(qg * 4 + t) * QSTR + dg * 8]) = ureg[i][t];
@@ -182,41 +158,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
       }
       if (tid < BQ) {
         const int q = min(it * BQ + tid, n - 1);
-        sL[tid] = lse[q] * kLog2e;
-        sDv[tid] = dvec[q];
+        sL[buf][tid] = lse[q] * kLog2e;
+        sDv[buf][tid] = dvec[q];
       }
     };
 
-    // One query tile: S = Q K^T and dP = dO V^T (lane = key, 16 queries per
-    // 32-query block), P = exp2(S c - L log2 e), dS = P (dP - D), then
-    // dV^T += dO^T P, dK^T += Q^T dS, dS to LDS, and dQ += scale dS K.
-    auto step = [&](int it, auto mask_tag) {
+    // Tile compute on LDS buffer `buf`: S = Q K^T and dP = dO V^T (lane =
+    // key, 16 queries per 32-query block), P = exp2(S c - L log2 e),
+    // dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS.
+    auto compute = [&](int it, int buf, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      __syncthreads();  // previous tile's LDS contents are no longer read
-      swrite(it);
-      __syncthreads();
-      gload(min(it + 1, n_qt - 1));
       const int q0 = it * BQ;
+      const bf16* tQ = sQ[buf];
+      const bf16* tdO = sdO[buf];
+      const bf16* tQt = sQt[buf];
+      const bf16* tdOt = sdOt[buf];
 
       f32x16 sv[NQB], dp[NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
+        bf16x8 qa[ND], ga[ND];
+#pragma unroll
+        for (int kd = 0; kd < ND; ++kd) {
+          qa[kd] = as_bf16x8(ld16(&tQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+          ga[kd] = as_bf16x8(ld16(&tdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+        }
         sv[qb] = f32x16{};
         dp[qb] = f32x16{};
 #pragma unroll
         for (int kd = 0; kd < ND; ++kd) {
-          const bf16x8 a = as_bf16x8(ld16(&sQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-          sv[qb] = mma32(a, kf[kd], sv[qb]);
-          const bf16x8 g = as_bf16x8(ld16(&sdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-          dp[qb] = mma32(g, vf[kd], dp[qb]);
+          sv[qb] = mma32(qa[kd], kf[kd], sv[qb]);
+          dp[qb] = mma32(ga[kd], vf[kd], dp[qb]);
         }
       }
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[qb * 32 + g * 8 + h * 4]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDv[qb * 32 + g * 8 + h * 4]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][qb * 32 + g * 8 + h * 4]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDv[buf][qb * 32 + g * 8 + h * 4]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = g * 4 + i;
@@ -242,56 +222,54 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
           }
           const bf16x8 pfr = as_bf16x8(pu);
           const bf16x8 sfr = as_bf16x8(su);
+          bf16x8 oa[NMB], qa[NMB];
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
             const int off = (mb * 32 + c) * TSTR + qb * 32 + qc * 16 + h * 4;
-            const u32x2 olo = ld8(&sdOt[off]);
-            const u32x2 ohi = ld8(&sdOt[off + 8]);
-            const u32x4 oa = {olo[0], olo[1], ohi[0], ohi[1]};
-            dv[mb] = mma32(as_bf16x8(oa), pfr, dv[mb]);
-            const u32x2 qlo = ld8(&sQt[off]);
-            const u32x2 qhi = ld8(&sQt[off + 8]);
-            const u32x4 qa = {qlo[0], qlo[1], qhi[0], qhi[1]};
-            dk[mb] = mma32(as_bf16x8(qa), sfr, dk[mb]);
+            const u32x2 olo = ld8(&tdOt[off]);
+            const u32x2 ohi = ld8(&tdOt[off + 8]);
+            oa[mb] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+            const u32x2 qlo = ld8(&tQt[off]);
+            const u32x2 qhi = ld8(&tQt[off + 8]);
+            qa[mb] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
           }
-          // dS (bf16) to LDS as [q][key] for the dQ product.
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int qa0 = qb * 32 + qc * 16 + (t >> 1) * 8 + h * 4 + (t & 1) * 2;
-            sdS[qa0 * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] & 0xffffu));
-            sdS[(qa0 + 1) * DSSTR + w * 32 + c] = __builtin_bit_cast(bf16, (uint16_t)(su[t] >> 16));
+          for (int mb = 0; mb < NMB; ++mb) {
+            dv[mb] = mma32(oa[mb], pfr, dv[mb]);
+            dk[mb] = mma32(qa[mb], sfr, dk[mb]);
           }
         }
-      __syncthreads();  // dS tile complete
+    };
 
-      // dQ[q][d] += scale * sum_key dS[q][key] K[key][d], one 32x32 block
-      // per wave and step.
-#pragma unroll
-      for (int blk = w; blk < NQB * NMB; blk += 4) {
-        const int qb = blk / NMB;
-        const int mb = blk % NMB;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int kc = 0; kc < kBKV / 16; ++kc) {
-          const bf16x8 a = as_bf16x8(ld16(&sdS[(qb * 32 + c) * DSSTR + kc * 16 + h * 8]));
-          const bf16x8 bk = as_bf16x8(ld16(&sKt[(mb * 32 + c) * KTSTR + kc * 16 + h * 8]));
-          acc = mma32(a, bk, acc);
+    auto run = [&](int it, int buf, auto mask_tag) {
+      if constexpr (NBUF == 2) {
+        // Buffer `buf` holds tile it. Tile it+1 goes to buf^1 while it is
+        // processed: buf^1 was last read before the previous barrier.
+        compute(it, buf, mask_tag);
+        if (it + 1 < n_qt) {
+          swrite(it + 1, buf ^ 1);
+          gload(min(it + 2, n_qt - 1));
         }
-        float* dst = dQa + (size_t)(q0 + qb * 32 + h * 4) * D + mb * 32 + c;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qo = (r >> 2) * 8 + (r & 3);
-          if (!MASK || q0 + qb * 32 + h * 4 + qo < n)
-            unsafeAtomicAdd(dst + (size_t)qo * D, dqs * acc[r]);
-        }
+        __syncthreads();  // tile it+1 complete; buf free for tile it+2
+      } else {
+        __syncthreads();  // previous tile's LDS contents are no longer read
+        swrite(it, 0);
+        __syncthreads();
+        gload(min(it + 1, n_qt - 1));
+        compute(it, 0, mask_tag);
       }
     };
 
     gload(it0);
+    if constexpr (NBUF == 2) {
+      swrite(it0, 0);
+      gload(min(it0 + 1, n_qt - 1));
+      __syncthreads();
+    }
     int it = it0;
-    for (; it < a_end; ++it) step(it, std::true_type{});
-    for (; it < b_end; ++it) step(it, std::false_type{});
-    for (; it < n_qt; ++it) step(it, std::true_type{});
+    for (; it < a_end; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
+    for (; it < b_end; ++it) run(it, (it - it0) & (NBUF - 1), std::false_type{});
+    for (; it < n_qt; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
   }
 
   // dK = scale * (dS^T Q), dV as accumulated.
@@ -313,25 +291,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(Params p) {
   }
 }
 
-template <int D, int BQ>
+template <int D, int BQ, int NBUF>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_c = (p.n + kBKV - 1) / kBKV;
   const long long total = (long long)t_c * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
   if (p.causal)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, BQ, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, NBUF, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, BQ, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, NBUF, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const Params& p, int d, hipStream_t s) {
+hipError_t launch_bwd_dkdv_bf16(const Params& p, int d, hipStream_t s) {
   switch (d) {
-    case 64: return launch_d<64, 64>(p, s);
-    case 128: return launch_d<128, 32>(p, s);
-    case 256: return launch_d<256, 32>(p, s);
+    case 64: return launch_d<64, 64, 2>(p, s);
+    case 128: return launch_d<128, 32, 2>(p, s);
+    case 256: return launch_d<256, 32, 1>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

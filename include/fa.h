@@ -98,9 +98,8 @@ fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
 
 /*
  * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: one
- * float32 per query row for D_i = sum_k dO_ik O_ik, plus (bf16 only) a
- * float32 dQ accumulator of batch*heads*n*d elements. Returns 0 for invalid
- * sizes.
+ * float32 per query row for D_i = sum_k dO_ik O_ik, rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n,
                               int64_t d, fa_dtype dtype);
@@ -124,8 +123,10 @@ size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n,
  *                     ignored and undefined on exit.
  *
  * Outputs and the workspace must not overlap each other or any input.
- * dQ is accumulated with float32 atomics, so its last bits may differ from
- * run to run; dK and dV are deterministic.
+ * bf16: dK and dV come from a key-outer kernel and dQ from a query-outer
+ * kernel, each accumulated in registers and written once, so all three are
+ * bitwise deterministic. fp32: dQ is accumulated into dq with float atomics,
+ * so its last bits may differ from run to run.
  */
 fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
                  int causal, float softmax_scale, fa_dtype dtype,
@@ -138,10 +139,11 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
 
 /*
  * fa_bwd_timed -- fa_bwd, additionally recording caller-owned HIP events on
- * `stream` between its three kernels, for measurement harnesses that time
- * each kernel with events. events[0] is recorded before the D_i / dQ-zeroing
- * kernel, events[1] before the main backward kernel, events[2] after it and
- * events[3] after the dQ conversion (bf16) -- i.e. at the end. Any entry may
+ * `stream` between its kernels, for measurement harnesses that time each
+ * kernel with events. events[0] is recorded before the D_i kernel,
+ * events[1] before the dK/dV kernel (fp32: the single backward kernel),
+ * events[2] after it and events[3] after the dQ kernel (bf16) -- i.e. at
+ * the end. Any entry may
  * be NULL (not recorded); `events` itself may be NULL, which makes the call
  * identical to fa_bwd. The events must have been created on the device that
  * owns `stream` (hipEventCreate); the library records them and nothing else.
