@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [
     os.path.join(CSRC, "fa_api.hip"),
     os.path.join(CSRC, "kernels", "fa_fwd_bf16.hip"),
+    os.path.join(CSRC, "kernels", "fa_fwd_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dq_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_aux.hip"),

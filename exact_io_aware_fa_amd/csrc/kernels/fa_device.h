@@ -65,6 +65,53 @@ __device__ __forceinline__ u32x2 column4(const u32x4 r[4], int e) {
   return out;
 }
 
+// ---------------------------------------------------------------------------
+// LDS helpers for tiles loaded straight from HBM into LDS.
+//
+// gload_lds16: 16 bytes from global address g (per lane) into LDS at
+// lds_base + 16 * lane; lds_base must be the same for the whole wave. The
+// data lands asynchronously and is tracked by vmcnt.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void gload_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding global loads (including the loads into
+// LDS) have completed; other counters are left alone. Encoding for gfx9:
+// vmcnt = 0, expcnt = 7 (no wait), lgkmcnt = 15 (no wait).
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte chunks addressed by lanes
+// 4j + i/4 (j = 0..3) of its group. With a row-major bf16 tile and lane
+// (c, h) = (lane % 32, lane / 32) pointing at
+//     tile[r0 + 4h + (c % 16) / 4][d0 + 16 * (c / 16) + 4 * (c % 4)],
+// lane (c, h) receives tile[r0 + 4h + j][d0 + c] for j = 0..3: four rows of
+// one column, i.e. a transposed 8-byte MFMA operand fragment.
+__device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_addr) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)lds_addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// XOR swizzles of the 16-byte chunk index within a tile row (rows of D bf16,
+// no padding), chosen so that both access patterns hit every LDS bank once
+// per 256 bytes:
+// * row reads (lane c reads 16 bytes of row c): rows r..r+15 must map a given
+//   chunk to 16 different bank groups;
+// * transposing reads (a half-wave reads 4 rows x 64 bytes): the 4 rows'
+//   chunk blocks must not overlap.
+template <int D>
+__device__ __forceinline__ int swz_row(int row) {
+  return D >= 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_tr(int row) {
+  return D >= 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 // Workgroup remap. The dispatcher places consecutive workgroup ids on the
 // eight XCDs in turn (id % 8), each XCD with its own L2. Hand each XCD a
 // contiguous range of the work list so that workgroups of the same

@@ -19,12 +19,12 @@
 //   combined once at the end).
 // * The probabilities, rounded to bf16, are already laid out as the B
 //   operand of O^T += V^T P^T, so P never leaves registers.
-// * K tiles are stored row-major in LDS (rows padded by 16 bytes); V tiles
-//   are stored transposed ([d][key], rows padded by 8 bytes) so the V^T
-//   operand is two 8-byte LDS reads per lane. Both layouts give each bank the
-//   minimum number of accesses for the wave's reads.
-// * The next K/V tile is fetched from HBM into registers (coalesced 16-byte
-//   loads) while the current tile is being computed.
+// * K and V tiles go from HBM straight into LDS (16 bytes per lane, no
+//   staging registers), row-major with an XOR swizzle of the 16-byte chunks,
+//   in two stages: tile j+1 streams in while tile j is used, one barrier per
+//   tile. K is read row-wise (A operand of K Q^T); V is read with the
+//   transposing LDS read, which yields the V^T operand directly. Both access
+//   patterns hit every LDS bank once per 256 bytes.
 // * exp2 with the log2(e) factor folded into the score scale; the max-shift
 //   and scale are one FMA per score.
 #include <type_traits>
@@ -38,24 +38,40 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
 
-template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
-  constexpr int KSTR = D + 8;    // K row stride in LDS (bf16 elements)
-  constexpr int VSTR = BC + 4;   // V^T row stride in LDS (bf16 elements)
-  constexpr int ND = D / 16;     // reduction steps of S^T = K Q^T
-  constexpr int NMB = D / 32;    // 32-row blocks of O^T
-  constexpr int NKB = BC / 32;   // 32-key blocks of S^T
-  constexpr int KCH = BC * D / 8 / kThreads;  // 16-byte K chunks per thread
-  constexpr int VUN = (BC / 4) * (D / 8);     // V units: 4 keys x 8 dims
-  constexpr int VUPT = (VUN + kThreads - 1) / kThreads;
-  static_assert(KCH * kThreads * 8 == BC * D, "K tile split");
+// Exchange with the other 32-lane half of the wave (v_permlane32_swap): the
+// two results hold the value of lane l % 32 and of lane l % 32 + 32 in some
+// order, so their max (or sum) is the same on every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int BC, int MINW, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int ROWB = D * 2;           // bytes per row
+  constexpr int TILEB = BC * ROWB;      // bytes per K or V tile
+  constexpr int LPW = TILEB / 1024 / 4; // 1 KB wave loads per tensor per wave
+  constexpr int RPL = 1024 / ROWB;      // rows per 1 KB load
+  constexpr int ND = D / 16;            // reduction steps of S^T = K Q^T
+  constexpr int NMB = D / 32;           // 32-row blocks of O^T
+  constexpr int NKB = BC / 32;          // 32-key blocks of S^T
+  static_assert(LPW * 4 * 1024 == TILEB && RPL >= 1, "tile split");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[D * VSTR];
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[BC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[BC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[BC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[BC * D];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
@@ -103,81 +119,66 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   f32x16 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
-  float m2 = kNegInf;   // reference max in scaled base-2 units (s * cs)
+  float m2 = kNegInf;   // running max in scaled base-2 units (s * cs)
   float lpart = 0.f;    // this half-wave's share of the running row sum
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VUPT][4];
-
-  // Fetch key/value tile j into registers. Rows at or past the key limit are
-  // read clamped to the last visible row: their scores are masked to -inf,
-  // so they contribute exactly 0, and padded rows are never read.
-  auto gload = [&](int j) {
+  // Loads of a key (or value) tile into LDS. Wave w fills rows
+  // [w * LPW * RPL, (w + 1) * LPW * RPL); lane l of a 1 KB load writes
+  // physical chunk l % CH of row l / CH, which holds logical chunk
+  // (l % CH) ^ swizzle(row). The per-lane element offsets do not depend on
+  // the tile; rows at or past the key limit are read clamped to the last
+  // visible row (their scores are masked, they contribute exactly 0).
+  int ld_row[LPW], ld_koff[LPW], ld_voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (w * LPW + i) * RPL + lane / CH;
+    ld_row[i] = row;
+    ld_koff[i] = row * D + ((lane % CH) ^ swz_row<D>(row)) * 8;
+    ld_voff[i] = row * D + ((lane % CH) ^ swz_tr<D>(row)) * 8;
+  }
+  auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) {
     const int kb0 = j * BC;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * kThreads;
-      const int key = min(kb0 + ch / (D / 8), kv_lim - 1);
-      kreg[i] = ld16(K + (size_t)key * D + (ch % (D / 8)) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VUPT; ++i) {
-      const int u = tid + i * kThreads;
-      if (VUN % kThreads == 0 || u < VUN) {
-        const int kg = (u >> 2) % (BC / 4);
-        const int dg = (u & 3) + 4 * (u / BC);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = min(kb0 + kg * 4 + r, kv_lim - 1);
-          vreg[i][r] = ld16(V + (size_t)key * D + dg * 8);
-        }
-      }
+    for (int i = 0; i < LPW; ++i) {
+      const int dr = min(kb0 + ld_row[i], kv_lim - 1) - ld_row[i];
+      gload_lds16(src + (size_t)dr * D + off[i], dst + (w * LPW + i) * RPL * D);
     }
   };
 
-  auto swrite = [&]() {
+  // Per-lane LDS element offsets of the MFMA operand reads (tile-invariant):
+  // K row c (rows kb*32 + c share the swizzle of c), logical chunk kd*2 + h;
+  // V transposing reads at row h*4 + (c%16)/4 (+16 kk, +8), column
+  // mb*32 + 16*(c/16) + 4*(c%4).
+  int koff[ND], voff[NMB];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * kThreads;
-      const int key = ch / (D / 8);
-      const int dc = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(&sK[key * KSTR + dc * 8]) = kreg[i];
+  for (int kd = 0; kd < ND; ++kd) koff[kd] = c * D + (((kd * 2 + h) ^ swz_row<D>(c)) << 3);
+  {
+    const int trow = h * 4 + ((c & 15) >> 2);
+    const int tcol = 16 * (c >> 4) + 4 * (c & 3);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const int col = mb * 32 + tcol;
+      voff[mb] = trow * D + ((((col >> 3) ^ swz_tr<D>(trow))) << 3) + (col & 7);
     }
-#pragma unroll
-    for (int i = 0; i < VUPT; ++i) {
-      const int u = tid + i * kThreads;
-      if (VUN % kThreads == 0 || u < VUN) {
-        const int kg = (u >> 2) % (BC / 4);
-        const int dg = (u & 3) + 4 * (u / BC);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<u32x2*>(&sVt[(dg * 8 + e) * VSTR + kg * 4]) =
-              column4(vreg[i], e);
-      }
-    }
-  };
+  }
 
-  auto step = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    __syncthreads();  // every wave is done reading the previous tile
-    swrite();
-    __syncthreads();  // tile j is in LDS
-    gload(min(j + 1, ntiles - 1));
-
-    const int kb0 = j * BC;
-    if (MASK && CAUSAL && kb0 > qw0 + 31) return;  // tile above this wave's diagonal
-
-    // S^T (keys x queries) = K Q^T, raw dot products.
-    f32x16 s[NKB];
+  // S^T (keys x queries) = K Q^T for the tile in sk, raw dot products.
+  auto scores = [&](const bf16* sk, f32x16 (&s)[NKB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16{};
 #pragma unroll
       for (int kd = 0; kd < ND; ++kd) {
-        const bf16x8 a = as_bf16x8(ld16(&sK[(kb * 32 + c) * KSTR + kd * 16 + h * 8]));
+        const bf16x8 a = as_bf16x8(ld16(sk + kb * 32 * D + koff[kd]));
         s[kb] = mma32(a, qf[kd], s[kb]);
       }
     }
+  };
+
+  // Online-softmax update with the scores of tile j, then O^T += V^T P^T.
+  auto softmax_pv = [&](int j, f32x16 (&s)[NKB], const bf16* sv, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int kb0 = j * BC;
     if (MASK) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -188,13 +189,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
           s[kb][r] = hidden ? kNegInf : s[kb][r];
         }
     }
-
-    float mt = kNegInf;
+    // Row max and row sum use four independent partial results each, so the
+    // dependent-instruction chains are a quarter as long.
+    float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kb][r]);
+    const float mt = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
     // The reference is the exact running max, so the row's largest
     // probability is exactly 1 before its bf16 rounding. The rescale of O~
     // is skipped (wave-uniform branch) when no row's max changed.
@@ -204,23 +206,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     const float alpha = __builtin_amdgcn_exp2f(m2 - mref);  // 1 if unchanged, 0 while empty
     m2 = m2n;
 
-    float rs = 0.f;
+    float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cs, -mref));
         s[kb][r] = e;
-        rs += e;
+        rp[r & 3] += e;
       }
-    lpart = fmaf(lpart, alpha, rs);
+    lpart = fmaf(lpart, alpha, (rp[0] + rp[1]) + (rp[2] + rp[3]));
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
     }
 
-    // P^T as bf16 B fragments: chunk (kb, kc) holds keys kb*32 + kc*16 +
-    // {h*4 + 0..3, 8 + h*4 + 0..3}.
+    // P^T as bf16 B fragments: chunk kk holds keys kk*16 + {h*4 + 0..3,
+    // 8 + h*4 + 0..3}.
     bf16x8 pf[NKB * 2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -233,26 +235,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         pf[kb * 2 + kc] = as_bf16x8(u);
       }
 
-    // O^T (d x queries) += V^T P^T.
+    // O^T (d x queries) += V^T P^T; the V^T fragment of (mb, kk) is two
+    // transposing reads: keys kk*16 + h*4 + 0..3 and kk*16 + 8 + h*4 + 0..3
+    // of column mb*32 + c.
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int kk = 0; kk < NKB * 2; ++kk) {
-        const bf16* row = &sVt[(mb * 32 + c) * VSTR + kk * 16 + h * 4];
-        const u32x2 lo = ld8(row);
-        const u32x2 hi = ld8(row + 8);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        acc[mb] = mma32(as_bf16x8(a), pf[kk], acc[mb]);
+        const u32x2 lo = ds_read_tr16(sv + kk * 16 * D + voff[mb]);
+        const u32x2 hi = ds_read_tr16(sv + (kk * 16 + 8) * D + voff[mb]);
+        acc[mb] = mma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[kk], acc[mb]);
       }
   };
 
-  if (ntiles > 0) gload(0);
-  int j = 0;
-  for (; j < j_unmasked; ++j) step(j, std::false_type{});
-  for (; j < ntiles; ++j) step(j, std::true_type{});
+  // Two LDS stages: at the top of iteration j this wave waits for its own
+  // loads of tile j, then the barrier makes every wave's loads of tile j
+  // visible and guarantees every wave has finished tile j-1, whose stage is
+  // refilled with tile j+1 right after. Waves above the causal diagonal of a
+  // tile skip it.
+  auto iter = [&](int j, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    wait_global_loads();
+    __syncthreads();
+    if (j + 1 < ntiles) {
+      issue(K, ld_koff, j + 1, nk);
+      issue(V, ld_voff, j + 1, nv);
+    }
+    if (MASK && CAUSAL && j * BC > qw0 + 31) return;
+    f32x16 sc[NKB];
+    scores(sk, sc);
+    softmax_pv(j, sc, sv, mask_tag);
+  };
+
+  if (ntiles > 0) {
+    issue(K, ld_koff, 0, sK0);
+    issue(V, ld_voff, 0, sV0);
+  }
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j < j_unmasked) iter(j, sK0, sV0, sK1, sV1, std::false_type{});
+    else iter(j, sK0, sV0, sK1, sV1, std::true_type{});
+    if (j + 1 >= ntiles) break;
+    if (j + 1 < j_unmasked) iter(j + 1, sK1, sV1, sK0, sV0, std::false_type{});
+    else iter(j + 1, sK1, sV1, sK0, sV0, std::true_type{});
+  }
 
   // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
-  const float l = lpart + __shfl_xor(lpart, 32);
+  const float l = halves_sum(lpart);
   if (qi < n) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16* orow = O + (size_t)qi * D;
@@ -270,15 +298,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   }
 }
 
-template <int D, int BC>
+template <int D, int BC, int MINW>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
   if (p.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, MINW, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, MINW, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -286,9 +314,9 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s) {
   switch (d) {
-    case 64: return launch_d<64, 64>(p, s);
-    case 128: return launch_d<128, 64>(p, s);
-    case 256: return launch_d<256, 32>(p, s);
+    case 64: return launch_d<64, 64, 2>(p, s);
+    case 128: return launch_d<128, 64, 2>(p, s);
+    case 256: return launch_fwd_bf16_staged(p, d, s);
     default: return hipErrorInvalidValue;
   }
 }

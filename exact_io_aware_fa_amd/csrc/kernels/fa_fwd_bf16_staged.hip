@@ -1,0 +1,278 @@
+// Fused attention forward, bf16, register-staged variant (used for d = 256).
+//
+// Same method and wave layout as fa_fwd_bf16.hip (page 2, "4. FlashAttention
+// 深度剖析", 4.3.2; page 1, "注意力为什么受限于显存带宽：用算术强度与分块把
+// FlashAttention 推导清楚", section 六): 4 wave64s x 32 query rows, S^T = K Q^T
+// on the 32x32x16 bf16 MFMA with Q in VGPRs, P kept in registers as the B
+// operand of O^T += V^T P^T. The difference is how tiles reach LDS: each
+// thread loads 16-byte chunks into registers and writes K row-major (rows
+// padded by 16 bytes) and V transposed ([d][key], rows padded by 8 bytes,
+// built with byte permutes), so every LDS operand read uses an immediate
+// offset. At d = 256 the O accumulator (128 VGPRs) and Q fragments (64)
+// leave no room for the per-lane address registers of the swizzled
+// direct-to-LDS layout, and this variant is more than twice as fast there.
+#include <type_traits>
+
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
+
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) {
+  constexpr int KSTR = D + 8;    // K row stride in LDS (bf16 elements)
+  constexpr int VSTR = BC + 4;   // V^T row stride in LDS (bf16 elements)
+  constexpr int ND = D / 16;     // reduction steps of S^T = K Q^T
+  constexpr int NMB = D / 32;    // 32-row blocks of O^T
+  constexpr int NKB = BC / 32;   // 32-key blocks of S^T
+  constexpr int KCH = BC * D / 8 / kThreads;  // 16-byte K chunks per thread
+  constexpr int VUN = (BC / 4) * (D / 8);     // V units: 4 keys x 8 dims
+  constexpr int VUPT = (VUN + kThreads - 1) / kThreads;
+  static_assert(KCH * kThreads * 8 == BC * D, "K tile split");
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+  const int n = p.n;
+
+  const int t_r = (n + kBR - 1) / kBR;
+  int bh, qb;
+  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
+  const int b = bh / p.heads;
+  const size_t base = (size_t)bh * (size_t)n * D;
+  const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
+  bf16* __restrict__ O = static_cast<bf16*>(p.o) + base;
+
+  const int kv_lim = kv_limit(p, b);
+  const int q0 = qb * kBR;
+  const int qw0 = q0 + w * 32;
+  const int qi = qw0 + c;
+  const float cs = p.c;
+
+  // Q rows of this wave as B fragments: Q[qi][kd*16 + h*8 + e]. A negative
+  // scale is applied by negating Q (exact); rows past n are zero.
+  bf16x8 qf[ND];
+  {
+    const uint32_t flip = p.q_neg ? 0x80008000u : 0u;
+    const int qr = min(qi, n - 1);
+#pragma unroll
+    for (int kd = 0; kd < ND; ++kd) {
+      const u32x4 v = ld16(Q + (size_t)qr * D + kd * 16 + h * 8) ^ flip;
+      qf[kd] = as_bf16x8(qi < n ? v : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  int kend = kv_lim;
+  if (CAUSAL) kend = min(kend, q0 + kBR);
+  const int ntiles = (kend + BC - 1) / BC;
+  // Tiles [0, j_unmasked) have every key visible to every query of the
+  // workgroup: wholly below the key limit and, if causal, at or below the
+  // workgroup's first query. The rest go through the masked path.
+  int j_unmasked = kv_lim / BC;
+  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
+  j_unmasked = min(j_unmasked, ntiles);
+
+  f32x16 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+  float m2 = kNegInf;   // reference max in scaled base-2 units (s * cs)
+  float lpart = 0.f;    // this half-wave's share of the running row sum
+
+  u32x4 kreg[KCH];
+  u32x4 vreg[VUPT][4];
+
+  // Fetch key/value tile j into registers. Rows at or past the key limit are
+  // read clamped to the last visible row: their scores are masked to -inf,
+  // so they contribute exactly 0, and padded rows are never read.
+  auto gload = [&](int j) {
+    const int kb0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      const int key = min(kb0 + ch / (D / 8), kv_lim - 1);
+      kreg[i] = ld16(K + (size_t)key * D + (ch % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VUPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (VUN % kThreads == 0 || u < VUN) {
+        const int kg = (u >> 2) % (BC / 4);
+        const int dg = (u & 3) + 4 * (u / BC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = min(kb0 + kg * 4 + r, kv_lim - 1);
+          vreg[i][r] = ld16(V + (size_t)key * D + dg * 8);
+        }
+      }
+    }
+  };
+
+  auto swrite = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      const int key = ch / (D / 8);
+      const int dc = ch % (D / 8);
+      *reinterpret_cast<u32x4*>(&sK[key * KSTR + dc * 8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VUPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (VUN % kThreads == 0 || u < VUN) {
+        const int kg = (u >> 2) % (BC / 4);
+        const int dg = (u & 3) + 4 * (u / BC);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<u32x2*>(&sVt[(dg * 8 + e) * VSTR + kg * 4]) =
+              column4(vreg[i], e);
+      }
+    }
+  };
+
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    __syncthreads();  // every wave is done reading the previous tile
+    swrite();
+    __syncthreads();  // tile j is in LDS
+    gload(min(j + 1, ntiles - 1));
+
+    const int kb0 = j * BC;
+    if (MASK && CAUSAL && kb0 > qw0 + 31) return;  // tile above this wave's diagonal
+
+    // S^T (keys x queries) = K Q^T, raw dot products.
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int kd = 0; kd < ND; ++kd) {
+        const bf16x8 a = as_bf16x8(ld16(&sK[(kb * 32 + c) * KSTR + kd * 16 + h * 8]));
+        s[kb] = mma32(a, qf[kd], s[kb]);
+      }
+    }
+    if (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+          s[kb][r] = hidden ? kNegInf : s[kb][r];
+        }
+    }
+
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // The reference is the exact running max, so the row's largest
+    // probability is exactly 1 before its bf16 rounding. The rescale of O~
+    // is skipped (wave-uniform branch) when no row's max changed.
+    const float mt2 = (mt == kNegInf) ? kNegInf : mt * cs;
+    const float m2n = fmaxf(m2, mt2);
+    const float mref = (m2n == kNegInf) ? 0.f : m2n;
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);  // 1 if unchanged, 0 while empty
+    m2 = m2n;
+
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cs, -mref));
+        s[kb][r] = e;
+        rs += e;
+      }
+    lpart = fmaf(lpart, alpha, rs);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    }
+
+    // P^T as bf16 B fragments: chunk (kb, kc) holds keys kb*32 + kc*16 +
+    // {h*4 + 0..3, 8 + h*4 + 0..3}.
+    bf16x8 pf[NKB * 2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4 u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          u[t] = pack_bf16x2(s[kb][kc * 8 + 2 * t], s[kb][kc * 8 + 2 * t + 1]);
+        pf[kb * 2 + kc] = as_bf16x8(u);
+      }
+
+    // O^T (d x queries) += V^T P^T.
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int kk = 0; kk < NKB * 2; ++kk) {
+        const bf16* row = &sVt[(mb * 32 + c) * VSTR + kk * 16 + h * 4];
+        const u32x2 lo = ld8(row);
+        const u32x2 hi = ld8(row + 8);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        acc[mb] = mma32(as_bf16x8(a), pf[kk], acc[mb]);
+      }
+  };
+
+  if (ntiles > 0) gload(0);
+  int j = 0;
+  for (; j < j_unmasked; ++j) step(j, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{});
+
+  // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
+  const float l = lpart + __shfl_xor(lpart, 32);
+  if (qi < n) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* orow = O + (size_t)qi * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 u;
+        u[0] = pack_bf16x2(acc[mb][g * 4 + 0] * inv, acc[mb][g * 4 + 1] * inv);
+        u[1] = pack_bf16x2(acc[mb][g * 4 + 2] * inv, acc[mb][g * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + mb * 32 + g * 8 + h * 4) = u;
+      }
+    if (h == 0)
+      p.lse[(size_t)bh * n + qi] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, int BC>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  const int t_r = (p.n + kBR - 1) / kBR;
+  const long long total = (long long)t_r * p.batch * p.heads;
+  dim3 grid((unsigned)total), block(kThreads);
+  if (p.causal)
+    hipLaunchKernelGGL((fwd_bf16_staged_kernel<D, BC, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_staged_kernel<D, BC, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_staged(const Params& p, int d, hipStream_t s) {
+  switch (d) {
+    case 256: return launch_d<256, 32>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa
