@@ -4,8 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-fa_fwd (O and LSE) followed by fa_bwd (D_i and dQ zeroing, the recompute
-backward, dQ conversion), all on torch's current stream, with the inputs
+fa_fwd (O and LSE) followed by fa_bwd (the D_i / L_i log2 e pass, the
+key-outer dK/dV kernel, the query-outer dQ kernel), all on torch's current
+stream, with the inputs
 already resident in device memory. W untimed steps, then exactly K timed steps
 between two device synchronisations. One JSON line is printed.
 
@@ -13,10 +14,12 @@ FLOPs follow the attention convention: 4 B H N^2 d for the forward (two
 N x N x d products), 2.5x that for the backward (five products), halved when
 causal. ``value`` is fwd+bwd TFLOP/s over the wall time of the timed steps.
 
-The ``roofline`` object is for the dominant kernel, the main backward
-kernel: its algorithmic FLOPs per launch divided by its average duration,
-measured with HIP events recorded on the launch stream immediately before and
-after it (fa_bwd_timed), against the bf16 dense matrix-core peak. ``traffic``
+The ``roofline`` object is for the dominant kernel, the backward's dK/dV
+kernel: its algorithmic FLOPs per launch (four of the backward's five
+N x N x d products: S, dP, dV, dK; 8 B H N^2 d, halved when causal) divided
+by its average duration, measured with HIP events recorded on the launch
+stream immediately before and after it (fa_bwd_timed), against the bf16 dense
+matrix-core peak. ``traffic``
 is read from the committed rocprofv3 counter summary for this kernel and
 workload when that summary was taken from the current kernel source, else
 null.
@@ -43,7 +46,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
 KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
                   "exact_io_aware_fa_amd/csrc/kernels/fa_device.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_bf16_long_causal_b1_h32_n16384_d128_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_long_causal_b1_h32_n16384_d128_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -136,10 +139,13 @@ def load_traffic(src_hash: str):
 
 
 def _short(name: str) -> str:
-    for key in ("fwd_bf16_kernel", "bwd_bf16_kernel", "bwd_prep_kernel", "dq_convert_kernel",
-                "fwd_fp32_kernel", "bwd_fp32_kernel", "copyBuffer"):
+    for key in ("fwd_bf16_kernel", "fwd_bf16_staged_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+                "bwd_prep_kernel", "fwd_fp32_kernel", "bwd_fp32_kernel", "copyBuffer"):
         if key in name:
-            return name if key == "copyBuffer" else key + name[name.find(key) + len(key):].split("(")[0]
+            if key == "copyBuffer":
+                return name
+            rest = name[name.find(key) + len(key):]
+            return key + rest.split("(")[0] if rest.startswith("<") else key
     return name[:60]
 
 
@@ -185,7 +191,7 @@ def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, o
         lines.append("| `%s` | %d | %.0f | %.0f | %.3f | %.3f |" % (k, len(v["FETCH_SIZE"]), fk, wk,
                                                                    rd / 1e9, wr / 1e9))
     open(out_md, "w").write("\n".join(lines) + "\n")
-    bwd = [k for k in traffic if k.startswith("bwd_bf16_kernel")]
+    bwd = [k for k in traffic if k.startswith("bwd_dkdv_kernel")]
     if bwd and out_json:
         t = traffic[bwd[0]]
         json.dump({"kernel": bwd[0], "kernel_source_hash": kernel_source_hash(),
@@ -289,6 +295,7 @@ def main() -> int:
 
     fwd_ms = [hip.elapsed_ms(ev_f0[i], ev_f1[i]) for i in range(nev)]
     main_ms = [hip.elapsed_ms(ev_b[i][1], ev_b[i][2]) for i in range(nev)]
+    dq_ms = [hip.elapsed_ms(ev_b[i][2], ev_b[i][3]) for i in range(nev)]
     bwd_ms = [hip.elapsed_ms(ev_b[i][0], ev_b[i][3]) for i in range(nev)]
     for e in ev_f0 + ev_f1 + [x for r in ev_b for x in r]:
         hip.destroy(e)
@@ -299,7 +306,8 @@ def main() -> int:
     avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
     fwd_tf = ff / (avg(fwd_ms) / 1e3) / 1e12
     bwd_tf = fb / (avg(bwd_ms) / 1e3) / 1e12
-    main_tf = fb / (avg(main_ms) / 1e3) / 1e12
+    f_dkdv = fb * 4 / 5  # S, dP, dV, dK of the backward's five products
+    main_tf = f_dkdv / (avg(main_ms) / 1e3) / 1e12
     src_hash = kernel_source_hash()
 
     out = {
@@ -323,9 +331,10 @@ def main() -> int:
                 "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
         "bwd": {"ms": round(avg(bwd_ms), 4), "tflops": round(bwd_tf, 2),
                 "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                "main_kernel_ms": round(avg(main_ms), 4)},
+                "dkdv_kernel_ms": round(avg(main_ms), 4),
+                "dq_kernel_ms": round(avg(dq_ms), 4)},
         "roofline": {
-            "kernel": "bwd_bf16_kernel (recompute backward, d=%d)" % d,
+            "kernel": "bwd_dkdv_kernel (recompute backward, dK and dV, d=%d)" % d,
             "bound": "mfma",
             "achieved": round(main_tf, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -43,8 +43,11 @@ fa_status check_common(int64_t batch, int64_t heads, int64_t n, int64_t d,
 
 size_t elem_size(fa_dtype t) { return t == FA_BF16 ? 2 : 4; }
 
-size_t dvec_bytes(int64_t batch, int64_t heads, int64_t n) {
-  const size_t b = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
+int64_t n_padded(int64_t n) { return (n + 63) / 64 * 64; }
+
+// One per-head-padded fp32 vector of the backward workspace (D or L log2 e).
+size_t vec_bytes(int64_t batch, int64_t heads, int64_t n) {
+  const size_t b = size_t(batch) * size_t(heads) * size_t(n_padded(n)) * sizeof(float);
   return (b + 255) & ~size_t(255);
 }
 
@@ -54,6 +57,7 @@ fa::Params base_params(int64_t batch, int64_t heads, int64_t n, int causal,
   p.batch = int(batch);
   p.heads = int(heads);
   p.n = int(n);
+  p.n_pad = int(n_padded(n));
   p.causal = causal ? 1 : 0;
   float c = fabsf(scale) * 1.4426950408889634f;
   p.c = c < FLT_MIN ? FLT_MIN : c;
@@ -85,7 +89,7 @@ const char* fa_status_str(fa_status s) {
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n, int64_t d,
                               fa_dtype dtype) {
   if (check_common(batch, heads, n, d, 1.f, dtype) != FA_OK) return 0;
-  return dvec_bytes(batch, heads, n);
+  return 2 * vec_bytes(batch, heads, n);
 }
 
 fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
@@ -177,6 +181,7 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d, int c
   p.dk = dk;
   p.dv = dv;
   p.dvec = static_cast<float*>(workspace);
+  p.l2vec = reinterpret_cast<float*>(static_cast<char*>(workspace) + vec_bytes(batch, heads, n));
   // fp32: the backward adds dQ into the caller's (zeroed) dq with atomics.
   p.dq_acc = (dtype == FA_FP32) ? static_cast<float*>(dq) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);

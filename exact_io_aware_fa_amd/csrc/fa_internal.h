@@ -22,11 +22,13 @@ struct Params {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;          // backward workspace: D_i = <dO_i, O_i>, [B,H,N]
+  float* dvec;          // backward workspace: D_i = <dO_i, O_i>, [B*H][n_pad]
+  float* l2vec;         // backward workspace: L_i * log2(e), [B*H][n_pad]
   float* dq_acc;        // fp32 dQ accumulator to zero (fp32 path: dq itself)
   int batch;
   int heads;
   int n;
+  int n_pad;            // n rounded up to a multiple of 64 (workspace rows)
   int causal;
   // Scores enter exp2 as s * c where c = |scale| * log2(e), raised to at
   // least FLT_MIN so that c > 0 and hidden entries (-inf) stay -inf; a

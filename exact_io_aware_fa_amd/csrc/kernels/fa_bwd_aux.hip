@@ -1,11 +1,13 @@
 // Backward helper kernels (HBM-bound, no matrix work).
 //
-// bwd_prep: D_i = sum_k dO_ik O_ik in fp32 for every query row -- the row
+// bwd_prep: for every query row, D_i = sum_k dO_ik O_ik in fp32 -- the row
 // term of dS = P * (dP - D) (ordinary softmax calculus: sum_j P_ij dP_ij =
-// <dO_i, O_i>; the pages name the backward's dS but print no formula) -- and,
-// when an accumulator is given (fp32 path), zero the dQ rows that the
-// backward kernel adds into. D/8 lanes share a row, each reading 8 elements
-// (16 bytes for bf16) of O and dO.
+// <dO_i, O_i>; the pages name the backward's dS but print no formula) -- and
+// L_i log2(e), the saved row statistic in the base-2 units the kernels use.
+// Both vectors are written per head padded to n_pad rows (padding = 0) so
+// the backward kernels can load any 64-row slice directly. When an
+// accumulator is given (fp32 path) the dQ rows are zeroed as well. D/8 lanes
+// share a row, each reading 8 elements (16 bytes for bf16) of O and dO.
 #include "fa_device.h"
 
 namespace fa {
@@ -37,19 +39,32 @@ template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Params p, long long rows) {
   constexpr int G = D / 8;            // lanes per row
   constexpr int RPB = kThreads / G;   // rows per block
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / G;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / G;  // padded row
   const int sub = threadIdx.x % G;
   if (row >= rows) return;  // whole G-lane groups leave together
-  const size_t off = (size_t)row * D + sub * 8;
+  const long long bh = row / p.n_pad;
+  const int i = (int)(row - bh * p.n_pad);
+  if (i >= p.n) {
+    if (sub == 0) {
+      p.dvec[row] = 0.f;
+      p.l2vec[row] = 0.f;
+    }
+    return;
+  }
+  const long long qrow = bh * p.n + i;
+  const size_t off = (size_t)qrow * D + sub * 8;
   float o[8], g[8];
   load8(static_cast<const T*>(p.o_in) + off, o);
   load8(static_cast<const T*>(p.d_o) + off, g);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s = fmaf(o[i], g[i], s);
+  for (int k = 0; k < 8; ++k) s = fmaf(o[k], g[k], s);
 #pragma unroll
   for (int m = 1; m < G; m <<= 1) s += __shfl_xor(s, m);
-  if (sub == 0) p.dvec[row] = s;
+  if (sub == 0) {
+    p.dvec[row] = s;
+    p.l2vec[row] = p.lse[qrow] * kLog2e;
+  }
   if (p.dq_acc != nullptr) {
     *reinterpret_cast<f32x4*>(p.dq_acc + off) = f32x4{};
     *reinterpret_cast<f32x4*>(p.dq_acc + off + 4) = f32x4{};
@@ -58,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Params p, long long 
 
 template <int D>
 hipError_t launch_prep_d(const Params& p, bool is_bf16, hipStream_t s) {
-  const long long rows = (long long)p.batch * p.heads * p.n;
+  const long long rows = (long long)p.batch * p.heads * p.n_pad;
   constexpr int RPB = kThreads / (D / 8);
   dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(kThreads);
   if (is_bf16)

@@ -72,8 +72,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
   const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
   const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
   const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
-  const float* __restrict__ lse = p.lse + (size_t)bh * n;
-  const float* __restrict__ dvec = p.dvec + (size_t)bh * n;
+  const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;
+  const float* __restrict__ dvec = p.dvec + (size_t)bh * p.n_pad;
   bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + base;
   bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + base;
 
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       }
       if (tid < BQ) {
         const int q = min(it * BQ + tid, n - 1);
-        sL[buf][tid] = lse[q] * kLog2e;
+        sL[buf][tid] = l2v[q];
         sDv[buf][tid] = dvec[q];
       }
     };

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
       gf[kd] = as_bf16x8(ld16(dO + (size_t)qr * D + kd * 16 + h * 8));
     }
   }
-  const float l2 = p.lse[(size_t)bh * n + qr] * kLog2e;
-  const float dd = p.dvec[(size_t)bh * n + qr];
+  const float l2 = p.l2vec[(size_t)bh * p.n_pad + qr];
+  const float dd = p.dvec[(size_t)bh * p.n_pad + qr];
 
   int kend = kv_lim;
   if (CAUSAL) kend = min(kend, q0 + kBR);

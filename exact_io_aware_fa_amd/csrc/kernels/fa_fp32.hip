@@ -155,8 +155,8 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
   const float* __restrict__ K = static_cast<const float*>(p.k) + base;
   const float* __restrict__ V = static_cast<const float*>(p.v) + base;
   const float* __restrict__ dO = static_cast<const float*>(p.d_o) + base;
-  const float* __restrict__ lse = p.lse + (size_t)bh * n;
-  const float* __restrict__ dvec = p.dvec + (size_t)bh * n;
+  const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;
+  const float* __restrict__ dvec = p.dvec + (size_t)bh * p.n_pad;
   float* __restrict__ dQ = static_cast<float*>(p.dq) + base;
   float* __restrict__ dK = static_cast<float*>(p.dk) + base;
   float* __restrict__ dV = static_cast<float*>(p.dv) + base;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
       }
       if (tid < BQ) {
         const int q = q0 + tid;
-        sL[tid] = (q < n) ? lse[q] * kLog2e : 0.f;
+        sL[tid] = (q < n) ? l2v[q] : 0.f;
         sDv[tid] = (q < n) ? dvec[q] : 0.f;
       }
       __syncthreads();

@@ -97,9 +97,10 @@ fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
                  void* stream);
 
 /*
- * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: one
- * float32 per query row for D_i = sum_k dO_ik O_ik, rounded up to 256 bytes.
- * Returns 0 for invalid sizes.
+ * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: two
+ * float32 vectors, D_i = sum_k dO_ik O_ik and L_i log2(e), each with the
+ * rows of every (batch, head) padded to a multiple of 64, each rounded up to
+ * 256 bytes. Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n,
                               int64_t d, fa_dtype dtype);

@@ -105,7 +105,7 @@ def test_fwd_validation(lib, kw, code):
     (dict(d=100), B.FA_E_UNSUPPORTED), (dict(batch=-1), B.FA_E_SHAPE),
     (dict(d_o=None), B.FA_E_NULLPTR), (dict(dk=None), B.FA_E_NULLPTR),
     (dict(workspace=None), B.FA_E_WORKSPACE),
-    (dict(workspace_bytes=256), B.FA_E_WORKSPACE),
+    (dict(workspace_bytes=1024), B.FA_E_WORKSPACE),
     (dict(workspace=WS + 16), B.FA_E_ALIGN), (dict(dv=DV + 2), B.FA_E_ALIGN),
     (dict(dq=DK), B.FA_E_ALIAS), (dict(dk=L), B.FA_E_ALIAS), (dict(workspace=DQ), B.FA_E_ALIAS),
     (dict(dv=Q + 256), B.FA_E_ALIAS), (dict(kv_len=DQ + 4), B.FA_E_ALIAS),
@@ -116,10 +116,10 @@ def test_bwd_validation(lib, kw, code):
 
 def test_workspace_size_closed_form(lib):
     b, h, n, d = 2, 3, 100, 128
-    rows = b * h * n * 4
-    dvec = (rows + 255) // 256 * 256
-    assert ws_bytes(B.FA_FP32, batch=b, heads=h, n=n, d=d) == dvec
-    assert ws_bytes(B.FA_BF16, batch=b, heads=h, n=n, d=d) == dvec
+    rows = b * h * 128 * 4          # n padded to a multiple of 64 per head
+    vec = (rows + 255) // 256 * 256
+    assert ws_bytes(B.FA_FP32, batch=b, heads=h, n=n, d=d) == 2 * vec
+    assert ws_bytes(B.FA_BF16, batch=b, heads=h, n=n, d=d) == 2 * vec
     assert ws_bytes(B.FA_BF16, d=48) == 0
     assert ws_bytes(B.FA_BF16, n=0) == 0
 
