@@ -77,6 +77,21 @@ __device__ __forceinline__ void gload_lds16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// Buffer resource for `bytes` bytes from base (raw buffer: stride 0, data
+// format word of the gfx9 family). base and bytes must be wave-uniform, so the
+// descriptor lives in scalar registers. Loads through it at byte offsets at or
+// past `bytes` are out of range: they read no memory and return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// bload_lds16: 16 bytes at byte offset voff (per lane) of a buffer into LDS
+// at lds_base + 16 * lane, like gload_lds16 but with a 32-bit lane offset
+// and range checking by the descriptor.
+__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
 // Wait until this wave's outstanding global loads (including the loads into
 // LDS) have completed; other counters are left alone. Encoding for gfx9:
 // vmcnt = 0, expcnt = 7 (no wait), lgkmcnt = 15 (no wait).

@@ -125,25 +125,38 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
   // Loads of a key (or value) tile into LDS. Wave w fills rows
   // [w * LPW * RPL, (w + 1) * LPW * RPL); lane l of a 1 KB load writes
   // physical chunk l % CH of row l / CH, which holds logical chunk
-  // (l % CH) ^ swizzle(row). The per-lane element offsets do not depend on
-  // the tile; rows at or past the key limit are read clamped to the last
-  // visible row (their scores are masked, they contribute exactly 0).
-  int ld_row[LPW], ld_koff[LPW], ld_voff[LPW];
+  // (l % CH) ^ swizzle(row). The loads go through a buffer descriptor whose
+  // base is the tile's first row and whose size stops at the key limit, so
+  // the per-lane byte offsets are tile-invariant and rows at or past the key
+  // limit are never read (their scores are masked, they contribute 0).
+  int ld_koff[LPW], ld_voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int row = (w * LPW + i) * RPL + lane / CH;
-    ld_row[i] = row;
-    ld_koff[i] = row * D + ((lane % CH) ^ swz_row<D>(row)) * 8;
-    ld_voff[i] = row * D + ((lane % CH) ^ swz_tr<D>(row)) * 8;
+    ld_koff[i] = (row * D + ((lane % CH) ^ swz_row<D>(row)) * 8) * 2;
+    ld_voff[i] = (row * D + ((lane % CH) ^ swz_tr<D>(row)) * 8) * 2;
   }
   auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) {
     const int kb0 = j * BC;
+    const auto r = buffer_rsrc(src + (size_t)kb0 * D, min(kv_lim - kb0, BC) * ROWB);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int dr = min(kb0 + ld_row[i], kv_lim - 1) - ld_row[i];
-      gload_lds16(src + (size_t)dr * D + off[i], dst + (w * LPW + i) * RPL * D);
-    }
+    for (int i = 0; i < LPW; ++i) bload_lds16(r, off[i], dst + (w * LPW + i) * RPL * D);
   };
+  // Out-of-range lanes of a partial tile may leave their LDS bytes as they
+  // were, so both stages start as zeros: whatever a masked row holds is then
+  // finite and its zero probability contributes exactly 0.
+  {
+    constexpr int NZ = 4 * TILEB / 16 / kThreads;
+    static_assert(NZ * 16 * kThreads == 4 * TILEB, "zero fill");
+#pragma unroll
+    for (int t = 0; t < NZ; ++t) {
+      const int idx = t * kThreads + tid;   // 16-byte chunk of the four tiles
+      const int which = idx / (TILEB / 16);
+      bf16* base = which == 0 ? sK0 : which == 1 ? sK1 : which == 2 ? sV0 : sV1;
+      *reinterpret_cast<u32x4*>(base + (idx % (TILEB / 16)) * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  }
 
   // Per-lane LDS element offsets of the MFMA operand reads (tile-invariant):
   // K row c (rows kb*32 + c share the swizzle of c), logical chunk kd*2 + h;
@@ -271,12 +284,18 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
     issue(K, ld_koff, 0, sK0);
     issue(V, ld_voff, 0, sV0);
   }
-  for (int j = 0; j < ntiles; j += 2) {
+  // Pairs of unmasked tiles (even tiles use stage 0, odd tiles stage 1),
+  // then the remaining tiles: at most one unmasked, the rest masked.
+  int j = 0;
+  for (; j + 1 < j_unmasked; j += 2) {
+    iter(j, sK0, sV0, sK1, sV1, std::false_type{});
+    iter(j + 1, sK1, sV1, sK0, sV0, std::false_type{});
+  }
+  for (; j < ntiles; j += 2) {
     if (j < j_unmasked) iter(j, sK0, sV0, sK1, sV1, std::false_type{});
     else iter(j, sK0, sV0, sK1, sV1, std::true_type{});
     if (j + 1 >= ntiles) break;
-    if (j + 1 < j_unmasked) iter(j + 1, sK1, sV1, sK0, sV0, std::false_type{});
-    else iter(j + 1, sK1, sV1, sK0, sV0, std::true_type{});
+    iter(j + 1, sK1, sV1, sK0, sV0, std::true_type{});
   }
 
   // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
