@@ -29,6 +29,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fa_fwd_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_fwd_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_bf16.hip"),
+    os.path.join(CSRC, "kernels", "fa_bwd_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dq_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_aux.hip"),
     os.path.join(CSRC, "kernels", "fa_fp32.hip"),

@@ -1,4 +1,5 @@
-// Attention backward, dK/dV part: bf16 in/out, fp32 accumulate, for gfx950.
+// Attention backward, dK/dV part: bf16 in/out, fp32 accumulate, for gfx950
+// (d = 64 and 128; d = 256 uses fa_bwd_bf16_staged.hip).
 //
 // Method: recomputation from the saved row statistic (page 1, "注意力为什么
 // 受限于显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 八; page 2,
@@ -13,19 +14,25 @@
 //
 // Mapping onto CDNA4:
 // * A workgroup is 4 wave64s and owns BKV = 128 keys (32 per wave) and their
-//   dK, dV accumulators (fp32, in AGPRs) for the whole query sweep; it loops
-//   over query tiles of BQ rows (key/value-outer order: dK and dV are each
+//   dK, dV accumulators (fp32) for the whole query sweep; it loops over
+//   query tiles of BQ rows (key/value-outer order: dK and dV are each
 //   written once, no atomics).
 // * Each wave keeps its 32 K and V rows in VGPRs as the B operands of
 //   S = Q K^T and dP = dO V^T; the results hold one key per lane and 16
-//   queries, which is exactly the B-operand layout of dV^T += dO^T P and
-//   dK^T += Q^T dS, so P and dS go to the matrix cores without leaving
-//   registers.
-// * Q and dO tiles are staged in LDS twice: row-major (A operand of S and
-//   dP) and transposed (A operand of dV^T and dK^T), double buffered so one
-//   barrier per query tile suffices.
-#include <type_traits>
-
+//   queries per 32-query block, which is exactly the B-operand layout of
+//   dV^T += dO^T P and dK^T += Q^T dS, so P and dS go to the matrix cores
+//   without leaving registers.
+// * Query tiles (Q, dO, and their L log2 e and D values) go from HBM
+//   straight into LDS through buffer descriptors, row-major with one XOR
+//   swizzle that makes both the row reads (A operands of S and dP) and the
+//   transposing reads (A operands of dV^T and dK^T, ds_read_b64_tr_b16)
+//   conflict-free. Three stages: tile i+2 streams in while tile i+1 is read
+//   row-wise and tile i transposed; one barrier per tile.
+// * Software pipeline: iteration i computes S and dP of tile i+1 on the
+//   matrix cores while the vector units turn S and dP of tile i into P and
+//   dS, then accumulates dV and dK of tile i. With one wave per SIMD (the
+//   accumulators and K/V fragments need more than half the register file)
+//   the overlap has to come from within the wave.
 #include "fa_device.h"
 
 namespace fa {
@@ -35,29 +42,34 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
 
-template <int D, int BQ, int NBUF, bool CAUSAL>
+template <int D, int NQB, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
-  constexpr int ND = D / 16;
-  constexpr int NMB = D / 32;
-  constexpr int NQB = BQ / 32;
-  constexpr int QSTR = D + 8;      // row-major Q / dO tiles
-  constexpr int TSTR = BQ + 4;     // transposed tiles [d][q]
-  constexpr int UPT = (BQ / 4) * (D / 8);  // 4x8 units per tensor tile
-  constexpr int UNITS = 2 * UPT;           // Q and dO
-  constexpr int UPTH = (UNITS + kThreads - 1) / kThreads;
-  static_assert(UNITS % kThreads == 0, "unit split");
+  constexpr int BQ = 32 * NQB;           // queries per tile
+  constexpr int ND = D / 16;             // reduction steps of S and dP
+  constexpr int NMB = D / 32;            // 32-row blocks of dK^T, dV^T
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int ROWB = D * 2;            // bytes per row
+  constexpr int TILE = BQ * D;           // elements per Q (or dO) tile
+  constexpr int TILEB = TILE * 2;
+  constexpr int LPW = TILEB / 1024 / 4;  // 1 KB wave loads per tensor per wave
+  constexpr int RPL = 1024 / ROWB;       // rows per 1 KB load
+  constexpr int HB = D >= 128 ? 2 : 1;   // block flip of the +8-row half (see toff)
+  static_assert(LPW * 4 * 1024 == TILEB && RPL >= 1, "tile split");
+  static_assert(BQ * 4 <= 1024 && 64 % BQ == 0, "L/D vector load");
 
-  // NBUF = 2: the Q/dO tiles, their transposes and L/D are double
-  // buffered, so one barrier per query tile suffices (see the loop below).
-  __shared__ __attribute__((aligned(16))) bf16 sQ[NBUF][BQ * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[NBUF][BQ * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[NBUF][D * TSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[NBUF][D * TSTR];
-  __shared__ __attribute__((aligned(16))) float sL[NBUF][BQ];
-  __shared__ __attribute__((aligned(16))) float sDv[NBUF][BQ];
+  // Stage s: Q tile at sm<s>[0], dO tile at sm<s>[TILE]; L log2 e and D
+  // of the tile's rows at sv<s>[0] and sv<s>[BQ]. Separate arrays per stage
+  // (selected at compile time) let the compiler see that reads of one stage
+  // never wait for the loads still in flight into another.
+  __shared__ __attribute__((aligned(1024))) bf16 sm0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sm1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sm2[2 * TILE];
+  __shared__ __attribute__((aligned(16))) float sv0[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float sv1[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float sv2[2 * BQ];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
@@ -109,167 +121,243 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         vf[kd] = as_bf16x8(kok ? bb : z);
       }
     }
+
+    // Out-of-range lanes of a partial tile may leave their LDS bytes as they
+    // were, so the stages start as zeros: whatever a masked row holds is then
+    // finite, and its zero probability and zero dS contribute exactly 0.
+    {
+      constexpr int NZ = 2 * TILEB / 16 / kThreads;
+      static_assert(NZ * 16 * kThreads == 2 * TILEB, "zero fill");
+#pragma unroll
+      for (int t = 0; t < NZ; ++t) {
+        const int e = (t * kThreads + tid) * 8;
+        *reinterpret_cast<u32x4*>(sm0 + e) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm1 + e) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm2 + e) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();  // the zeros land before any wave's tile loads
+    }
+
     const int n_qt = (n + BQ - 1) / BQ;
     const int it0 = CAUSAL ? (k0 / BQ) : 0;
-    // Tiles that need masking: the causal diagonal band (some key of this
-    // workgroup lies above some query of the tile), every tile when the
-    // workgroup straddles the key limit, and a partial last tile.
-    int a_end = it0;
-    if (k0 + kBKV > kv_lim) a_end = n_qt;
-    else if (CAUSAL) a_end = min(n_qt, (k0 + kBKV - 2) / BQ + 1);
-    const int b_end = max(a_end, (n % BQ) ? n_qt - 1 : n_qt);
+    // Every tile is masked, branch-free: a pair (query q, key) is hidden iff
+    // q < lo or q >= n, with lo = the key itself when causal, 0 otherwise,
+    // and lo = n for keys at or past the key limit (all hidden).
+    const int qlo = mykey >= kv_lim ? n : (CAUSAL ? mykey : 0);
 
-    // Register staging of the next Q / dO tile: unit u < UPT is a Q unit,
-    // else a dO unit; a unit is 4 rows x 8 dims. Rows past n are read
-    // clamped to row n-1; every product involving them is masked (P = 0,
-    // dS = 0) and their dQ rows are not written.
-    u32x4 ureg[UPTH][4];
-    auto gload = [&](int it) {
-      const int q0 = it * BQ;
+    // Loads of query tile it into a stage (sm: Q and dO, sv: L and D). Wave
+    // w fills rows
+    // [w * LPW * RPL, (w + 1) * LPW * RPL) of the Q and dO tiles; lane l of
+    // a 1 KB load writes physical chunk l % CH of row l / CH, holding logical
+    // chunk (l % CH) ^ swz_both(row). The descriptors span the head's n
+    // rows, so rows past n are never read. Wave 0 also loads the tile's
+    // L log2 e and D values (16 bytes per lane; the vectors are padded per
+    // head to a multiple of 64 rows, so a tile is always in range).
+    int ld_off[LPW];
 #pragma unroll
-      for (int i = 0; i < UPTH; ++i) {
-        const int u0 = tid + i * kThreads;
-        const bool isq = u0 < UPT;
-        const int u = isq ? u0 : u0 - UPT;
-        const int qg = (u >> 2) % (BQ / 4);
-        const int dg = (u & 3) + 4 * (u / BQ);
-        const bf16* src = (isq ? Q : dO) + dg * 8;
+    for (int i = 0; i < LPW; ++i) {
+      const int row = (w * LPW + i) * RPL + lane / CH;
+      ld_off[i] = (row * D + ((lane % CH) ^ swz_both<D>(row)) * 8) * 2;
+    }
+    const auto rq = buffer_rsrc(Q, n * ROWB);
+    const auto rg = buffer_rsrc(dO, n * ROWB);
+    const auto rl = buffer_rsrc(l2v, p.n_pad * 4);
+    const auto rd = buffer_rsrc(dvec, p.n_pad * 4);
+    auto issue = [&](int it, bf16* sm, float* sv) {
+      const int qb0 = it * BQ * ROWB;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          ureg[i][t] = ld16(src + (size_t)min(q0 + qg * 4 + t, n - 1) * D);
+      for (int i = 0; i < LPW; ++i) {
+        bload_lds16(rq, qb0 + ld_off[i], sm + (w * LPW + i) * RPL * D);
+        bload_lds16(rg, qb0 + ld_off[i], sm + TILE + (w * LPW + i) * RPL * D);
       }
-    };
-    auto swrite = [&](int it, int buf) {
-#pragma unroll
-      for (int i = 0; i < UPTH; ++i) {
-        const int u0 = tid + i * kThreads;
-        const bool isq = u0 < UPT;
-        const int u = isq ? u0 : u0 - UPT;
-        const int qg = (u >> 2) % (BQ / 4);
-        const int dg = (u & 3) + 4 * (u / BQ);
-        bf16* rm = isq ? sQ[buf] : sdO[buf];
-        bf16* tr = isq ? sQt[buf] : sdOt[buf];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          *reinterpret_cast<u32x4*>(&rm[(qg * 4 + t) * QSTR + dg * 8]) = ureg[i][t];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<u32x2*>(&tr[(dg * 8 + e) * TSTR + qg * 4]) = column4(ureg[i], e);
-      }
-      if (tid < BQ) {
-        const int q = min(it * BQ + tid, n - 1);
-        sL[buf][tid] = l2v[q];
-        sDv[buf][tid] = dvec[q];
+      if (w == 0 && lane < BQ / 4) {
+        bload_lds16(rl, it * BQ * 4 + lane * 16, sv);
+        bload_lds16(rd, it * BQ * 4 + lane * 16, sv + BQ);
       }
     };
 
-    // Tile compute on LDS buffer `buf`: S = Q K^T and dP = dO V^T (lane =
-    // key, 16 queries per 32-query block), P = exp2(S c - L log2 e),
-    // dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS.
-    auto compute = [&](int it, int buf, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      const int q0 = it * BQ;
-      const bf16* tQ = sQ[buf];
-      const bf16* tdO = sdO[buf];
-      const bf16* tQt = sQt[buf];
-      const bf16* tdOt = sdOt[buf];
+    // Per-lane LDS element offsets (tile-invariant). Row reads: row c of a
+    // 32-row block, logical chunk kd*2 + h. Transposing reads: row
+    // h*4 + (c%16)/4 of a 16-row block, column mb*32 + 16*(c/16) + 4*(c%4);
+    // the second read of a fragment (rows +8) lands in block mb ^ HB.
+    int qoff[ND], toff[NMB];
+#pragma unroll
+    for (int kd = 0; kd < ND; ++kd) qoff[kd] = c * D + (((kd * 2 + h) ^ swz_both<D>(c)) << 3);
+    {
+      const int trow = h * 4 + ((c & 15) >> 2);
+      const int tcol = 16 * (c >> 4) + 4 * (c & 3);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int col = mb * 32 + tcol;
+        toff[mb] = trow * D + (((col >> 3) ^ swz_both<D>(trow)) << 3) + (col & 7);
+      }
+    }
 
-      f32x16 sv[NQB], dp[NQB];
+    // S = Q K^T and dP = dO V^T of the tile in stage sm (lane = key, 16
+    // queries per 32-query block); used once, before the loop.
+    auto sdp = [&](const bf16* sm, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        bf16x8 qa[ND], ga[ND];
+        s[qb] = f32x16{};
+        g[qb] = f32x16{};
 #pragma unroll
         for (int kd = 0; kd < ND; ++kd) {
-          qa[kd] = as_bf16x8(ld16(&tQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-          ga[kd] = as_bf16x8(ld16(&tdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-        }
-        sv[qb] = f32x16{};
-        dp[qb] = f32x16{};
-#pragma unroll
-        for (int kd = 0; kd < ND; ++kd) {
-          sv[qb] = mma32(qa[kd], kf[kd], sv[qb]);
-          dp[qb] = mma32(ga[kd], vf[kd], dp[qb]);
+          s[qb] = mma32(as_bf16x8(ld16(sm + qb * 32 * D + qoff[kd])), kf[kd], s[qb]);
+          g[qb] = mma32(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[kd])), vf[kd], g[qb]);
         }
       }
+    };
+
+    // P = exp2(S c - L log2 e) and dS = P (dP - D) for element e of the
+    // lane's 16 NQB values, in place in s and g. Query of element
+    // (qb, gi, i) is q0 + 4h + (qb*32 + gi*8 + i); the pair is hidden iff
+    // that offset is < lo or >= hi, and a hidden pair gets P = 0, dS = 0.
+    auto pds1 = [&](int e, int lo, int hi, const f32x4 (&l4)[NQB][4], const f32x4 (&d4)[NQB][4],
+                    f32x16 (&s)[NQB], f32x16 (&g)[NQB]) {
+      const int qb = e / 16, r = e % 16, gi = r / 4, i = r % 4;
+      const int off = qb * 32 + gi * 8 + i;
+      const float x = (off < lo || off >= hi) ? kNegInf : s[qb][r];
+      const float pr = __builtin_amdgcn_exp2f(fmaf(x, cs, -l4[qb][gi][i]));
+      s[qb][r] = pr;
+      g[qb][r] = pr * (g[qb][r] - d4[qb][gi][i]);
+    };
+
+    // A fragments of the transposing reads for (qb, qc, mb): dO^T and Q^T of
+    // 16 queries x 32 dims of the tile in sm.
+    auto trfrag = [&](const bf16* sm, int qb, int qc, int mb, bf16x8& fo, bf16x8& fq) {
+      const int r0 = (qb * 32 + qc * 16) * D;
+      const int r1 = r0 + 8 * D;
+      const u32x2 olo = ds_read_tr16(sm + TILE + r0 + toff[mb]);
+      const u32x2 ohi = ds_read_tr16(sm + TILE + r1 + toff[mb ^ HB]);
+      const u32x2 qlo = ds_read_tr16(sm + r0 + toff[mb]);
+      const u32x2 qhi = ds_read_tr16(sm + r1 + toff[mb ^ HB]);
+      fo = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+      fq = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+    };
+
+    // One query tile, software-pipelined and issued in a fixed order (the
+    // sched_barrier fences pin it): phase 1 computes S and dP of tile it+1
+    // (stage mB, row reads two products ahead) while the vector units turn
+    // S and dP of tile it (in s, g; L and D in vA) into P and dS, 16/ND
+    // values per product pair; phase 2 accumulates dV^T and dK^T of tile it
+    // from stage mA (transposing reads one pair ahead).
+    constexpr int NS = NQB * ND;        // phase-1 slots (2 products each)
+    constexpr int EPS = 16 / ND;        // P/dS values per phase-1 slot
+    constexpr int NP = NQB * 2 * NMB;   // phase-2 slots (2 products each)
+    f32x16 s[NQB], g[NQB];
+    auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB, bool next) {
+      const int qh = it * BQ + h * 4;
+      const int lo = qlo - qh;
+      const int hi = n - qh;
+      f32x4 l4[NQB][4], d4[NQB][4];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][qb * 32 + g * 8 + h * 4]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDv[buf][qb * 32 + g * 8 + h * 4]);
+        for (int gi = 0; gi < 4; ++gi) {
+          l4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[qb * 32 + gi * 8 + h * 4]);
+          d4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[BQ + qb * 32 + gi * 8 + h * 4]);
+        }
+      f32x16 s2[NQB], g2[NQB];
+      bf16x8 rq[3], rg[3];
+      if (next) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = g * 4 + i;
-            float pr = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], cs, -l4[i]));
-            if (MASK) {
-              const int q = q0 + qb * 32 + g * 8 + h * 4 + i;
-              const bool hidden = q >= n || mykey >= kv_lim || (CAUSAL && mykey > q);
-              pr = hidden ? 0.f : pr;
-            }
-            sv[qb][r] = pr;
-            dp[qb][r] = pr * (dp[qb][r] - d4[i]);
+        for (int qb = 0; qb < NQB; ++qb) {
+          s2[qb] = f32x16{};
+          g2[qb] = f32x16{};
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          rq[j] = as_bf16x8(ld16(mB + (j / ND) * 32 * D + qoff[j % ND]));
+          rg[j] = as_bf16x8(ld16(mB + TILE + (j / ND) * 32 * D + qoff[j % ND]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        if (next) {
+          const int qb = j / ND, kd = j % ND;
+          s2[qb] = mma32(rq[j % 3], kf[kd], s2[qb]);
+          g2[qb] = mma32(rg[j % 3], vf[kd], g2[qb]);
+          if (j + 2 < NS) {
+            const int j2 = j + 2;
+            rq[j2 % 3] = as_bf16x8(ld16(mB + (j2 / ND) * 32 * D + qoff[j2 % ND]));
+            rg[j2 % 3] = as_bf16x8(ld16(mB + TILE + (j2 / ND) * 32 * D + qoff[j2 % ND]));
           }
         }
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+        for (int e = j * EPS; e < (j + 1) * EPS; ++e) pds1(e, lo, hi, l4, d4, s, g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8 fo[2], fq[2];
+      trfrag(mA, 0, 0, 0, fo[0], fq[0]);
+      bf16x8 pfr, sfr;
 #pragma unroll
-        for (int qc = 0; qc < 2; ++qc) {
+      for (int k = 0; k < NP; ++k) {
+        const int qb = k / (2 * NMB), qc = (k / NMB) % 2, mb = k % NMB;
+        if (k + 1 < NP) {
+          const int k1 = k + 1;
+          trfrag(mA, k1 / (2 * NMB), (k1 / NMB) % 2, k1 % NMB, fo[k1 % 2], fq[k1 % 2]);
+        }
+        if (mb == 0) {
           u32x4 pu, su;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            pu[t] = pack_bf16x2(sv[qb][qc * 8 + 2 * t], sv[qb][qc * 8 + 2 * t + 1]);
-            su[t] = pack_bf16x2(dp[qb][qc * 8 + 2 * t], dp[qb][qc * 8 + 2 * t + 1]);
+            pu[t] = pack_bf16x2(s[qb][qc * 8 + 2 * t], s[qb][qc * 8 + 2 * t + 1]);
+            su[t] = pack_bf16x2(g[qb][qc * 8 + 2 * t], g[qb][qc * 8 + 2 * t + 1]);
           }
-          const bf16x8 pfr = as_bf16x8(pu);
-          const bf16x8 sfr = as_bf16x8(su);
-          bf16x8 oa[NMB], qa[NMB];
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) {
-            const int off = (mb * 32 + c) * TSTR + qb * 32 + qc * 16 + h * 4;
-            const u32x2 olo = ld8(&tdOt[off]);
-            const u32x2 ohi = ld8(&tdOt[off + 8]);
-            oa[mb] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
-            const u32x2 qlo = ld8(&tQt[off]);
-            const u32x2 qhi = ld8(&tQt[off + 8]);
-            qa[mb] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
-          }
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) {
-            dv[mb] = mma32(oa[mb], pfr, dv[mb]);
-            dk[mb] = mma32(qa[mb], sfr, dk[mb]);
-          }
+          pfr = as_bf16x8(pu);
+          sfr = as_bf16x8(su);
         }
-    };
-
-    auto run = [&](int it, int buf, auto mask_tag) {
-      if constexpr (NBUF == 2) {
-        // Buffer `buf` holds tile it. Tile it+1 goes to buf^1 while it is
-        // processed: buf^1 was last read before the previous barrier.
-        compute(it, buf, mask_tag);
-        if (it + 1 < n_qt) {
-          swrite(it + 1, buf ^ 1);
-          gload(min(it + 2, n_qt - 1));
+        dv[mb] = mma32(fo[k % 2], pfr, dv[mb]);
+        dk[mb] = mma32(fq[k % 2], sfr, dk[mb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (next) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          s[qb] = s2[qb];
+          g[qb] = g2[qb];
         }
-        __syncthreads();  // tile it+1 complete; buf free for tile it+2
-      } else {
-        __syncthreads();  // previous tile's LDS contents are no longer read
-        swrite(it, 0);
-        __syncthreads();
-        gload(min(it + 1, n_qt - 1));
-        compute(it, 0, mask_tag);
       }
     };
 
-    gload(it0);
-    if constexpr (NBUF == 2) {
-      swrite(it0, 0);
-      gload(min(it0 + 1, n_qt - 1));
+    // Stages: tile it in A, tile it+1 in B, tile it+2 goes to C (rotating
+    // with the loop unrolled by three). At the top of an iteration each wave
+    // waits for its own loads of tile it+1; the barrier then makes every
+    // wave's loads visible and guarantees that every wave has finished the
+    // previous iteration, the last reader of stage C (tile it-1).
+    auto step = [&](int it, bf16* mA, float* vA, bf16* mB, bf16* mC, float* vC) {
+      wait_global_loads();
       __syncthreads();
-    }
+      if (it + 2 < n_qt) issue(it + 2, mC, vC);
+      body(it, mA, vA, mB, true);
+    };
+    auto finish = [&](int it, bf16* mA, float* vA) { body(it, mA, vA, nullptr, false); };
+
+    issue(it0, sm0, sv0);
+    if (it0 + 1 < n_qt) issue(it0 + 1, sm1, sv1);
+    wait_global_loads();
+    __syncthreads();
+    sdp(sm0, s, g);
     int it = it0;
-    for (; it < a_end; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
-    for (; it < b_end; ++it) run(it, (it - it0) & (NBUF - 1), std::false_type{});
-    for (; it < n_qt; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
+    const int last = n_qt - 1;
+    for (; it + 3 <= last; it += 3) {
+      step(it, sm0, sv0, sm1, sm2, sv2);
+      step(it + 1, sm1, sv1, sm2, sm0, sv0);
+      step(it + 2, sm2, sv2, sm0, sm1, sv1);
+    }
+    // last - it is 0, 1 or 2 here; the last tile has no successor.
+    if (it == last) {
+      finish(it, sm0, sv0);
+    } else {
+      step(it, sm0, sv0, sm1, sm2, sv2);
+      if (it + 1 == last) {
+        finish(it + 1, sm1, sv1);
+      } else {
+        step(it + 1, sm1, sv1, sm2, sm0, sv0);
+        finish(it + 2, sm2, sv2);
+      }
+    }
   }
 
   // dK = scale * (dS^T Q), dV as accumulated.
@@ -278,28 +366,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const size_t off = (size_t)mykey * D + mb * 32 + g * 8 + h * 4;
+      for (int gi = 0; gi < 4; ++gi) {
+        const size_t off = (size_t)mykey * D + mb * 32 + gi * 8 + h * 4;
         u32x2 uk, uv;
-        uk[0] = pack_bf16x2(dk[mb][g * 4 + 0] * ks, dk[mb][g * 4 + 1] * ks);
-        uk[1] = pack_bf16x2(dk[mb][g * 4 + 2] * ks, dk[mb][g * 4 + 3] * ks);
-        uv[0] = pack_bf16x2(dv[mb][g * 4 + 0], dv[mb][g * 4 + 1]);
-        uv[1] = pack_bf16x2(dv[mb][g * 4 + 2], dv[mb][g * 4 + 3]);
+        uk[0] = pack_bf16x2(dk[mb][gi * 4 + 0] * ks, dk[mb][gi * 4 + 1] * ks);
+        uk[1] = pack_bf16x2(dk[mb][gi * 4 + 2] * ks, dk[mb][gi * 4 + 3] * ks);
+        uv[0] = pack_bf16x2(dv[mb][gi * 4 + 0], dv[mb][gi * 4 + 1]);
+        uv[1] = pack_bf16x2(dv[mb][gi * 4 + 2], dv[mb][gi * 4 + 3]);
         *reinterpret_cast<u32x2*>(dK + off) = uk;
         *reinterpret_cast<u32x2*>(dV + off) = uv;
       }
   }
 }
 
-template <int D, int BQ, int NBUF>
+template <int D, int NQB>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_c = (p.n + kBKV - 1) / kBKV;
   const long long total = (long long)t_c * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
   if (p.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, NBUF, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NQB, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, NBUF, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NQB, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -307,9 +395,9 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 
 hipError_t launch_bwd_dkdv_bf16(const Params& p, int d, hipStream_t s) {
   switch (d) {
-    case 64: return launch_d<64, 64, 2>(p, s);
-    case 128: return launch_d<128, 32, 2>(p, s);
-    case 256: return launch_d<256, 32, 1>(p, s);
+    case 64: return launch_d<64, 2>(p, s);
+    case 128: return launch_d<128, 1>(p, s);
+    case 256: return launch_bwd_dkdv_bf16_staged(p, d, s);
     default: return hipErrorInvalidValue;
   }
 }

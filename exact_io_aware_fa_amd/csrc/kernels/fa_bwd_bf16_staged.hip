@@ -1,0 +1,302 @@
+// Attention backward, dK/dV part, register-staged variant (used for d = 256).
+//
+// Same method and wave layout as fa_bwd_bf16.hip (page 1, "注意力为什么受限于
+// 显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 八; page 2,
+// "4. FlashAttention 深度剖析", 4.3.4): a workgroup owns 128 keys (32 per
+// wave) and their dK, dV accumulators for the whole query sweep; K and V rows
+// are B operands held in VGPRs; P and dS stay in registers as B operands of
+// dV^T += dO^T P and dK^T += Q^T dS. The difference is how the query tiles
+// reach LDS: each thread loads 16-byte chunks into registers and writes
+// every tile twice, row-major (rows padded by 16 bytes) and transposed
+// ([d][query], rows padded by 8 bytes, built with byte permutes), one tile
+// at a time. At d = 256 the dK and dV accumulators alone take 256 registers,
+// which leaves no room for the software pipeline of the d <= 128 kernel.
+#include <type_traits>
+
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
+
+template <int D, int BQ, int NBUF, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) {
+  constexpr int ND = D / 16;
+  constexpr int NMB = D / 32;
+  constexpr int NQB = BQ / 32;
+  constexpr int QSTR = D + 8;      // row-major Q / dO tiles
+  constexpr int TSTR = BQ + 4;     // transposed tiles [d][q]
+  constexpr int UPT = (BQ / 4) * (D / 8);  // 4x8 units per tensor tile
+  constexpr int UNITS = 2 * UPT;           // Q and dO
+  constexpr int UPTH = (UNITS + kThreads - 1) / kThreads;
+  static_assert(UNITS % kThreads == 0, "unit split");
+
+  // NBUF = 2: the Q/dO tiles, their transposes and L/D are double
+  // buffered, so one barrier per query tile suffices (see the loop below).
+  __shared__ __attribute__((aligned(16))) bf16 sQ[NBUF][BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[NBUF][BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sQt[NBUF][D * TSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdOt[NBUF][D * TSTR];
+  __shared__ __attribute__((aligned(16))) float sL[NBUF][BQ];
+  __shared__ __attribute__((aligned(16))) float sDv[NBUF][BQ];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+  const int n = p.n;
+
+  const int t_c = (n + kBKV - 1) / kBKV;
+  int bh, kt;
+  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, bh, kt);
+  const int b = bh / p.heads;
+  const size_t base = (size_t)bh * (size_t)n * D;
+  const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
+  const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
+  const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;
+  const float* __restrict__ dvec = p.dvec + (size_t)bh * p.n_pad;
+  bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + base;
+  bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + base;
+
+  const int kv_lim = kv_limit(p, b);
+  const int k0 = kt * kBKV;
+  const int kw0 = k0 + w * 32;
+  const int mykey = kw0 + c;
+  const float cs = p.c;
+  // A negative scale is applied by negating K (exact in bf16): the scores
+  // use K' = -K with |scale|, and dK = scale dS^T Q with the true Q.
+  const uint32_t kflip = p.q_neg ? 0x80008000u : 0u;
+
+  f32x16 dk[NMB], dv[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    dk[mb] = f32x16{};
+    dv[mb] = f32x16{};
+  }
+
+  if (k0 < kv_lim) {
+    // K and V rows of this wave as B fragments: [mykey][kd*16 + h*8 + e].
+    // Rows past the key limit are read clamped and replaced by zeros.
+    bf16x8 kf[ND], vf[ND];
+    {
+      const bool kok = mykey < kv_lim;
+      const int kr = kok ? mykey : kv_lim - 1;
+#pragma unroll
+      for (int kd = 0; kd < ND; ++kd) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 a = ld16(K + (size_t)kr * D + kd * 16 + h * 8);
+        const u32x4 bb = ld16(V + (size_t)kr * D + kd * 16 + h * 8);
+        kf[kd] = as_bf16x8(kok ? (a ^ kflip) : z);
+        vf[kd] = as_bf16x8(kok ? bb : z);
+      }
+    }
+    const int n_qt = (n + BQ - 1) / BQ;
+    const int it0 = CAUSAL ? (k0 / BQ) : 0;
+    // Tiles that need masking: the causal diagonal band (some key of this
+    // workgroup lies above some query of the tile), every tile when the
+    // workgroup straddles the key limit, and a partial last tile.
+    int a_end = it0;
+    if (k0 + kBKV > kv_lim) a_end = n_qt;
+    else if (CAUSAL) a_end = min(n_qt, (k0 + kBKV - 2) / BQ + 1);
+    const int b_end = max(a_end, (n % BQ) ? n_qt - 1 : n_qt);
+
+    // Register staging of the next Q / dO tile: unit u < UPT is a Q unit,
+    // else a dO unit; a unit is 4 rows x 8 dims. Rows past n are read
+    // clamped to row n-1; every product involving them is masked (P = 0,
+    // dS = 0) and their dQ rows are not written.
+    u32x4 ureg[UPTH][4];
+    auto gload = [&](int it) {
+      const int q0 = it * BQ;
+#pragma unroll
+      for (int i = 0; i < UPTH; ++i) {
+        const int u0 = tid + i * kThreads;
+        const bool isq = u0 < UPT;
+        const int u = isq ? u0 : u0 - UPT;
+        const int qg = (u >> 2) % (BQ / 4);
+        const int dg = (u & 3) + 4 * (u / BQ);
+        const bf16* src = (isq ? Q : dO) + dg * 8;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          ureg[i][t] = ld16(src + (size_t)min(q0 + qg * 4 + t, n - 1) * D);
+      }
+    };
+    auto swrite = [&](int it, int buf) {
+#pragma unroll
+      for (int i = 0; i < UPTH; ++i) {
+        const int u0 = tid + i * kThreads;
+        const bool isq = u0 < UPT;
+        const int u = isq ? u0 : u0 - UPT;
+        const int qg = (u >> 2) % (BQ / 4);
+        const int dg = (u & 3) + 4 * (u / BQ);
+        bf16* rm = isq ? sQ[buf] : sdO[buf];
+        bf16* tr = isq ? sQt[buf] : sdOt[buf];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<u32x4*>(&rm[(qg * 4 + t) * QSTR + dg * 8]) = ureg[i][t];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<u32x2*>(&tr[(dg * 8 + e) * TSTR + qg * 4]) = column4(ureg[i], e);
+      }
+      if (tid < BQ) {
+        const int q = min(it * BQ + tid, n - 1);
+        sL[buf][tid] = l2v[q];
+        sDv[buf][tid] = dvec[q];
+      }
+    };
+
+    // Tile compute on LDS buffer `buf`: S = Q K^T and dP = dO V^T (lane =
+    // key, 16 queries per 32-query block), P = exp2(S c - L log2 e),
+    // dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS.
+    auto compute = [&](int it, int buf, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int q0 = it * BQ;
+      const bf16* tQ = sQ[buf];
+      const bf16* tdO = sdO[buf];
+      const bf16* tQt = sQt[buf];
+      const bf16* tdOt = sdOt[buf];
+
+      f32x16 sv[NQB], dp[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        bf16x8 qa[ND], ga[ND];
+#pragma unroll
+        for (int kd = 0; kd < ND; ++kd) {
+          qa[kd] = as_bf16x8(ld16(&tQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+          ga[kd] = as_bf16x8(ld16(&tdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+        }
+        sv[qb] = f32x16{};
+        dp[qb] = f32x16{};
+#pragma unroll
+        for (int kd = 0; kd < ND; ++kd) {
+          sv[qb] = mma32(qa[kd], kf[kd], sv[qb]);
+          dp[qb] = mma32(ga[kd], vf[kd], dp[qb]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][qb * 32 + g * 8 + h * 4]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDv[buf][qb * 32 + g * 8 + h * 4]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = g * 4 + i;
+            float pr = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], cs, -l4[i]));
+            if (MASK) {
+              const int q = q0 + qb * 32 + g * 8 + h * 4 + i;
+              const bool hidden = q >= n || mykey >= kv_lim || (CAUSAL && mykey > q);
+              pr = hidden ? 0.f : pr;
+            }
+            sv[qb][r] = pr;
+            dp[qb][r] = pr * (dp[qb][r] - d4[i]);
+          }
+        }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+          u32x4 pu, su;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            pu[t] = pack_bf16x2(sv[qb][qc * 8 + 2 * t], sv[qb][qc * 8 + 2 * t + 1]);
+            su[t] = pack_bf16x2(dp[qb][qc * 8 + 2 * t], dp[qb][qc * 8 + 2 * t + 1]);
+          }
+          const bf16x8 pfr = as_bf16x8(pu);
+          const bf16x8 sfr = as_bf16x8(su);
+          bf16x8 oa[NMB], qa[NMB];
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            const int off = (mb * 32 + c) * TSTR + qb * 32 + qc * 16 + h * 4;
+            const u32x2 olo = ld8(&tdOt[off]);
+            const u32x2 ohi = ld8(&tdOt[off + 8]);
+            oa[mb] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+            const u32x2 qlo = ld8(&tQt[off]);
+            const u32x2 qhi = ld8(&tQt[off + 8]);
+            qa[mb] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+          }
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            dv[mb] = mma32(oa[mb], pfr, dv[mb]);
+            dk[mb] = mma32(qa[mb], sfr, dk[mb]);
+          }
+        }
+    };
+
+    auto run = [&](int it, int buf, auto mask_tag) {
+      if constexpr (NBUF == 2) {
+        // Buffer `buf` holds tile it. Tile it+1 goes to buf^1 while it is
+        // processed: buf^1 was last read before the previous barrier.
+        compute(it, buf, mask_tag);
+        if (it + 1 < n_qt) {
+          swrite(it + 1, buf ^ 1);
+          gload(min(it + 2, n_qt - 1));
+        }
+        __syncthreads();  // tile it+1 complete; buf free for tile it+2
+      } else {
+        __syncthreads();  // previous tile's LDS contents are no longer read
+        swrite(it, 0);
+        __syncthreads();
+        gload(min(it + 1, n_qt - 1));
+        compute(it, 0, mask_tag);
+      }
+    };
+
+    gload(it0);
+    if constexpr (NBUF == 2) {
+      swrite(it0, 0);
+      gload(min(it0 + 1, n_qt - 1));
+      __syncthreads();
+    }
+    int it = it0;
+    for (; it < a_end; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
+    for (; it < b_end; ++it) run(it, (it - it0) & (NBUF - 1), std::false_type{});
+    for (; it < n_qt; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
+  }
+
+  // dK = scale * (dS^T Q), dV as accumulated.
+  if (mykey < n) {
+    const float ks = p.scale;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const size_t off = (size_t)mykey * D + mb * 32 + g * 8 + h * 4;
+        u32x2 uk, uv;
+        uk[0] = pack_bf16x2(dk[mb][g * 4 + 0] * ks, dk[mb][g * 4 + 1] * ks);
+        uk[1] = pack_bf16x2(dk[mb][g * 4 + 2] * ks, dk[mb][g * 4 + 3] * ks);
+        uv[0] = pack_bf16x2(dv[mb][g * 4 + 0], dv[mb][g * 4 + 1]);
+        uv[1] = pack_bf16x2(dv[mb][g * 4 + 2], dv[mb][g * 4 + 3]);
+        *reinterpret_cast<u32x2*>(dK + off) = uk;
+        *reinterpret_cast<u32x2*>(dV + off) = uv;
+      }
+  }
+}
+
+template <int D, int BQ, int NBUF>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  const int t_c = (p.n + kBKV - 1) / kBKV;
+  const long long total = (long long)t_c * p.batch * p.heads;
+  dim3 grid((unsigned)total), block(kThreads);
+  if (p.causal)
+    hipLaunchKernelGGL((bwd_dkdv_staged_kernel<D, BQ, NBUF, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_staged_kernel<D, BQ, NBUF, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkdv_bf16_staged(const Params& p, int d, hipStream_t s) {
+  switch (d) {
+    case 256: return launch_d<256, 32, 1>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

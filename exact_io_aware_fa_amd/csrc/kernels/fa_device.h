@@ -127,6 +127,16 @@ __device__ __forceinline__ int swz_tr(int row) {
   return D >= 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
+// One swizzle serving both patterns on the same tile: it is a bijection on
+// any 16 consecutive rows (same parity for d = 64) and moves any 4
+// consecutive rows (from a multiple of 4) to 4 different 64-byte blocks.
+template <int D>
+__device__ __forceinline__ int swz_both(int row) {
+  if (D >= 128) return (row & 15) ^ ((row & 3) << 2);
+  const int v = (row >> 1) & 7;
+  return v ^ ((v & 1) << 2);
+}
+
 // Workgroup remap. The dispatcher places consecutive workgroup ids on the
 // eight XCDs in turn (id % 8), each XCD with its own L2. Hand each XCD a
 // contiguous range of the work list so that workgroups of the same
