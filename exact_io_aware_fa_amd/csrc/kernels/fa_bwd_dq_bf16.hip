@@ -1,4 +1,5 @@
-// Attention backward, dQ part: bf16 in/out, fp32 accumulate, for gfx950.
+// Attention backward, dQ part: bf16 in/out, fp32 accumulate, for gfx950
+// (d = 64 and 128; d = 256 uses fa_bwd_dq_bf16_staged.hip).
 //
 // dQ = scale * dS K with dS = P * (dP - D), dP = dO V^T, and P rebuilt from
 // the saved row statistic, P_ij = exp(scale q_i.k_j - L_i) (page 1, "注意力
@@ -18,9 +19,12 @@
 // bf16 MFMA with Q and dO rows held in VGPRs as B operands, so a lane owns one
 // query row and 16 keys of every 32-key block; L_i and D_i are per-lane
 // constants. dS^T rounded to bf16 is already the B operand of
-// dQ^T += K^T dS^T, whose A operand comes from a transposed copy of the K tile
-// in LDS. K and V tiles are also kept row-major in LDS (A operands of S^T and
-// dP^T). The next key tile is fetched into registers during the current one.
+// dQ^T += K^T dS^T. K and V tiles go from HBM straight into LDS through
+// buffer descriptors, in two stages (one barrier per tile). K is stored with
+// a swizzle that serves both its row reads (A operand of S^T) and the
+// transposing reads (ds_read_b64_tr_b16) that yield the K^T operand; V with
+// the row-read swizzle. Two workgroups share each compute unit, so one wave's
+// softmax arithmetic overlaps the other's matrix work.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -34,23 +38,25 @@ constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
 
 template <int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
-  constexpr int KSTR = D + 8;    // row-major K / V tiles (bf16 elements)
-  constexpr int TSTR = BC + 4;   // transposed K tile [d][key]
-  constexpr int ND = D / 16;
-  constexpr int NMB = D / 32;
-  constexpr int NKB = BC / 32;
-  constexpr int KUN = (BC / 4) * (D / 8);  // K units: 4 keys x 8 dims
-  constexpr int KUPT = (KUN + kThreads - 1) / kThreads;
-  constexpr int VCH = BC * D / 8 / kThreads;  // 16-byte V chunks per thread
-  static_assert(VCH * kThreads * 8 == BC * D, "V tile split");
-  static_assert(KUN % kThreads == 0 || KUN < kThreads, "K unit split");
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int ROWB = D * 2;           // bytes per row
+  constexpr int TILEB = BC * ROWB;      // bytes per K or V tile
+  constexpr int LPW = TILEB / 1024 / 4; // 1 KB wave loads per tensor per wave
+  constexpr int RPL = 1024 / ROWB;      // rows per 1 KB load
+  constexpr int ND = D / 16;            // reduction steps of S^T and dP^T
+  constexpr int NMB = D / 32;           // 32-row blocks of dQ^T
+  constexpr int NKB = BC / 32;          // 32-key blocks of S^T
+  constexpr int HB = D >= 128 ? 2 : 1;  // block flip of the +8-row half (see toff)
+  static_assert(LPW * 4 * 1024 == TILEB && RPL >= 1, "tile split");
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sV[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * TSTR];
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[BC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[BC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[BC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[BC * D];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
@@ -91,6 +97,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   int kend = kv_lim;
   if (CAUSAL) kend = min(kend, q0 + kBR);
   const int ntiles = (kend + BC - 1) / BC;
+  // Tiles [0, j_unmasked) have every key visible to every query of the
+  // workgroup; the rest go through the masked path.
   int j_unmasked = kv_lim / BC;
   if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
   j_unmasked = min(j_unmasked, ntiles);
@@ -99,94 +107,98 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
 
-  u32x4 kreg[KUPT][4];
-  u32x4 vreg[VCH];
-
-  // Key rows at or past the key limit are read clamped to the last visible
-  // row; their probabilities are masked to exactly 0.
-  auto gload = [&](int j) {
+  // Tile loads, as in the forward: wave w fills rows [w*LPW*RPL,
+  // (w+1)*LPW*RPL); lane l of a 1 KB load writes physical chunk l % CH of
+  // row l / CH, holding logical chunk (l % CH) ^ swizzle(row). The
+  // descriptor's base is the tile's first row and its size stops at the key
+  // limit, so rows at or past it are never read.
+  int ld_koff[LPW], ld_voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (w * LPW + i) * RPL + lane / CH;
+    ld_koff[i] = (row * D + ((lane % CH) ^ swz_both<D>(row)) * 8) * 2;
+    ld_voff[i] = (row * D + ((lane % CH) ^ swz_row<D>(row)) * 8) * 2;
+  }
+  auto issue = [&](int j, bf16* dk, bf16* dv) {
     const int kb0 = j * BC;
+    const int bytes = min(kv_lim - kb0, BC) * ROWB;
+    const auto rk = buffer_rsrc(K + (size_t)kb0 * D, bytes);
+    const auto rv = buffer_rsrc(V + (size_t)kb0 * D, bytes);
 #pragma unroll
-    for (int i = 0; i < KUPT; ++i) {
-      const int u = tid + i * kThreads;
-      if (KUN % kThreads == 0 || u < KUN) {
-        const int kg = (u >> 2) % (BC / 4);
-        const int dg = (u & 3) + 4 * (u / BC);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          kreg[i][r] = ld16(K + (size_t)min(kb0 + kg * 4 + r, kv_lim - 1) * D + dg * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ch = tid + i * kThreads;
-      const int key = min(kb0 + ch / (D / 8), kv_lim - 1);
-      vreg[i] = ld16(V + (size_t)key * D + (ch % (D / 8)) * 8);
+    for (int i = 0; i < LPW; ++i) {
+      bload_lds16(rk, ld_koff[i], dk + (w * LPW + i) * RPL * D);
+      bload_lds16(rv, ld_voff[i], dv + (w * LPW + i) * RPL * D);
     }
   };
-
-  auto swrite = [&]() {
+  // Out-of-range lanes of a partial tile may leave their LDS bytes as they
+  // were, so both stages start as zeros (finite data under every masked
+  // score), and the zeros land before any wave's first loads.
+  {
+    constexpr int NZ = TILEB / 16 / kThreads;
+    static_assert(NZ * 16 * kThreads == TILEB, "zero fill");
 #pragma unroll
-    for (int i = 0; i < KUPT; ++i) {
-      const int u = tid + i * kThreads;
-      if (KUN % kThreads == 0 || u < KUN) {
-        const int kg = (u >> 2) % (BC / 4);
-        const int dg = (u & 3) + 4 * (u / BC);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<u32x4*>(&sK[(kg * 4 + r) * KSTR + dg * 8]) = kreg[i][r];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<u32x2*>(&sKt[(dg * 8 + e) * TSTR + kg * 4]) = column4(kreg[i], e);
-      }
+    for (int t = 0; t < NZ; ++t) {
+      const int e = (t * kThreads + tid) * 8;
+      *reinterpret_cast<u32x4*>(sK0 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sK1 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sV0 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sV1 + e) = u32x4{0u, 0u, 0u, 0u};
     }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ch = tid + i * kThreads;
-      *reinterpret_cast<u32x4*>(&sV[(ch / (D / 8)) * KSTR + (ch % (D / 8)) * 8]) = vreg[i];
-    }
-  };
-
-  auto step = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    __syncthreads();  // every wave is done reading the previous tile
-    swrite();
     __syncthreads();
-    gload(min(j + 1, ntiles - 1));
+  }
 
+  // Per-lane LDS element offsets (tile-invariant). Row reads of K and V: row
+  // c of a 32-row block, logical chunk kd*2 + h. Transposing reads of K:
+  // row h*4 + (c%16)/4 of a 16-row block, column mb*32 + 16*(c/16) +
+  // 4*(c%4); the second read of a fragment (rows +8) lands in block mb ^ HB.
+  int koff[ND], voff[ND], toff[NMB];
+#pragma unroll
+  for (int kd = 0; kd < ND; ++kd) {
+    koff[kd] = c * D + (((kd * 2 + h) ^ swz_both<D>(c)) << 3);
+    voff[kd] = c * D + (((kd * 2 + h) ^ swz_row<D>(c)) << 3);
+  }
+  {
+    const int trow = h * 4 + ((c & 15) >> 2);
+    const int tcol = 16 * (c >> 4) + 4 * (c & 3);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const int col = mb * 32 + tcol;
+      toff[mb] = trow * D + (((col >> 3) ^ swz_both<D>(trow)) << 3) + (col & 7);
+    }
+  }
+
+  // One key tile: S^T = K Q^T and dP^T = V dO^T (keys x queries), then
+  // P^T = exp2(S^T c - L log2 e), dS^T = P^T (dP^T - D) as bf16 B fragments
+  // (chunk (kb, kc) holds keys kb*32 + kc*16 + {h*4 + 0..3, 8 + h*4 + 0..3}),
+  // then dQ^T += K^T dS^T.
+  auto compute = [&](int j, const bf16* sk, const bf16* sv, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int kb0 = j * BC;
-    if (MASK && CAUSAL && kb0 > qw0 + 31) return;  // tile above this wave's diagonal
-
-    // S^T = K Q^T and dP^T = V dO^T (keys x queries).
-    f32x16 sv[NKB], dp[NKB];
+    f32x16 s[NKB], g[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      sv[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      s[kb] = f32x16{};
+      g[kb] = f32x16{};
 #pragma unroll
       for (int kd = 0; kd < ND; ++kd) {
-        const bf16x8 ka = as_bf16x8(ld16(&sK[(kb * 32 + c) * KSTR + kd * 16 + h * 8]));
-        const bf16x8 va = as_bf16x8(ld16(&sV[(kb * 32 + c) * KSTR + kd * 16 + h * 8]));
-        sv[kb] = mma32(ka, qf[kd], sv[kb]);
-        dp[kb] = mma32(va, gf[kd], dp[kb]);
+        s[kb] = mma32(as_bf16x8(ld16(sk + kb * 32 * D + koff[kd])), qf[kd], s[kb]);
+        g[kb] = mma32(as_bf16x8(ld16(sv + kb * 32 * D + voff[kd])), gf[kd], g[kb]);
       }
     }
-    // P^T = exp2(S^T c - L log2 e), dS^T = P^T (dP^T - D), as bf16 B
-    // fragments: chunk (kb, kc) holds keys kb*32 + kc*16 + {h*4 + 0..3,
-    // 8 + h*4 + 0..3}.
     bf16x8 sf[NKB * 2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], cs, -l2));
+        float x = s[kb][r];
         if (MASK) {
           const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
           const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
-          pr = hidden ? 0.f : pr;
+          x = hidden ? kNegInf : x;
         }
-        ds[r] = pr * (dp[kb][r] - dd);
+        const float pr = __builtin_amdgcn_exp2f(fmaf(x, cs, -l2));
+        ds[r] = pr * (g[kb][r] - dd);
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
@@ -196,23 +208,42 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
         sf[kb * 2 + kc] = as_bf16x8(u);
       }
     }
-    // dQ^T (d x queries) += K^T dS^T.
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int kk = 0; kk < NKB * 2; ++kk) {
-        const bf16* row = &sKt[(mb * 32 + c) * TSTR + kk * 16 + h * 4];
-        const u32x2 lo = ld8(row);
-        const u32x2 hi = ld8(row + 8);
+        const u32x2 lo = ds_read_tr16(sk + kk * 16 * D + toff[mb]);
+        const u32x2 hi = ds_read_tr16(sk + (kk * 16 + 8) * D + toff[mb ^ HB]);
         acc[mb] = mma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sf[kk], acc[mb]);
       }
-    }
   };
 
-  if (ntiles > 0) gload(0);
+  // Two LDS stages, one barrier per tile (as in the forward): at the top of
+  // iteration j this wave waits for its own loads of tile j, the barrier
+  // makes every wave's loads visible and guarantees every wave has finished
+  // tile j-1, whose stage is then refilled with tile j+1. Waves wholly below
+  // the causal diagonal of a tile skip it.
+  auto iter = [&](int j, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    wait_global_loads();
+    __syncthreads();
+    if (j + 1 < ntiles) issue(j + 1, nk, nv);
+    if (MASK && CAUSAL && j * BC > qw0 + 31) return;
+    compute(j, sk, sv, mask_tag);
+  };
+
+  if (ntiles > 0) issue(0, sK0, sV0);
   int j = 0;
-  for (; j < j_unmasked; ++j) step(j, std::false_type{});
-  for (; j < ntiles; ++j) step(j, std::true_type{});
+  for (; j + 1 < j_unmasked; j += 2) {
+    iter(j, sK0, sV0, sK1, sV1, std::false_type{});
+    iter(j + 1, sK1, sV1, sK0, sV0, std::false_type{});
+  }
+  for (; j < ntiles; j += 2) {
+    if (j < j_unmasked) iter(j, sK0, sV0, sK1, sV1, std::false_type{});
+    else iter(j, sK0, sV0, sK1, sV1, std::true_type{});
+    if (j + 1 >= ntiles) break;
+    iter(j + 1, sK1, sV1, sK0, sV0, std::true_type{});
+  }
 
   // dQ = scale * (dS K): the scores used Q' = sign(scale) Q with |scale|, the
   // accumulated sum is dS K with the true dS, so the signed scale applies.
@@ -222,11 +253,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gi = 0; gi < 4; ++gi) {
         u32x2 u;
-        u[0] = pack_bf16x2(acc[mb][g * 4 + 0] * sc, acc[mb][g * 4 + 1] * sc);
-        u[1] = pack_bf16x2(acc[mb][g * 4 + 2] * sc, acc[mb][g * 4 + 3] * sc);
-        *reinterpret_cast<u32x2*>(row + mb * 32 + g * 8 + h * 4) = u;
+        u[0] = pack_bf16x2(acc[mb][gi * 4 + 0] * sc, acc[mb][gi * 4 + 1] * sc);
+        u[1] = pack_bf16x2(acc[mb][gi * 4 + 2] * sc, acc[mb][gi * 4 + 3] * sc);
+        *reinterpret_cast<u32x2*>(row + mb * 32 + gi * 8 + h * 4) = u;
       }
   }
 }
@@ -249,7 +280,7 @@ hipError_t launch_bwd_dq_bf16(const Params& p, int d, hipStream_t s) {
   switch (d) {
     case 64: return launch_d<64, 64>(p, s);
     case 128: return launch_d<128, 64>(p, s);
-    case 256: return launch_d<256, 32>(p, s);
+    case 256: return launch_bwd_dq_bf16_staged(p, d, s);
     default: return hipErrorInvalidValue;
   }
 }

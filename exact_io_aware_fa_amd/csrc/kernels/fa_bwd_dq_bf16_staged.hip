@@ -1,0 +1,243 @@
+// Attention backward, dQ part, register-staged variant (used for d = 256).
+//
+// Same method and wave layout as fa_bwd_dq_bf16.hip (page 1, "注意力为什么受限
+// 于显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 八; page 2,
+// "4. FlashAttention 深度剖析", 4.3.4): a workgroup owns 128 query rows (32 per
+// wave), recomputes S^T and dP^T with Q and dO rows held as B operands, and
+// accumulates dQ^T += K^T dS^T in registers. The difference is how key tiles
+// reach LDS: each thread loads 16-byte chunks into registers and writes K
+// row-major and transposed (byte permutes) and V row-major, one tile at a
+// time with two barriers. At d = 256 the dQ accumulator and the Q and dO
+// fragments alone fill the register budget of two waves per SIMD.
+#include <type_traits>
+
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
+
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
+  constexpr int KSTR = D + 8;    // row-major K / V tiles (bf16 elements)
+  constexpr int TSTR = BC + 4;   // transposed K tile [d][key]
+  constexpr int ND = D / 16;
+  constexpr int NMB = D / 32;
+  constexpr int NKB = BC / 32;
+  constexpr int KUN = (BC / 4) * (D / 8);  // K units: 4 keys x 8 dims
+  constexpr int KUPT = (KUN + kThreads - 1) / kThreads;
+  constexpr int VCH = BC * D / 8 / kThreads;  // 16-byte V chunks per thread
+  static_assert(VCH * kThreads * 8 == BC * D, "V tile split");
+  static_assert(KUN % kThreads == 0 || KUN < kThreads, "K unit split");
+
+  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sV[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sKt[D * TSTR];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+  const int n = p.n;
+
+  const int t_r = (n + kBR - 1) / kBR;
+  int bh, qb;
+  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
+  const int b = bh / p.heads;
+  const size_t base = (size_t)bh * (size_t)n * D;
+  const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
+  const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
+  bf16* __restrict__ dQ = static_cast<bf16*>(p.dq) + base;
+
+  const int kv_lim = kv_limit(p, b);
+  const int q0 = qb * kBR;
+  const int qw0 = q0 + w * 32;
+  const int qi = qw0 + c;
+  const int qr = min(qi, n - 1);
+  const float cs = p.c;
+
+  // Q (sign-flipped for a negative scale) and dO rows of this wave as B
+  // fragments [qi][kd*16 + h*8 + e]; rows past n read row n-1 (never stored).
+  bf16x8 qf[ND], gf[ND];
+  {
+    const uint32_t flip = p.q_neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kd = 0; kd < ND; ++kd) {
+      qf[kd] = as_bf16x8(ld16(Q + (size_t)qr * D + kd * 16 + h * 8) ^ flip);
+      gf[kd] = as_bf16x8(ld16(dO + (size_t)qr * D + kd * 16 + h * 8));
+    }
+  }
+  const float l2 = p.l2vec[(size_t)bh * p.n_pad + qr];
+  const float dd = p.dvec[(size_t)bh * p.n_pad + qr];
+
+  int kend = kv_lim;
+  if (CAUSAL) kend = min(kend, q0 + kBR);
+  const int ntiles = (kend + BC - 1) / BC;
+  int j_unmasked = kv_lim / BC;
+  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
+  j_unmasked = min(j_unmasked, ntiles);
+
+  f32x16 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+
+  u32x4 kreg[KUPT][4];
+  u32x4 vreg[VCH];
+
+  // Key rows at or past the key limit are read clamped to the last visible
+  // row; their probabilities are masked to exactly 0.
+  auto gload = [&](int j) {
+    const int kb0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < KUPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (KUN % kThreads == 0 || u < KUN) {
+        const int kg = (u >> 2) % (BC / 4);
+        const int dg = (u & 3) + 4 * (u / BC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          kreg[i][r] = ld16(K + (size_t)min(kb0 + kg * 4 + r, kv_lim - 1) * D + dg * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int ch = tid + i * kThreads;
+      const int key = min(kb0 + ch / (D / 8), kv_lim - 1);
+      vreg[i] = ld16(V + (size_t)key * D + (ch % (D / 8)) * 8);
+    }
+  };
+
+  auto swrite = [&]() {
+#pragma unroll
+    for (int i = 0; i < KUPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (KUN % kThreads == 0 || u < KUN) {
+        const int kg = (u >> 2) % (BC / 4);
+        const int dg = (u & 3) + 4 * (u / BC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<u32x4*>(&sK[(kg * 4 + r) * KSTR + dg * 8]) = kreg[i][r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<u32x2*>(&sKt[(dg * 8 + e) * TSTR + kg * 4]) = column4(kreg[i], e);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int ch = tid + i * kThreads;
+      *reinterpret_cast<u32x4*>(&sV[(ch / (D / 8)) * KSTR + (ch % (D / 8)) * 8]) = vreg[i];
+    }
+  };
+
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    __syncthreads();  // every wave is done reading the previous tile
+    swrite();
+    __syncthreads();
+    gload(min(j + 1, ntiles - 1));
+
+    const int kb0 = j * BC;
+    if (MASK && CAUSAL && kb0 > qw0 + 31) return;  // tile above this wave's diagonal
+
+    // S^T = K Q^T and dP^T = V dO^T (keys x queries).
+    f32x16 sv[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sv[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int kd = 0; kd < ND; ++kd) {
+        const bf16x8 ka = as_bf16x8(ld16(&sK[(kb * 32 + c) * KSTR + kd * 16 + h * 8]));
+        const bf16x8 va = as_bf16x8(ld16(&sV[(kb * 32 + c) * KSTR + kd * 16 + h * 8]));
+        sv[kb] = mma32(ka, qf[kd], sv[kb]);
+        dp[kb] = mma32(va, gf[kd], dp[kb]);
+      }
+    }
+    // P^T = exp2(S^T c - L log2 e), dS^T = P^T (dP^T - D), as bf16 B
+    // fragments: chunk (kb, kc) holds keys kb*32 + kc*16 + {h*4 + 0..3,
+    // 8 + h*4 + 0..3}.
+    bf16x8 sf[NKB * 2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], cs, -l2));
+        if (MASK) {
+          const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+          pr = hidden ? 0.f : pr;
+        }
+        ds[r] = pr * (dp[kb][r] - dd);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        u32x4 u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) u[t] = pack_bf16x2(ds[kc * 8 + 2 * t], ds[kc * 8 + 2 * t + 1]);
+        sf[kb * 2 + kc] = as_bf16x8(u);
+      }
+    }
+    // dQ^T (d x queries) += K^T dS^T.
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int kk = 0; kk < NKB * 2; ++kk) {
+        const bf16* row = &sKt[(mb * 32 + c) * TSTR + kk * 16 + h * 4];
+        const u32x2 lo = ld8(row);
+        const u32x2 hi = ld8(row + 8);
+        acc[mb] = mma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sf[kk], acc[mb]);
+      }
+    }
+  };
+
+  if (ntiles > 0) gload(0);
+  int j = 0;
+  for (; j < j_unmasked; ++j) step(j, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{});
+
+  // dQ = scale * (dS K): the scores used Q' = sign(scale) Q with |scale|, the
+  // accumulated sum is dS K with the true dS, so the signed scale applies.
+  if (qi < n) {
+    const float sc = p.scale;
+    bf16* row = dQ + (size_t)qi * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 u;
+        u[0] = pack_bf16x2(acc[mb][g * 4 + 0] * sc, acc[mb][g * 4 + 1] * sc);
+        u[1] = pack_bf16x2(acc[mb][g * 4 + 2] * sc, acc[mb][g * 4 + 3] * sc);
+        *reinterpret_cast<u32x2*>(row + mb * 32 + g * 8 + h * 4) = u;
+      }
+  }
+}
+
+template <int D, int BC>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  const int t_r = (p.n + kBR - 1) / kBR;
+  const long long total = (long long)t_r * p.batch * p.heads;
+  dim3 grid((unsigned)total), block(kThreads);
+  if (p.causal)
+    hipLaunchKernelGGL((bwd_dq_staged_kernel<D, BC, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_staged_kernel<D, BC, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_bf16_staged(const Params& p, int d, hipStream_t s) {
+  switch (d) {
+    case 256: return launch_d<256, 32>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa
