@@ -17,6 +17,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// For lambdas inside kernels: a call that is not inlined would pass the
+// captured state through memory, which costs registers, scratch traffic and
+// the knowledge that values are wave-uniform.
+#define FA_INLINE __attribute__((always_inline))
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;

@@ -1,4 +1,5 @@
-// Fused attention forward, bf16 in/out, fp32 accumulate, for gfx950.
+// Fused attention forward, bf16 in/out, fp32 accumulate, for gfx950
+// (d = 128; d = 64 uses fa_fwd_bf16_d64.hip, d = 256 fa_fwd_bf16_staged.hip).
 //
 // Method: the tiled forward of page 2 ("4. FlashAttention 深度剖析", 4.3.2)
 // with the per-block (m, l, O) update of page 1 ("注意力为什么受限于显存带宽：
@@ -9,9 +10,9 @@
 // "深入浅出 FlashAttention" 第八部分).
 //
 // Mapping onto CDNA4:
-// * A workgroup is 4 wave64s and owns BR = 128 query rows; each wave owns 32
-//   of them for the whole key sweep (split over queries, so no cross-wave
-//   reduction of m or l is ever needed).
+// * A workgroup is 8 wave64s (two per SIMD) and owns BR = 256 query rows;
+//   each wave owns 32 of them for the whole key sweep (split over queries,
+//   so no cross-wave reduction of m or l is ever needed).
 // * Each wave keeps its Q rows in VGPRs as the B operand of the 32x32x16
 //   bf16 MFMA and computes S^T = K Q^T, so a lane owns one query row and 16
 //   keys of every 32-key block: the row max and row sum are in-lane, plus one
@@ -19,12 +20,20 @@
 //   combined once at the end).
 // * The probabilities, rounded to bf16, are already laid out as the B
 //   operand of O^T += V^T P^T, so P never leaves registers.
-// * K and V tiles go from HBM straight into LDS (16 bytes per lane, no
-//   staging registers), row-major with an XOR swizzle of the 16-byte chunks,
-//   in two stages: tile j+1 streams in while tile j is used, one barrier per
-//   tile. K is read row-wise (A operand of K Q^T); V is read with the
-//   transposing LDS read, which yields the V^T operand directly. Both access
-//   patterns hit every LDS bank once per 256 bytes.
+// * Ping-pong between the two waves of a SIMD: waves 0-3 (group A) and 4-7
+//   (group B) alternate half-periods separated by workgroup barriers. In
+//   each half-period one group runs its matrix phase (S of tile m and
+//   O += P V of tile m-1) while the other runs its softmax phase (row max,
+//   exp2, row sum, rescale and packing of tile m-1 or m). A wave issues
+//   little vector work next to its own matrix products, but the other wave
+//   on the SIMD can, so the two phases overlap on every SIMD.
+// * K and V tiles go from HBM straight into LDS through buffer descriptors
+//   whose size ends at the key limit (rows past it are never read),
+//   row-major with an XOR swizzle of the 16-byte chunks, two stages each:
+//   K of tile m+1 and V of tile m stream in during tile m's half-periods.
+//   K is read row-wise (A operand of K Q^T); V is read with the transposing
+//   LDS read, which yields the V^T operand directly. Both access patterns
+//   hit every LDS bank once per 256 bytes.
 // * exp2 with the log2(e) factor folded into the score scale; the max-shift
 //   and scale are one FMA per score.
 #include <type_traits>
@@ -35,8 +44,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int kThreads = 512;
+constexpr int kBR = 256;  // query rows per workgroup (8 waves x 32)
 
 // Exchange with the other 32-lane half of the wave (v_permlane32_swap): the
 // two results hold the value of lane l % 32 and of lane l % 32 + 32 in some
@@ -52,17 +61,18 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, int MINW, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;           // bytes per row
   constexpr int TILEB = BC * ROWB;      // bytes per K or V tile
-  constexpr int LPW = TILEB / 1024 / 4; // 1 KB wave loads per tensor per wave
+  constexpr int NW = kThreads / 64;     // waves per workgroup
+  constexpr int LPW = TILEB / 1024 / NW;  // 1 KB wave loads per tensor per wave
   constexpr int RPL = 1024 / ROWB;      // rows per 1 KB load
   constexpr int ND = D / 16;            // reduction steps of S^T = K Q^T
   constexpr int NMB = D / 32;           // 32-row blocks of O^T
   constexpr int NKB = BC / 32;          // 32-key blocks of S^T
-  static_assert(LPW * 4 * 1024 == TILEB && RPL >= 1, "tile split");
+  static_assert(LPW * NW * 1024 == TILEB && RPL >= 1, "tile split");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(1024))) bf16 sK0[BC * D];
@@ -72,6 +82,7 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2;  // 0: group A, 1: group B
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
@@ -109,26 +120,28 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
   int kend = kv_lim;
   if (CAUSAL) kend = min(kend, q0 + kBR);
   const int ntiles = (kend + BC - 1) / BC;
-  // Tiles [0, j_unmasked) have every key visible to every query of the
-  // workgroup: wholly below the key limit and, if causal, at or below the
-  // workgroup's first query. The rest go through the masked path.
-  int j_unmasked = kv_lim / BC;
-  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
-  j_unmasked = min(j_unmasked, ntiles);
+  // This wave's tiles: [0, jlast]; tiles [0, junm) have every key visible to
+  // every query of the wave (below the key limit and, if causal, at or below
+  // the wave's first query), the rest are masked.
+  int jlast = ntiles - 1;
+  if (CAUSAL) jlast = min(jlast, (qw0 + 31) / BC);
+  int junm = kv_lim / BC;
+  if (CAUSAL) junm = min(junm, (qw0 + 1) / BC);
 
   f32x16 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
   float m2 = kNegInf;   // running max in scaled base-2 units (s * cs)
   float lpart = 0.f;    // this half-wave's share of the running row sum
+  f32x16 sc[NKB];       // scores of the tile between the two phases
+  bf16x8 pf[NKB * 2];   // P^T fragments of the tile between the two phases
 
   // Loads of a key (or value) tile into LDS. Wave w fills rows
   // [w * LPW * RPL, (w + 1) * LPW * RPL); lane l of a 1 KB load writes
   // physical chunk l % CH of row l / CH, which holds logical chunk
-  // (l % CH) ^ swizzle(row). The loads go through a buffer descriptor whose
-  // base is the tile's first row and whose size stops at the key limit, so
-  // the per-lane byte offsets are tile-invariant and rows at or past the key
-  // limit are never read (their scores are masked, they contribute 0).
+  // (l % CH) ^ swizzle(row). The descriptor's base is the tile's first row
+  // and its size ends at the key limit, so the per-lane byte offsets are
+  // tile-invariant and rows at or past the limit are never read.
   int ld_koff[LPW], ld_voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
@@ -136,24 +149,25 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
     ld_koff[i] = (row * D + ((lane % CH) ^ swz_row<D>(row)) * 8) * 2;
     ld_voff[i] = (row * D + ((lane % CH) ^ swz_tr<D>(row)) * 8) * 2;
   }
-  auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) {
+  auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) FA_INLINE {
     const int kb0 = j * BC;
     const auto r = buffer_rsrc(src + (size_t)kb0 * D, min(kv_lim - kb0, BC) * ROWB);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) bload_lds16(r, off[i], dst + (w * LPW + i) * RPL * D);
   };
   // Out-of-range lanes of a partial tile may leave their LDS bytes as they
-  // were, so both stages start as zeros: whatever a masked row holds is then
+  // were, so all stages start as zeros: whatever a masked row holds is then
   // finite and its zero probability contributes exactly 0.
   {
-    constexpr int NZ = 4 * TILEB / 16 / kThreads;
-    static_assert(NZ * 16 * kThreads == 4 * TILEB, "zero fill");
+    constexpr int NZ = TILEB / 16 / kThreads;
+    static_assert(NZ * 16 * kThreads == TILEB, "zero fill");
 #pragma unroll
     for (int t = 0; t < NZ; ++t) {
-      const int idx = t * kThreads + tid;   // 16-byte chunk of the four tiles
-      const int which = idx / (TILEB / 16);
-      bf16* base = which == 0 ? sK0 : which == 1 ? sK1 : which == 2 ? sV0 : sV1;
-      *reinterpret_cast<u32x4*>(base + (idx % (TILEB / 16)) * 8) = u32x4{0u, 0u, 0u, 0u};
+      const int e = (t * kThreads + tid) * 8;
+      *reinterpret_cast<u32x4*>(sK0 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sK1 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sV0 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sV1 + e) = u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
   }
@@ -175,21 +189,64 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
     }
   }
 
-  // S^T (keys x queries) = K Q^T for the tile in sk, raw dot products.
-  auto scores = [&](const bf16* sk, f32x16 (&s)[NKB]) {
+  // Matrix phase of step m: O^T += V^T P^T of tile m-1 (V in sv, P^T in
+  // pf) and S^T of tile m (K in sk) into sc, as a fixed sequence of product
+  // slots: the O^T slots first (four independent accumulators in turn), then
+  // the S^T slots. Each slot's A fragment is read PF slots ahead (a ring of
+  // PF + 1), and the sched_barrier fences keep the compiler from hoisting
+  // every read to the top of the phase, which would exhaust the registers.
+  constexpr int NPV = NMB * NKB * 2;  // O^T slots
+  constexpr int PF = 6;               // read-ahead distance in slots
+  constexpr int NS = NKB * ND;        // S^T slots
+  auto rd_pv = [&](const bf16* sv, int k) FA_INLINE {
+    const int mb = k % NMB, kk = k / NMB;
+    const u32x2 lo = ds_read_tr16(sv + kk * 16 * D + voff[mb]);
+    const u32x2 hi = ds_read_tr16(sv + (kk * 16 + 8) * D + voff[mb]);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  auto rd_s = [&](const bf16* sk, int k) FA_INLINE {
+    const int kb = k % NKB, kd = k / NKB;
+    return as_bf16x8(ld16(sk + kb * 32 * D + koff[kd]));
+  };
+  auto slots = [&](const bf16* sk, const bf16* sv, auto pv_tag, auto s_tag) FA_INLINE {
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool SS = decltype(s_tag)::value;
+    constexpr int K0 = PV ? 0 : NPV;           // first slot
+    constexpr int K1 = SS ? NPV + NS : NPV;    // one past the last slot
+    auto rd = [&](int k) FA_INLINE { return k < NPV ? rd_pv(sv, k) : rd_s(sk, k - NPV); };
+    if (SS) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
+      for (int kb = 0; kb < NKB; ++kb) sc[kb] = f32x16{};
+    }
+    bf16x8 fr[PF + 1];
 #pragma unroll
-      for (int kd = 0; kd < ND; ++kd) {
-        const bf16x8 a = as_bf16x8(ld16(sk + kb * 32 * D + koff[kd]));
-        s[kb] = mma32(a, qf[kd], s[kb]);
+    for (int k = K0; k < K0 + PF && k < K1; ++k) fr[k % (PF + 1)] = rd(k);
+#pragma unroll
+    for (int k = K0; k < K1; ++k) {
+      if (k + PF < K1) fr[(k + PF) % (PF + 1)] = rd(k + PF);
+      if (k < NPV) {
+        const int mb = k % NMB, kk = k / NMB;
+        acc[mb] = mma32(fr[k % (PF + 1)], pf[kk], acc[mb]);
+      } else {
+        const int kb = (k - NPV) % NKB, kd = (k - NPV) / NKB;
+        sc[kb] = mma32(fr[k % (PF + 1)], qf[kd], sc[kb]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto mfma_phase = [&](int m, const bf16* sk, const bf16* sv) FA_INLINE {
+    const bool pv = m >= 1 && m - 1 <= jlast;
+    const bool ss = m < ntiles && m <= jlast;
+    if (pv && ss) slots(sk, sv, std::true_type{}, std::true_type{});
+    else if (pv) slots(sk, sv, std::true_type{}, std::false_type{});
+    else if (ss) slots(sk, sv, std::false_type{}, std::true_type{});
+  };
 
-  // Online-softmax update with the scores of tile j, then O^T += V^T P^T.
-  auto softmax_pv = [&](int j, f32x16 (&s)[NKB], const bf16* sv, auto mask_tag) {
+  // Softmax phase of tile j: online update of (m, l) with the scores in sc,
+  // rescale of O~ (skipped, wave-uniformly, when no row max changed), and
+  // P^T as bf16 B fragments in pf (chunk kk holds keys kk*16 + {h*4 + 0..3,
+  // 8 + h*4 + 0..3}).
+  auto softmax = [&](int j, auto mask_tag) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kb0 = j * BC;
     if (MASK) {
@@ -199,7 +256,7 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
         for (int r = 0; r < 16; ++r) {
           const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
           const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
-          s[kb][r] = hidden ? kNegInf : s[kb][r];
+          sc[kb][r] = hidden ? kNegInf : sc[kb][r];
         }
     }
     // Row max and row sum use four independent partial results each, so the
@@ -208,11 +265,10 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kb][r]);
+      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sc[kb][r]);
     const float mt = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
     // The reference is the exact running max, so the row's largest
-    // probability is exactly 1 before its bf16 rounding. The rescale of O~
-    // is skipped (wave-uniform branch) when no row's max changed.
+    // probability is exactly 1 before its bf16 rounding.
     const float mt2 = (mt == kNegInf) ? kNegInf : mt * cs;
     const float m2n = fmaxf(m2, mt2);
     const float mref = (m2n == kNegInf) ? 0.f : m2n;
@@ -224,8 +280,8 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cs, -mref));
-        s[kb][r] = e;
+        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], cs, -mref));
+        sc[kb][r] = e;
         rp[r & 3] += e;
       }
     lpart = fmaf(lpart, alpha, (rp[0] + rp[1]) + (rp[2] + rp[3]));
@@ -233,10 +289,6 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
     }
-
-    // P^T as bf16 B fragments: chunk kk holds keys kk*16 + {h*4 + 0..3,
-    // 8 + h*4 + 0..3}.
-    bf16x8 pf[NKB * 2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -244,58 +296,108 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
         u32x4 u;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          u[t] = pack_bf16x2(s[kb][kc * 8 + 2 * t], s[kb][kc * 8 + 2 * t + 1]);
+          u[t] = pack_bf16x2(sc[kb][kc * 8 + 2 * t], sc[kb][kc * 8 + 2 * t + 1]);
         pf[kb * 2 + kc] = as_bf16x8(u);
       }
-
-    // O^T (d x queries) += V^T P^T; the V^T fragment of (mb, kk) is two
-    // transposing reads: keys kk*16 + h*4 + 0..3 and kk*16 + 8 + h*4 + 0..3
-    // of column mb*32 + c.
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int kk = 0; kk < NKB * 2; ++kk) {
-        const u32x2 lo = ds_read_tr16(sv + kk * 16 * D + voff[mb]);
-        const u32x2 hi = ds_read_tr16(sv + (kk * 16 + 8) * D + voff[mb]);
-        acc[mb] = mma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[kk], acc[mb]);
-      }
+  };
+  auto valu_phase = [&](int j) FA_INLINE {
+    if (j < 0 || j >= ntiles || j > jlast) return;
+    if (j < junm) softmax(j, std::false_type{});
+    else softmax(j, std::true_type{});
   };
 
-  // Two LDS stages: at the top of iteration j this wave waits for its own
-  // loads of tile j, then the barrier makes every wave's loads of tile j
-  // visible and guarantees every wave has finished tile j-1, whose stage is
-  // refilled with tile j+1 right after. Waves above the causal diagonal of a
-  // tile skip it.
-  auto iter = [&](int j, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    wait_global_loads();
+  // Step m covers two half-periods, each opening with a workgroup barrier.
+  // At the first, K of tile m (stage m % 2) and V of tile m-1 (the other
+  // stage) are resident; the loads of K of tile m+1 and V of tile m go into
+  // the stages those tiles' predecessors held (last read in the previous
+  // step's half-periods, which every wave has finished at this barrier).
+  // Each wave waits for its own loads of a step before the next step's
+  // first barrier. Group A: matrix phase m, then softmax phase m; group B:
+  // softmax phase m-1, then matrix phase m. Each group runs its own loop;
+  // both pass the same number of barriers.
+  // Workgroup barriers that no instruction is scheduled across (the
+  // compiler may otherwise move register-only work, such as softmax
+  // arithmetic, over them into the other phase, which would undo the
+  // ping-pong). The step-opening barrier is a full __syncthreads (it
+  // publishes the tile loads each wave has waited for); the one between the
+  // two phases of a step orders no memory, so it is a bare s_barrier and does
+  // not wait for the loads still in flight.
+  auto phase_barrier = [&]() FA_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    if (j + 1 < ntiles) {
-      issue(K, ld_koff, j + 1, nk);
-      issue(V, ld_voff, j + 1, nv);
-    }
-    if (MASK && CAUSAL && j * BC > qw0 + 31) return;
-    f32x16 sc[NKB];
-    scores(sk, sc);
-    softmax_pv(j, sc, sv, mask_tag);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mid_barrier = [&]() FA_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto open_step = [&](int m, bf16* nk, bf16* nv) FA_INLINE {
+    if (m > 0) wait_global_loads();
+    phase_barrier();
+    if (m + 1 < ntiles) issue(K, ld_koff, m + 1, nk);
+    if (m < ntiles) issue(V, ld_voff, m, nv);
+  };
+  auto step_a = [&](int m, const bf16* sk, bf16* nk, bf16* nv, const bf16* sv) FA_INLINE {
+    open_step(m, nk, nv);
+    mfma_phase(m, sk, sv);
+    mid_barrier();
+    valu_phase(m);
+  };
+  auto step_b = [&](int m, const bf16* sk, bf16* nk, bf16* nv, const bf16* sv) FA_INLINE {
+    open_step(m, nk, nv);
+    valu_phase(m - 1);
+    mid_barrier();
+    mfma_phase(m, sk, sv);
+  };
+  // The same steps when both products run and the softmax is unmasked: one
+  // straight path, so the accumulators never cross a control-flow merge
+  // (which would cost register copies of all of them).
+  auto hot_a = [&](int m, const bf16* sk, bf16* nk, bf16* nv, const bf16* sv) FA_INLINE {
+    open_step(m, nk, nv);
+    slots(sk, sv, std::true_type{}, std::true_type{});
+    mid_barrier();
+    softmax(m, std::false_type{});
+  };
+  auto hot_b = [&](int m, const bf16* sk, bf16* nk, bf16* nv, const bf16* sv) FA_INLINE {
+    open_step(m, nk, nv);
+    softmax(m - 1, std::false_type{});
+    mid_barrier();
+    slots(sk, sv, std::true_type{}, std::true_type{});
   };
 
-  if (ntiles > 0) {
-    issue(K, ld_koff, 0, sK0);
-    issue(V, ld_voff, 0, sV0);
-  }
-  // Pairs of unmasked tiles (even tiles use stage 0, odd tiles stage 1),
-  // then the remaining tiles: at most one unmasked, the rest masked.
-  int j = 0;
-  for (; j + 1 < j_unmasked; j += 2) {
-    iter(j, sK0, sV0, sK1, sV1, std::false_type{});
-    iter(j + 1, sK1, sV1, sK0, sV0, std::false_type{});
-  }
-  for (; j < ntiles; j += 2) {
-    if (j < j_unmasked) iter(j, sK0, sV0, sK1, sV1, std::false_type{});
-    else iter(j, sK0, sV0, sK1, sV1, std::true_type{});
-    if (j + 1 >= ntiles) break;
-    iter(j + 1, sK1, sV1, sK0, sV0, std::true_type{});
+  // Steps [1, hot_end) are hot for this wave: tile m exists and is this
+  // wave's (S^T of tile m), and the softmax tile (m for group A, m-1 for
+  // group B) is unmasked. Step 0 and the steps from the first non-hot one
+  // on take the general path. The hot loop runs pairs of steps starting at
+  // an odd step, so every loop keeps a fixed stage assignment.
+  const int hot_end = min(min(ntiles, jlast + 1), grp == 0 ? junm : junm + 1);
+  if (ntiles > 0) issue(K, ld_koff, 0, sK0);
+  wait_global_loads();
+  if (grp == 0) {
+    step_a(0, sK0, sK1, sV0, sV1);
+    int m = 1;
+    for (; m + 1 < hot_end; m += 2) {
+      hot_a(m, sK1, sK0, sV1, sV0);
+      hot_a(m + 1, sK0, sK1, sV0, sV1);
+    }
+    for (; m <= ntiles; m += 2) {
+      step_a(m, sK1, sK0, sV1, sV0);
+      if (m + 1 > ntiles) break;
+      step_a(m + 1, sK0, sK1, sV0, sV1);
+    }
+  } else {
+    step_b(0, sK0, sK1, sV0, sV1);
+    int m = 1;
+    for (; m + 1 < hot_end; m += 2) {
+      hot_b(m, sK1, sK0, sV1, sV0);
+      hot_b(m + 1, sK0, sK1, sV0, sV1);
+    }
+    for (; m <= ntiles; m += 2) {
+      step_b(m, sK1, sK0, sV1, sV0);
+      if (m + 1 > ntiles) break;
+      step_b(m + 1, sK0, sK1, sV0, sV1);
+    }
   }
 
   // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
@@ -317,15 +419,15 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_kernel(Params p) {
   }
 }
 
-template <int D, int BC, int MINW>
+template <int D, int BC>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
   if (p.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, MINW, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, MINW, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -333,8 +435,8 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s) {
   switch (d) {
-    case 64: return launch_d<64, 64, 2>(p, s);
-    case 128: return launch_d<128, 64, 2>(p, s);
+    case 64: return launch_fwd_bf16_d64(p, d, s);
+    case 128: return launch_d<128, 64>(p, s);
     case 256: return launch_fwd_bf16_staged(p, d, s);
     default: return hipErrorInvalidValue;
   }
