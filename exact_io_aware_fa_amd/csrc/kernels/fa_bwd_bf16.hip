@@ -33,6 +33,8 @@
 //   dS, then accumulates dV and dK of tile i. With one wave per SIMD (the
 //   accumulators and K/V fragments need more than half the register file)
 //   the overlap has to come from within the wave.
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
     const auto rg = buffer_rsrc(dO, n * ROWB);
     const auto rl = buffer_rsrc(l2v, p.n_pad * 4);
     const auto rd = buffer_rsrc(dvec, p.n_pad * 4);
-    auto issue = [&](int it, bf16* sm, float* sv) {
+    auto issue = [&](int it, bf16* sm, float* sv) FA_INLINE {
       const int qb0 = it * BQ * ROWB;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
     // S = Q K^T and dP = dO V^T of the tile in stage sm (lane = key, 16
     // queries per 32-query block); used once, before the loop.
-    auto sdp = [&](const bf16* sm, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) {
+    auto sdp = [&](const bf16* sm, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) FA_INLINE {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         s[qb] = f32x16{};
@@ -213,10 +215,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
     // (qb, gi, i) is q0 + 4h + (qb*32 + gi*8 + i); the pair is hidden iff
     // that offset is < lo or >= hi, and a hidden pair gets P = 0, dS = 0.
     auto pds1 = [&](int e, int lo, int hi, const f32x4 (&l4)[NQB][4], const f32x4 (&d4)[NQB][4],
-                    f32x16 (&s)[NQB], f32x16 (&g)[NQB]) {
+                    f32x16 (&s)[NQB], f32x16 (&g)[NQB], auto mask_tag) FA_INLINE {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int qb = e / 16, r = e % 16, gi = r / 4, i = r % 4;
       const int off = qb * 32 + gi * 8 + i;
-      const float x = (off < lo || off >= hi) ? kNegInf : s[qb][r];
+      const float x = (MASK && (off < lo || off >= hi)) ? kNegInf : s[qb][r];
       const float pr = __builtin_amdgcn_exp2f(fmaf(x, cs, -l4[qb][gi][i]));
       s[qb][r] = pr;
       g[qb][r] = pr * (g[qb][r] - d4[qb][gi][i]);
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
     // A fragments of the transposing reads for (qb, qc, mb): dO^T and Q^T of
     // 16 queries x 32 dims of the tile in sm.
-    auto trfrag = [&](const bf16* sm, int qb, int qc, int mb, bf16x8& fo, bf16x8& fq) {
+    auto trfrag = [&](const bf16* sm, int qb, int qc, int mb, bf16x8& fo, bf16x8& fq) FA_INLINE {
       const int r0 = (qb * 32 + qc * 16) * D;
       const int r1 = r0 + 8 * D;
       const u32x2 olo = ds_read_tr16(sm + TILE + r0 + toff[mb]);
@@ -245,7 +248,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
     constexpr int EPS = 16 / ND;        // P/dS values per phase-1 slot
     constexpr int NP = NQB * 2 * NMB;   // phase-2 slots (2 products each)
     f32x16 s[NQB], g[NQB];
-    auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB, bool next) {
+    auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB, bool next,
+                    auto mask_tag) FA_INLINE {
       const int qh = it * BQ + h * 4;
       const int lo = qlo - qh;
       const int hi = n - qh;
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
           }
         }
 #pragma unroll
-        for (int e = j * EPS; e < (j + 1) * EPS; ++e) pds1(e, lo, hi, l4, d4, s, g);
+        for (int e = j * EPS; e < (j + 1) * EPS; ++e) pds1(e, lo, hi, l4, d4, s, g, mask_tag);
         __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8 fo[2], fq[2];
@@ -326,13 +330,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
     // waits for its own loads of tile it+1; the barrier then makes every
     // wave's loads visible and guarantees that every wave has finished the
     // previous iteration, the last reader of stage C (tile it-1).
-    auto step = [&](int it, bf16* mA, float* vA, bf16* mB, bf16* mC, float* vC) {
+    auto step = [&](int it, bf16* mA, float* vA, bf16* mB, bf16* mC, float* vC,
+                    auto mask_tag) FA_INLINE {
       wait_global_loads();
       __syncthreads();
       if (it + 2 < n_qt) issue(it + 2, mC, vC);
-      body(it, mA, vA, mB, true);
+      body(it, mA, vA, mB, true, mask_tag);
     };
-    auto finish = [&](int it, bf16* mA, float* vA) { body(it, mA, vA, nullptr, false); };
+    auto finish = [&](int it, bf16* mA, float* vA) FA_INLINE {
+      body(it, mA, vA, nullptr, false, std::true_type{});
+    };
+
+    // Masked steps: the causal diagonal band (the first kBKV / BQ tiles of
+    // the sweep, rounded up to a multiple of three so the unmasked loop
+    // starts with the same stage rotation), every step when the workgroup
+    // straddles the key limit, and the last tile (always masked: it may be
+    // partial). The unmasked steps skip the mask arithmetic.
+    constexpr int HEAD = (kBKV / BQ + 2) / 3 * 3;
+    const int last = n_qt - 1;
+    const bool straddle = k0 + kBKV > kv_lim;
+    const int head = straddle ? last : (CAUSAL ? min(it0 + HEAD, last) : it0);
 
     issue(it0, sm0, sv0);
     if (it0 + 1 < n_qt) issue(it0 + 1, sm1, sv1);
@@ -340,21 +357,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
     __syncthreads();
     sdp(sm0, s, g);
     int it = it0;
-    const int last = n_qt - 1;
+    for (; it + 3 <= head; it += 3) {
+      step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
+      step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
+      step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
+    }
+    // Here either it == head with (it - it0) % 3 == 0, or head == last and
+    // fewer than three steps remain before it, so the unmasked loop below
+    // does not run.
     for (; it + 3 <= last; it += 3) {
-      step(it, sm0, sv0, sm1, sm2, sv2);
-      step(it + 1, sm1, sv1, sm2, sm0, sv0);
-      step(it + 2, sm2, sv2, sm0, sm1, sv1);
+      step(it, sm0, sv0, sm1, sm2, sv2, std::false_type{});
+      step(it + 1, sm1, sv1, sm2, sm0, sv0, std::false_type{});
+      step(it + 2, sm2, sv2, sm0, sm1, sv1, std::false_type{});
     }
     // last - it is 0, 1 or 2 here; the last tile has no successor.
     if (it == last) {
       finish(it, sm0, sv0);
     } else {
-      step(it, sm0, sv0, sm1, sm2, sv2);
+      step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
       if (it + 1 == last) {
         finish(it + 1, sm1, sv1);
       } else {
-        step(it + 1, sm1, sv1, sm2, sm0, sv0);
+        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
         finish(it + 2, sm2, sv2);
       }
     }
