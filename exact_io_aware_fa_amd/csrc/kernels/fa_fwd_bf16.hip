@@ -100,7 +100,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
 
   const int kv_lim = kv_limit(p, b);
   const int q0 = qb * kBR;
-  const int qw0 = q0 + w * 32;
+  // Rows of wave w: the two waves of a SIMD (w and w + 4) take neighbouring
+  // 32-row blocks, so both groups span the workgroup's 256 rows and reach
+  // the causal diagonal at about the same step.
+  const int qw0 = q0 + 32 * (2 * (w & 3) + grp);
   const int qi = qw0 + c;
   const float cs = p.c;
 
@@ -135,6 +138,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   float lpart = 0.f;    // this half-wave's share of the running row sum
   f32x16 sc[NKB];       // scores of the tile between the two phases
   bf16x8 pf[NKB * 2];   // P^T fragments of the tile between the two phases
+#pragma unroll
+  for (int kk = 0; kk < NKB * 2; ++kk) pf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 
   // Loads of a key (or value) tile into LDS. Wave w fills rows
   // [w * LPW * RPL, (w + 1) * LPW * RPL); lane l of a 1 KB load writes
@@ -234,31 +239,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // The matrix phase always runs both products: at step 0 and after a
+  // skipped tile P^T is zero (and the V stage holds finite data), so O~ is
+  // unchanged; scores computed for a tile this wave will not use are
+  // discarded.
   auto mfma_phase = [&](int m, const bf16* sk, const bf16* sv) FA_INLINE {
-    const bool pv = m >= 1 && m - 1 <= jlast;
-    const bool ss = m < ntiles && m <= jlast;
-    if (pv && ss) slots(sk, sv, std::true_type{}, std::true_type{});
-    else if (pv) slots(sk, sv, std::true_type{}, std::false_type{});
-    else if (ss) slots(sk, sv, std::false_type{}, std::true_type{});
+    (void)m;
+    slots(sk, sv, std::true_type{}, std::true_type{});
   };
 
   // Softmax phase of tile j: online update of (m, l) with the scores in sc,
   // rescale of O~ (skipped, wave-uniformly, when no row max changed), and
   // P^T as bf16 B fragments in pf (chunk kk holds keys kk*16 + {h*4 + 0..3,
   // 8 + h*4 + 0..3}).
-  auto softmax = [&](int j, auto mask_tag) FA_INLINE {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto apply_mask = [&](int j) FA_INLINE {
     const int kb0 = j * BC;
-    if (MASK) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
-          sc[kb][r] = hidden ? kNegInf : sc[kb][r];
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+        sc[kb][r] = hidden ? kNegInf : sc[kb][r];
+      }
+  };
+  auto softmax = [&](int j) FA_INLINE {
     // Row max and row sum use four independent partial results each, so the
     // dependent-instruction chains are a quarter as long.
     float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
@@ -300,10 +305,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
         pf[kb * 2 + kc] = as_bf16x8(u);
       }
   };
+  // General softmax phase of tile j: tiles this wave does not own (before
+  // the first, past its causal diagonal or the last) leave P^T zero, so the
+  // next matrix phase, which always runs both products, adds exactly 0.
+  // Masking only edits the scores ahead of the common softmax body.
   auto valu_phase = [&](int j) FA_INLINE {
-    if (j < 0 || j >= ntiles || j > jlast) return;
-    if (j < junm) softmax(j, std::false_type{});
-    else softmax(j, std::true_type{});
+    if (j >= 0 && j < ntiles && j <= jlast) {
+      if (j >= junm) apply_mask(j);
+      softmax(j);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKB * 2; ++kk) pf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
   };
 
   // Step m covers two half-periods, each opening with a workgroup barrier.
@@ -357,11 +370,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     open_step(m, nk, nv);
     slots(sk, sv, std::true_type{}, std::true_type{});
     mid_barrier();
-    softmax(m, std::false_type{});
+    softmax(m);
   };
   auto hot_b = [&](int m, const bf16* sk, bf16* nk, bf16* nv, const bf16* sv) FA_INLINE {
     open_step(m, nk, nv);
-    softmax(m - 1, std::false_type{});
+    softmax(m - 1);
     mid_barrier();
     slots(sk, sv, std::true_type{}, std::true_type{});
   };
