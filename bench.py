@@ -27,6 +27,17 @@ null.
 ``cpu_baseline`` times the fp64 CPU oracle (materialised S and P, NumPy/BLAS)
 on a bounded sample of the same workload -- whole heads, fwd+bwd, until about
 10 s of CPU work -- and scales it to the same TFLOP/s convention.
+
+    python bench.py --sweep [--out FILE]
+
+times fa_fwd and fa_bwd separately on every parity workload with a backward
+(the BERT- and GPT-2-shaped ones and the 18-point (N, d, causal) sweep):
+10 warm-up iterations, then at least 50 timed iterations and 200 ms, HIP
+events around each call; median and minimum. Per point it reports TFLOP/s,
+the fraction of the bf16 matrix-core peak and of the binding roof
+(min(peak, arithmetic intensity x 8 TB/s) over compulsory HBM bytes), and the
+compulsory bytes per second. Points whose working set is at most 256 MB are
+also timed cold: a 512 MB buffer is written between calls.
 """
 
 from __future__ import annotations
@@ -44,6 +55,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth (published)
 KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
                   "exact_io_aware_fa_amd/csrc/kernels/fa_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_long_causal_b1_h32_n16384_d128_traffic.json")
@@ -201,6 +213,132 @@ def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, o
                    "summary": os.path.basename(out_md)}, open(out_json, "w"), indent=1)
 
 
+def comp_bytes(w) -> tuple[float, float]:
+    """Compulsory HBM bytes of the forward and the backward of a workload:
+    forward reads Q, K, V and writes O and LSE; backward reads Q, K, V, O,
+    dO and LSE, writes and reads back the D vector, writes dQ, dK, dV."""
+    e = 2 if w.dtype == "bf16" else 4
+    bhn = w.batch * w.heads * w.n
+    return 4.0 * bhn * w.d * e + 4 * bhn, 8.0 * bhn * w.d * e + 4 * bhn + 8 * bhn
+
+
+def _gpu_clocks() -> str:
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError) as exc:
+        return "rocm-smi unavailable (%s)" % exc
+    keep = [l.strip() for l in r.stdout.splitlines() if "sclk" in l or "mclk" in l]
+    return "; ".join(keep) if keep else "rocm-smi printed no clock lines"
+
+
+def run_sweep(out_path: str | None) -> int:
+    import statistics
+
+    import torch
+
+    from exact_io_aware_fa_amd import binding as B
+    from exact_io_aware_fa_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py --sweep needs a GPU", file=sys.stderr)
+        return 1
+    B.lib()
+    dev = torch.device("cuda:0")
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    names = [n for n, w in WORKLOADS.items() if w.backward and n.startswith(("bert", "gpt2", "sweep"))]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ev = [hip.create() for _ in range(2)]
+    clocks_before = _gpu_clocks()
+    rows = []
+    for name in names:
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+        kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)
+        kv_ptr = None if kvl is None else kvl.data_ptr()
+        bsz, hh, n, d = q.shape
+        dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
+        scale = w.softmax_scale
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, hh, n), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        wsb = B.fa_bwd_workspace_bytes(bsz, hh, n, d, dt)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            B.check(B.fa_fwd(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
+                             v.data_ptr(), kv_ptr, o.data_ptr(), lse.data_ptr(), stream))
+
+        def bwd():
+            B.check(B.fa_bwd(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
+                             v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), kv_ptr,
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), wsb,
+                             stream))
+
+        def timed(fn, cold):
+            if cold:
+                flush.fill_(1)
+            hip.record(ev[0], stream)
+            fn()
+            hip.record(ev[1], stream)
+            return hip.elapsed_ms(ev[0], ev[1])
+
+        for _ in range(10):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        tf, tb, spent = [], [], 0.0
+        while len(tf) < 50 or spent < 200.0:
+            tf.append(timed(fwd, False))
+            tb.append(timed(bwd, False))
+            spent += tf[-1] + tb[-1]
+        working = sum(t.numel() * t.element_size() for t in (q, k, v, o, do, dq, dk, dv, lse, ws))
+        cf = cb = None
+        if working <= 256 << 20:
+            cf = statistics.median(timed(fwd, True) for _ in range(20))
+            cb = statistics.median(timed(bwd, True) for _ in range(20))
+        ff, fb = w.flops_fwd(), w.flops_bwd()
+        bf, bb = comp_bytes(w)
+        mf, mb = statistics.median(tf), statistics.median(tb)
+        roof_f = min(PEAK_BF16_TFLOPS, ff / bf * PEAK_HBM_GBS / 1e3)
+        roof_b = min(PEAK_BF16_TFLOPS, fb / bb * PEAK_HBM_GBS / 1e3)
+        tff, tfb = ff / mf / 1e9, fb / mb / 1e9
+        rows.append((name, mf, min(tf), tff, tff / PEAK_BF16_TFLOPS, tff / roof_f, bf / mf / 1e6,
+                     mb, min(tb), tfb, tfb / PEAK_BF16_TFLOPS, tfb / roof_b, bb / mb / 1e6,
+                     3.5 * ff / (mf + mb) / 1e9, cf, cb))
+        print(json.dumps({"workload": name, "fwd_ms_median": round(mf, 4), "bwd_ms_median": round(mb, 4),
+                          "fwd_tflops": round(tff, 1), "bwd_tflops": round(tfb, 1)}), flush=True)
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    for e_ in ev:
+        hip.destroy(e_)
+    lines = ["# Attention sweep on one MI355X", "",
+             "Command: `python bench.py --sweep --out <this file>` (from the repository root).", "",
+             "Clocks before the sweep (rocm-smi): " + clocks_before,
+             "Clocks after the sweep (rocm-smi): " + _gpu_clocks(), "",
+             "Times are medians (min in parentheses) over >= 50 calls and >= 200 ms, warm "
+             "cache; `cold` medians write a 512 MB buffer before each call. Peak = bf16 dense "
+             "MFMA %.0f TFLOP/s; roof = min(peak, compulsory-byte AI x %.0f GB/s); GB/s = "
+             "compulsory bytes / time. FLOPs: 4BHN^2d forward (x2.5 backward), halved when "
+             "causal; the padded workload counts nominal FLOPs." % (PEAK_BF16_TFLOPS, PEAK_HBM_GBS), "",
+             "| workload | fwd ms | fwd TFLOP/s | fwd % peak | fwd % roof | fwd GB/s | bwd ms | "
+             "bwd TFLOP/s | bwd % peak | bwd % roof | bwd GB/s | fwd+bwd TFLOP/s | cold fwd / bwd ms |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        cold = "-" if r[14] is None else "%.4f / %.4f" % (r[14], r[15])
+        lines.append("| %s | %.4f (%.4f) | %.1f | %.1f | %.1f | %.0f | %.4f (%.4f) | %.1f | %.1f | %.1f | %.0f | %.1f | %s |"
+                     % (r[0], r[1], r[2], r[3], 100 * r[4], 100 * r[5], r[6], r[7], r[8], r[9],
+                        100 * r[10], 100 * r[11], r[12], r[13], cold))
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
+
+
 def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "summarize":
         sp = argparse.ArgumentParser(prog="bench.py summarize")
@@ -221,11 +359,16 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time fwd and bwd on every sweep workload and print a table")
+    ap.add_argument("--out", default=None, help="with --sweep: also write the table here")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device three times (a plain copy "
                          "kernel of known size, to scale HBM byte counters)")
     args = ap.parse_args()
 
+    if args.sweep:
+        return run_sweep(args.out)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the work shards by (batch, head) with no exchange; see the design notes). "
