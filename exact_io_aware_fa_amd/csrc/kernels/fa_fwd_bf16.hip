@@ -304,6 +304,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
           u[t] = pack_bf16x2(sc[kb][kc * 8 + 2 * t], sc[kb][kc * 8 + 2 * t + 1]);
         pf[kb * 2 + kc] = as_bf16x8(u);
       }
+    // Pin the results here: otherwise the compiler sinks the exponentials
+    // and the packing past the next barrier, next to their use in the
+    // matrix phase, where they would no longer overlap the other group's
+    // matrix work.
+#pragma unroll
+    for (int kk = 0; kk < NKB * 2; ++kk) asm volatile("" : "+v"(pf[kk]));
+    asm volatile("" : "+v"(lpart));
   };
   // General softmax phase of tile j: tiles this wave does not own (before
   // the first, past its causal diagonal or the last) leave P^T zero, so the
