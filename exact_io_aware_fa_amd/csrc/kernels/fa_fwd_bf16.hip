@@ -194,10 +194,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     }
   }
 
-  // Matrix phase of step m: O^T += V^T P^T of tile m-1 (V in sv, P^T in
-  // pf) and S^T of tile m (K in sk) into sc, as a fixed sequence of product
-  // slots: the O^T slots first (four independent accumulators in turn), then
-  // the S^T slots. Each slot's A fragment is read PF slots ahead (a ring of
+  // Matrix phase of step m: S^T of tile m (K in sk) into sc and
+  // O^T += V^T P^T of tile m-1 (V in sv, P^T in pf), as a fixed sequence of
+  // product slots: the S^T slots first (so the scores are ready early for a
+  // softmax phase that follows at once), then the O^T slots (four
+  // independent accumulators in turn). Each slot's A fragment is read PF
+  // slots ahead (a ring of
   // PF + 1), and the sched_barrier fences keep the compiler from hoisting
   // every read to the top of the phase, which would exhaust the registers.
   constexpr int NPV = NMB * NKB * 2;  // O^T slots
@@ -216,9 +218,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   auto slots = [&](const bf16* sk, const bf16* sv, auto pv_tag, auto s_tag) FA_INLINE {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr bool SS = decltype(s_tag)::value;
-    constexpr int K0 = PV ? 0 : NPV;           // first slot
-    constexpr int K1 = SS ? NPV + NS : NPV;    // one past the last slot
-    auto rd = [&](int k) FA_INLINE { return k < NPV ? rd_pv(sv, k) : rd_s(sk, k - NPV); };
+    constexpr int K0 = SS ? 0 : NS;            // first slot
+    constexpr int K1 = PV ? NS + NPV : NS;     // one past the last slot
+    auto rd = [&](int k) FA_INLINE { return k < NS ? rd_s(sk, k) : rd_pv(sv, k - NS); };
     if (SS) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sc[kb] = f32x16{};
@@ -229,12 +231,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
 #pragma unroll
     for (int k = K0; k < K1; ++k) {
       if (k + PF < K1) fr[(k + PF) % (PF + 1)] = rd(k + PF);
-      if (k < NPV) {
-        const int mb = k % NMB, kk = k / NMB;
-        acc[mb] = mma32(fr[k % (PF + 1)], pf[kk], acc[mb]);
-      } else {
-        const int kb = (k - NPV) % NKB, kd = (k - NPV) / NKB;
+      if (k < NS) {
+        const int kb = k % NKB, kd = k / NKB;
         sc[kb] = mma32(fr[k % (PF + 1)], qf[kd], sc[kb]);
+      } else {
+        const int mb = (k - NS) % NMB, kk = (k - NS) / NMB;
+        acc[mb] = mma32(fr[k % (PF + 1)], pf[kk], acc[mb]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
