@@ -142,9 +142,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
     const int n_qt = (n + BQ - 1) / BQ;
     const int it0 = CAUSAL ? (k0 / BQ) : 0;
-    // Every tile is masked, branch-free: a pair (query q, key) is hidden iff
-    // q < lo or q >= n, with lo = the key itself when causal, 0 otherwise,
-    // and lo = n for keys at or past the key limit (all hidden).
+    // The mask, applied branch-free on the masked steps (see below): a pair
+    // (query q, key) is hidden iff q < lo or q >= n, with lo = the key itself
+    // when causal, 0 otherwise, and lo = n for keys at or past the key limit
+    // (all hidden).
     const int qlo = mykey >= kv_lim ? n : (CAUSAL ? mykey : 0);
 
     // Loads of query tile it into a stage (sm: Q and dO, sv: L and D). Wave
