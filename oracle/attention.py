@@ -38,6 +38,16 @@ f = sum(O * dO) for softmax attention:
     dK = scale * dS^T Q
 
 Hidden entries have P = 0, hence dS = 0, so dK/dV rows of padded keys are 0.
+
+Grouped K/V heads (GQA / MQA) -- page 1 section 九 notes that several query
+heads may share one K/V head, and page 4 下篇 section 六 fixes only that the
+query head count H is a multiple of the K/V head count H_kv. The reading
+here: contiguous groups, query head h uses K/V head h // (H // H_kv). Each
+query head is then plain attention against its K/V head, and because a
+shared K/V head enters every query head of its group, its gradients are the
+sums over the group:
+
+    dK[g] = sum_{h in group g} dK_h,    dV[g] = sum_{h in group g} dV_h.
 """
 
 from __future__ import annotations
@@ -128,21 +138,30 @@ def _kv_len_of(kv_len, b: int):
     return None if kv_len is None else int(np.asarray(kv_len).reshape(-1)[b])
 
 
+def _group(heads: int, heads_kv: int) -> int:
+    if heads_kv < 1 or heads % heads_kv:
+        raise ValueError(f"query heads {heads} not a multiple of K/V heads {heads_kv}")
+    return heads // heads_kv
+
+
 def attention_fwd(q, k, v, causal: bool = False, scale: float | None = None,
                   kv_len=None):
-    """Forward over [B, H, N, d] inputs, one head at a time.
+    """Forward over q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv divides H;
+    H_kv = H is ordinary multi-head attention), one query head at a time;
+    query head h uses K/V head h // (H // H_kv).
 
     Returns (o [B,H,N,d] float64, lse [B,H,N] float64, natural log).
     """
     q = _f64(q)
     bsz, heads, n, d = q.shape
+    grp = _group(heads, np.shape(k)[1])
     scale = default_scale(d) if scale is None else float(scale)
     o = np.empty_like(q)
     lse = np.empty((bsz, heads, n))
     for b in range(bsz):
         kvl = _kv_len_of(kv_len, b)
         for h in range(heads):
-            r = head_forward(q[b, h], k[b, h], v[b, h], scale, causal, kvl)
+            r = head_forward(q[b, h], k[b, h // grp], v[b, h // grp], scale, causal, kvl)
             o[b, h] = r["o"]
             lse[b, h] = r["lse"]
     return o, lse
@@ -150,20 +169,25 @@ def attention_fwd(q, k, v, causal: bool = False, scale: float | None = None,
 
 def attention_bwd(q, k, v, do, causal: bool = False,
                   scale: float | None = None, kv_len=None):
-    """Backward over [B, H, N, d] inputs, one head at a time.
+    """Backward over q, do [B, H, N, d] and k, v [B, H_kv, N, d], one query
+    head at a time; dK and dV of a shared K/V head are summed over its group.
 
-    Returns (dq, dk, dv), each [B,H,N,d] float64.
+    Returns (dq [B,H,N,d], dk [B,H_kv,N,d], dv [B,H_kv,N,d]), float64.
     """
     q = _f64(q)
     bsz, heads, n, d = q.shape
+    heads_kv = np.shape(k)[1]
+    grp = _group(heads, heads_kv)
     scale = default_scale(d) if scale is None else float(scale)
     dq = np.empty_like(q)
-    dk = np.empty_like(q)
-    dv = np.empty_like(q)
+    dk = np.zeros((bsz, heads_kv, n, d))
+    dv = np.zeros((bsz, heads_kv, n, d))
     for b in range(bsz):
         kvl = _kv_len_of(kv_len, b)
         for h in range(heads):
-            r = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale,
+            r = head_backward(q[b, h], k[b, h // grp], v[b, h // grp], do[b, h], scale,
                               causal, kvl)
-            dq[b, h], dk[b, h], dv[b, h] = r["dq"], r["dk"], r["dv"]
+            dq[b, h] = r["dq"]
+            dk[b, h // grp] += r["dk"]
+            dv[b, h // grp] += r["dv"]
     return dq, dk, dv

@@ -14,7 +14,8 @@ The oracle is checked against things other than itself:
   D_i = sum_j P_ij dP_ij = <dO_i, O_i>;
 * central finite differences of f = sum(O * dO) for every input entry;
 * a library cross-check against torch's CPU float64
-  scaled_dot_product_attention and its autograd.
+  scaled_dot_product_attention and its autograd, also with grouped K/V heads
+  (enable_gqa), where finite differences pin the summed K/V gradients too.
 
 The last test plants plausible mistakes in copies of the oracle and checks
 that at least one pin rejects each of them.
@@ -360,6 +361,102 @@ def test_cross_check_against_torch_cpu_float64_sdpa(causal, padded):
     if mask is not None:
         s = s.masked_fill(~mask, -math.inf)
     np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Grouped K/V heads (GQA / MQA)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("heads_kv", [1, 2, 3])
+@pytest.mark.parametrize("causal,padded", [(False, False), (True, False), (True, True)])
+def test_grouped_heads_cross_check_against_torch_sdpa_enable_gqa(heads_kv, causal, padded):
+    """torch's CPU float64 SDPA with enable_gqa (query head h uses K/V head
+    h // (H // H_kv)) and its autograd, which sums the gradients of a shared
+    K/V head over its group."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    g = torch.Generator().manual_seed(31 + heads_kv)
+    b, hh, n, d = 2, 6, 17, 8
+    q, do = (torch.randn(b, hh, n, d, generator=g, dtype=torch.float64) for _ in range(2))
+    k, v = (torch.randn(b, heads_kv, n, d, generator=g, dtype=torch.float64) for _ in range(2))
+    kv_len = np.array([11, 17]) if padded else None
+    scale = 0.37
+    mask = None
+    if padded or causal:
+        vis = np.stack([visible_mask(n, causal, None if kv_len is None else kv_len[i])
+                        for i in range(b)])[:, None]
+        mask = torch.from_numpy(vis)
+    qt, kt, vt = (x.clone().requires_grad_(True) for x in (q, k, v))
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=True)
+    ref.backward(do)
+    o, _ = oracle.attention_fwd(q.numpy(), k.numpy(), v.numpy(), causal, scale, kv_len)
+    dq, dk, dv = oracle.attention_bwd(q.numpy(), k.numpy(), v.numpy(), do.numpy(),
+                                      causal, scale, kv_len)
+    assert dk.shape == (b, heads_kv, n, d)
+    np.testing.assert_allclose(o, ref.detach().numpy(), rtol=1e-12, atol=1e-13)
+    for mine, theirs in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        np.testing.assert_allclose(mine, theirs.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def _fd_grouped(fwd, bwd, causal, h=1e-6):
+    """Central differences of f = sum(O * dO) over every entry of q, k, v for a
+    tiny grouped problem (4 query heads, 2 K/V heads)."""
+    rng = np.random.default_rng(17)
+    q, do = rng.standard_normal((1, 4, 6, 3)), rng.standard_normal((1, 4, 6, 3))
+    k, v = rng.standard_normal((1, 2, 6, 3)), rng.standard_normal((1, 2, 6, 3))
+    scale = 0.8
+    grads = bwd(q, k, v, do, causal, scale)
+
+    def f(args):
+        return float((fwd(*args, causal, scale)[0] * do).sum())
+
+    worst = 0.0
+    for pos, x in enumerate((q, k, v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            ap, am = [q, k, v], [q, k, v]
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap[pos], am[pos] = xp, xm
+            num[idx] = (f(ap) - f(am)) / (2 * h)
+        worst = max(worst, np.abs(num - grads[pos]).max() / np.abs(num).max())
+    return worst
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_backward_matches_finite_differences(causal):
+    assert _fd_grouped(oracle.attention_fwd, oracle.attention_bwd, causal) <= 1e-6
+
+
+def test_grouped_heads_planted_mistakes_are_rejected():
+    """Two plausible slips: interleaved head mapping (h % H_kv) and dK/dV
+    taken from the first head of a group instead of summed over it."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+
+    def fwd_interleaved(q, k, v, causal, scale, kv_len=None):
+        hkv = k.shape[1]
+        o = np.empty_like(q)
+        for h in range(q.shape[1]):
+            o[0, h] = head_forward(q[0, h], k[0, h % hkv], v[0, h % hkv], scale, causal)["o"]
+        return o, None
+
+    def bwd_first_only(q, k, v, do, causal, scale, kv_len=None):
+        grp = q.shape[1] // k.shape[1]
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, scale)
+        for g in range(k.shape[1]):
+            r = head_backward(q[0, g * grp], k[0, g], v[0, g], do[0, g * grp], scale, causal)
+            dk[0, g], dv[0, g] = r["dk"], r["dv"]
+        return dq, dk, dv
+
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((1, 4, 7, 3)), rng.standard_normal((1, 2, 7, 3)), rng.standard_normal((1, 2, 7, 3))
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)),
+                                         scale=0.5, enable_gqa=True).numpy()
+    assert not np.allclose(fwd_interleaved(q, k, v, False, 0.5)[0], ref, atol=1e-6)
+    assert np.allclose(oracle.attention_fwd(q, k, v, False, 0.5)[0], ref, atol=1e-12)
+    assert _fd_grouped(oracle.attention_fwd, bwd_first_only, False) > 1e-3
 
 
 # --------------------------------------------------------------------------
