@@ -58,7 +58,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth (published)
 KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
                   "exact_io_aware_fa_amd/csrc/kernels/fa_device.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_long_causal_b1_h32_n16384_d128_traffic.json")
+TRAFFIC_WORKLOAD = "long_causal_b1_h32_n16384_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_%s_traffic.json" % TRAFFIC_WORKLOAD)
 
 
 def kernel_source_hash() -> str:
@@ -114,9 +115,11 @@ def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
 
     heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
     kv = inp["kv_len"]
+    group = w.heads // w.kv_heads
     spent, done = 0.0, 0
     for b, h in heads:
-        args = [inp[x][b, h].float().double().numpy() for x in ("q", "k", "v", "do")]
+        args = [inp[x][b, h if x in ("q", "do") else h // group].float().double().numpy()
+                for x in ("q", "k", "v", "do")]
         t0 = time.perf_counter()
         oracle.head_backward(*args, w.softmax_scale, w.causal,
                              None if kv is None else int(kv[b]))
@@ -139,7 +142,11 @@ def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
     }
 
 
-def load_traffic(src_hash: str):
+def load_traffic(src_hash: str, workload: str):
+    """HBM bytes per dK/dV launch from the committed counter summary, or None
+    when that summary is for another workload or an older kernel source."""
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -216,10 +223,14 @@ def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, o
 def comp_bytes(w) -> tuple[float, float]:
     """Compulsory HBM bytes of the forward and the backward of a workload:
     forward reads Q, K, V and writes O and LSE; backward reads Q, K, V, O,
-    dO and LSE, writes and reads back the D vector, writes dQ, dK, dV."""
+    dO and LSE, writes and reads back the D vector, writes dQ, dK, dV. K, V,
+    dK and dV have the K/V heads' size."""
     e = 2 if w.dtype == "bf16" else 4
     bhn = w.batch * w.heads * w.n
-    return 4.0 * bhn * w.d * e + 4 * bhn, 8.0 * bhn * w.d * e + 4 * bhn + 8 * bhn
+    bkn = w.batch * w.kv_heads * w.n
+    fwd = (2.0 * bhn + 2.0 * bkn) * w.d * e + 4 * bhn
+    bwd = (4.0 * bhn + 4.0 * bkn) * w.d * e + 4 * bhn + 8 * bhn
+    return fwd, bwd
 
 
 def _gpu_clocks() -> str:
@@ -259,23 +270,25 @@ def run_sweep(out_path: str | None) -> int:
         kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)
         kv_ptr = None if kvl is None else kvl.data_ptr()
         bsz, hh, n, d = q.shape
+        hkv = k.shape[1]
         dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
         scale = w.softmax_scale
         o = torch.empty_like(q)
         lse = torch.empty((bsz, hh, n), dtype=torch.float32, device=dev)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         wsb = B.fa_bwd_workspace_bytes(bsz, hh, n, d, dt)
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
         def fwd():
-            B.check(B.fa_fwd(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
-                             v.data_ptr(), kv_ptr, o.data_ptr(), lse.data_ptr(), stream))
+            B.check(B.fa_fwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                                 k.data_ptr(), v.data_ptr(), kv_ptr, o.data_ptr(),
+                                 lse.data_ptr(), stream))
 
         def bwd():
-            B.check(B.fa_bwd(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
-                             v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), kv_ptr,
-                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), wsb,
-                             stream))
+            B.check(B.fa_bwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                                 k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                 lse.data_ptr(), kv_ptr, dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), ws.data_ptr(), wsb, stream))
 
         def timed(fn, cold):
             if cold:
@@ -398,10 +411,11 @@ def main() -> int:
     q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
     kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)
     bsz, hh, n, d = q.shape
+    hkv = k.shape[1]
     dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
     o = torch.empty_like(q)
     lse = torch.empty((bsz, hh, n), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_bytes = B.fa_bwd_workspace_bytes(bsz, hh, n, d, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
@@ -417,14 +431,15 @@ def main() -> int:
     def step(i=None):
         if i is not None:
             hip.record(ev_f0[i], stream)
-        B.check(B.fa_fwd(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
-                         v.data_ptr(), kv_ptr, o.data_ptr(), lse.data_ptr(), stream))
+        B.check(B.fa_fwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                             k.data_ptr(), v.data_ptr(), kv_ptr, o.data_ptr(),
+                             lse.data_ptr(), stream))
         if i is not None:
             hip.record(ev_f1[i], stream)
-        B.check(B.fa_bwd_timed(bsz, hh, n, d, w.causal, scale, dt, q.data_ptr(), k.data_ptr(),
-                               v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                               kv_ptr, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                               ws.data_ptr(), ws_bytes, stream,
+        B.check(B.fa_bwd_timed(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                               k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), kv_ptr, dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), ws.data_ptr(), ws_bytes, stream,
                                None if i is None else ev_b[i]))
 
     for _ in range(args.warmup):
@@ -466,7 +481,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if dt == B.FA_BF16 else "fp32",
         "data": "synthetic (seeded normal inputs; Q,K std %g, V,dO std 1)" % w.qk_sigma,
-        "config": {"workload": w.name, "batch": bsz, "heads": hh, "seq_len": n,
+        "config": {"workload": w.name, "batch": bsz, "heads": hh, "heads_kv": hkv, "seq_len": n,
                    "head_dim": d, "causal": w.causal, "key_padding": w.padded,
                    "softmax_scale": scale},
         "frac_of_peak_fwd_bwd": round(value / PEAK_BF16_TFLOPS, 4),
@@ -483,7 +498,7 @@ def main() -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(main_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(src_hash),
+            "traffic": load_traffic(src_hash, w.name),
             "kernel_source_hash": src_hash,
         },
     }

@@ -23,10 +23,17 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [batch, heads, n, d]")
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one [batch, heads, n, d] shape")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [batch, heads, n, d] and k, v one "
+                         "[batch, heads_kv, n, d] shape")
+    b, h, n, d = q.shape
+    hkv = k.shape[1]
+    if k.shape[0] != b or k.shape[2:] != q.shape[2:] or hkv < 1 or h % hkv:
+        raise ValueError("k and v need q's batch, n and d, and a head count "
+                         "heads_kv that divides q's")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must all be bfloat16 or all float32")
+    return hkv
 
 
 def _kv_len_arg(kv_len, batch, n, device):
@@ -47,24 +54,28 @@ def _stream() -> int:
 
 
 def flash_attn_fwd(q, k, v, causal=False, softmax_scale=None, kv_len=None):
-    """Forward: returns (o, lse); o like q, lse float32 [batch, heads, n]."""
-    _check_qkv(q, k, v)
+    """Forward: returns (o, lse); o like q, lse float32 [batch, heads, n].
+
+    k and v may have fewer heads than q (grouped or multi-query attention):
+    query head i then uses K/V head i // (heads // heads_kv)."""
+    hkv = _check_qkv(q, k, v)
     b, h, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     kvl = _kv_len_arg(kv_len, b, n, q.device)
     o = torch.empty_like(q)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
-    _b.check(_b.fa_fwd(b, h, n, d, causal, scale, _DTYPES[q.dtype],
-                       q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                       None if kvl is None else kvl.data_ptr(),
-                       o.data_ptr(), lse.data_ptr(), _stream()))
+    _b.check(_b.fa_fwd_gqa(b, h, hkv, n, d, causal, scale, _DTYPES[q.dtype],
+                           q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           None if kvl is None else kvl.data_ptr(),
+                           o.data_ptr(), lse.data_ptr(), _stream()))
     return o, lse
 
 
 def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
                    kv_len=None):
-    """Backward from the saved LSE: returns (dq, dk, dv)."""
-    _check_qkv(q, k, v)
+    """Backward from the saved LSE: returns (dq, dk, dv); dk, dv shaped like
+    k, v (summed over each K/V head's group of query heads)."""
+    hkv = _check_qkv(q, k, v)
     if o.shape != q.shape or do.shape != q.shape or o.dtype != q.dtype or do.dtype != q.dtype:
         raise ValueError("o and do must match q in shape and dtype")
     o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
@@ -75,12 +86,12 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_bytes = _b.fa_bwd_workspace_bytes(b, h, n, d, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    _b.check(_b.fa_bwd(b, h, n, d, causal, scale, dt,
-                       q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                       do.data_ptr(), lse.data_ptr(),
-                       None if kvl is None else kvl.data_ptr(),
-                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                       ws.data_ptr(), ws_bytes, _stream()))
+    _b.check(_b.fa_bwd_gqa(b, h, hkv, n, d, causal, scale, dt,
+                           q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           do.data_ptr(), lse.data_ptr(),
+                           None if kvl is None else kvl.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           ws.data_ptr(), ws_bytes, _stream()))
     return dq, dk, dv
 
 

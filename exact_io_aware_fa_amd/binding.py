@@ -28,8 +28,11 @@ FA_E_LAUNCH = 6
 FA_E_ALIGN = 7
 
 # Every symbol include/fa.h declares.
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_bytes",
-            "fa_status_str", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_bwd_gqa", "fa_bwd_timed",
+            "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version")
+
+# The FA_ABI_VERSION this binding was written against.
+ABI_VERSION = 2
 
 _lock = threading.Lock()
 _lib = None
@@ -56,14 +59,22 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
                              ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.fa_fwd_gqa.restype = ctypes.c_int
+        L.fa_fwd_gqa.argtypes = L.fa_fwd.argtypes[:2] + [_i64] + L.fa_fwd.argtypes[2:]
+        L.fa_bwd_gqa.restype = ctypes.c_int
+        L.fa_bwd_gqa.argtypes = L.fa_bwd.argtypes[:2] + [_i64] + L.fa_bwd.argtypes[2:]
         L.fa_bwd_timed.restype = ctypes.c_int
-        L.fa_bwd_timed.argtypes = L.fa_bwd.argtypes + [ctypes.POINTER(_vp)]
+        L.fa_bwd_timed.argtypes = L.fa_bwd_gqa.argtypes + [ctypes.POINTER(_vp)]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_status_str.argtypes = [ctypes.c_int]
         L.fa_abi_version.restype = ctypes.c_int
         L.fa_abi_version.argtypes = []
+        if L.fa_abi_version() != ABI_VERSION:
+            raise RuntimeError(
+                f"{LIB_PATH} has ABI version {L.fa_abi_version()}, this binding "
+                f"needs {ABI_VERSION}: rebuild it")
         _lib = L
         return L
 
@@ -74,6 +85,13 @@ def fa_fwd(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, kv_len,
                         int(dtype), q, k, v, kv_len, o, lse, stream)
 
 
+def fa_fwd_gqa(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k,
+               v, kv_len, o, lse, stream) -> int:
+    return lib().fa_fwd_gqa(batch, heads, heads_kv, n, d, int(causal),
+                            float(softmax_scale), int(dtype), q, k, v, kv_len, o,
+                            lse, stream)
+
+
 def fa_bwd(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o, d_o,
            lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream) -> int:
     return lib().fa_bwd(batch, heads, n, d, int(causal), float(softmax_scale),
@@ -81,16 +99,26 @@ def fa_bwd(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o, d_o,
                         workspace, int(workspace_bytes), stream)
 
 
-def fa_bwd_timed(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o,
-                 d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
-                 events) -> int:
+def fa_bwd_gqa(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k,
+               v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes,
+               stream) -> int:
+    return lib().fa_bwd_gqa(batch, heads, heads_kv, n, d, int(causal),
+                            float(softmax_scale), int(dtype), q, k, v, o, d_o, lse,
+                            kv_len, dq, dk, dv, workspace, int(workspace_bytes),
+                            stream)
+
+
+def fa_bwd_timed(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k,
+                 v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes,
+                 stream, events) -> int:
     """``events``: four raw hipEvent_t handles (ints or None), or None."""
     arr = None
     if events is not None:
         arr = (_vp * 4)(*[e if e else None for e in events])
-    return lib().fa_bwd_timed(batch, heads, n, d, int(causal), float(softmax_scale),
-                              int(dtype), q, k, v, o, d_o, lse, kv_len, dq, dk, dv,
-                              workspace, int(workspace_bytes), stream, arr)
+    return lib().fa_bwd_timed(batch, heads, heads_kv, n, d, int(causal),
+                              float(softmax_scale), int(dtype), q, k, v, o, d_o,
+                              lse, kv_len, dq, dk, dv, workspace,
+                              int(workspace_bytes), stream, arr)
 
 
 def fa_bwd_workspace_bytes(batch, heads, n, d, dtype) -> int:

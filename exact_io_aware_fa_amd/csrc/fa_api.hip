@@ -27,10 +27,12 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-fa_status check_common(int64_t batch, int64_t heads, int64_t n, int64_t d,
-                       float scale, fa_dtype dtype) {
+fa_status check_common(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n,
+                       int64_t d, float scale, fa_dtype dtype) {
   if (batch < 1 || heads < 1 || n < 1 || n > kMaxN) return FA_E_SHAPE;
   if (batch > INT32_MAX || heads > INT32_MAX) return FA_E_SHAPE;
+  // Grouped K/V heads: every K/V head serves the same number of query heads.
+  if (heads_kv < 1 || heads_kv > heads || heads % heads_kv != 0) return FA_E_SHAPE;
   if (d != 64 && d != 128 && d != 256) return FA_E_UNSUPPORTED;
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_E_UNSUPPORTED;
   if (!isfinite(scale)) return FA_E_UNSUPPORTED;
@@ -51,11 +53,13 @@ size_t vec_bytes(int64_t batch, int64_t heads, int64_t n) {
   return (b + 255) & ~size_t(255);
 }
 
-fa::Params base_params(int64_t batch, int64_t heads, int64_t n, int causal,
-                       float scale) {
+fa::Params base_params(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n,
+                       int causal, float scale) {
   fa::Params p{};
   p.batch = int(batch);
   p.heads = int(heads);
+  p.heads_kv = int(heads_kv);
+  p.group = int(heads / heads_kv);
   p.n = int(n);
   p.n_pad = int(n_padded(n));
   p.causal = causal ? 1 : 0;
@@ -76,7 +80,7 @@ const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK";
     case FA_E_NULLPTR: return "FA_E_NULLPTR: a required pointer is NULL";
-    case FA_E_SHAPE: return "FA_E_SHAPE: batch, heads or n out of range";
+    case FA_E_SHAPE: return "FA_E_SHAPE: batch, heads, heads_kv or n out of range";
     case FA_E_UNSUPPORTED: return "FA_E_UNSUPPORTED: unsupported d, dtype or scale";
     case FA_E_WORKSPACE: return "FA_E_WORKSPACE: workspace missing or too small";
     case FA_E_ALIAS: return "FA_E_ALIAS: an output overlaps an input or another output";
@@ -88,7 +92,7 @@ const char* fa_status_str(fa_status s) {
 
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n, int64_t d,
                               fa_dtype dtype) {
-  if (check_common(batch, heads, n, d, 1.f, dtype) != FA_OK) return 0;
+  if (check_common(batch, heads, 1, n, d, 1.f, dtype) != FA_OK) return 0;
   return 2 * vec_bytes(batch, heads, n);
 }
 
@@ -96,15 +100,25 @@ fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                  float softmax_scale, fa_dtype dtype, const void* q, const void* k,
                  const void* v, const int32_t* kv_len, void* o, float* lse,
                  void* stream) {
-  fa_status st = check_common(batch, heads, n, d, softmax_scale, dtype);
+  return fa_fwd_gqa(batch, heads, heads, n, d, causal, softmax_scale, dtype, q, k, v,
+                    kv_len, o, lse, stream);
+}
+
+fa_status fa_fwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
+                     int causal, float softmax_scale, fa_dtype dtype, const void* q,
+                     const void* k, const void* v, const int32_t* kv_len, void* o,
+                     float* lse, void* stream) {
+  fa_status st = check_common(batch, heads, heads_kv, n, d, softmax_scale, dtype);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_E_ALIGN;
   if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u)) return FA_E_ALIGN;
-  const size_t tb = size_t(batch) * size_t(heads) * size_t(n) * size_t(d) * elem_size(dtype);
+  const size_t row = size_t(n) * size_t(d) * elem_size(dtype);
+  const size_t tb = size_t(batch) * size_t(heads) * row;
+  const size_t kb = size_t(batch) * size_t(heads_kv) * row;
   const size_t lb = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
-  const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range ins[3] = {range_of(q, tb), range_of(k, kb), range_of(v, kb)};
   const Range ro = range_of(o, tb), rl = range_of(lse, lb);
   if (overlaps(ro, rl)) return FA_E_ALIAS;
   for (const Range& r : ins)
@@ -114,7 +128,7 @@ fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
     if (overlaps(rk, ro) || overlaps(rk, rl)) return FA_E_ALIAS;
   }
 
-  fa::Params p = base_params(batch, heads, n, causal, softmax_scale);
+  fa::Params p = base_params(batch, heads, heads_kv, n, causal, softmax_scale);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -132,17 +146,29 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                  const void* v, const void* o, const void* d_o, const float* lse,
                  const int32_t* kv_len, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  return fa_bwd_timed(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o, d_o,
-                      lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream, nullptr);
+  return fa_bwd_timed(batch, heads, heads, n, d, causal, softmax_scale, dtype, q, k, v, o,
+                      d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
+                      nullptr);
 }
 
-fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
+fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
+                     int causal, float softmax_scale, fa_dtype dtype, const void* q,
+                     const void* k, const void* v, const void* o, const void* d_o,
+                     const float* lse, const int32_t* kv_len, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_timed(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k, v,
+                      o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
+                      nullptr);
+}
+
+fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
+                       int causal,
                        float softmax_scale, fa_dtype dtype, const void* q, const void* k,
                        const void* v, const void* o, const void* d_o, const float* lse,
                        const int32_t* kv_len, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, void* stream,
                        void* const events[4]) {
-  fa_status st = check_common(batch, heads, n, d, softmax_scale, dtype);
+  fa_status st = check_common(batch, heads, heads_kv, n, d, softmax_scale, dtype);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return FA_E_NULLPTR;
   if (!workspace) return FA_E_WORKSPACE;
@@ -154,13 +180,15 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d, int c
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_E_ALIGN;
   if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u)) return FA_E_ALIGN;
 
-  const size_t tb = size_t(batch) * size_t(heads) * size_t(n) * size_t(d) * elem_size(dtype);
+  const size_t row = size_t(n) * size_t(d) * elem_size(dtype);
+  const size_t tb = size_t(batch) * size_t(heads) * row;
+  const size_t kb = size_t(batch) * size_t(heads_kv) * row;
   const size_t lb = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
-  Range ins[7] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
+  Range ins[7] = {range_of(q, tb), range_of(k, kb), range_of(v, kb), range_of(o, tb),
                   range_of(d_o, tb), range_of(lse, lb), Range{0, 0}};
   int nin = 6;
   if (kv_len) ins[nin++] = range_of(kv_len, size_t(batch) * sizeof(int32_t));
-  const Range outs[4] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
+  const Range outs[4] = {range_of(dq, tb), range_of(dk, kb), range_of(dv, kb),
                          range_of(workspace, need)};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < nin; ++j)
@@ -169,7 +197,7 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d, int c
       if (overlaps(outs[i], outs[j])) return FA_E_ALIAS;
   }
 
-  fa::Params p = base_params(batch, heads, n, causal, softmax_scale);
+  fa::Params p = base_params(batch, heads, heads_kv, n, causal, softmax_scale);
   p.q = q;
   p.k = k;
   p.v = v;

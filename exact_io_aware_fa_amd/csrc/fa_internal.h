@@ -26,7 +26,9 @@ struct Params {
   float* l2vec;         // backward workspace: L_i * log2(e), [B*H][n_pad]
   float* dq_acc;        // fp32 dQ accumulator to zero (fp32 path: dq itself)
   int batch;
-  int heads;
+  int heads;            // query heads (Q, O, dO, dQ, LSE)
+  int heads_kv;         // K/V heads (K, V, dK, dV); divides heads
+  int group;            // heads / heads_kv: query heads per K/V head
   int n;
   int n_pad;            // n rounded up to a multiple of 64 (workspace rows)
   int causal;

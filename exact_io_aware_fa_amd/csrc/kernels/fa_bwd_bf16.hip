@@ -78,18 +78,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
   const int n = p.n;
 
   const int t_c = (n + kBKV - 1) / kBKV;
-  int bh, kt;
-  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, bh, kt);
-  const int b = bh / p.heads;
-  const size_t base = (size_t)bh * (size_t)n * D;
-  const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
-  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
-  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
-  const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
-  const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;
-  const float* __restrict__ dvec = p.dvec + (size_t)bh * p.n_pad;
-  bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + base;
-  bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + base;
+  // kbh indexes (batch, K/V head); the workgroup sweeps the queries of every
+  // query head in that K/V head's group, one after the other.
+  int kbh, kt;
+  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, kbh, kt);
+  const int b = kbh / p.heads_kv;
+  const size_t kvbase = (size_t)kbh * (size_t)n * D;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + kvbase;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + kvbase;
+  bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + kvbase;
+  bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + kvbase;
 
   const int kv_lim = kv_limit(p, b);
   const int k0 = kt * kBKV;
@@ -142,6 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
     const int n_qt = (n + BQ - 1) / BQ;
     const int it0 = CAUSAL ? (k0 / BQ) : 0;
+    const int qsw = p.group;
     // The mask, applied branch-free on the masked steps (see below): a pair
     // (query q, key) is hidden iff q < lo or q >= n, with lo = the key itself
     // when causal, 0 otherwise, and lo = n for keys at or past the key limit
@@ -162,23 +161,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       const int row = (w * LPW + i) * RPL + lane / CH;
       ld_off[i] = (row * D + ((lane % CH) ^ swz_both<D>(row)) * 8) * 2;
     }
-    const auto rq = buffer_rsrc(Q, n * ROWB);
-    const auto rg = buffer_rsrc(dO, n * ROWB);
-    const auto rl = buffer_rsrc(l2v, p.n_pad * 4);
-    const auto rd = buffer_rsrc(dvec, p.n_pad * 4);
-    auto issue = [&](int it, bf16* sm, float* sv) FA_INLINE {
-      const int qb0 = it * BQ * ROWB;
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        bload_lds16(rq, qb0 + ld_off[i], sm + (w * LPW + i) * RPL * D);
-        bload_lds16(rg, qb0 + ld_off[i], sm + TILE + (w * LPW + i) * RPL * D);
-      }
-      if (w == 0 && lane < BQ / 4) {
-        bload_lds16(rl, it * BQ * 4 + lane * 16, sv);
-        bload_lds16(rd, it * BQ * 4 + lane * 16, sv + BQ);
-      }
-    };
-
     // Per-lane LDS element offsets (tile-invariant). Row reads: row c of a
     // 32-row block, logical chunk kd*2 + h. Transposing reads: row
     // h*4 + (c%16)/4 of a 16-row block, column mb*32 + 16*(c/16) + 4*(c%4);
@@ -196,193 +178,218 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       }
     }
 
-    // S = Q K^T and dP = dO V^T of the tile in stage sm (lane = key, 16
-    // queries per 32-query block); used once, before the loop.
-    auto sdp = [&](const bf16* sm, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) FA_INLINE {
+    for (int gq = 0; gq < qsw; ++gq) {
+      // Query head gq of the group: its Q, dO and row vectors.
+      const int bh = q_index(p, kbh, gq);
+      const size_t base = (size_t)bh * (size_t)n * D;
+      const auto rq = buffer_rsrc(static_cast<const bf16*>(p.q) + base, n * ROWB);
+      const auto rg = buffer_rsrc(static_cast<const bf16*>(p.d_o) + base, n * ROWB);
+      const auto rl = buffer_rsrc(p.l2vec + (size_t)bh * p.n_pad, p.n_pad * 4);
+      const auto rd = buffer_rsrc(p.dvec + (size_t)bh * p.n_pad, p.n_pad * 4);
+      // Waves may still be reading the previous head's last tiles from the
+      // stages; every wave is past them before they are refilled.
+      if (gq > 0) __syncthreads();
+      auto issue = [&](int it, bf16* sm, float* sv) FA_INLINE {
+        const int qb0 = it * BQ * ROWB;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        s[qb] = f32x16{};
-        g[qb] = f32x16{};
-#pragma unroll
-        for (int kd = 0; kd < ND; ++kd) {
-          s[qb] = mma32(as_bf16x8(ld16(sm + qb * 32 * D + qoff[kd])), kf[kd], s[qb]);
-          g[qb] = mma32(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[kd])), vf[kd], g[qb]);
+        for (int i = 0; i < LPW; ++i) {
+          bload_lds16(rq, qb0 + ld_off[i], sm + (w * LPW + i) * RPL * D);
+          bload_lds16(rg, qb0 + ld_off[i], sm + TILE + (w * LPW + i) * RPL * D);
         }
-      }
-    };
-
-    // P = exp2(S c - L log2 e) and dS = P (dP - D) for element e of the
-    // lane's 16 NQB values, in place in s and g. Query of element
-    // (qb, gi, i) is q0 + 4h + (qb*32 + gi*8 + i); the pair is hidden iff
-    // that offset is < lo or >= hi, and a hidden pair gets P = 0, dS = 0.
-    auto pds1 = [&](int e, int lo, int hi, const f32x4 (&l4)[NQB][4], const f32x4 (&d4)[NQB][4],
-                    f32x16 (&s)[NQB], f32x16 (&g)[NQB], auto mask_tag) FA_INLINE {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      const int qb = e / 16, r = e % 16, gi = r / 4, i = r % 4;
-      const int off = qb * 32 + gi * 8 + i;
-      const float x = (MASK && (off < lo || off >= hi)) ? kNegInf : s[qb][r];
-      const float pr = __builtin_amdgcn_exp2f(fmaf(x, cs, -l4[qb][gi][i]));
-      s[qb][r] = pr;
-      g[qb][r] = pr * (g[qb][r] - d4[qb][gi][i]);
-    };
-
-    // A fragments of the transposing reads for (qb, qc, mb): dO^T and Q^T of
-    // 16 queries x 32 dims of the tile in sm.
-    auto trfrag = [&](const bf16* sm, int qb, int qc, int mb, bf16x8& fo, bf16x8& fq) FA_INLINE {
-      const int r0 = (qb * 32 + qc * 16) * D;
-      const int r1 = r0 + 8 * D;
-      const u32x2 olo = ds_read_tr16(sm + TILE + r0 + toff[mb]);
-      const u32x2 ohi = ds_read_tr16(sm + TILE + r1 + toff[mb ^ HB]);
-      const u32x2 qlo = ds_read_tr16(sm + r0 + toff[mb]);
-      const u32x2 qhi = ds_read_tr16(sm + r1 + toff[mb ^ HB]);
-      fo = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
-      fq = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
-    };
-
-    // One query tile, software-pipelined and issued in a fixed order (the
-    // sched_barrier fences pin it): phase 1 computes S and dP of tile it+1
-    // (stage mB, row reads two products ahead) while the vector units turn
-    // S and dP of tile it (in s, g; L and D in vA) into P and dS, 16/ND
-    // values per product pair; phase 2 accumulates dV^T and dK^T of tile it
-    // from stage mA (transposing reads one pair ahead).
-    constexpr int NS = NQB * ND;        // phase-1 slots (2 products each)
-    constexpr int EPS = 16 / ND;        // P/dS values per phase-1 slot
-    constexpr int NP = NQB * 2 * NMB;   // phase-2 slots (2 products each)
-    f32x16 s[NQB], g[NQB];
-    auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB, bool next,
-                    auto mask_tag) FA_INLINE {
-      const int qh = it * BQ + h * 4;
-      const int lo = qlo - qh;
-      const int hi = n - qh;
-      f32x4 l4[NQB][4], d4[NQB][4];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          l4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[qb * 32 + gi * 8 + h * 4]);
-          d4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[BQ + qb * 32 + gi * 8 + h * 4]);
+        if (w == 0 && lane < BQ / 4) {
+          bload_lds16(rl, it * BQ * 4 + lane * 16, sv);
+          bload_lds16_at(rd, it * BQ * 4 + lane * 16, sv, BQ * 4);
         }
-      f32x16 s2[NQB], g2[NQB];
-      bf16x8 rq[3], rg[3];
-      if (next) {
+      };
+
+      // S = Q K^T and dP = dO V^T of the tile in stage sm (lane = key, 16
+      // queries per 32-query block); used once, before the loop.
+      auto sdp = [&](const bf16* sm, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) FA_INLINE {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          s2[qb] = f32x16{};
-          g2[qb] = f32x16{};
-        }
+          s[qb] = f32x16{};
+          g[qb] = f32x16{};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          rq[j] = as_bf16x8(ld16(mB + (j / ND) * 32 * D + qoff[j % ND]));
-          rg[j] = as_bf16x8(ld16(mB + TILE + (j / ND) * 32 * D + qoff[j % ND]));
+          for (int kd = 0; kd < ND; ++kd) {
+            s[qb] = mma32(as_bf16x8(ld16(sm + qb * 32 * D + qoff[kd])), kf[kd], s[qb]);
+            g[qb] = mma32(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[kd])), vf[kd], g[qb]);
+          }
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      };
+
+      // P = exp2(S c - L log2 e) and dS = P (dP - D) for element e of the
+      // lane's 16 NQB values, in place in s and g. Query of element
+      // (qb, gi, i) is q0 + 4h + (qb*32 + gi*8 + i); the pair is hidden iff
+      // that offset is < lo or >= hi, and a hidden pair gets P = 0, dS = 0.
+      auto pds1 = [&](int e, int lo, int hi, const f32x4 (&l4)[NQB][4], const f32x4 (&d4)[NQB][4],
+                      f32x16 (&s)[NQB], f32x16 (&g)[NQB], auto mask_tag) FA_INLINE {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int qb = e / 16, r = e % 16, gi = r / 4, i = r % 4;
+        const int off = qb * 32 + gi * 8 + i;
+        const float x = (MASK && (off < lo || off >= hi)) ? kNegInf : s[qb][r];
+        const float pr = __builtin_amdgcn_exp2f(fmaf(x, cs, -l4[qb][gi][i]));
+        s[qb][r] = pr;
+        g[qb][r] = pr * (g[qb][r] - d4[qb][gi][i]);
+      };
+
+      // A fragments of the transposing reads for (qb, qc, mb): dO^T and Q^T of
+      // 16 queries x 32 dims of the tile in sm.
+      auto trfrag = [&](const bf16* sm, int qb, int qc, int mb, bf16x8& fo, bf16x8& fq) FA_INLINE {
+        const int r0 = (qb * 32 + qc * 16) * D;
+        const int r1 = r0 + 8 * D;
+        const u32x2 olo = ds_read_tr16(sm + TILE + r0 + toff[mb]);
+        const u32x2 ohi = ds_read_tr16(sm + TILE + r1 + toff[mb ^ HB]);
+        const u32x2 qlo = ds_read_tr16(sm + r0 + toff[mb]);
+        const u32x2 qhi = ds_read_tr16(sm + r1 + toff[mb ^ HB]);
+        fo = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+        fq = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+      };
+
+      // One query tile, software-pipelined and issued in a fixed order (the
+      // sched_barrier fences pin it): phase 1 computes S and dP of tile it+1
+      // (stage mB, row reads two products ahead) while the vector units turn
+      // S and dP of tile it (in s, g; L and D in vA) into P and dS, 16/ND
+      // values per product pair; phase 2 accumulates dV^T and dK^T of tile it
+      // from stage mA (transposing reads one pair ahead).
+      constexpr int NS = NQB * ND;        // phase-1 slots (2 products each)
+      constexpr int EPS = 16 / ND;        // P/dS values per phase-1 slot
+      constexpr int NP = NQB * 2 * NMB;   // phase-2 slots (2 products each)
+      f32x16 s[NQB], g[NQB];
+      auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB, bool next,
+                      auto mask_tag) FA_INLINE {
+        const int qh = it * BQ + h * 4;
+        const int lo = qlo - qh;
+        const int hi = n - qh;
+        f32x4 l4[NQB][4], d4[NQB][4];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi) {
+            l4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[qb * 32 + gi * 8 + h * 4]);
+            d4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[BQ + qb * 32 + gi * 8 + h * 4]);
+          }
+        f32x16 s2[NQB], g2[NQB];
+        bf16x8 rq[3], rg[3];
         if (next) {
-          const int qb = j / ND, kd = j % ND;
-          s2[qb] = mma32(rq[j % 3], kf[kd], s2[qb]);
-          g2[qb] = mma32(rg[j % 3], vf[kd], g2[qb]);
-          if (j + 2 < NS) {
-            const int j2 = j + 2;
-            rq[j2 % 3] = as_bf16x8(ld16(mB + (j2 / ND) * 32 * D + qoff[j2 % ND]));
-            rg[j2 % 3] = as_bf16x8(ld16(mB + TILE + (j2 / ND) * 32 * D + qoff[j2 % ND]));
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            s2[qb] = f32x16{};
+            g2[qb] = f32x16{};
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            rq[j] = as_bf16x8(ld16(mB + (j / ND) * 32 * D + qoff[j % ND]));
+            rg[j] = as_bf16x8(ld16(mB + TILE + (j / ND) * 32 * D + qoff[j % ND]));
           }
         }
-#pragma unroll
-        for (int e = j * EPS; e < (j + 1) * EPS; ++e) pds1(e, lo, hi, l4, d4, s, g, mask_tag);
         __builtin_amdgcn_sched_barrier(0);
-      }
-      bf16x8 fo[2], fq[2];
-      trfrag(mA, 0, 0, 0, fo[0], fq[0]);
-      bf16x8 pfr, sfr;
 #pragma unroll
-      for (int k = 0; k < NP; ++k) {
-        const int qb = k / (2 * NMB), qc = (k / NMB) % 2, mb = k % NMB;
-        if (k + 1 < NP) {
-          const int k1 = k + 1;
-          trfrag(mA, k1 / (2 * NMB), (k1 / NMB) % 2, k1 % NMB, fo[k1 % 2], fq[k1 % 2]);
-        }
-        if (mb == 0) {
-          u32x4 pu, su;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            pu[t] = pack_bf16x2(s[qb][qc * 8 + 2 * t], s[qb][qc * 8 + 2 * t + 1]);
-            su[t] = pack_bf16x2(g[qb][qc * 8 + 2 * t], g[qb][qc * 8 + 2 * t + 1]);
+        for (int j = 0; j < NS; ++j) {
+          if (next) {
+            const int qb = j / ND, kd = j % ND;
+            s2[qb] = mma32(rq[j % 3], kf[kd], s2[qb]);
+            g2[qb] = mma32(rg[j % 3], vf[kd], g2[qb]);
+            if (j + 2 < NS) {
+              const int j2 = j + 2;
+              rq[j2 % 3] = as_bf16x8(ld16(mB + (j2 / ND) * 32 * D + qoff[j2 % ND]));
+              rg[j2 % 3] = as_bf16x8(ld16(mB + TILE + (j2 / ND) * 32 * D + qoff[j2 % ND]));
+            }
           }
-          pfr = as_bf16x8(pu);
-          sfr = as_bf16x8(su);
-        }
-        dv[mb] = mma32(fo[k % 2], pfr, dv[mb]);
-        dk[mb] = mma32(fq[k % 2], sfr, dk[mb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (next) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          s[qb] = s2[qb];
-          g[qb] = g2[qb];
+          for (int e = j * EPS; e < (j + 1) * EPS; ++e) pds1(e, lo, hi, l4, d4, s, g, mask_tag);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-    };
+        bf16x8 fo[2], fq[2];
+        trfrag(mA, 0, 0, 0, fo[0], fq[0]);
+        bf16x8 pfr, sfr;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const int qb = k / (2 * NMB), qc = (k / NMB) % 2, mb = k % NMB;
+          if (k + 1 < NP) {
+            const int k1 = k + 1;
+            trfrag(mA, k1 / (2 * NMB), (k1 / NMB) % 2, k1 % NMB, fo[k1 % 2], fq[k1 % 2]);
+          }
+          if (mb == 0) {
+            u32x4 pu, su;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              pu[t] = pack_bf16x2(s[qb][qc * 8 + 2 * t], s[qb][qc * 8 + 2 * t + 1]);
+              su[t] = pack_bf16x2(g[qb][qc * 8 + 2 * t], g[qb][qc * 8 + 2 * t + 1]);
+            }
+            pfr = as_bf16x8(pu);
+            sfr = as_bf16x8(su);
+          }
+          dv[mb] = mma32(fo[k % 2], pfr, dv[mb]);
+          dk[mb] = mma32(fq[k % 2], sfr, dk[mb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (next) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            s[qb] = s2[qb];
+            g[qb] = g2[qb];
+          }
+        }
+      };
 
-    // Stages: tile it in A, tile it+1 in B, tile it+2 goes to C (rotating
-    // with the loop unrolled by three). At the top of an iteration each wave
-    // waits for its own loads of tile it+1; the barrier then makes every
-    // wave's loads visible and guarantees that every wave has finished the
-    // previous iteration, the last reader of stage C (tile it-1).
-    auto step = [&](int it, bf16* mA, float* vA, bf16* mB, bf16* mC, float* vC,
-                    auto mask_tag) FA_INLINE {
+      // Stages: tile it in A, tile it+1 in B, tile it+2 goes to C (rotating
+      // with the loop unrolled by three). At the top of an iteration each wave
+      // waits for its own loads of tile it+1; the barrier then makes every
+      // wave's loads visible and guarantees that every wave has finished the
+      // previous iteration, the last reader of stage C (tile it-1).
+      auto step = [&](int it, bf16* mA, float* vA, bf16* mB, bf16* mC, float* vC,
+                      auto mask_tag) FA_INLINE {
+        wait_global_loads();
+        __syncthreads();
+        if (it + 2 < n_qt) issue(it + 2, mC, vC);
+        body(it, mA, vA, mB, true, mask_tag);
+      };
+      auto finish = [&](int it, bf16* mA, float* vA) FA_INLINE {
+        body(it, mA, vA, nullptr, false, std::true_type{});
+      };
+
+      // Masked steps: the causal diagonal band (the first kBKV / BQ tiles of
+      // the sweep, rounded up to a multiple of three so the unmasked loop
+      // starts with the same stage rotation), every step when the workgroup
+      // straddles the key limit, and the last tile (always masked: it may be
+      // partial). The unmasked steps skip the mask arithmetic.
+      constexpr int HEAD = (kBKV / BQ + 2) / 3 * 3;
+      const int last = n_qt - 1;
+      const bool straddle = k0 + kBKV > kv_lim;
+      const int head = straddle ? last : (CAUSAL ? min(it0 + HEAD, last) : it0);
+
+      issue(it0, sm0, sv0);
+      if (it0 + 1 < n_qt) issue(it0 + 1, sm1, sv1);
       wait_global_loads();
       __syncthreads();
-      if (it + 2 < n_qt) issue(it + 2, mC, vC);
-      body(it, mA, vA, mB, true, mask_tag);
-    };
-    auto finish = [&](int it, bf16* mA, float* vA) FA_INLINE {
-      body(it, mA, vA, nullptr, false, std::true_type{});
-    };
-
-    // Masked steps: the causal diagonal band (the first kBKV / BQ tiles of
-    // the sweep, rounded up to a multiple of three so the unmasked loop
-    // starts with the same stage rotation), every step when the workgroup
-    // straddles the key limit, and the last tile (always masked: it may be
-    // partial). The unmasked steps skip the mask arithmetic.
-    constexpr int HEAD = (kBKV / BQ + 2) / 3 * 3;
-    const int last = n_qt - 1;
-    const bool straddle = k0 + kBKV > kv_lim;
-    const int head = straddle ? last : (CAUSAL ? min(it0 + HEAD, last) : it0);
-
-    issue(it0, sm0, sv0);
-    if (it0 + 1 < n_qt) issue(it0 + 1, sm1, sv1);
-    wait_global_loads();
-    __syncthreads();
-    sdp(sm0, s, g);
-    int it = it0;
-    for (; it + 3 <= head; it += 3) {
-      step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
-      step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
-      step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
-    }
-    // Here either it == head with (it - it0) % 3 == 0, or head == last and
-    // fewer than three steps remain before it, so the unmasked loop below
-    // does not run.
-    for (; it + 3 <= last; it += 3) {
-      step(it, sm0, sv0, sm1, sm2, sv2, std::false_type{});
-      step(it + 1, sm1, sv1, sm2, sm0, sv0, std::false_type{});
-      step(it + 2, sm2, sv2, sm0, sm1, sv1, std::false_type{});
-    }
-    // last - it is 0, 1 or 2 here; the last tile has no successor.
-    if (it == last) {
-      finish(it, sm0, sv0);
-    } else {
-      step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
-      if (it + 1 == last) {
-        finish(it + 1, sm1, sv1);
-      } else {
+      sdp(sm0, s, g);
+      int it = it0;
+      for (; it + 3 <= head; it += 3) {
+        step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
         step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
-        finish(it + 2, sm2, sv2);
+        step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
       }
-    }
+      // Here either it == head with (it - it0) % 3 == 0, or head == last and
+      // fewer than three steps remain before it, so the unmasked loop below
+      // does not run.
+      for (; it + 3 <= last; it += 3) {
+        step(it, sm0, sv0, sm1, sm2, sv2, std::false_type{});
+        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::false_type{});
+        step(it + 2, sm2, sv2, sm0, sm1, sv1, std::false_type{});
+      }
+      // last - it is 0, 1 or 2 here; the last tile has no successor.
+      if (it == last) {
+        finish(it, sm0, sv0);
+      } else {
+        step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
+        if (it + 1 == last) {
+          finish(it + 1, sm1, sv1);
+        } else {
+          step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
+          finish(it + 2, sm2, sv2);
+        }
+      }
+    }  // query heads of the group
   }
 
   // dK = scale * (dS^T Q), dV as accumulated.
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 template <int D, int NQB>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_c = (p.n + kBKV - 1) / kBKV;
-  const long long total = (long long)t_c * p.batch * p.heads;
+  const long long total = (long long)t_c * p.batch * p.heads_kv;
   dim3 grid((unsigned)total), block(kThreads);
   if (p.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NQB, true>), grid, block, 0, s, p);

@@ -51,18 +51,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
   const int n = p.n;
 
   const int t_c = (n + kBKV - 1) / kBKV;
-  int bh, kt;
-  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, bh, kt);
-  const int b = bh / p.heads;
-  const size_t base = (size_t)bh * (size_t)n * D;
-  const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
-  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
-  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
-  const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
-  const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;
-  const float* __restrict__ dvec = p.dvec + (size_t)bh * p.n_pad;
-  bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + base;
-  bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + base;
+  // kbh indexes (batch, K/V head); the workgroup sweeps the queries of every
+  // query head in that K/V head's group, one after the other.
+  int kbh, kt;
+  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, kbh, kt);
+  const int b = kbh / p.heads_kv;
+  const size_t kvbase = (size_t)kbh * (size_t)n * D;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + kvbase;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + kvbase;
+  bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + kvbase;
+  bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + kvbase;
+  // Q, dO and the row vectors of the query head being swept.
+  const bf16* __restrict__ Q = nullptr;
+  const bf16* __restrict__ dO = nullptr;
+  const float* __restrict__ l2v = nullptr;
+  const float* __restrict__ dvec = nullptr;
 
   const int kv_lim = kv_limit(p, b);
   const int k0 = kt * kBKV;
@@ -247,16 +250,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
       }
     };
 
-    gload(it0);
-    if constexpr (NBUF == 2) {
-      swrite(it0, 0);
-      gload(min(it0 + 1, n_qt - 1));
-      __syncthreads();
+    // One sweep per query head of the group. A sweep's first LDS write is
+    // safe: with two buffers every step ends on a barrier, with one every
+    // step starts on one.
+    for (int gq = 0; gq < p.group; ++gq) {
+      const int bh = q_index(p, kbh, gq);
+      const size_t base = (size_t)bh * (size_t)n * D;
+      Q = static_cast<const bf16*>(p.q) + base;
+      dO = static_cast<const bf16*>(p.d_o) + base;
+      l2v = p.l2vec + (size_t)bh * p.n_pad;
+      dvec = p.dvec + (size_t)bh * p.n_pad;
+      gload(it0);
+      if constexpr (NBUF == 2) {
+        swrite(it0, 0);
+        gload(min(it0 + 1, n_qt - 1));
+        __syncthreads();
+      }
+      int it = it0;
+      for (; it < a_end; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
+      for (; it < b_end; ++it) run(it, (it - it0) & (NBUF - 1), std::false_type{});
+      for (; it < n_qt; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
     }
-    int it = it0;
-    for (; it < a_end; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
-    for (; it < b_end; ++it) run(it, (it - it0) & (NBUF - 1), std::false_type{});
-    for (; it < n_qt; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
   }
 
   // dK = scale * (dS^T Q), dV as accumulated.
@@ -281,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
 template <int D, int BQ, int NBUF>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_c = (p.n + kBKV - 1) / kBKV;
-  const long long total = (long long)t_c * p.batch * p.heads;
+  const long long total = (long long)t_c * p.batch * p.heads_kv;
   dim3 grid((unsigned)total), block(kThreads);
   if (p.causal)
     hipLaunchKernelGGL((bwd_dkdv_staged_kernel<D, BQ, NBUF, true>), grid, block, 0, s, p);

@@ -49,9 +49,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
   remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
   const int b = bh / p.heads;
   const size_t base = (size_t)bh * (size_t)n * D;
+  // K and V of the K/V head this query head uses (grouped heads).
+  const size_t kvbase = (size_t)kv_index(p, bh) * (size_t)n * D;
   const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
-  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
-  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + kvbase;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + kvbase;
   const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
   bf16* __restrict__ dQ = static_cast<bf16*>(p.dq) + base;
 

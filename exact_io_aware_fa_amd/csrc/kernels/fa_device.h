@@ -97,6 +97,17 @@ __device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t r, int voff, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
 }
 
+// bload_lds16 into LDS at lds_base + lds_off bytes, the offset applied after
+// the cast to the LDS address space. (A constant offset applied to the
+// generic pointer of a __shared__ array first leaves a constant cast that the
+// gfx950 instruction selector rejects when it sits inside a loop.)
+__device__ __forceinline__ void bload_lds16_at(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base,
+                                               int lds_off) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((lds_char*)lds_base + lds_off), 16,
+                                           voff, 0, 0, 0);
+}
+
 // Wait until this wave's outstanding global loads (including the loads into
 // LDS) have completed; other counters are left alone. Encoding for gfx9:
 // vmcnt = 0, expcnt = 7 (no wait), lgkmcnt = 15 (no wait).
@@ -160,6 +171,18 @@ __device__ __forceinline__ void remap_workgroup(int wg, int total, int tiles,
   bh = idx / tiles;
   const int t = idx - bh * tiles;
   tile = heavy_last_index ? (tiles - 1 - t) : t;
+}
+
+// Grouped K/V heads: query head h of a batch entry uses K/V head
+// h / group (contiguous groups). kv_index maps a flat (batch, query head)
+// index to the flat (batch, K/V head) index; q_index maps a flat
+// (batch, K/V head) index and a member g of its group to the flat
+// (batch, query head) index.
+__device__ __forceinline__ int kv_index(const Params& p, int bh) {
+  return (bh / p.heads) * p.heads_kv + (bh % p.heads) / p.group;
+}
+__device__ __forceinline__ int q_index(const Params& p, int kbh, int g) {
+  return (kbh / p.heads_kv) * p.heads + (kbh % p.heads_kv) * p.group + g;
 }
 
 // Keys j >= kv_limit are hidden for this batch entry (clamped to [0, n]).

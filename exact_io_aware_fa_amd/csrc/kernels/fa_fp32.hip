@@ -50,9 +50,11 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
   remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
   const int b = bh / p.heads;
   const size_t base = (size_t)bh * (size_t)n * D;
+  // K and V of the K/V head this query head uses (grouped heads).
+  const size_t kvbase = (size_t)kv_index(p, bh) * (size_t)n * D;
   const float* __restrict__ Q = static_cast<const float*>(p.q) + base;
-  const float* __restrict__ K = static_cast<const float*>(p.k) + base;
-  const float* __restrict__ V = static_cast<const float*>(p.v) + base;
+  const float* __restrict__ K = static_cast<const float*>(p.k) + kvbase;
+  const float* __restrict__ V = static_cast<const float*>(p.v) + kvbase;
   float* __restrict__ O = static_cast<float*>(p.o) + base;
   const int kv_lim = kv_limit(p, b);
   const int q0 = qb * BR;
@@ -147,19 +149,16 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
   const int sub = tid & 3;
   const int n = p.n;
   const int t_c = (n + BK - 1) / BK;
-  int bh, kt;
-  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, bh, kt);
-  const int b = bh / p.heads;
-  const size_t base = (size_t)bh * (size_t)n * D;
-  const float* __restrict__ Q = static_cast<const float*>(p.q) + base;
-  const float* __restrict__ K = static_cast<const float*>(p.k) + base;
-  const float* __restrict__ V = static_cast<const float*>(p.v) + base;
-  const float* __restrict__ dO = static_cast<const float*>(p.d_o) + base;
-  const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;
-  const float* __restrict__ dvec = p.dvec + (size_t)bh * p.n_pad;
-  float* __restrict__ dQ = static_cast<float*>(p.dq) + base;
-  float* __restrict__ dK = static_cast<float*>(p.dk) + base;
-  float* __restrict__ dV = static_cast<float*>(p.dv) + base;
+  // kbh indexes (batch, K/V head); the workgroup sweeps the queries of every
+  // query head in that K/V head's group, one after the other.
+  int kbh, kt;
+  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, kbh, kt);
+  const int b = kbh / p.heads_kv;
+  const size_t kvbase = (size_t)kbh * (size_t)n * D;
+  const float* __restrict__ K = static_cast<const float*>(p.k) + kvbase;
+  const float* __restrict__ V = static_cast<const float*>(p.v) + kvbase;
+  float* __restrict__ dK = static_cast<float*>(p.dk) + kvbase;
+  float* __restrict__ dV = static_cast<float*>(p.dv) + kvbase;
   const int kv_lim = kv_limit(p, b);
   const int k0 = kt * BK;
   const int key = k0 + kr;
@@ -183,64 +182,75 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
                                     : f32x4{};
     }
     const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
-    for (int q0 = qstart; q0 < n; q0 += BQ) {
-      __syncthreads();
-      for (int x = tid; x < BQ * C4; x += kThreads) {
-        const int r = x / C4, ch = x % C4;
-        const int q = q0 + r;
-        f32x4 a = f32x4{}, g = f32x4{};
-        if (q < n) {
-          a = *reinterpret_cast<const f32x4*>(Q + (size_t)q * D + ch * 4) * qsgn;
-          g = *reinterpret_cast<const f32x4*>(dO + (size_t)q * D + ch * 4);
+    for (int gq = 0; gq < p.group; ++gq) {
+      const int bh = q_index(p, kbh, gq);
+      const size_t base = (size_t)bh * (size_t)n * D;
+      const float* __restrict__ Q = static_cast<const float*>(p.q) + base;
+      const float* __restrict__ dO = static_cast<const float*>(p.d_o) + base;
+      const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;
+      const float* __restrict__ dvec = p.dvec + (size_t)bh * p.n_pad;
+      float* __restrict__ dQ = static_cast<float*>(p.dq) + base;
+      // Each query tile starts on a barrier, so the LDS tiles of the previous
+      // head are no longer read when this head's first tile is stored.
+      for (int q0 = qstart; q0 < n; q0 += BQ) {
+        __syncthreads();
+        for (int x = tid; x < BQ * C4; x += kThreads) {
+          const int r = x / C4, ch = x % C4;
+          const int q = q0 + r;
+          f32x4 a = f32x4{}, g = f32x4{};
+          if (q < n) {
+            a = *reinterpret_cast<const f32x4*>(Q + (size_t)q * D + ch * 4) * qsgn;
+            g = *reinterpret_cast<const f32x4*>(dO + (size_t)q * D + ch * 4);
+          }
+          sQ[r][ch] = a;
+          sdO[r][ch] = g;
         }
-        sQ[r][ch] = a;
-        sdO[r][ch] = g;
-      }
-      if (tid < BQ) {
-        const int q = q0 + tid;
-        sL[tid] = (q < n) ? l2v[q] : 0.f;
-        sDv[tid] = (q < n) ? dvec[q] : 0.f;
-      }
-      __syncthreads();
+        if (tid < BQ) {
+          const int q = q0 + tid;
+          sL[tid] = (q < n) ? l2v[q] : 0.f;
+          sDv[tid] = (q < n) ? dvec[q] : 0.f;
+        }
+        __syncthreads();
 
 #pragma unroll 4
-      for (int t = 0; t < BQ; ++t) {
-        const int q = q0 + t;
-        float sp = 0.f, dpp = 0.f;
+        for (int t = 0; t < BQ; ++t) {
+          const int q = q0 + t;
+          float sp = 0.f, dpp = 0.f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          sp += dot4(sQ[t][sub + 4 * i], k4[i]);
-          dpp += dot4(sdO[t][sub + 4 * i], v4[i]);
-        }
-        sp = quad_sum(sp);
-        dpp = quad_sum(dpp);
-        const bool hidden = q >= n || key >= kv_lim || (CAUSAL && key > q);
-        const float pr = hidden ? 0.f : __builtin_amdgcn_exp2f(fmaf(sp, cs, -sL[t]));
-        const float ds = pr * (dpp - sDv[t]);
+          for (int i = 0; i < NV; ++i) {
+            sp += dot4(sQ[t][sub + 4 * i], k4[i]);
+            dpp += dot4(sdO[t][sub + 4 * i], v4[i]);
+          }
+          sp = quad_sum(sp);
+          dpp = quad_sum(dpp);
+          const bool hidden = q >= n || key >= kv_lim || (CAUSAL && key > q);
+          const float pr = hidden ? 0.f : __builtin_amdgcn_exp2f(fmaf(sp, cs, -sL[t]));
+          const float ds = pr * (dpp - sDv[t]);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          dv4[i] += pr * sdO[t][sub + 4 * i];
-          dk4[i] += ds * sQ[t][sub + 4 * i];
+          for (int i = 0; i < NV; ++i) {
+            dv4[i] += pr * sdO[t][sub + 4 * i];
+            dk4[i] += ds * sQ[t][sub + 4 * i];
+          }
+          if (sub == 0) sdS[t][kr] = ds;
         }
-        if (sub == 0) sdS[t][kr] = ds;
-      }
-      __syncthreads();
+        __syncthreads();
 
-      // dQ[q0 + t][col] += scale * sum_r dS[t][r] K[r][col]; 16 lanes per row.
-      {
-        const int t = tid >> 4;
-        const int q = q0 + t;
-        const float* kf = reinterpret_cast<const float*>(&sK[0][0]);
-        if (q < n) {
-          for (int col = tid & 15; col < D; col += 16) {
-            float sum = 0.f;
+        // dQ[q0 + t][col] += scale * sum_r dS[t][r] K[r][col]; 16 lanes per row.
+        {
+          const int t = tid >> 4;
+          const int q = q0 + t;
+          const float* kf = reinterpret_cast<const float*>(&sK[0][0]);
+          if (q < n) {
+            for (int col = tid & 15; col < D; col += 16) {
+              float sum = 0.f;
 #pragma unroll 8
-            for (int r = 0; r < BK; ++r) sum = fmaf(sdS[t][r], kf[r * D + col], sum);
-            unsafeAtomicAdd(&dQ[(size_t)q * D + col], p.scale * sum);
+              for (int r = 0; r < BK; ++r) sum = fmaf(sdS[t][r], kf[r * D + col], sum);
+              unsafeAtomicAdd(&dQ[(size_t)q * D + col], p.scale * sum);
+            }
           }
         }
       }
-    }
+    }  // query heads of the group
   }
 
   if (key < n) {
@@ -266,7 +276,7 @@ hipError_t launch_fwd_d(const Params& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_bwd_d(const Params& p, hipStream_t s) {
-  const long long total = (long long)((p.n + 63) / 64) * p.batch * p.heads;
+  const long long total = (long long)((p.n + 63) / 64) * p.batch * p.heads_kv;
   dim3 grid((unsigned)total), block(kThreads);
   if (p.causal)
     hipLaunchKernelGGL((bwd_fp32_kernel<D, true>), grid, block, 0, s, p);

@@ -66,9 +66,11 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
   remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
   const int b = bh / p.heads;
   const size_t base = (size_t)bh * (size_t)n * D;
+  // K and V of the K/V head this query head uses (grouped heads).
+  const size_t kvbase = (size_t)kv_index(p, bh) * (size_t)n * D;
   const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
-  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + base;
-  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + base;
+  const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + kvbase;
+  const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + kvbase;
   bf16* __restrict__ O = static_cast<bf16*>(p.o) + base;
 
   const int kv_lim = kv_limit(p, b);

@@ -5,7 +5,8 @@ This module holds no attention arithmetic: it only names the workloads
 Both the HIP path and the CPU oracle are fed from it, so they see identical
 values. Draw order per workload: Q, K, V, dO as float32 standard normals
 (Q and K multiplied by ``qk_sigma``), each rounded to the workload dtype
-(bf16: round to nearest even), then the per-batch key lengths.
+(bf16: round to nearest even), then the per-batch key lengths. K and V have
+``heads_kv`` heads (grouped K/V heads), Q and dO ``heads``.
 """
 
 from __future__ import annotations
@@ -30,6 +31,11 @@ class Workload:
     padded: bool = False    # per-batch key lengths, uniform in [n/2, n]
     backward: bool = True
     scale: float | None = None  # default 1/sqrt(d)
+    heads_kv: int | None = None  # K/V heads (divides heads); default heads
+
+    @property
+    def kv_heads(self) -> int:
+        return self.heads if self.heads_kv is None else self.heads_kv
 
     @property
     def softmax_scale(self) -> float:
@@ -75,6 +81,9 @@ WORKLOADS = {w.name: w for w in [
     # long-sequence causal attention with peaky rows (Q, K ~ N(0, 3^2))
     Workload("long_causal_b1_h32_n16384_d128", 1, 32, 16384, 128, "bf16", True,
              seed=4, qk_sigma=3.0),
+    # grouped-query attention: 32 query heads sharing 8 K/V heads (groups of 4)
+    Workload("gqa_causal_b1_h32_hkv8_n16384_d128", 1, 32, 16384, 128, "bf16", True,
+             seed=5, qk_sigma=3.0, heads_kv=8),
     *_sweep(),
 ]}
 
@@ -84,24 +93,26 @@ HEADLINE = "long_causal_b1_h32_n16384_d128"
 def make_inputs(w: Workload, with_grad_out: bool = True) -> dict:
     """CPU tensors q, k, v (and do), plus kv_len (int32 [batch]) or None."""
     g = torch.Generator(device="cpu").manual_seed(w.seed)
-    shape = (w.batch, w.heads, w.n, w.d)
+    qshape = (w.batch, w.heads, w.n, w.d)
+    kvshape = (w.batch, w.kv_heads, w.n, w.d)
     dt = w.torch_dtype
 
-    def draw(sigma):
+    def draw(shape, sigma):
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         if sigma != 1.0:
             x.mul_(sigma)
         return x.to(dt)
 
-    out = {"q": draw(w.qk_sigma), "k": draw(w.qk_sigma), "v": draw(1.0)}
-    out["do"] = draw(1.0) if with_grad_out else None
+    out = {"q": draw(qshape, w.qk_sigma), "k": draw(kvshape, w.qk_sigma),
+           "v": draw(kvshape, 1.0)}
+    out["do"] = draw(qshape, 1.0) if with_grad_out else None
     out["kv_len"] = (torch.randint(w.n // 2, w.n + 1, (w.batch,), generator=g,
                                    dtype=torch.int32) if w.padded else None)
     return out
 
 
 def custom(name, batch, heads, n, d, dtype="bf16", causal=False, seed=0,
-           qk_sigma=1.0, padded=False, scale=None) -> Workload:
+           qk_sigma=1.0, padded=False, scale=None, heads_kv=None) -> Workload:
     """An ad-hoc workload (tests of edge cases: ragged n, tiny shapes...)."""
     return Workload(name, batch, heads, n, d, dtype, causal, seed, qk_sigma,
-                    padded, True, scale)
+                    padded, True, scale, heads_kv)

@@ -18,7 +18,9 @@
  * Layout:    every tensor Q, K, V, O, dO, dQ, dK, dV is a contiguous
  *            [batch, heads, n, d] array (d fastest); LSE is a contiguous
  *            [batch, heads, n] float32 array. Queries and keys have the same
- *            length n (self-attention).
+ *            length n (self-attention). The *_gqa entry points take K, V, dK
+ *            and dV as [batch, heads_kv, n, d] instead (grouped K/V heads,
+ *            below).
  * Pointers:  device pointers (memory from hipMalloc or an allocator on top of
  *            it), at least 16-byte aligned. The caller owns every buffer;
  *            the library only borrows pointers until the work it enqueued on
@@ -47,6 +49,14 @@
  *            FA_E_* code is returned. A failed kernel launch returns
  *            FA_E_LAUNCH. Faults during execution surface at the caller's
  *            next synchronisation, as with any HIP kernel.
+ * Grouped K/V heads (GQA, MQA): heads_kv divides heads, and query head h
+ *            attends with K/V head h / (heads / heads_kv): consecutive runs
+ *            of heads / heads_kv query heads share one K/V head. heads_kv =
+ *            heads is ordinary multi-head attention, heads_kv = 1 multi-query
+ *            attention. The gradient of a shared K/V head is the sum over the
+ *            query heads that use it. (Grouped and multi-query attention as
+ *            supported variants: page 1, section 九; page 4, "FlashAttention
+ *            原理深入剖析（下篇）", section 六.)
  * Threads:   entry points are reentrant; concurrent calls on different
  *            streams may share inputs but must not share outputs.
  */
@@ -60,14 +70,14 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
 
 typedef enum {
   FA_OK = 0,
   FA_E_NULLPTR = 1,     /* a required pointer is NULL                        */
-  FA_E_SHAPE = 2,       /* batch, heads or n < 1, or n too large             */
+  FA_E_SHAPE = 2,       /* bad batch, heads, heads_kv or n                   */
   FA_E_UNSUPPORTED = 3, /* d not in {64,128,256}, unknown dtype, bad scale   */
   FA_E_WORKSPACE = 4,   /* workspace NULL or smaller than required           */
   FA_E_ALIAS = 5,       /* an output overlaps an input or another output     */
@@ -97,10 +107,25 @@ fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
                  void* stream);
 
 /*
+ * fa_fwd_gqa -- fa_fwd with grouped K/V heads: k and v are
+ * [batch, heads_kv, n, d]; q, o and lse as for fa_fwd. heads_kv must be in
+ * [1, heads] and divide heads (else FA_E_SHAPE). fa_fwd(...) is
+ * fa_fwd_gqa(batch, heads, heads, ...).
+ */
+fa_status fa_fwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv,
+                     int64_t n, int64_t d,
+                     int causal, float softmax_scale, fa_dtype dtype,
+                     const void* q, const void* k, const void* v,
+                     const int32_t* kv_len,
+                     void* o, float* lse,
+                     void* stream);
+
+/*
  * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: two
  * float32 vectors, D_i = sum_k dO_ik O_ik and L_i log2(e), each with the
  * rows of every (batch, head) padded to a multiple of 64, each rounded up to
- * 256 bytes. Returns 0 for invalid sizes.
+ * 256 bytes. Returns 0 for invalid sizes. The size depends on the query
+ * heads only, so it serves fa_bwd_gqa too.
  */
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n,
                               int64_t d, fa_dtype dtype);
@@ -139,18 +164,37 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d,
                  void* stream);
 
 /*
- * fa_bwd_timed -- fa_bwd, additionally recording caller-owned HIP events on
+ * fa_bwd_gqa -- fa_bwd with grouped K/V heads: k, v, dk and dv are
+ * [batch, heads_kv, n, d]; every other tensor as for fa_bwd. dK and dV of a
+ * K/V head are the sums of the gradients through each query head of its
+ * group; they are accumulated in registers by the workgroup that owns the
+ * key tile, in a fixed head order, and written once, so they stay bitwise
+ * deterministic in bf16. heads_kv as for fa_fwd_gqa.
+ */
+fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv,
+                     int64_t n, int64_t d,
+                     int causal, float softmax_scale, fa_dtype dtype,
+                     const void* q, const void* k, const void* v,
+                     const void* o, const void* d_o, const float* lse,
+                     const int32_t* kv_len,
+                     void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * fa_bwd_timed -- fa_bwd_gqa, additionally recording caller-owned HIP events on
  * `stream` between its kernels, for measurement harnesses that time each
  * kernel with events. events[0] is recorded before the D_i kernel,
  * events[1] before the dK/dV kernel (fp32: the single backward kernel),
  * events[2] after it and events[3] after the dQ kernel (bf16) -- i.e. at
  * the end. Any entry may
  * be NULL (not recorded); `events` itself may be NULL, which makes the call
- * identical to fa_bwd. The events must have been created on the device that
+ * identical to fa_bwd_gqa. The events must have been created on the device that
  * owns `stream` (hipEventCreate); the library records them and nothing else.
  * A failed hipEventRecord returns FA_E_LAUNCH.
  */
-fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t n, int64_t d,
+fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t heads_kv,
+                       int64_t n, int64_t d,
                        int causal, float softmax_scale, fa_dtype dtype,
                        const void* q, const void* k, const void* v,
                        const void* o, const void* d_o, const float* lse,

@@ -57,9 +57,17 @@ def kv_len_of(inp, b):
     return None if inp["kv_len"] is None else int(inp["kv_len"][b])
 
 
+def group_of(inp) -> int:
+    """Query heads per K/V head (1 for ordinary multi-head inputs)."""
+    return inp["q"].shape[1] // inp["k"].shape[1]
+
+
 def check_forward_head(w, inp, gpu, b, h, rows=None, peaky=False):
-    """Compare O and LSE of head (b, h) (optionally only query ``rows``)."""
-    q, k, v = (f64(inp[x][b, h]) for x in ("q", "k", "v"))
+    """Compare O and LSE of query head (b, h) (optionally only query
+    ``rows``); K and V come from the K/V head that query head uses."""
+    j = h // group_of(inp)
+    q = f64(inp["q"][b, h])
+    k, v = (f64(inp[x][b, j]) for x in ("k", "v"))
     ref = oracle.head_forward(q, k, v, w.softmax_scale, w.causal, kv_len_of(inp, b), rows=rows)
     go = f64(gpu["o"][b, h])
     gl = gpu["lse"][b, h].cpu().double().numpy()
@@ -77,12 +85,24 @@ def check_forward_head(w, inp, gpu, b, h, rows=None, peaky=False):
 
 
 def check_backward_head(w, inp, gpu, b, h):
-    q, k, v, do = (f64(inp[x][b, h]) for x in ("q", "k", "v", "do"))
-    ref = oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal, kv_len_of(inp, b))
+    """Compare dQ of query head (b, h) and dK, dV of the K/V head it uses.
+    With grouped K/V heads the oracle runs every query head of that group
+    and sums their dK and dV (the gradient of a shared head), and the dQ of
+    each of them is compared too."""
+    grp = group_of(inp)
+    j = h // grp
+    k, v = (f64(inp[x][b, j]) for x in ("k", "v"))
     tol = FP32_REL if w.dtype == "fp32" else BF16_GRAD_REL
     errs = {}
-    for name in ("dq", "dk", "dv"):
-        errs[name] = normwise_rel(f64(gpu[name][b, h]), ref[name])
+    dk = dv = 0.0
+    for hh in range(j * grp, (j + 1) * grp):
+        q, do = (f64(inp[x][b, hh]) for x in ("q", "do"))
+        ref = oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal, kv_len_of(inp, b))
+        errs[f"dq{hh}"] = normwise_rel(f64(gpu["dq"][b, hh]), ref["dq"])
+        dk = dk + ref["dk"]
+        dv = dv + ref["dv"]
+    errs["dk"] = normwise_rel(f64(gpu["dk"][b, j]), dk)
+    errs["dv"] = normwise_rel(f64(gpu["dv"][b, j]), dv)
     assert all(e <= tol for e in errs.values()), (b, h, errs)
     return errs
 

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.fa_abi_version() == 1
+    assert B.fa_abi_version() == B.ABI_VERSION == 2
     for code, tag in ((0, "FA_OK"), (1, "FA_E_NULLPTR"), (2, "FA_E_SHAPE"),
                       (3, "FA_E_UNSUPPORTED"), (4, "FA_E_WORKSPACE"), (5, "FA_E_ALIAS"),
                       (6, "FA_E_LAUNCH"), (7, "FA_E_ALIGN")):
@@ -112,6 +112,62 @@ def test_fwd_validation(lib, kw, code):
 ])
 def test_bwd_validation(lib, kw, code):
     assert bwd(**kw) == code
+
+
+def fwd_gqa(heads_kv, **kw):
+    a = dict(SHAPE, causal=0, softmax_scale=0.125, dtype=B.FA_BF16, q=Q, k=K, v=V,
+             kv_len=None, o=O, lse=L, stream=None)
+    a.update(kw)
+    return B.fa_fwd_gqa(a["batch"], a["heads"], heads_kv, a["n"], a["d"], a["causal"],
+                        a["softmax_scale"], a["dtype"], a["q"], a["k"], a["v"],
+                        a["kv_len"], a["o"], a["lse"], a["stream"])
+
+
+def bwd_gqa(heads_kv, **kw):
+    a = dict(SHAPE, causal=1, softmax_scale=0.125, dtype=B.FA_BF16, q=Q, k=K, v=V, o=O,
+             d_o=DO, lse=L, kv_len=None, dq=DQ, dk=DK, dv=DV, workspace=WS,
+             workspace_bytes=None, stream=None)
+    a.update(kw)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = ws_bytes(a["dtype"])
+    return B.fa_bwd_gqa(a["batch"], a["heads"], heads_kv, a["n"], a["d"], a["causal"],
+                        a["softmax_scale"], a["dtype"], a["q"], a["k"], a["v"], a["o"],
+                        a["d_o"], a["lse"], a["kv_len"], a["dq"], a["dk"], a["dv"],
+                        a["workspace"], a["workspace_bytes"], a["stream"])
+
+
+# SHAPE has 3 query heads: heads_kv must be 1 or 3. One K/V head of
+# SHAPE is 64 * 64 * 2 = 8 KiB, so K + 8192 is the end of a one-head K.
+@pytest.mark.parametrize("heads_kv,kw,code", [
+    (0, {}, B.FA_E_SHAPE), (-1, {}, B.FA_E_SHAPE), (2, {}, B.FA_E_SHAPE),
+    (4, {}, B.FA_E_SHAPE), (6, {}, B.FA_E_SHAPE),
+    (1, dict(d=96), B.FA_E_UNSUPPORTED), (1, dict(k=None), B.FA_E_NULLPTR),
+    (1, dict(v=V + 8), B.FA_E_ALIGN),
+    (1, dict(o=K + 8192 - 16), B.FA_E_ALIAS),   # inside the one-head K
+    (1, dict(lse=V + 4096), B.FA_E_ALIAS),
+    (3, dict(o=K + 3 * 8192 - 16), B.FA_E_ALIAS),  # inside the three-head K
+])
+def test_fwd_gqa_validation(lib, heads_kv, kw, code):
+    assert fwd_gqa(heads_kv, **kw) == code
+
+
+@pytest.mark.parametrize("heads_kv,kw,code", [
+    (0, {}, B.FA_E_SHAPE), (2, {}, B.FA_E_SHAPE), (5, {}, B.FA_E_SHAPE),
+    (1, dict(dq=None), B.FA_E_NULLPTR), (1, dict(workspace_bytes=8), B.FA_E_WORKSPACE),
+    (1, dict(dk=K + 8192 - 16), B.FA_E_ALIAS),   # dK overlaps the one-head K
+    (1, dict(dv=DK + 8192 - 16), B.FA_E_ALIAS),  # dV overlaps the one-head dK
+    (1, dict(dq=DV + 4096), B.FA_E_ALIAS),
+    (3, dict(dv=DK + 3 * 8192 - 16), B.FA_E_ALIAS),
+])
+def test_bwd_gqa_validation(lib, heads_kv, kw, code):
+    assert bwd_gqa(heads_kv, **kw) == code
+
+
+def test_plain_entry_points_are_the_full_head_case(lib):
+    # fa_fwd / fa_bwd behave as heads_kv = heads: the K range covers all
+    # three heads, so an output placed inside the third head's K is caught.
+    assert fwd(o=K + 3 * 8192 - 16) == B.FA_E_ALIAS
+    assert bwd(dk=K + 3 * 8192 - 16) == B.FA_E_ALIAS
 
 
 def test_workspace_size_closed_form(lib):
