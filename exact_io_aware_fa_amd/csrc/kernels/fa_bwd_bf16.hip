@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       constexpr int EPS = 16 / ND;        // P/dS values per phase-1 slot
       constexpr int NP = NQB * 2 * NMB;   // phase-2 slots (2 products each)
       f32x16 s[NQB], g[NQB];
-      auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB, bool next,
+      auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB,
                       auto mask_tag) FA_INLINE {
         const int qh = it * BQ + h * 4;
         const int lo = qlo - qh;
@@ -270,22 +270,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
           }
         f32x16 s2[NQB], g2[NQB];
         bf16x8 rq[3], rg[3];
-        if (next) {
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            s2[qb] = f32x16{};
-            g2[qb] = f32x16{};
-          }
+        for (int qb = 0; qb < NQB; ++qb) {
+          s2[qb] = f32x16{};
+          g2[qb] = f32x16{};
+        }
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            rq[j] = as_bf16x8(ld16(mB + (j / ND) * 32 * D + qoff[j % ND]));
-            rg[j] = as_bf16x8(ld16(mB + TILE + (j / ND) * 32 * D + qoff[j % ND]));
-          }
+        for (int j = 0; j < 2; ++j) {
+          rq[j] = as_bf16x8(ld16(mB + (j / ND) * 32 * D + qoff[j % ND]));
+          rg[j] = as_bf16x8(ld16(mB + TILE + (j / ND) * 32 * D + qoff[j % ND]));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          if (next) {
+          {
             const int qb = j / ND, kd = j % ND;
             s2[qb] = mma32(rq[j % 3], kf[kd], s2[qb]);
             g2[qb] = mma32(rg[j % 3], vf[kd], g2[qb]);
@@ -323,12 +321,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
           dk[mb] = mma32(fq[k % 2], sfr, dk[mb]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (next) {
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            s[qb] = s2[qb];
-            g[qb] = g2[qb];
-          }
+        for (int qb = 0; qb < NQB; ++qb) {
+          s[qb] = s2[qb];
+          g[qb] = g2[qb];
         }
       };
 
@@ -342,10 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         wait_global_loads();
         __syncthreads();
         if (it + 2 < n_qt) issue(it + 2, mC, vC);
-        body(it, mA, vA, mB, true, mask_tag);
-      };
-      auto finish = [&](int it, bf16* mA, float* vA) FA_INLINE {
-        body(it, mA, vA, nullptr, false, std::true_type{});
+        body(it, mA, vA, mB, mask_tag);
       };
 
       // Masked steps: the causal diagonal band (the first kBKV / BQ tiles of
@@ -377,17 +370,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         step(it + 1, sm1, sv1, sm2, sm0, sv0, std::false_type{});
         step(it + 2, sm2, sv2, sm0, sm1, sv1, std::false_type{});
       }
-      // last - it is 0, 1 or 2 here; the last tile has no successor.
-      if (it == last) {
-        finish(it, sm0, sv0);
-      } else {
-        step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
-        if (it + 1 == last) {
-          finish(it + 1, sm1, sv1);
-        } else {
-          step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
-          finish(it + 2, sm2, sv2);
-        }
+      // last - it is 0, 1 or 2 here: one masked step per remaining tile. The
+      // step of the last tile also computes S and dP of a successor that does
+      // not exist, from the finite data left in its stage, and drops them
+      // (one tile's two products per sweep): a separate finishing body needs
+      // registers of its own and made the compiler spill the accumulators.
+      step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
+      if (it + 1 <= last) {
+        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
+        if (it + 2 <= last) step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
       }
     }  // query heads of the group
   }
