@@ -24,7 +24,8 @@ Pages this package follows (cited by title and section throughout):
 Modules:
 
 * ``attention`` -- the definition written out: S = scale * Q K^T, mask, row
-  softmax, O = P V, LSE = m + ln l, and the gradients of sum(O * dO).
+  softmax, O = P V, LSE = m + ln l, and the gradients of sum(O * dO); grouped
+  K/V heads; packed variable-length batches (page 2 4.7.2, 4.7.4).
 * ``online``    -- the pages' online-softmax algebra (three-, two- and
   one-pass forms, per-block update, associative block merge), used to pin
   ``attention`` and as the reading of the tiled recurrence.
@@ -40,6 +41,8 @@ from .attention import (  # noqa: F401
     head_backward,
     attention_fwd,
     attention_bwd,
+    varlen_fwd,
+    varlen_bwd,
     default_scale,
 )
 from . import online  # noqa: F401

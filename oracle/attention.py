@@ -48,6 +48,16 @@ shared K/V head enters every query head of its group, its gradients are the
 sums over the group:
 
     dK[g] = sum_{h in group g} dK_h,    dV[g] = sum_{h in group g} dV_h.
+
+Packed variable-length batches -- page 2 4.7.2 and 4.7.4 list attention over
+variable-length sequences without padding as a supported call, and 4.9.3
+names the padding waste it avoids; none of them fixes a layout or a mask.
+The reading here: the sequences of a batch are stored back to back, head by
+head ([H, T, d] with T the total length), sequence s occupying rows
+cu[s] .. cu[s+1]-1 of every head; each sequence is its own self-attention
+problem -- its queries see only its own keys, and the causal triangle
+counts positions from the sequence's first row -- so the whole batch is one
+block-diagonal attention over the T rows.
 """
 
 from __future__ import annotations
@@ -190,4 +200,62 @@ def attention_bwd(q, k, v, do, causal: bool = False,
             dq[b, h] = r["dq"]
             dk[b, h // grp] += r["dk"]
             dv[b, h // grp] += r["dv"]
+    return dq, dk, dv
+
+
+def _spans(cu_seqlens):
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    if len(cu) < 2 or cu[0] != 0 or any(b < a for a, b in zip(cu[:-1], cu[1:])):
+        raise ValueError("cu_seqlens must start at 0 and be non-decreasing")
+    return list(zip(cu[:-1], cu[1:]))
+
+
+def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, scale: float | None = None):
+    """Forward over a packed variable-length batch: q [H, T, d], k, v
+    [H_kv, T, d]; sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1 of
+    every head, attended to on its own (causal positions counted from its
+    first row); query head h uses K/V head h // (H // H_kv).
+
+    Returns (o [H, T, d], lse [H, T]) float64; rows past cu_seqlens[-1] stay
+    0 and -inf.
+    """
+    q = _f64(q)
+    heads, total, d = q.shape
+    grp = _group(heads, np.shape(k)[0])
+    scale = default_scale(d) if scale is None else float(scale)
+    o = np.zeros_like(q)
+    lse = np.full((heads, total), -np.inf)
+    for a, e in _spans(cu_seqlens):
+        if e == a:
+            continue
+        for h in range(heads):
+            r = head_forward(q[h, a:e], k[h // grp, a:e], v[h // grp, a:e], scale, causal)
+            o[h, a:e] = r["o"]
+            lse[h, a:e] = r["lse"]
+    return o, lse
+
+
+def varlen_bwd(q, k, v, do, cu_seqlens, causal: bool = False,
+               scale: float | None = None):
+    """Backward of ``varlen_fwd`` (gradients of sum(O * dO)); dK and dV of a
+    shared K/V head are summed over its group. Returns (dq [H,T,d],
+    dk [H_kv,T,d], dv [H_kv,T,d]) float64; rows outside every sequence are 0.
+    """
+    q = _f64(q)
+    heads, total, d = q.shape
+    heads_kv = np.shape(k)[0]
+    grp = _group(heads, heads_kv)
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros((heads_kv, total, d))
+    dv = np.zeros((heads_kv, total, d))
+    for a, e in _spans(cu_seqlens):
+        if e == a:
+            continue
+        for h in range(heads):
+            r = head_backward(q[h, a:e], k[h // grp, a:e], v[h // grp, a:e], do[h, a:e],
+                              scale, causal)
+            dq[h, a:e] = r["dq"]
+            dk[h // grp, a:e] += r["dk"]
+            dv[h // grp, a:e] += r["dv"]
     return dq, dk, dv

@@ -460,6 +460,113 @@ def test_grouped_heads_planted_mistakes_are_rejected():
 
 
 # --------------------------------------------------------------------------
+# Packed variable-length batches (page 2 4.7.2 / 4.7.4). The pins build the
+# block-diagonal mask from a segment id per row -- independently of the
+# oracle's span loop -- and hand the whole packed batch to torch's CPU float64
+# SDPA (and its autograd, and torch.logsumexp for the LSE).
+
+VARLEN_CU = [0, 5, 6, 6, 19, 27]   # lengths 5, 1, 0 (empty), 13, 8
+
+
+def _varlen_inputs(heads, heads_kv, d, seed):
+    rng = np.random.default_rng(seed)
+    t = VARLEN_CU[-1]
+    q, do = rng.standard_normal((heads, t, d)), rng.standard_normal((heads, t, d))
+    k, v = rng.standard_normal((heads_kv, t, d)), rng.standard_normal((heads_kv, t, d))
+    return q, k, v, do
+
+
+def _block_diagonal(cu, causal):
+    t = cu[-1]
+    seg = np.zeros(t, dtype=np.int64)
+    for s, (a, e) in enumerate(zip(cu[:-1], cu[1:])):
+        seg[a:e] = s
+    i, j = np.arange(t)[:, None], np.arange(t)[None, :]
+    vis = seg[:, None] == seg[None, :]
+    if causal:
+        vis &= j <= i
+    return vis
+
+
+def _torch_varlen(q, k, v, do, cu, causal, scale):
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    mask = torch.from_numpy(_block_diagonal(cu, causal))
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qt[None], kt[None], vt[None], attn_mask=mask,
+                                       scale=scale, enable_gqa=True)[0]
+    o.backward(torch.from_numpy(do))
+    grp = q.shape[0] // k.shape[0]
+    s = scale * torch.matmul(torch.from_numpy(q), torch.from_numpy(np.repeat(k, grp, 0)).transpose(1, 2))
+    lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1)
+    return (o.detach().numpy(), lse.numpy(), qt.grad.numpy(), kt.grad.numpy(),
+            vt.grad.numpy())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("heads_kv", [1, 2, 4])
+def test_varlen_matches_block_diagonal_sdpa(causal, heads_kv):
+    q, k, v, do = _varlen_inputs(4, heads_kv, 8, seed=40 + heads_kv)
+    scale = 0.41
+    o_ref, lse_ref, dq_ref, dk_ref, dv_ref = _torch_varlen(q, k, v, do, VARLEN_CU, causal, scale)
+    o, lse = oracle.varlen_fwd(q, k, v, VARLEN_CU, causal, scale)
+    dq, dk, dv = oracle.varlen_bwd(q, k, v, do, VARLEN_CU, causal, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+    for mine, theirs in ((dq, dq_ref), (dk, dk_ref), (dv, dv_ref)):
+        np.testing.assert_allclose(mine, theirs, rtol=1e-11, atol=1e-12)
+
+
+def test_varlen_single_row_sequence_returns_its_value_row():
+    # A sequence of one row sees only itself: O = V row, LSE = scale q.k.
+    q, k, v, _ = _varlen_inputs(2, 2, 4, seed=3)
+    o, lse = oracle.varlen_fwd(q, k, v, VARLEN_CU, False, 0.7)
+    np.testing.assert_array_equal(o[:, 5], v[:, 5])
+    np.testing.assert_allclose(lse[:, 5], 0.7 * (q[:, 5] * k[:, 5]).sum(-1), rtol=1e-14)
+
+
+def test_varlen_sequence_order_is_irrelevant():
+    # Permuting whole sequences permutes the outputs the same way.
+    q, k, v, do = _varlen_inputs(2, 1, 4, seed=9)
+    spans = list(zip(VARLEN_CU[:-1], VARLEN_CU[1:]))
+    order = [3, 0, 4, 1, 2]
+    rows = np.concatenate([np.arange(*spans[s]) for s in order]).astype(np.int64)
+    cu2 = np.cumsum([0] + [spans[s][1] - spans[s][0] for s in order])
+    o, _ = oracle.varlen_fwd(q, k, v, VARLEN_CU, True, 0.5)
+    o2, _ = oracle.varlen_fwd(q[:, rows], k[:, rows], v[:, rows], cu2, True, 0.5)
+    np.testing.assert_allclose(o2, o[:, rows], rtol=0, atol=1e-15)
+    dq, dk, _ = oracle.varlen_bwd(q, k, v, do, VARLEN_CU, True, 0.5)
+    dq2, dk2, _ = oracle.varlen_bwd(q[:, rows], k[:, rows], v[:, rows], do[:, rows], cu2, True, 0.5)
+    np.testing.assert_allclose(dq2, dq[:, rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dk2, dk[:, rows], rtol=0, atol=1e-14)
+
+
+def test_varlen_planted_mistakes_are_rejected(monkeypatch):
+    """Sequence spans that start one row early (the previous sequence's last
+    key leaks in, visible even under the causal mask) and the packed batch
+    treated as one sequence are both caught by the block-diagonal SDPA pin."""
+    import oracle.attention as oa
+    q, k, v, do = _varlen_inputs(2, 2, 4, seed=12)
+    o_ref = _torch_varlen(q, k, v, do, VARLEN_CU, True, 0.6)[0]
+    good = oa._spans
+    monkeypatch.setattr(oa, "_spans", lambda cu: [(max(a - 1, 0), e) for a, e in good(cu)])
+    assert not np.allclose(oracle.varlen_fwd(q, k, v, VARLEN_CU, True, 0.6)[0], o_ref, atol=1e-6)
+    monkeypatch.setattr(oa, "_spans", lambda cu: [(0, VARLEN_CU[-1])])
+    assert not np.allclose(oracle.varlen_fwd(q, k, v, VARLEN_CU, True, 0.6)[0], o_ref, atol=1e-6)
+    monkeypatch.setattr(oa, "_spans", good)
+    np.testing.assert_allclose(oracle.varlen_fwd(q, k, v, VARLEN_CU, True, 0.6)[0], o_ref,
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_varlen_rejects_bad_offsets():
+    q, k, v, _ = _varlen_inputs(1, 1, 4, seed=1)
+    with pytest.raises(ValueError):
+        oracle.varlen_fwd(q, k, v, [1, 27], False)
+    with pytest.raises(ValueError):
+        oracle.varlen_fwd(q, k, v, [0, 9, 5, 27], False)
+
+
+# --------------------------------------------------------------------------
 # Planted mistakes: each must be rejected by at least one pin
 # --------------------------------------------------------------------------
 
