@@ -28,10 +28,12 @@ null.
 on a bounded sample of the same workload -- whole heads, fwd+bwd, until about
 10 s of CPU work -- and scales it to the same TFLOP/s convention.
 
-    python bench.py --sweep [--out FILE]
+    python bench.py --sweep [--out FILE] [--only PREFIX ...]
 
 times fa_fwd and fa_bwd separately on every parity workload with a backward
-(the BERT- and GPT-2-shaped ones and the 18-point (N, d, causal) sweep):
+(the BERT- and GPT-2-shaped ones, the grouped-head one, the 18-point
+(N, d, causal) sweep and the packed variable-length batches, which use
+fa_fwd_varlen / fa_bwd_varlen):
 10 warm-up iterations, then at least 50 timed iterations and 200 ms, HIP
 events around each call; median and minimum. Per point it reports TFLOP/s,
 the fraction of the bf16 matrix-core peak and of the binding roof
@@ -243,13 +245,84 @@ def _gpu_clocks() -> str:
     return "; ".join(keep) if keep else "rocm-smi printed no clock lines"
 
 
-def run_sweep(out_path: str | None) -> int:
+def _sweep_calls(name, dev, stream):
+    """(fwd, bwd, tensors, flops_fwd, flops_bwd, bytes_fwd, bytes_bwd) of one
+    sweep workload: a padded batch (with grouped heads when k has fewer) or a
+    packed variable-length batch."""
+    import torch
+
+    from exact_io_aware_fa_amd import binding as B
+    from exact_io_aware_fa_amd.inputs import PACKED, WORKLOADS, make_inputs, make_packed_inputs
+
+    if name in PACKED:
+        w = PACKED[name]
+        inp = make_packed_inputs(w)
+        q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+        cu = inp["cu_seqlens"].to(dev)
+        hh, total, d = q.shape
+        hkv = k.shape[0]
+        nseq, mx = cu.numel() - 1, max(w.seqlens())
+        dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
+        o = torch.empty_like(q)
+        lse = torch.empty((hh, total), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        wsb = B.fa_bwd_workspace_bytes(nseq, hh, mx, d, dt)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        sc = w.softmax_scale
+
+        def fwd():
+            B.check(B.fa_fwd_varlen(nseq, hh, hkv, total, mx, d, cu.data_ptr(), w.causal, sc, dt,
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), stream))
+
+        def bwd():
+            B.check(B.fa_bwd_varlen(nseq, hh, hkv, total, mx, d, cu.data_ptr(), w.causal, sc, dt,
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                    dv.data_ptr(), ws.data_ptr(), wsb, stream))
+        e = 2 if w.dtype == "bf16" else 4
+        bf = (2.0 * hh + 2.0 * hkv) * total * d * e + 4 * hh * total
+        bb = (4.0 * hh + 4.0 * hkv) * total * d * e + 12 * hh * total
+        tensors = (q, k, v, o, do, dq, dk, dv, lse, ws, cu)
+        return fwd, bwd, tensors, w.flops_fwd(), w.flops_bwd(), bf, bb
+
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)
+    kv_ptr = None if kvl is None else kvl.data_ptr()
+    bsz, hh, n, d = q.shape
+    hkv = k.shape[1]
+    dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
+    scale = w.softmax_scale
+    o = torch.empty_like(q)
+    lse = torch.empty((bsz, hh, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsb = B.fa_bwd_workspace_bytes(bsz, hh, n, d, dt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        B.check(B.fa_fwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                             k.data_ptr(), v.data_ptr(), kv_ptr, o.data_ptr(),
+                             lse.data_ptr(), stream))
+
+    def bwd():
+        B.check(B.fa_bwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                             k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                             lse.data_ptr(), kv_ptr, dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), ws.data_ptr(), wsb, stream))
+    bf, bb = comp_bytes(w)
+    tensors = (q, k, v, o, do, dq, dk, dv, lse, ws)
+    return fwd, bwd, tensors, w.flops_fwd(), w.flops_bwd(), bf, bb
+
+
+def run_sweep(out_path: str | None, only=None) -> int:
     import statistics
 
     import torch
 
     from exact_io_aware_fa_amd import binding as B
-    from exact_io_aware_fa_amd.inputs import WORKLOADS, make_inputs
+    from exact_io_aware_fa_amd.inputs import PACKED, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py --sweep needs a GPU", file=sys.stderr)
@@ -258,37 +331,16 @@ def run_sweep(out_path: str | None) -> int:
     dev = torch.device("cuda:0")
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
-    names = [n for n, w in WORKLOADS.items() if w.backward and n.startswith(("bert", "gpt2", "sweep"))]
+    names = [n for n, w in WORKLOADS.items()
+             if w.backward and n.startswith(("bert", "gpt2", "gqa", "sweep"))] + list(PACKED)
+    if only:
+        names = [n for n in names if any(n.startswith(o) for o in only)]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     ev = [hip.create() for _ in range(2)]
     clocks_before = _gpu_clocks()
     rows = []
     for name in names:
-        w = WORKLOADS[name]
-        inp = make_inputs(w)
-        q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
-        kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)
-        kv_ptr = None if kvl is None else kvl.data_ptr()
-        bsz, hh, n, d = q.shape
-        hkv = k.shape[1]
-        dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
-        scale = w.softmax_scale
-        o = torch.empty_like(q)
-        lse = torch.empty((bsz, hh, n), dtype=torch.float32, device=dev)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        wsb = B.fa_bwd_workspace_bytes(bsz, hh, n, d, dt)
-        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-
-        def fwd():
-            B.check(B.fa_fwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
-                                 k.data_ptr(), v.data_ptr(), kv_ptr, o.data_ptr(),
-                                 lse.data_ptr(), stream))
-
-        def bwd():
-            B.check(B.fa_bwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
-                                 k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                 lse.data_ptr(), kv_ptr, dq.data_ptr(), dk.data_ptr(),
-                                 dv.data_ptr(), ws.data_ptr(), wsb, stream))
+        fwd, bwd, tensors, ff, fb, bf, bb = _sweep_calls(name, dev, stream)
 
         def timed(fn, cold):
             if cold:
@@ -307,13 +359,11 @@ def run_sweep(out_path: str | None) -> int:
             tf.append(timed(fwd, False))
             tb.append(timed(bwd, False))
             spent += tf[-1] + tb[-1]
-        working = sum(t.numel() * t.element_size() for t in (q, k, v, o, do, dq, dk, dv, lse, ws))
+        working = sum(t.numel() * t.element_size() for t in tensors)
         cf = cb = None
         if working <= 256 << 20:
             cf = statistics.median(timed(fwd, True) for _ in range(20))
             cb = statistics.median(timed(bwd, True) for _ in range(20))
-        ff, fb = w.flops_fwd(), w.flops_bwd()
-        bf, bb = comp_bytes(w)
         mf, mb = statistics.median(tf), statistics.median(tb)
         roof_f = min(PEAK_BF16_TFLOPS, ff / bf * PEAK_HBM_GBS / 1e3)
         roof_b = min(PEAK_BF16_TFLOPS, fb / bb * PEAK_HBM_GBS / 1e3)
@@ -323,7 +373,7 @@ def run_sweep(out_path: str | None) -> int:
                      3.5 * ff / (mf + mb) / 1e9, cf, cb))
         print(json.dumps({"workload": name, "fwd_ms_median": round(mf, 4), "bwd_ms_median": round(mb, 4),
                           "fwd_tflops": round(tff, 1), "bwd_tflops": round(tfb, 1)}), flush=True)
-        del q, k, v, do, o, lse, dq, dk, dv, ws
+        del fwd, bwd, tensors
         torch.cuda.empty_cache()
     for e_ in ev:
         hip.destroy(e_)
@@ -335,7 +385,8 @@ def run_sweep(out_path: str | None) -> int:
              "cache; `cold` medians write a 512 MB buffer before each call. Peak = bf16 dense "
              "MFMA %.0f TFLOP/s; roof = min(peak, compulsory-byte AI x %.0f GB/s); GB/s = "
              "compulsory bytes / time. FLOPs: 4BHN^2d forward (x2.5 backward), halved when "
-             "causal; the padded workload counts nominal FLOPs." % (PEAK_BF16_TFLOPS, PEAK_HBM_GBS), "",
+             "causal; the padded workload counts nominal FLOPs; packed (varlen) workloads "
+             "count 4Hd sum_s L_s^2." % (PEAK_BF16_TFLOPS, PEAK_HBM_GBS), "",
              "| workload | fwd ms | fwd TFLOP/s | fwd % peak | fwd % roof | fwd GB/s | bwd ms | "
              "bwd TFLOP/s | bwd % peak | bwd % roof | bwd GB/s | fwd+bwd TFLOP/s | cold fwd / bwd ms |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -375,13 +426,15 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time fwd and bwd on every sweep workload and print a table")
     ap.add_argument("--out", default=None, help="with --sweep: also write the table here")
+    ap.add_argument("--only", nargs="*", default=None, metavar="PREFIX",
+                    help="with --sweep: only the workloads whose names start so")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device three times (a plain copy "
                          "kernel of known size, to scale HBM byte counters)")
     args = ap.parse_args()
 
     if args.sweep:
-        return run_sweep(args.out)
+        return run_sweep(args.out, args.only)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the work shards by (batch, head) with no exchange; see the design notes). "

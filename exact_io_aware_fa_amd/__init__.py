@@ -2,10 +2,15 @@
 
 Python surface:
 
-* ``binding``   -- ctypes view of include/fa.h (fa_fwd, fa_bwd,
-                   fa_bwd_workspace_bytes, fa_status_str, fa_abi_version).
-* ``attention`` -- torch wrappers: ``flash_attn_fwd``, ``flash_attn_bwd`` and
-                   the autograd-enabled ``flash_attention``.
+* ``binding``   -- ctypes view of include/fa.h (fa_fwd, fa_fwd_gqa,
+                   fa_fwd_varlen, fa_bwd, fa_bwd_gqa, fa_bwd_varlen,
+                   fa_bwd_timed, fa_bwd_workspace_bytes, fa_status_str,
+                   fa_abi_version).
+* ``attention`` -- torch wrappers: ``flash_attn_fwd``, ``flash_attn_bwd``
+                   (grouped K/V heads when k, v have fewer heads),
+                   ``flash_attn_varlen_fwd``, ``flash_attn_varlen_bwd`` and the
+                   autograd-enabled ``flash_attention``,
+                   ``flash_attention_varlen``.
 * ``inputs``    -- seeded synthetic workloads.
 * ``build``     -- hipcc build of libexact_fa.so (in-tree).
 """
@@ -19,7 +24,9 @@ def __getattr__(name):
     # torch-facing helpers are imported on first use so that importing the
     # package (e.g. to build it) does not require torch.
     if name in ("flash_attention", "flash_attn_fwd", "flash_attn_bwd",
-                "FlashAttentionFunction"):
+                "FlashAttentionFunction", "flash_attention_varlen",
+                "flash_attn_varlen_fwd", "flash_attn_varlen_bwd",
+                "FlashAttentionVarlenFunction"):
         from . import attention
         return getattr(attention, name)
     raise AttributeError(name)

@@ -95,6 +95,81 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
     return dq, dk, dv
 
 
+def _check_packed(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [heads, total, d]")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q must be [heads, total, d] and k, v one [heads_kv, total, d] shape")
+    h, total, d = q.shape
+    hkv = k.shape[0]
+    if k.shape[1:] != q.shape[1:] or hkv < 1 or h % hkv:
+        raise ValueError("k and v need q's total and d, and a head count heads_kv that "
+                         "divides q's")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    return hkv
+
+
+def _cu_seqlens_arg(cu_seqlens, total, max_seqlen, device):
+    """(device int32 offsets, num_seqs, max_seqlen), checked on the host:
+    they start at 0, never decrease and end at total."""
+    host = torch.as_tensor(cu_seqlens).detach().to("cpu", torch.int64).reshape(-1)
+    if host.numel() < 2 or int(host[0]) != 0 or int(host[-1]) != total:
+        raise ValueError(f"cu_seqlens must run from 0 to total = {total}")
+    lens = host[1:] - host[:-1]
+    if int(lens.min()) < 0:
+        raise ValueError("cu_seqlens must be non-decreasing")
+    longest = max(int(lens.max()), 1)
+    if max_seqlen is None:
+        max_seqlen = longest
+    elif int(max_seqlen) < longest:
+        raise ValueError(f"max_seqlen {max_seqlen} is below the longest sequence {longest}")
+    return host.to(torch.int32).to(device), host.numel() - 1, int(max_seqlen)
+
+
+def flash_attn_varlen_fwd(q, k, v, cu_seqlens, max_seqlen=None, causal=False,
+                          softmax_scale=None):
+    """Forward over a packed variable-length batch: q [heads, total, d], k, v
+    [heads_kv, total, d]; sequence s is rows cu_seqlens[s]..cu_seqlens[s+1]-1
+    of every head and attends only to itself. Returns (o like q, lse float32
+    [heads, total])."""
+    hkv = _check_packed(q, k, v)
+    h, total, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    cu, nseq, mx = _cu_seqlens_arg(cu_seqlens, total, max_seqlen, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((h, total), dtype=torch.float32, device=q.device)
+    _b.check(_b.fa_fwd_varlen(nseq, h, hkv, total, mx, d, cu.data_ptr(), causal, scale,
+                              _DTYPES[q.dtype], q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              o.data_ptr(), lse.data_ptr(), _stream()))
+    return o, lse
+
+
+def flash_attn_varlen_bwd(q, k, v, o, lse, do, cu_seqlens, max_seqlen=None, causal=False,
+                          softmax_scale=None):
+    """Backward of ``flash_attn_varlen_fwd`` from the saved LSE: returns
+    (dq, dk, dv) shaped like q, k, v."""
+    hkv = _check_packed(q, k, v)
+    if o.shape != q.shape or do.shape != q.shape or o.dtype != q.dtype or do.dtype != q.dtype:
+        raise ValueError("o and do must match q in shape and dtype")
+    o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
+    h, total, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    cu, nseq, mx = _cu_seqlens_arg(cu_seqlens, total, max_seqlen, q.device)
+    dt = _DTYPES[q.dtype]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = _b.fa_bwd_workspace_bytes(nseq, h, mx, d, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _b.check(_b.fa_bwd_varlen(nseq, h, hkv, total, mx, d, cu.data_ptr(), causal, scale, dt,
+                              q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), ws.data_ptr(), ws_bytes, _stream()))
+    return dq, dk, dv
+
+
 class FlashAttentionFunction(torch.autograd.Function):
     """Autograd wrapper: saves q, k, v, o and the LSE; recomputes P in the
     backward kernel."""
@@ -117,3 +192,27 @@ class FlashAttentionFunction(torch.autograd.Function):
 def flash_attention(q, k, v, causal=False, softmax_scale=None, kv_len=None):
     """O = softmax(scale * Q K^T + mask) V with autograd support."""
     return FlashAttentionFunction.apply(q, k, v, causal, softmax_scale, kv_len)
+
+
+class FlashAttentionVarlenFunction(torch.autograd.Function):
+    """Autograd wrapper of the packed variable-length calls."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, softmax_scale):
+        o, lse = flash_attn_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal, softmax_scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (cu_seqlens, max_seqlen, causal, softmax_scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = flash_attn_varlen_bwd(q, k, v, o, lse, do.contiguous(), *ctx.args)
+        return dq, dk, dv, None, None, None, None
+
+
+def flash_attention_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=False,
+                           softmax_scale=None):
+    """Packed variable-length attention with autograd support."""
+    return FlashAttentionVarlenFunction.apply(q, k, v, cu_seqlens, max_seqlen, causal,
+                                              softmax_scale)

@@ -28,11 +28,12 @@ FA_E_LAUNCH = 6
 FA_E_ALIGN = 7
 
 # Every symbol include/fa.h declares.
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_bwd_gqa", "fa_bwd_timed",
-            "fa_bwd_workspace_bytes", "fa_status_str", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_bwd", "fa_bwd_gqa",
+            "fa_bwd_varlen", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_status_str",
+            "fa_abi_version")
 
 # The FA_ABI_VERSION this binding was written against.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +64,14 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_gqa.argtypes = L.fa_fwd.argtypes[:2] + [_i64] + L.fa_fwd.argtypes[2:]
         L.fa_bwd_gqa.restype = ctypes.c_int
         L.fa_bwd_gqa.argtypes = L.fa_bwd.argtypes[:2] + [_i64] + L.fa_bwd.argtypes[2:]
+        # num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens, causal,
+        # scale, dtype, then the tensors and the stream.
+        _vl = [_i64, _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_int, ctypes.c_float,
+               ctypes.c_int]
+        L.fa_fwd_varlen.restype = ctypes.c_int
+        L.fa_fwd_varlen.argtypes = _vl + [_vp, _vp, _vp, _vp, _vp, _vp]
+        L.fa_bwd_varlen.restype = ctypes.c_int
+        L.fa_bwd_varlen.argtypes = _vl + [_vp] * 9 + [_vp, ctypes.c_size_t, _vp]
         L.fa_bwd_timed.restype = ctypes.c_int
         L.fa_bwd_timed.argtypes = L.fa_bwd_gqa.argtypes + [ctypes.POINTER(_vp)]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -90,6 +99,22 @@ def fa_fwd_gqa(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k,
     return lib().fa_fwd_gqa(batch, heads, heads_kv, n, d, int(causal),
                             float(softmax_scale), int(dtype), q, k, v, kv_len, o,
                             lse, stream)
+
+
+def fa_fwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens, causal,
+                  softmax_scale, dtype, q, k, v, o, lse, stream) -> int:
+    return lib().fa_fwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens,
+                               int(causal), float(softmax_scale), int(dtype), q, k, v, o,
+                               lse, stream)
+
+
+def fa_bwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens, causal,
+                  softmax_scale, dtype, q, k, v, o, d_o, lse, dq, dk, dv, workspace,
+                  workspace_bytes, stream) -> int:
+    return lib().fa_bwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens,
+                               int(causal), float(softmax_scale), int(dtype), q, k, v, o,
+                               d_o, lse, dq, dk, dv, workspace, int(workspace_bytes),
+                               stream)
 
 
 def fa_bwd(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o, d_o,

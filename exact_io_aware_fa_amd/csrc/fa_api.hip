@@ -27,47 +27,187 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-fa_status check_common(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n,
-                       int64_t d, float scale, fa_dtype dtype) {
-  if (batch < 1 || heads < 1 || n < 1 || n > kMaxN) return FA_E_SHAPE;
-  if (batch > INT32_MAX || heads > INT32_MAX) return FA_E_SHAPE;
-  // Grouped K/V heads: every K/V head serves the same number of query heads.
-  if (heads_kv < 1 || heads_kv > heads || heads % heads_kv != 0) return FA_E_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_E_UNSUPPORTED;
-  if (dtype != FA_BF16 && dtype != FA_FP32) return FA_E_UNSUPPORTED;
-  if (!isfinite(scale)) return FA_E_UNSUPPORTED;
-  // Per-head element offsets are 32-bit; workgroup counts must fit a grid.
-  if (n * d >= (int64_t(1) << 31)) return FA_E_SHAPE;
-  const int64_t tiles = (n + 63) / 64;
-  if (tiles * batch * heads >= (int64_t(1) << 31)) return FA_E_SHAPE;
-  return FA_OK;
-}
-
 size_t elem_size(fa_dtype t) { return t == FA_BF16 ? 2 : 4; }
 
 int64_t n_padded(int64_t n) { return (n + 63) / 64 * 64; }
 
-// One per-head-padded fp32 vector of the backward workspace (D or L log2 e).
-size_t vec_bytes(int64_t batch, int64_t heads, int64_t n) {
-  const size_t b = size_t(batch) * size_t(heads) * size_t(n_padded(n)) * sizeof(float);
+// The shape of one call. A batch entry is a batch element (padded layout,
+// [batch, heads, n, d]) or one sequence of a packed batch ([heads, total, d]
+// with offsets cu_seqlens); see Params for how kernels address them.
+struct Shape {
+  int64_t entries;   // batch elements, or sequences of a packed batch
+  int64_t heads;
+  int64_t heads_kv;
+  int64_t n;         // sequence length (packed: the longest sequence)
+  int64_t rows;      // rows per head in memory (n, or the packed total)
+  int64_t mem_batch; // leading dimension in memory (entries, or 1 if packed)
+  int64_t d;
+  const int32_t* cu_seqlens;  // packed batches only
+};
+
+Shape padded_shape(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d) {
+  return Shape{batch, heads, heads_kv, n, n, batch, d, nullptr};
+}
+
+Shape packed_shape(int64_t num_seqs, int64_t heads, int64_t heads_kv, int64_t total,
+                   int64_t max_seqlen, int64_t d, const int32_t* cu_seqlens) {
+  return Shape{num_seqs, heads, heads_kv, max_seqlen, total, 1, d, cu_seqlens};
+}
+
+fa_status check_shape(const Shape& s, float scale, fa_dtype dtype) {
+  if (s.entries < 1 || s.heads < 1 || s.n < 1 || s.n > kMaxN) return FA_E_SHAPE;
+  if (s.rows < s.n) return FA_E_SHAPE;  // a packed sequence fits in the total
+  if (s.entries > INT32_MAX - 1 || s.heads > INT32_MAX || s.rows > INT32_MAX) return FA_E_SHAPE;
+  // Grouped K/V heads: every K/V head serves the same number of query heads.
+  if (s.heads_kv < 1 || s.heads_kv > s.heads || s.heads % s.heads_kv != 0) return FA_E_SHAPE;
+  if (s.d != 64 && s.d != 128 && s.d != 256) return FA_E_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_FP32) return FA_E_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_E_UNSUPPORTED;
+  // Byte offsets inside one head's rows are 31-bit; workgroup counts must fit
+  // a grid.
+  if (s.rows * s.d * int64_t(elem_size(dtype)) >= (int64_t(1) << 31)) return FA_E_SHAPE;
+  const int64_t tiles = (s.n + 63) / 64;
+  if (tiles * s.entries * s.heads >= (int64_t(1) << 31)) return FA_E_SHAPE;
+  return FA_OK;
+}
+
+// One per-entry-padded fp32 vector of the backward workspace (D or L log2 e).
+size_t vec_bytes(int64_t entries, int64_t heads, int64_t n) {
+  const size_t b = size_t(entries) * size_t(heads) * size_t(n_padded(n)) * sizeof(float);
   return (b + 255) & ~size_t(255);
 }
 
-fa::Params base_params(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n,
-                       int causal, float scale) {
+// Bytes of a tensor with `nh` heads, and of the LSE.
+size_t tensor_bytes(const Shape& s, int64_t nh, fa_dtype dtype) {
+  return size_t(s.mem_batch) * size_t(nh) * size_t(s.rows) * size_t(s.d) * elem_size(dtype);
+}
+size_t lse_bytes(const Shape& s) {
+  return size_t(s.mem_batch) * size_t(s.heads) * size_t(s.rows) * sizeof(float);
+}
+
+fa::Params base_params(const Shape& s, int causal, float scale) {
   fa::Params p{};
-  p.batch = int(batch);
-  p.heads = int(heads);
-  p.heads_kv = int(heads_kv);
-  p.group = int(heads / heads_kv);
-  p.n = int(n);
-  p.n_pad = int(n_padded(n));
+  p.cu_seqlens = s.cu_seqlens;
+  p.batch = int(s.entries);
+  p.heads = int(s.heads);
+  p.heads_kv = int(s.heads_kv);
+  p.group = int(s.heads / s.heads_kv);
+  p.n = int(s.n);
+  p.rows = int(s.rows);
+  p.n_pad = int(n_padded(s.n));
   p.causal = causal ? 1 : 0;
   float c = fabsf(scale) * 1.4426950408889634f;
   p.c = c < FLT_MIN ? FLT_MIN : c;
   p.scale = scale;
   p.q_neg = scale < 0.f ? 1 : 0;
   return p;
+}
+
+// The small device array an entry point reads besides the tensors: the key
+// lengths (padded batches) or the sequence offsets (packed batches).
+Range aux_range(const Shape& sh, const int32_t* kv_len) {
+  if (kv_len) return range_of(kv_len, size_t(sh.entries) * sizeof(int32_t));
+  if (sh.cu_seqlens) return range_of(sh.cu_seqlens, size_t(sh.entries + 1) * sizeof(int32_t));
+  return Range{0, 0};
+}
+
+fa_status fwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dtype,
+                   const void* q, const void* k, const void* v, const int32_t* kv_len,
+                   void* o, float* lse, void* stream) {
+  fa_status st = check_shape(sh, softmax_scale, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_E_ALIGN;
+  const Range ra = aux_range(sh, kv_len);
+  if (ra.lo & 3u) return FA_E_ALIGN;
+  const size_t tb = tensor_bytes(sh, sh.heads, dtype);
+  const size_t kb = tensor_bytes(sh, sh.heads_kv, dtype);
+  const Range ins[3] = {range_of(q, tb), range_of(k, kb), range_of(v, kb)};
+  const Range ro = range_of(o, tb), rl = range_of(lse, lse_bytes(sh));
+  if (overlaps(ro, rl)) return FA_E_ALIAS;
+  for (const Range& r : ins)
+    if (overlaps(r, ro) || overlaps(r, rl)) return FA_E_ALIAS;
+  if (overlaps(ra, ro) || overlaps(ra, rl)) return FA_E_ALIAS;
+
+  fa::Params p = base_params(sh, causal, softmax_scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.kv_len = kv_len;
+  p.o = o;
+  p.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, int(sh.d), s)
+                                          : fa::launch_fwd_fp32(p, int(sh.d), s);
+  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
+}
+
+fa_status bwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dtype,
+                   const void* q, const void* k, const void* v, const void* o,
+                   const void* d_o, const float* lse, const int32_t* kv_len, void* dq,
+                   void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                   void* stream, void* const events[4]) {
+  fa_status st = check_shape(sh, softmax_scale, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return FA_E_NULLPTR;
+  if (!workspace) return FA_E_WORKSPACE;
+  const size_t need = 2 * vec_bytes(sh.entries, sh.heads, sh.n);
+  if (workspace_bytes < need) return FA_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_E_ALIGN;
+  const Range ra = aux_range(sh, kv_len);
+  if (ra.lo & 3u) return FA_E_ALIGN;
+
+  const size_t tb = tensor_bytes(sh, sh.heads, dtype);
+  const size_t kb = tensor_bytes(sh, sh.heads_kv, dtype);
+  const Range ins[7] = {range_of(q, tb), range_of(k, kb),  range_of(v, kb),
+                        range_of(o, tb), range_of(d_o, tb), range_of(lse, lse_bytes(sh)),
+                        ra};
+  const Range outs[4] = {range_of(dq, tb), range_of(dk, kb), range_of(dv, kb),
+                         range_of(workspace, need)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], ins[j])) return FA_E_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return FA_E_ALIAS;
+  }
+
+  fa::Params p = base_params(sh, causal, softmax_scale);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o_in = o;
+  p.d_o = d_o;
+  p.lse = const_cast<float*>(lse);
+  p.kv_len = kv_len;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dvec = static_cast<float*>(workspace);
+  p.l2vec = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     vec_bytes(sh.entries, sh.heads, sh.n));
+  // fp32: the backward adds dQ into the caller's dq with atomics, after the
+  // prep kernel has zeroed the rows it covers.
+  p.dq_acc = (dtype == FA_FP32) ? static_cast<float*>(dq) : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    if (events == nullptr || events[i] == nullptr) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  };
+  const int d = int(sh.d);
+  const bool bf = dtype == FA_BF16;
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = fa::launch_bwd_prep(p, d, bf, s);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess)
+    e = bf ? fa::launch_bwd_dkdv_bf16(p, d, s) : fa::launch_bwd_fp32(p, d, s);
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess && bf) e = fa::launch_bwd_dq_bf16(p, d, s);
+  if (e == hipSuccess) e = mark(3);
+  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
 }
 
 }  // namespace
@@ -80,7 +220,7 @@ const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK";
     case FA_E_NULLPTR: return "FA_E_NULLPTR: a required pointer is NULL";
-    case FA_E_SHAPE: return "FA_E_SHAPE: batch, heads, heads_kv or n out of range";
+    case FA_E_SHAPE: return "FA_E_SHAPE: batch, heads, heads_kv, n or total out of range";
     case FA_E_UNSUPPORTED: return "FA_E_UNSUPPORTED: unsupported d, dtype or scale";
     case FA_E_WORKSPACE: return "FA_E_WORKSPACE: workspace missing or too small";
     case FA_E_ALIAS: return "FA_E_ALIAS: an output overlaps an input or another output";
@@ -92,7 +232,9 @@ const char* fa_status_str(fa_status s) {
 
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n, int64_t d,
                               fa_dtype dtype) {
-  if (check_common(batch, heads, 1, n, d, 1.f, dtype) != FA_OK) return 0;
+  // One padded slice per (batch entry, query head); a packed batch passes its
+  // sequence count and longest length.
+  if (check_shape(padded_shape(batch, heads, 1, n, d), 1.f, dtype) != FA_OK) return 0;
   return 2 * vec_bytes(batch, heads, n);
 }
 
@@ -100,45 +242,25 @@ fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                  float softmax_scale, fa_dtype dtype, const void* q, const void* k,
                  const void* v, const int32_t* kv_len, void* o, float* lse,
                  void* stream) {
-  return fa_fwd_gqa(batch, heads, heads, n, d, causal, softmax_scale, dtype, q, k, v,
-                    kv_len, o, lse, stream);
+  return fwd_impl(padded_shape(batch, heads, heads, n, d), causal, softmax_scale, dtype, q, k,
+                  v, kv_len, o, lse, stream);
 }
 
 fa_status fa_fwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
                      int causal, float softmax_scale, fa_dtype dtype, const void* q,
                      const void* k, const void* v, const int32_t* kv_len, void* o,
                      float* lse, void* stream) {
-  fa_status st = check_common(batch, heads, heads_kv, n, d, softmax_scale, dtype);
-  if (st != FA_OK) return st;
-  if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA_E_ALIGN;
-  if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u)) return FA_E_ALIGN;
-  const size_t row = size_t(n) * size_t(d) * elem_size(dtype);
-  const size_t tb = size_t(batch) * size_t(heads) * row;
-  const size_t kb = size_t(batch) * size_t(heads_kv) * row;
-  const size_t lb = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
-  const Range ins[3] = {range_of(q, tb), range_of(k, kb), range_of(v, kb)};
-  const Range ro = range_of(o, tb), rl = range_of(lse, lb);
-  if (overlaps(ro, rl)) return FA_E_ALIAS;
-  for (const Range& r : ins)
-    if (overlaps(r, ro) || overlaps(r, rl)) return FA_E_ALIAS;
-  if (kv_len) {
-    const Range rk = range_of(kv_len, size_t(batch) * sizeof(int32_t));
-    if (overlaps(rk, ro) || overlaps(rk, rl)) return FA_E_ALIAS;
-  }
+  return fwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
+                  k, v, kv_len, o, lse, stream);
+}
 
-  fa::Params p = base_params(batch, heads, heads_kv, n, causal, softmax_scale);
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.kv_len = kv_len;
-  p.o = o;
-  p.lse = lse;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = (dtype == FA_BF16) ? fa::launch_fwd_bf16(p, int(d), s)
-                                          : fa::launch_fwd_fp32(p, int(d), s);
-  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
+fa_status fa_fwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv, int64_t total,
+                        int64_t max_seqlen, int64_t d, const int32_t* cu_seqlens, int causal,
+                        float softmax_scale, fa_dtype dtype, const void* q, const void* k,
+                        const void* v, void* o, float* lse, void* stream) {
+  if (!cu_seqlens) return FA_E_NULLPTR;
+  return fwd_impl(packed_shape(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens),
+                  causal, softmax_scale, dtype, q, k, v, nullptr, o, lse, stream);
 }
 
 fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
@@ -146,9 +268,9 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                  const void* v, const void* o, const void* d_o, const float* lse,
                  const int32_t* kv_len, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  return fa_bwd_timed(batch, heads, heads, n, d, causal, softmax_scale, dtype, q, k, v, o,
-                      d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
-                      nullptr);
+  return bwd_impl(padded_shape(batch, heads, heads, n, d), causal, softmax_scale, dtype, q, k,
+                  v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
+                  nullptr);
 }
 
 fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
@@ -156,77 +278,32 @@ fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, 
                      const void* k, const void* v, const void* o, const void* d_o,
                      const float* lse, const int32_t* kv_len, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return fa_bwd_timed(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k, v,
-                      o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
-                      nullptr);
+  return bwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
+                  k, v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
+                  nullptr);
+}
+
+fa_status fa_bwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv, int64_t total,
+                        int64_t max_seqlen, int64_t d, const int32_t* cu_seqlens, int causal,
+                        float softmax_scale, fa_dtype dtype, const void* q, const void* k,
+                        const void* v, const void* o, const void* d_o, const float* lse,
+                        void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return FA_E_NULLPTR;
+  return bwd_impl(packed_shape(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens),
+                  causal, softmax_scale, dtype, q, k, v, o, d_o, lse, nullptr, dq, dk, dv,
+                  workspace, workspace_bytes, stream, nullptr);
 }
 
 fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
-                       int causal,
-                       float softmax_scale, fa_dtype dtype, const void* q, const void* k,
-                       const void* v, const void* o, const void* d_o, const float* lse,
-                       const int32_t* kv_len, void* dq, void* dk, void* dv,
+                       int causal, float softmax_scale, fa_dtype dtype, const void* q,
+                       const void* k, const void* v, const void* o, const void* d_o,
+                       const float* lse, const int32_t* kv_len, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, void* stream,
                        void* const events[4]) {
-  fa_status st = check_common(batch, heads, heads_kv, n, d, softmax_scale, dtype);
-  if (st != FA_OK) return st;
-  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return FA_E_NULLPTR;
-  if (!workspace) return FA_E_WORKSPACE;
-  const size_t need = fa_bwd_workspace_bytes(batch, heads, n, d, dtype);
-  if (workspace_bytes < need) return FA_E_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
-      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_E_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_E_ALIGN;
-  if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u)) return FA_E_ALIGN;
-
-  const size_t row = size_t(n) * size_t(d) * elem_size(dtype);
-  const size_t tb = size_t(batch) * size_t(heads) * row;
-  const size_t kb = size_t(batch) * size_t(heads_kv) * row;
-  const size_t lb = size_t(batch) * size_t(heads) * size_t(n) * sizeof(float);
-  Range ins[7] = {range_of(q, tb), range_of(k, kb), range_of(v, kb), range_of(o, tb),
-                  range_of(d_o, tb), range_of(lse, lb), Range{0, 0}};
-  int nin = 6;
-  if (kv_len) ins[nin++] = range_of(kv_len, size_t(batch) * sizeof(int32_t));
-  const Range outs[4] = {range_of(dq, tb), range_of(dk, kb), range_of(dv, kb),
-                         range_of(workspace, need)};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < nin; ++j)
-      if (overlaps(outs[i], ins[j])) return FA_E_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], outs[j])) return FA_E_ALIAS;
-  }
-
-  fa::Params p = base_params(batch, heads, heads_kv, n, causal, softmax_scale);
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o_in = o;
-  p.d_o = d_o;
-  p.lse = const_cast<float*>(lse);
-  p.kv_len = kv_len;
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  p.dvec = static_cast<float*>(workspace);
-  p.l2vec = reinterpret_cast<float*>(static_cast<char*>(workspace) + vec_bytes(batch, heads, n));
-  // fp32: the backward adds dQ into the caller's (zeroed) dq with atomics.
-  p.dq_acc = (dtype == FA_FP32) ? static_cast<float*>(dq) : nullptr;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> hipError_t {
-    if (events == nullptr || events[i] == nullptr) return hipSuccess;
-    return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
-  };
-  const bool bf = dtype == FA_BF16;
-  hipError_t e = mark(0);
-  if (e == hipSuccess) e = fa::launch_bwd_prep(p, int(d), bf, s);
-  if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = bf ? fa::launch_bwd_dkdv_bf16(p, int(d), s) : fa::launch_bwd_fp32(p, int(d), s);
-  if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess && bf) e = fa::launch_bwd_dq_bf16(p, int(d), s);
-  if (e == hipSuccess) e = mark(3);
-  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
+  return bwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
+                  k, v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
+                  events);
 }
 
 }  // extern "C"

@@ -8,8 +8,15 @@
 namespace fa {
 
 // Everything a kernel needs about one call; passed by value as a kernel
-// argument. Element offsets inside one (batch, head) slice fit in 32 bits
-// (n * d < 2^31 is enforced by validation); slice bases are 64-bit.
+// argument. Byte offsets inside one head's rows fit in 31 bits (enforced by
+// validation); head bases are 64-bit.
+//
+// Batch entries and memory: entry b (a batch element, or one sequence of a
+// packed variable-length batch) owns rows start .. start + len - 1 of each
+// head. Without cu_seqlens, entry b is memory batch b with start = 0 and
+// len = rows = n. With cu_seqlens, every entry lives in the single memory
+// batch [heads, rows, d], start = cu_seqlens[b], len = its length (at most
+// n, the longest), and rows = the packed total.
 struct Params {
   const void* q;
   const void* k;
@@ -17,19 +24,21 @@ struct Params {
   const void* o_in;     // backward: forward output
   const void* d_o;      // backward: upstream gradient
   const int32_t* kv_len;  // nullable, device int32[batch]
+  const int32_t* cu_seqlens;  // nullable, device int32[batch + 1]: packed batch
   void* o;              // forward output
-  float* lse;           // forward output / backward input, [B,H,N] fp32
+  float* lse;           // forward output / backward input, fp32, one per Q row
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;          // backward workspace: D_i = <dO_i, O_i>, [B*H][n_pad]
-  float* l2vec;         // backward workspace: L_i * log2(e), [B*H][n_pad]
+  float* dvec;          // backward workspace: D_i = <dO_i, O_i>, [batch*H][n_pad]
+  float* l2vec;         // backward workspace: L_i * log2(e), [batch*H][n_pad]
   float* dq_acc;        // fp32 dQ accumulator to zero (fp32 path: dq itself)
   int batch;
   int heads;            // query heads (Q, O, dO, dQ, LSE)
   int heads_kv;         // K/V heads (K, V, dK, dV); divides heads
   int group;            // heads / heads_kv: query heads per K/V head
-  int n;
+  int n;                // sequence length (packed batch: the longest one)
+  int rows;             // rows per head in memory (n, or the packed total)
   int n_pad;            // n rounded up to a multiple of 64 (workspace rows)
   int causal;
   // Scores enter exp2 as s * c where c = |scale| * log2(e), raised to at

@@ -4,8 +4,9 @@
 // term of dS = P * (dP - D) (ordinary softmax calculus: sum_j P_ij dP_ij =
 // <dO_i, O_i>; the pages name the backward's dS but print no formula) -- and
 // L_i log2(e), the saved row statistic in the base-2 units the kernels use.
-// Both vectors are written per head padded to n_pad rows (padding = 0) so
-// the backward kernels can load any 64-row slice directly. When an
+// Both vectors are written per (batch entry, head) padded to n_pad rows
+// (padding and rows past a shorter packed sequence = 0) so the backward
+// kernels can load any 64-row slice directly. When an
 // accumulator is given (fp32 path) the dQ rows are zeroed as well. D/8 lanes
 // share a row, each reading 8 elements (16 bytes for bf16) of O and dO.
 #include "fa_device.h"
@@ -42,17 +43,20 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Params p, long long 
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / G;  // padded row
   const int sub = threadIdx.x % G;
   if (row >= rows) return;  // whole G-lane groups leave together
-  const long long bh = row / p.n_pad;
-  const int i = (int)(row - bh * p.n_pad);
-  if (i >= p.n) {
+  // Work entry bh = (batch entry, query head) and its row i.
+  const int bh = (int)(row / p.n_pad);
+  const int i = (int)(row - (long long)bh * p.n_pad);
+  const int b = bh / p.heads;
+  const Span sp = batch_span(p, b);
+  if (i >= sp.len) {
     if (sub == 0) {
       p.dvec[row] = 0.f;
       p.l2vec[row] = 0.f;
     }
     return;
   }
-  const long long qrow = bh * p.n + i;
-  const size_t off = (size_t)qrow * D + sub * 8;
+  const size_t qrow = span_row0(p, sp, p.heads, bh - b * p.heads) + i;
+  const size_t off = qrow * D + sub * 8;
   float o[8], g[8];
   load8(static_cast<const T*>(p.o_in) + off, o);
   load8(static_cast<const T*>(p.d_o) + off, g);

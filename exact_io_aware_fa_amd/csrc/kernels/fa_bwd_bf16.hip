@@ -75,21 +75,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
-  const int n = p.n;
 
-  const int t_c = (n + kBKV - 1) / kBKV;
-  // kbh indexes (batch, K/V head); the workgroup sweeps the queries of every
-  // query head in that K/V head's group, one after the other.
-  int kbh, kt;
-  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, kbh, kt);
-  const int b = kbh / p.heads_kv;
-  const size_t kvbase = (size_t)kbh * (size_t)n * D;
+  const int t_c = (p.n + kBKV - 1) / kBKV;
+  // The workgroup owns a key tile of K/V head hk of batch entry b and sweeps
+  // the queries of every query head in that K/V head's group in turn.
+  int b, hk, kt;
+  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, p.batch, b, hk, kt);
+  const Span sp = batch_span(p, b);
+  const int n = sp.len;
+  if (kt * kBKV >= n) return;  // past the end of a shorter packed sequence
+  const size_t kvbase = span_row0(p, sp, p.heads_kv, hk) * D;
   const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + kvbase;
   const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + kvbase;
   bf16* __restrict__ dK = static_cast<bf16*>(p.dk) + kvbase;
   bf16* __restrict__ dV = static_cast<bf16*>(p.dv) + kvbase;
 
-  const int kv_lim = kv_limit(p, b);
+  const int kv_lim = kv_limit(p, b, n);
   const int k0 = kt * kBKV;
   const int kw0 = k0 + w * 32;
   const int mykey = kw0 + c;
@@ -180,8 +181,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
     for (int gq = 0; gq < qsw; ++gq) {
       // Query head gq of the group: its Q, dO and row vectors.
-      const int bh = q_index(p, kbh, gq);
-      const size_t base = (size_t)bh * (size_t)n * D;
+      // Work entry of query head hk * group + gq (workspace rows).
+      const int bh = b * p.heads + hk * p.group + gq;
+      const size_t base = span_row0(p, sp, p.heads, hk * p.group + gq) * D;
       const auto rq = buffer_rsrc(static_cast<const bf16*>(p.q) + base, n * ROWB);
       const auto rg = buffer_rsrc(static_cast<const bf16*>(p.d_o) + base, n * ROWB);
       const auto rl = buffer_rsrc(p.l2vec + (size_t)bh * p.n_pad, p.n_pad * 4);

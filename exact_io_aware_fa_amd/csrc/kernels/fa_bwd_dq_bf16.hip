@@ -60,22 +60,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
-  const int n = p.n;
 
-  const int t_r = (n + kBR - 1) / kBR;
-  int bh, qb;
-  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
-  const int b = bh / p.heads;
-  const size_t base = (size_t)bh * (size_t)n * D;
-  // K and V of the K/V head this query head uses (grouped heads).
-  const size_t kvbase = (size_t)kv_index(p, bh) * (size_t)n * D;
+  const int t_r = (p.n + kBR - 1) / kBR;
+  int b, hq, qb;
+  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, p.batch, b, hq, qb);
+  const int bh = b * p.heads + hq;  // work entry (workspace rows)
+  // Rows of this batch entry; K and V come from the K/V head this query
+  // head uses (grouped heads).
+  const Span sp = batch_span(p, b);
+  const int n = sp.len;
+  if (qb * kBR >= n) return;  // past the end of a shorter packed sequence
+  const size_t qrow0 = span_row0(p, sp, p.heads, hq);
+  const size_t base = qrow0 * D;
+  const size_t kvbase = span_row0(p, sp, p.heads_kv, hq / p.group) * D;
   const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
   const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + kvbase;
   const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + kvbase;
   const bf16* __restrict__ dO = static_cast<const bf16*>(p.d_o) + base;
   bf16* __restrict__ dQ = static_cast<bf16*>(p.dq) + base;
 
-  const int kv_lim = kv_limit(p, b);
+  const int kv_lim = kv_limit(p, b, n);
   const int q0 = qb * kBR;
   const int qw0 = q0 + w * 32;
   const int qi = qw0 + c;

@@ -155,42 +155,61 @@ __device__ __forceinline__ int swz_both(int row) {
 
 // Workgroup remap. The dispatcher places consecutive workgroup ids on the
 // eight XCDs in turn (id % 8), each XCD with its own L2. Hand each XCD a
-// contiguous range of the work list so that workgroups of the same
-// (batch, head) share one L2, and order the list head-major. Within a head,
-// `tile` runs from the most expensive tile down when `heavy_last_index` is
-// set (causal forward: the last query tile sees the most keys), else up from
-// tile 0 (causal backward: the first key tile sees the most queries).
+// contiguous range of the work list, ordered head-major, then by tile, with
+// the batch entry fastest: an XCD then holds a block of heads for every batch
+// entry (the same work per XCD even when the entries of a packed batch have
+// very different lengths), and within a head the tiles run from the most
+// expensive down (largest work first). `tile` counts down from the last tile
+// when `heavy_last_index` is set (causal forward: the last query tile sees
+// the most keys), else up from tile 0 (causal backward: the first key tile
+// sees the most queries).
 __device__ __forceinline__ void remap_workgroup(int wg, int total, int tiles,
-                                                bool heavy_last_index,
-                                                int& bh, int& tile) {
+                                                bool heavy_last_index, int batch,
+                                                int& b, int& head, int& tile) {
   const int xcd = wg & 7;
   const int slot = wg >> 3;
   const int per = total >> 3;
   const int rem = total & 7;
   const int idx = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  bh = idx / tiles;
-  const int t = idx - bh * tiles;
+  const int ht = idx / batch;  // head * tiles + t
+  b = idx - ht * batch;
+  head = ht / tiles;
+  const int t = ht - head * tiles;
   tile = heavy_last_index ? (tiles - 1 - t) : t;
 }
 
-// Grouped K/V heads: query head h of a batch entry uses K/V head
-// h / group (contiguous groups). kv_index maps a flat (batch, query head)
-// index to the flat (batch, K/V head) index; q_index maps a flat
-// (batch, K/V head) index and a member g of its group to the flat
-// (batch, query head) index.
-__device__ __forceinline__ int kv_index(const Params& p, int bh) {
-  return (bh / p.heads) * p.heads_kv + (bh % p.heads) / p.group;
+// Grouped K/V heads: query head h uses K/V head h / group (contiguous
+// groups of `group` query heads share one K/V head).
+
+// Rows of batch entry b: start .. start + len - 1 of each head of memory
+// batch mb (see Params). The offsets of a packed batch are clamped so that
+// every row lies inside the head's rows, whatever the device array holds.
+struct Span {
+  int start;
+  int len;
+  int mb;
+};
+__device__ __forceinline__ Span batch_span(const Params& p, int b) {
+  if (p.cu_seqlens == nullptr) return Span{0, p.n, b};
+  int a = p.cu_seqlens[b];
+  int e = p.cu_seqlens[b + 1];
+  a = a < 0 ? 0 : (a > p.rows ? p.rows : a);
+  e = e < a ? a : (e > p.rows ? p.rows : e);
+  const int len = e - a;
+  return Span{a, len < p.n ? len : p.n, 0};
 }
-__device__ __forceinline__ int q_index(const Params& p, int kbh, int g) {
-  return (kbh / p.heads_kv) * p.heads + (kbh % p.heads_kv) * p.group + g;
+// Index of the first row of entry s in head hh of a tensor with nh heads.
+__device__ __forceinline__ size_t span_row0(const Params& p, const Span& s, int nh, int hh) {
+  return ((size_t)s.mb * nh + hh) * (size_t)p.rows + s.start;
 }
 
-// Keys j >= kv_limit are hidden for this batch entry (clamped to [0, n]).
-__device__ __forceinline__ int kv_limit(const Params& p, int b) {
-  if (p.kv_len == nullptr) return p.n;
+// Keys j >= kv_limit are hidden for batch entry b of length n (clamped to
+// [0, n]).
+__device__ __forceinline__ int kv_limit(const Params& p, int b, int n) {
+  if (p.kv_len == nullptr) return n;
   int v = p.kv_len[b];
   v = v < 0 ? 0 : v;
-  return v > p.n ? p.n : v;
+  return v > n ? n : v;
 }
 
 }  // namespace fa

@@ -44,19 +44,22 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
   const int tid = threadIdx.x;
   const int row = tid >> 2;
   const int sub = tid & 3;
-  const int n = p.n;
-  const int t_r = (n + BR - 1) / BR;
-  int bh, qb;
-  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
-  const int b = bh / p.heads;
-  const size_t base = (size_t)bh * (size_t)n * D;
-  // K and V of the K/V head this query head uses (grouped heads).
-  const size_t kvbase = (size_t)kv_index(p, bh) * (size_t)n * D;
+  const int t_r = (p.n + BR - 1) / BR;
+  int b, hq, qb;
+  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, p.batch, b, hq, qb);
+  // Rows of this batch entry; K and V come from the K/V head this query
+  // head uses (grouped heads).
+  const Span sp = batch_span(p, b);
+  const int n = sp.len;
+  if (qb * BR >= n) return;  // past the end of a shorter packed sequence
+  const size_t qrow0 = span_row0(p, sp, p.heads, hq);
+  const size_t base = qrow0 * D;
+  const size_t kvbase = span_row0(p, sp, p.heads_kv, hq / p.group) * D;
   const float* __restrict__ Q = static_cast<const float*>(p.q) + base;
   const float* __restrict__ K = static_cast<const float*>(p.k) + kvbase;
   const float* __restrict__ V = static_cast<const float*>(p.v) + kvbase;
   float* __restrict__ O = static_cast<float*>(p.o) + base;
-  const int kv_lim = kv_limit(p, b);
+  const int kv_lim = kv_limit(p, b, n);
   const int q0 = qb * BR;
   const int qi = q0 + row;
   const float cs = p.c;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
     for (int i = 0; i < NV; ++i)
       *reinterpret_cast<f32x4*>(O + (size_t)qi * D + (sub + 4 * i) * 4) = acc[i] * inv;
     if (sub == 0)
-      p.lse[(size_t)bh * n + qi] = l > 0.f ? (m2 + log2f(l)) * kLn2 : kNegInf;
+      p.lse[qrow0 + qi] = l > 0.f ? (m2 + log2f(l)) * kLn2 : kNegInf;
   }
 }
 
@@ -147,19 +150,20 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
   const int tid = threadIdx.x;
   const int kr = tid >> 2;
   const int sub = tid & 3;
-  const int n = p.n;
-  const int t_c = (n + BK - 1) / BK;
-  // kbh indexes (batch, K/V head); the workgroup sweeps the queries of every
-  // query head in that K/V head's group, one after the other.
-  int kbh, kt;
-  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, kbh, kt);
-  const int b = kbh / p.heads_kv;
-  const size_t kvbase = (size_t)kbh * (size_t)n * D;
+  const int t_c = (p.n + BK - 1) / BK;
+  // The workgroup owns a key tile of K/V head hk of batch entry b and sweeps
+  // the queries of every query head in that K/V head's group in turn.
+  int b, hk, kt;
+  remap_workgroup(blockIdx.x, gridDim.x, t_c, false, p.batch, b, hk, kt);
+  const Span sp = batch_span(p, b);
+  const int n = sp.len;
+  if (kt * BK >= n) return;  // past the end of a shorter packed sequence
+  const size_t kvbase = span_row0(p, sp, p.heads_kv, hk) * D;
   const float* __restrict__ K = static_cast<const float*>(p.k) + kvbase;
   const float* __restrict__ V = static_cast<const float*>(p.v) + kvbase;
   float* __restrict__ dK = static_cast<float*>(p.dk) + kvbase;
   float* __restrict__ dV = static_cast<float*>(p.dv) + kvbase;
-  const int kv_lim = kv_limit(p, b);
+  const int kv_lim = kv_limit(p, b, n);
   const int k0 = kt * BK;
   const int key = k0 + kr;
   const float cs = p.c;
@@ -183,8 +187,9 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
     }
     const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
     for (int gq = 0; gq < p.group; ++gq) {
-      const int bh = q_index(p, kbh, gq);
-      const size_t base = (size_t)bh * (size_t)n * D;
+      // Work entry of query head hk * group + gq (workspace rows).
+      const int bh = b * p.heads + hk * p.group + gq;
+      const size_t base = span_row0(p, sp, p.heads, hk * p.group + gq) * D;
       const float* __restrict__ Q = static_cast<const float*>(p.q) + base;
       const float* __restrict__ dO = static_cast<const float*>(p.d_o) + base;
       const float* __restrict__ l2v = p.l2vec + (size_t)bh * p.n_pad;

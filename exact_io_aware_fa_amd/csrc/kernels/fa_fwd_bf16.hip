@@ -86,21 +86,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
-  const int n = p.n;
 
-  const int t_r = (n + kBR - 1) / kBR;
-  int bh, qb;
-  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, bh, qb);
-  const int b = bh / p.heads;
-  const size_t base = (size_t)bh * (size_t)n * D;
-  // K and V of the K/V head this query head uses (grouped heads).
-  const size_t kvbase = (size_t)kv_index(p, bh) * (size_t)n * D;
+  const int t_r = (p.n + kBR - 1) / kBR;
+  int b, hq, qb;
+  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, p.batch, b, hq, qb);
+  // Rows of this batch entry; K and V come from the K/V head this query
+  // head uses (grouped heads).
+  const Span sp = batch_span(p, b);
+  const int n = sp.len;
+  if (qb * kBR >= n) return;  // past the end of a shorter packed sequence
+  const size_t qrow0 = span_row0(p, sp, p.heads, hq);
+  const size_t base = qrow0 * D;
+  const size_t kvbase = span_row0(p, sp, p.heads_kv, hq / p.group) * D;
   const bf16* __restrict__ Q = static_cast<const bf16*>(p.q) + base;
   const bf16* __restrict__ K = static_cast<const bf16*>(p.k) + kvbase;
   const bf16* __restrict__ V = static_cast<const bf16*>(p.v) + kvbase;
   bf16* __restrict__ O = static_cast<bf16*>(p.o) + base;
 
-  const int kv_lim = kv_limit(p, b);
+  const int kv_lim = kv_limit(p, b, n);
   const int q0 = qb * kBR;
   // Rows of wave w: the two waves of a SIMD (w and w + 4) take neighbouring
   // 32-row blocks, so both groups span the workgroup's 256 rows and reach
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
         *reinterpret_cast<u32x2*>(orow + mb * 32 + g * 8 + h * 4) = u;
       }
     if (h == 0)
-      p.lse[(size_t)bh * n + qi] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+      p.lse[qrow0 + qi] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
   }
 }
 

@@ -55,6 +55,84 @@ class Workload:
         return 2.5 * self.flops_fwd()
 
 
+@dataclasses.dataclass(frozen=True)
+class PackedWorkload:
+    """A packed variable-length batch: sequences back to back per head,
+    [heads, total, d]. Lengths are drawn uniformly from ``len_range`` until
+    they reach ``total`` (the last one cut to fit), unless given."""
+    name: str
+    heads: int
+    heads_kv: int
+    total: int
+    len_range: tuple
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+    qk_sigma: float = 1.0
+    scale: float | None = None
+    lengths: tuple | None = None
+    backward: bool = True
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def _draw_lengths(self, g) -> list:
+        if self.lengths is not None:
+            return [int(x) for x in self.lengths]
+        lo, hi = self.len_range
+        out, left = [], self.total
+        while left > 0:
+            x = int(torch.randint(lo, hi + 1, (1,), generator=g))
+            out.append(min(x, left))
+            left -= out[-1]
+        return out
+
+    def seqlens(self) -> list:
+        return self._draw_lengths(torch.Generator(device="cpu").manual_seed(self.seed))
+
+    def cu_seqlens(self) -> list:
+        out = [0]
+        for x in self.seqlens():
+            out.append(out[-1] + x)
+        return out
+
+    def flops_fwd(self) -> float:
+        """4 H d sum_s L_s^2, halved when causal."""
+        f = 4.0 * self.heads * self.d * sum(x * x for x in self.seqlens())
+        return f / 2 if self.causal else f
+
+    def flops_bwd(self) -> float:
+        return 2.5 * self.flops_fwd()
+
+
+def make_packed_inputs(w: PackedWorkload, with_grad_out: bool = True) -> dict:
+    """CPU tensors q [H, T, d], k, v [H_kv, T, d] (and do), and cu_seqlens
+    (int32 [num_seqs + 1]). Draw order: the lengths, then Q, K, V, dO."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    lens = w._draw_lengths(g)
+    total = sum(lens)
+    dt = w.torch_dtype
+
+    def draw(heads, sigma):
+        x = torch.randn((heads, total, w.d), generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        return x.to(dt)
+
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    out = {"q": draw(w.heads, w.qk_sigma), "k": draw(w.heads_kv, w.qk_sigma),
+           "v": draw(w.heads_kv, 1.0), "cu_seqlens": cu}
+    out["do"] = draw(w.heads, 1.0) if with_grad_out else None
+    return out
+
+
 def _sweep():
     out = []
     idx = 0
@@ -85,6 +163,15 @@ WORKLOADS = {w.name: w for w in [
     Workload("gqa_causal_b1_h32_hkv8_n16384_d128", 1, 32, 16384, 128, "bf16", True,
              seed=5, qk_sigma=3.0, heads_kv=8),
     *_sweep(),
+]}
+
+# Packed variable-length batches (no padding): a causal mix of document
+# lengths for long-context training and a BERT-like encoder mix.
+PACKED = {w.name: w for w in [
+    PackedWorkload("varlen_causal_h32_t16384_d128", 32, 32, 16384, (256, 4096), 128, "bf16",
+                   True, seed=6),
+    PackedWorkload("varlen_bert_h16_t32768_d64", 16, 16, 32768, (64, 512), 64, "bf16",
+                   False, seed=7),
 ]}
 
 HEADLINE = "long_causal_b1_h32_n16384_d128"

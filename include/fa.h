@@ -20,7 +20,7 @@
  *            [batch, heads, n] float32 array. Queries and keys have the same
  *            length n (self-attention). The *_gqa entry points take K, V, dK
  *            and dV as [batch, heads_kv, n, d] instead (grouped K/V heads,
- *            below).
+ *            below); the *_varlen entry points take packed batches (below).
  * Pointers:  device pointers (memory from hipMalloc or an allocator on top of
  *            it), at least 16-byte aligned. The caller owns every buffer;
  *            the library only borrows pointers until the work it enqueued on
@@ -32,6 +32,9 @@
  *            nearest-even. FA_FP32 -- every tensor is float32 and every step
  *            computes in float32 (no bf16 rounding anywhere).
  * d:         64, 128 or 256 (bf16 and fp32).
+ * Sizes:     1 <= n <= 2^22 (packed batches: max_seqlen, with total >=
+ *            max_seqlen); one head's rows must occupy less than 2 GiB
+ *            (rows x d x element size < 2^31 bytes); otherwise FA_E_SHAPE.
  * Masks:     causal != 0 hides key j from query i when j > i (the upper-right
  *            triangle). kv_len, when not NULL, is a device int32[batch]; key
  *            j of batch b is hidden from every query row when
@@ -57,6 +60,20 @@
  *            query heads that use it. (Grouped and multi-query attention as
  *            supported variants: page 1, section 九; page 4, "FlashAttention
  *            原理深入剖析（下篇）", section 六.)
+ * Packed variable-length batches (*_varlen): num_seqs sequences stored
+ *            back to back, head by head: Q, O, dO, dQ are [heads, total, d],
+ *            K, V, dK, dV [heads_kv, total, d], LSE [heads, total] float32.
+ *            cu_seqlens is a device int32[num_seqs + 1] of offsets:
+ *            sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1] - 1 of
+ *            every head, and attends only to itself; causal positions count
+ *            from its first row (a block-diagonal mask over the total rows).
+ *            The offsets must start at 0, be non-decreasing, and no length
+ *            may exceed max_seqlen. They are read on the device only (no
+ *            host synchronisation); the kernels clamp them to [0, total] and
+ *            each length to max_seqlen, so other values cannot cause an
+ *            out-of-bounds access, and rows outside every sequence are left
+ *            unwritten. (Variable-length batches without padding: page 2,
+ *            "4. FlashAttention 深度剖析", 4.7.2 and 4.7.4.)
  * Threads:   entry points are reentrant; concurrent calls on different
  *            streams may share inputs but must not share outputs.
  */
@@ -70,14 +87,14 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
 
 typedef enum {
   FA_OK = 0,
   FA_E_NULLPTR = 1,     /* a required pointer is NULL                        */
-  FA_E_SHAPE = 2,       /* bad batch, heads, heads_kv or n                   */
+  FA_E_SHAPE = 2,       /* bad batch, heads, heads_kv, n or total            */
   FA_E_UNSUPPORTED = 3, /* d not in {64,128,256}, unknown dtype, bad scale   */
   FA_E_WORKSPACE = 4,   /* workspace NULL or smaller than required           */
   FA_E_ALIAS = 5,       /* an output overlaps an input or another output     */
@@ -121,11 +138,26 @@ fa_status fa_fwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv,
                      void* stream);
 
 /*
+ * fa_fwd_varlen -- forward over a packed variable-length batch (layout and
+ * offsets as described above). total >= max_seqlen >= 1; q, o: [heads,
+ * total, d]; k, v: [heads_kv, total, d]; lse: float32 [heads, total]. No key
+ * padding argument: each sequence's keys are exactly its rows.
+ */
+fa_status fa_fwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv,
+                        int64_t total, int64_t max_seqlen, int64_t d,
+                        const int32_t* cu_seqlens,
+                        int causal, float softmax_scale, fa_dtype dtype,
+                        const void* q, const void* k, const void* v,
+                        void* o, float* lse,
+                        void* stream);
+
+/*
  * fa_bwd_workspace_bytes -- size of the scratch buffer fa_bwd needs: two
  * float32 vectors, D_i = sum_k dO_ik O_ik and L_i log2(e), each with the
- * rows of every (batch, head) padded to a multiple of 64, each rounded up to
- * 256 bytes. Returns 0 for invalid sizes. The size depends on the query
- * heads only, so it serves fa_bwd_gqa too.
+ * rows of every (batch entry, head) padded to a multiple of 64, each rounded
+ * up to 256 bytes. Returns 0 for invalid sizes. The size depends on the
+ * query heads only, so it serves fa_bwd_gqa too; for fa_bwd_varlen pass
+ * batch = num_seqs and n = max_seqlen.
  */
 size_t fa_bwd_workspace_bytes(int64_t batch, int64_t heads, int64_t n,
                               int64_t d, fa_dtype dtype);
@@ -180,6 +212,23 @@ fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv,
                      void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * fa_bwd_varlen -- backward over a packed variable-length batch: the
+ * gradients of fa_bwd for each sequence on its own, with the layouts of
+ * fa_fwd_varlen (dq like q; dk, dv like k, v). workspace: at least
+ * fa_bwd_workspace_bytes(num_seqs, heads, max_seqlen, d, dtype) bytes. Rows
+ * outside every sequence are left unwritten.
+ */
+fa_status fa_bwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv,
+                        int64_t total, int64_t max_seqlen, int64_t d,
+                        const int32_t* cu_seqlens,
+                        int causal, float softmax_scale, fa_dtype dtype,
+                        const void* q, const void* k, const void* v,
+                        const void* o, const void* d_o, const float* lse,
+                        void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * fa_bwd_timed -- fa_bwd_gqa, additionally recording caller-owned HIP events on

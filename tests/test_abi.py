@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.fa_abi_version() == B.ABI_VERSION == 2
+    assert B.fa_abi_version() == B.ABI_VERSION == 3
     for code, tag in ((0, "FA_OK"), (1, "FA_E_NULLPTR"), (2, "FA_E_SHAPE"),
                       (3, "FA_E_UNSUPPORTED"), (4, "FA_E_WORKSPACE"), (5, "FA_E_ALIAS"),
                       (6, "FA_E_LAUNCH"), (7, "FA_E_ALIGN")):
@@ -168,6 +168,66 @@ def test_plain_entry_points_are_the_full_head_case(lib):
     # three heads, so an output placed inside the third head's K is caught.
     assert fwd(o=K + 3 * 8192 - 16) == B.FA_E_ALIAS
     assert bwd(dk=K + 3 * 8192 - 16) == B.FA_E_ALIAS
+
+
+CU = 0x0c00_0000  # fake offsets array, below every tensor
+PACKED = dict(num_seqs=3, heads=2, heads_kv=1, total=200, max_seqlen=90, d=64)
+
+
+def fwd_varlen(**kw):
+    a = dict(PACKED, cu=CU, causal=1, softmax_scale=0.125, dtype=B.FA_BF16, q=Q, k=K, v=V,
+             o=O, lse=L, stream=None)
+    a.update(kw)
+    return B.fa_fwd_varlen(a["num_seqs"], a["heads"], a["heads_kv"], a["total"],
+                           a["max_seqlen"], a["d"], a["cu"], a["causal"], a["softmax_scale"],
+                           a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["stream"])
+
+
+def bwd_varlen(**kw):
+    a = dict(PACKED, cu=CU, causal=1, softmax_scale=0.125, dtype=B.FA_BF16, q=Q, k=K, v=V,
+             o=O, d_o=DO, lse=L, dq=DQ, dk=DK, dv=DV, workspace=WS, workspace_bytes=None,
+             stream=None)
+    a.update(kw)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = B.fa_bwd_workspace_bytes(a["num_seqs"], a["heads"],
+                                                        a["max_seqlen"], a["d"], a["dtype"])
+    return B.fa_bwd_varlen(a["num_seqs"], a["heads"], a["heads_kv"], a["total"],
+                           a["max_seqlen"], a["d"], a["cu"], a["causal"], a["softmax_scale"],
+                           a["dtype"], a["q"], a["k"], a["v"], a["o"], a["d_o"], a["lse"],
+                           a["dq"], a["dk"], a["dv"], a["workspace"], a["workspace_bytes"],
+                           a["stream"])
+
+
+# One head of PACKED is 200 * 64 * 2 = 25600 bytes; its LSE 800 bytes per head.
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), B.FA_E_NULLPTR), (dict(num_seqs=0), B.FA_E_SHAPE),
+    (dict(max_seqlen=0), B.FA_E_SHAPE), (dict(max_seqlen=201), B.FA_E_SHAPE),
+    (dict(heads_kv=3), B.FA_E_SHAPE), (dict(d=80), B.FA_E_UNSUPPORTED),
+    (dict(total=1 << 23, max_seqlen=1 << 22, d=256), B.FA_E_SHAPE),  # a head >= 2 GiB
+    (dict(cu=CU + 2), B.FA_E_ALIGN), (dict(q=Q + 8), B.FA_E_ALIGN),
+    (dict(o=K + 25600 - 16), B.FA_E_ALIAS),      # inside the one-head K
+    (dict(o=Q + 2 * 25600 - 16), B.FA_E_ALIAS),  # inside the two-head Q
+    (dict(lse=CU), B.FA_E_ALIAS),                # over the offsets
+    (dict(lse=O + 256), B.FA_E_ALIAS),
+])
+def test_fwd_varlen_validation(lib, kw, code):
+    assert fwd_varlen(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), B.FA_E_NULLPTR), (dict(max_seqlen=300), B.FA_E_SHAPE),
+    (dict(dk=None), B.FA_E_NULLPTR), (dict(workspace_bytes=64), B.FA_E_WORKSPACE),
+    (dict(cu=CU + 1), B.FA_E_ALIGN),
+    (dict(dq=CU), B.FA_E_ALIAS), (dict(dv=DK + 25600 - 16), B.FA_E_ALIAS),
+    (dict(workspace=L), B.FA_E_ALIAS),
+])
+def test_bwd_varlen_validation(lib, kw, code):
+    assert bwd_varlen(**kw) == code
+
+
+def test_varlen_workspace_is_per_sequence_and_head(lib):
+    # num_seqs x heads slices of max_seqlen rows padded to 64: 3 x 2 x 128.
+    assert B.fa_bwd_workspace_bytes(3, 2, 90, 64, B.FA_BF16) == 2 * 3072
 
 
 def test_workspace_size_closed_form(lib):
