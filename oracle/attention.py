@@ -49,6 +49,19 @@ sums over the group:
 
     dK[g] = sum_{h in group g} dK_h,    dV[g] = sum_{h in group g} dV_h.
 
+Sliding windows and block-sparse masks -- page 4 下篇 section 六 shows the
+flash-attn call's ``window_size=(-1, -1)`` argument (full attention by
+default, a sliding window otherwise) and page 2 4.8.1 names the sliding
+window of Mistral; page 3 第八部分 describes block-sparse attention with a
+coarse block-level mask matrix whose fully masked blocks are skipped. The
+readings here: a window (left, right) keeps key j for query i iff
+i - left <= j <= i + right, where -1 leaves that side unbounded (so causal
+is the same as right = 0); a block mask is a boolean matrix over blocks of
+BLOCK x BLOCK (query block i // BLOCK, key block j // BLOCK), BLOCK = 128,
+and a key is visible only where its block is. Every mask combines with the
+others by logical AND; a query row left with no visible key gets O = 0,
+LSE = -inf and zero gradients (as above).
+
 Packed variable-length batches -- page 2 4.7.2 and 4.7.4 list attention over
 variable-length sequences without padding as a supported call, and 4.9.3
 names the padding waste it avoids; none of them fixes a layout or a mask.
@@ -73,12 +86,17 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
+BLOCK = 128  # side of a block of the block-sparse mask (rows and keys)
+
+
 def visible_mask(n: int, causal: bool, kv_len_b: int | None = None,
-                 rows=None) -> np.ndarray:
+                 rows=None, window=(-1, -1), block_mask=None) -> np.ndarray:
     """Boolean [len(rows), n]: True where key j is visible to query i.
 
     Causal hides j > i (page 3 第八部分, upper-right triangle); key padding
-    hides j >= kv_len_b for every query row.
+    hides j >= kv_len_b for every query row; a window (left, right) hides
+    j < i - left (left >= 0) and j > i + right (right >= 0); a block mask
+    hides j wherever block_mask[i // BLOCK][j // BLOCK] is false.
     """
     i = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
     j = np.arange(n)
@@ -87,6 +105,14 @@ def visible_mask(n: int, causal: bool, kv_len_b: int | None = None,
         vis &= (j[None, :] < int(kv_len_b))
     if causal:
         vis &= (j[None, :] <= i[:, None])
+    left, right = int(window[0]), int(window[1])
+    if left >= 0:
+        vis &= (j[None, :] >= i[:, None] - left)
+    if right >= 0:
+        vis &= (j[None, :] <= i[:, None] + right)
+    if block_mask is not None:
+        bm = np.asarray(block_mask).astype(bool)
+        vis &= bm[i[:, None] // BLOCK, j[None, :] // BLOCK]
     return vis
 
 
@@ -96,7 +122,7 @@ def _f64(x) -> np.ndarray:
 
 def head_forward(q, k, v, scale: float, causal: bool,
                  kv_len_b: int | None = None, rows=None,
-                 want_p: bool = False) -> dict:
+                 want_p: bool = False, window=(-1, -1), block_mask=None) -> dict:
     """Forward of one head. q, k, v: [n, d] (any real dtype, upcast exactly).
 
     ``rows`` selects query rows (each output row depends on its own query row
@@ -106,7 +132,7 @@ def head_forward(q, k, v, scale: float, causal: bool,
     q, k, v = _f64(q), _f64(k), _f64(v)
     n = k.shape[0]
     qr = q if rows is None else q[np.asarray(rows, dtype=np.int64)]
-    vis = visible_mask(n, causal, kv_len_b, rows)
+    vis = visible_mask(n, causal, kv_len_b, rows, window, block_mask)
 
     s = scale * (qr @ k.T)
     s = np.where(vis, s, -np.inf)
@@ -126,13 +152,14 @@ def head_forward(q, k, v, scale: float, causal: bool,
 
 
 def head_backward(q, k, v, do, scale: float, causal: bool,
-                  kv_len_b: int | None = None) -> dict:
+                  kv_len_b: int | None = None, window=(-1, -1), block_mask=None) -> dict:
     """Gradients of f = sum(O * dO) for one head; q, k, v, do: [n, d].
 
     Returns dict(dq, dk, dv, d=D vector, o, lse).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    fw = head_forward(q, k, v, scale, causal, kv_len_b, want_p=True)
+    fw = head_forward(q, k, v, scale, causal, kv_len_b, want_p=True, window=window,
+                      block_mask=block_mask)
     p = fw.pop("p")
     dv = p.T @ do
     dp = do @ v.T
@@ -155,7 +182,7 @@ def _group(heads: int, heads_kv: int) -> int:
 
 
 def attention_fwd(q, k, v, causal: bool = False, scale: float | None = None,
-                  kv_len=None):
+                  kv_len=None, window=(-1, -1), block_mask=None):
     """Forward over q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv divides H;
     H_kv = H is ordinary multi-head attention), one query head at a time;
     query head h uses K/V head h // (H // H_kv).
@@ -171,14 +198,15 @@ def attention_fwd(q, k, v, causal: bool = False, scale: float | None = None,
     for b in range(bsz):
         kvl = _kv_len_of(kv_len, b)
         for h in range(heads):
-            r = head_forward(q[b, h], k[b, h // grp], v[b, h // grp], scale, causal, kvl)
+            r = head_forward(q[b, h], k[b, h // grp], v[b, h // grp], scale, causal, kvl,
+                             window=window, block_mask=block_mask)
             o[b, h] = r["o"]
             lse[b, h] = r["lse"]
     return o, lse
 
 
 def attention_bwd(q, k, v, do, causal: bool = False,
-                  scale: float | None = None, kv_len=None):
+                  scale: float | None = None, kv_len=None, window=(-1, -1), block_mask=None):
     """Backward over q, do [B, H, N, d] and k, v [B, H_kv, N, d], one query
     head at a time; dK and dV of a shared K/V head are summed over its group.
 
@@ -196,7 +224,7 @@ def attention_bwd(q, k, v, do, causal: bool = False,
         kvl = _kv_len_of(kv_len, b)
         for h in range(heads):
             r = head_backward(q[b, h], k[b, h // grp], v[b, h // grp], do[b, h], scale,
-                              causal, kvl)
+                              causal, kvl, window, block_mask)
             dq[b, h] = r["dq"]
             dk[b, h // grp] += r["dk"]
             dv[b, h // grp] += r["dv"]
@@ -210,7 +238,8 @@ def _spans(cu_seqlens):
     return list(zip(cu[:-1], cu[1:]))
 
 
-def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, scale: float | None = None):
+def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, scale: float | None = None,
+               window=(-1, -1), block_mask=None):
     """Forward over a packed variable-length batch: q [H, T, d], k, v
     [H_kv, T, d]; sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1 of
     every head, attended to on its own (causal positions counted from its
@@ -229,14 +258,15 @@ def varlen_fwd(q, k, v, cu_seqlens, causal: bool = False, scale: float | None = 
         if e == a:
             continue
         for h in range(heads):
-            r = head_forward(q[h, a:e], k[h // grp, a:e], v[h // grp, a:e], scale, causal)
+            r = head_forward(q[h, a:e], k[h // grp, a:e], v[h // grp, a:e], scale, causal,
+                             window=window, block_mask=block_mask)
             o[h, a:e] = r["o"]
             lse[h, a:e] = r["lse"]
     return o, lse
 
 
 def varlen_bwd(q, k, v, do, cu_seqlens, causal: bool = False,
-               scale: float | None = None):
+               scale: float | None = None, window=(-1, -1), block_mask=None):
     """Backward of ``varlen_fwd`` (gradients of sum(O * dO)); dK and dV of a
     shared K/V head are summed over its group. Returns (dq [H,T,d],
     dk [H_kv,T,d], dv [H_kv,T,d]) float64; rows outside every sequence are 0.
@@ -254,7 +284,7 @@ def varlen_bwd(q, k, v, do, cu_seqlens, causal: bool = False,
             continue
         for h in range(heads):
             r = head_backward(q[h, a:e], k[h // grp, a:e], v[h // grp, a:e], do[h, a:e],
-                              scale, causal)
+                              scale, causal, None, window, block_mask)
             dq[h, a:e] = r["dq"]
             dk[h // grp, a:e] += r["dk"]
             dv[h // grp, a:e] += r["dv"]

@@ -650,3 +650,113 @@ def test_planted_mistakes_are_rejected():
     for kind in ("dropped_d_term", "transposed_ds_in_dk", "dropped_scale_in_dq",
                  "dv_not_transposed"):
         assert _fd_check(head_forward, mutate_backward(kind), True, 6) > 1e-3, kind
+
+
+# --------------------------------------------------------------------------
+# Sliding windows and block-sparse masks (page 4 下篇 section 六's
+# window_size; page 3 第八部分's block-level mask). The pins build the mask
+# element by element in plain Python loops -- independently of the oracle's
+# vectorised visible_mask -- and hand it to torch's CPU float64 SDPA.
+
+def _brute_visible(n, causal, kv_len, window, block_mask, block=128):
+    vis = np.zeros((n, n), dtype=bool)
+    left, right = window
+    for i in range(n):
+        for j in range(n):
+            ok = True
+            if causal and j > i:
+                ok = False
+            if kv_len is not None and j >= kv_len:
+                ok = False
+            if left >= 0 and j < i - left:
+                ok = False
+            if right >= 0 and j > i + right:
+                ok = False
+            if block_mask is not None and not block_mask[i // block][j // block]:
+                ok = False
+            vis[i, j] = ok
+    return vis
+
+
+def _asym_block_mask(n, seed):
+    nb = (n + 127) // 128
+    rng = np.random.default_rng(seed)
+    bm = rng.random((nb, nb)) < 0.6
+    bm[0, 1], bm[1, 0] = True, False  # not symmetric: a transposed mask differs
+    return bm
+
+
+MASK_CASES = [
+    # (causal, kv_len, window, use_block_mask)
+    (False, None, (37, 5), False),
+    (True, None, (100, -1), False),
+    (False, 250, (-1, 60), False),
+    (False, None, (-1, -1), True),
+    (True, 280, (-1, -1), True),
+    (False, None, (150, 150), True),
+]
+
+
+@pytest.mark.parametrize("causal,kv_len,window,use_bm", MASK_CASES)
+def test_window_and_block_masks_match_brute_force_sdpa(causal, kv_len, window, use_bm):
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    n, d, scale = 300, 8, 0.3
+    bm = _asym_block_mask(n, 7) if use_bm else None
+    vis = _brute_visible(n, causal, kv_len, window, bm)
+    np.testing.assert_array_equal(visible_mask(n, causal, kv_len, None, window, bm), vis)
+    rng = np.random.default_rng(11)
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    keep = vis.any(axis=1)  # SDPA gives NaN on rows with no visible key
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    o_ref = F.scaled_dot_product_attention(qt[None], kt[None], vt[None],
+                                           attn_mask=torch.from_numpy(vis), scale=scale)[0]
+    o_ref = torch.where(torch.from_numpy(keep)[:, None], o_ref, torch.zeros_like(o_ref))
+    o_ref.backward(torch.from_numpy(do))
+    r = head_backward(q, k, v, do, scale, causal, kv_len, window, bm)
+    np.testing.assert_allclose(r["o"], o_ref.detach().numpy(), rtol=1e-12, atol=1e-13)
+    for name, t in (("dq", qt), ("dk", kt), ("dv", vt)):
+        g = np.nan_to_num(t.grad.numpy())
+        np.testing.assert_allclose(r[name], g, rtol=1e-11, atol=1e-12)
+    assert np.all(r["lse"][~keep] == -np.inf) and np.all(r["o"][~keep] == 0.0)
+
+
+def test_zero_window_returns_each_rows_own_value():
+    rng = np.random.default_rng(2)
+    q, k, v = (rng.standard_normal((50, 4)) for _ in range(3))
+    r = head_forward(q, k, v, 0.9, False, window=(0, 0))
+    np.testing.assert_array_equal(r["o"], v)
+    np.testing.assert_allclose(r["lse"], 0.9 * (q * k).sum(1), rtol=1e-14)
+
+
+def test_diagonal_block_mask_equals_packed_sequences_of_one_block():
+    # Only the diagonal blocks kept = independent sequences of 128 rows: the
+    # packed-batch oracle (slices, no block mask) must agree.
+    rng = np.random.default_rng(4)
+    n, d = 384, 8
+    q, k, v, do = (rng.standard_normal((1, n, d)) for _ in range(4))
+    bm = np.eye(3, dtype=bool)
+    o, lse = oracle.attention_fwd(q[None], k[None], v[None], True, 0.4, block_mask=bm)
+    o2, lse2 = oracle.varlen_fwd(q, k, v, [0, 128, 256, 384], True, 0.4)
+    np.testing.assert_allclose(o[0], o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse[0], lse2, rtol=1e-13)
+    g = oracle.attention_bwd(q[None], k[None], v[None], do[None], True, 0.4, block_mask=bm)
+    g2 = oracle.varlen_bwd(q, k, v, do, [0, 128, 256, 384], True, 0.4)
+    for a, b in zip(g, g2):
+        np.testing.assert_allclose(a[0], b, rtol=1e-12, atol=1e-13)
+
+
+def test_window_and_block_planted_mistakes_are_rejected():
+    n = 300
+    bm = _asym_block_mask(n, 7)
+    ref = _brute_visible(n, False, None, (37, 5), None)
+    # window lower edge off by one (j > i - left instead of j >= i - left)
+    i, j = np.arange(n)[:, None], np.arange(n)[None, :]
+    wrong = (j > i - 37) & (j <= i + 5)
+    assert not np.array_equal(wrong, ref)
+    assert np.array_equal(visible_mask(n, False, None, None, (37, 5)), ref)
+    # block mask read transposed
+    ref_b = _brute_visible(n, False, None, (-1, -1), bm)
+    wrong_b = visible_mask(n, False, None, None, (-1, -1), bm.T)
+    assert not np.array_equal(wrong_b, ref_b)
+    assert np.array_equal(visible_mask(n, False, None, None, (-1, -1), bm), ref_b)
