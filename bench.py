@@ -272,14 +272,14 @@ def _sweep_calls(name, dev, stream):
 
         def fwd():
             B.check(B.fa_fwd_varlen(nseq, hh, hkv, total, mx, d, cu.data_ptr(), w.causal, sc, dt,
-                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                    lse.data_ptr(), stream))
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), None,
+                                    o.data_ptr(), lse.data_ptr(), stream))
 
         def bwd():
             B.check(B.fa_bwd_varlen(nseq, hh, hkv, total, mx, d, cu.data_ptr(), w.causal, sc, dt,
                                     q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                    dv.data_ptr(), ws.data_ptr(), wsb, stream))
+                                    do.data_ptr(), lse.data_ptr(), None, dq.data_ptr(),
+                                    dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), wsb, stream))
         e = 2 if w.dtype == "bf16" else 4
         bf = (2.0 * hh + 2.0 * hkv) * total * d * e + 4 * hh * total
         bb = (4.0 * hh + 4.0 * hkv) * total * d * e + 12 * hh * total

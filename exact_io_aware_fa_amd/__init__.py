@@ -10,7 +10,9 @@ Python surface:
                    (grouped K/V heads when k, v have fewer heads),
                    ``flash_attn_varlen_fwd``, ``flash_attn_varlen_bwd`` and the
                    autograd-enabled ``flash_attention``,
-                   ``flash_attention_varlen``.
+                   ``flash_attention_varlen``; ``window`` and ``block_index``
+                   arguments (``build_block_index``) for sliding windows and
+                   block-sparse masks.
 * ``inputs``    -- seeded synthetic workloads.
 * ``build``     -- hipcc build of libexact_fa.so (in-tree).
 """
@@ -26,7 +28,7 @@ def __getattr__(name):
     if name in ("flash_attention", "flash_attn_fwd", "flash_attn_bwd",
                 "FlashAttentionFunction", "flash_attention_varlen",
                 "flash_attn_varlen_fwd", "flash_attn_varlen_bwd",
-                "FlashAttentionVarlenFunction"):
+                "FlashAttentionVarlenFunction", "build_block_index"):
         from . import attention
         return getattr(attention, name)
     raise AttributeError(name)

@@ -53,26 +53,61 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def flash_attn_fwd(q, k, v, causal=False, softmax_scale=None, kv_len=None):
+def build_block_index(block_mask, n):
+    """Block-sparse index (int32 GPU tensor) of a boolean block mask for
+    sequences of length n: block_mask[i][j] keeps key block j (keys
+    j*128 .. j*128+127) for query block i; both dimensions ceil(n / 128).
+    Built on the GPU by the library; reuse it for every call with that mask."""
+    nb = (int(n) + _b.FA_BLOCK - 1) // _b.FA_BLOCK
+    if tuple(block_mask.shape) != (nb, nb):
+        raise ValueError(f"block_mask must be [{nb}, {nb}] for n = {n}")
+    if not block_mask.is_cuda:
+        raise ValueError("block_mask must be a GPU tensor")
+    m = block_mask.to(torch.uint8).contiguous()
+    nbytes = _b.fa_block_index_bytes(int(n))
+    if nbytes == 0:
+        raise ValueError(f"block masks support n <= {1024 * _b.FA_BLOCK}")
+    index = torch.empty(nbytes // 4, dtype=torch.int32, device=block_mask.device)
+    _b.check(_b.fa_block_index_build(int(n), m.data_ptr(), index.data_ptr(), _stream()))
+    return index
+
+
+def _mask(window, block_index, n):
+    if block_index is not None:
+        if not block_index.is_cuda or block_index.dtype != torch.int32:
+            raise ValueError("block_index must come from build_block_index")
+        if block_index.numel() * 4 != _b.fa_block_index_bytes(int(n)):
+            raise ValueError("block_index was built for another sequence length")
+    window = (-1, -1) if window is None else tuple(int(x) for x in window)
+    if len(window) != 2 or min(window) < -1:
+        raise ValueError("window must be (left, right) with -1 for an unbounded side")
+    return _b.mask_arg(window, None if block_index is None else block_index.data_ptr())
+
+
+def flash_attn_fwd(q, k, v, causal=False, softmax_scale=None, kv_len=None, window=None,
+                   block_index=None):
     """Forward: returns (o, lse); o like q, lse float32 [batch, heads, n].
 
     k and v may have fewer heads than q (grouped or multi-query attention):
-    query head i then uses K/V head i // (heads // heads_kv)."""
+    query head i then uses K/V head i // (heads // heads_kv). ``window`` =
+    (left, right) keeps keys i-left .. i+right (-1: unbounded);
+    ``block_index`` (from ``build_block_index``) applies a block mask."""
     hkv = _check_qkv(q, k, v)
     b, h, n, d = q.shape
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     kvl = _kv_len_arg(kv_len, b, n, q.device)
     o = torch.empty_like(q)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
-    _b.check(_b.fa_fwd_gqa(b, h, hkv, n, d, causal, scale, _DTYPES[q.dtype],
-                           q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                           None if kvl is None else kvl.data_ptr(),
-                           o.data_ptr(), lse.data_ptr(), _stream()))
+    mask = _mask(window, block_index, n)
+    _b.check(_b.fa_fwd_masked(b, h, hkv, n, d, causal, scale, _DTYPES[q.dtype],
+                              q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              None if kvl is None else kvl.data_ptr(), mask,
+                              o.data_ptr(), lse.data_ptr(), _stream()))
     return o, lse
 
 
 def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
-                   kv_len=None):
+                   kv_len=None, window=None, block_index=None):
     """Backward from the saved LSE: returns (dq, dk, dv); dk, dv shaped like
     k, v (summed over each K/V head's group of query heads)."""
     hkv = _check_qkv(q, k, v)
@@ -86,12 +121,13 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_bytes = _b.fa_bwd_workspace_bytes(b, h, n, d, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    _b.check(_b.fa_bwd_gqa(b, h, hkv, n, d, causal, scale, dt,
-                           q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                           do.data_ptr(), lse.data_ptr(),
-                           None if kvl is None else kvl.data_ptr(),
-                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                           ws.data_ptr(), ws_bytes, _stream()))
+    mask = _mask(window, block_index, n)
+    _b.check(_b.fa_bwd_masked(b, h, hkv, n, d, causal, scale, dt,
+                              q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              do.data_ptr(), lse.data_ptr(),
+                              None if kvl is None else kvl.data_ptr(), mask,
+                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              ws.data_ptr(), ws_bytes, _stream()))
     return dq, dk, dv
 
 
@@ -131,7 +167,7 @@ def _cu_seqlens_arg(cu_seqlens, total, max_seqlen, device):
 
 
 def flash_attn_varlen_fwd(q, k, v, cu_seqlens, max_seqlen=None, causal=False,
-                          softmax_scale=None):
+                          softmax_scale=None, window=None, block_index=None):
     """Forward over a packed variable-length batch: q [heads, total, d], k, v
     [heads_kv, total, d]; sequence s is rows cu_seqlens[s]..cu_seqlens[s+1]-1
     of every head and attends only to itself. Returns (o like q, lse float32
@@ -142,14 +178,15 @@ def flash_attn_varlen_fwd(q, k, v, cu_seqlens, max_seqlen=None, causal=False,
     cu, nseq, mx = _cu_seqlens_arg(cu_seqlens, total, max_seqlen, q.device)
     o = torch.empty_like(q)
     lse = torch.empty((h, total), dtype=torch.float32, device=q.device)
+    mask = _mask(window, block_index, mx)
     _b.check(_b.fa_fwd_varlen(nseq, h, hkv, total, mx, d, cu.data_ptr(), causal, scale,
                               _DTYPES[q.dtype], q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              o.data_ptr(), lse.data_ptr(), _stream()))
+                              mask, o.data_ptr(), lse.data_ptr(), _stream()))
     return o, lse
 
 
 def flash_attn_varlen_bwd(q, k, v, o, lse, do, cu_seqlens, max_seqlen=None, causal=False,
-                          softmax_scale=None):
+                          softmax_scale=None, window=None, block_index=None):
     """Backward of ``flash_attn_varlen_fwd`` from the saved LSE: returns
     (dq, dk, dv) shaped like q, k, v."""
     hkv = _check_packed(q, k, v)
@@ -163,10 +200,12 @@ def flash_attn_varlen_bwd(q, k, v, o, lse, do, cu_seqlens, max_seqlen=None, caus
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_bytes = _b.fa_bwd_workspace_bytes(nseq, h, mx, d, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    mask = _mask(window, block_index, mx)
     _b.check(_b.fa_bwd_varlen(nseq, h, hkv, total, mx, d, cu.data_ptr(), causal, scale, dt,
                               q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                              dv.data_ptr(), ws.data_ptr(), ws_bytes, _stream()))
+                              do.data_ptr(), lse.data_ptr(), mask, dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws_bytes,
+                              _stream()))
     return dq, dk, dv
 
 
@@ -175,44 +214,47 @@ class FlashAttentionFunction(torch.autograd.Function):
     backward kernel."""
 
     @staticmethod
-    def forward(ctx, q, k, v, causal, softmax_scale, kv_len):
-        o, lse = flash_attn_fwd(q, k, v, causal, softmax_scale, kv_len)
+    def forward(ctx, q, k, v, causal, softmax_scale, kv_len, window, block_index):
+        o, lse = flash_attn_fwd(q, k, v, causal, softmax_scale, kv_len, window, block_index)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.causal, ctx.scale, ctx.kv_len = causal, softmax_scale, kv_len
+        ctx.args = (causal, softmax_scale, kv_len, window, block_index)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = flash_attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.causal,
-                                    ctx.scale, ctx.kv_len)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = flash_attn_bwd(q, k, v, o, lse, do.contiguous(), *ctx.args)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def flash_attention(q, k, v, causal=False, softmax_scale=None, kv_len=None):
+def flash_attention(q, k, v, causal=False, softmax_scale=None, kv_len=None, window=None,
+                    block_index=None):
     """O = softmax(scale * Q K^T + mask) V with autograd support."""
-    return FlashAttentionFunction.apply(q, k, v, causal, softmax_scale, kv_len)
+    return FlashAttentionFunction.apply(q, k, v, causal, softmax_scale, kv_len, window,
+                                        block_index)
 
 
 class FlashAttentionVarlenFunction(torch.autograd.Function):
     """Autograd wrapper of the packed variable-length calls."""
 
     @staticmethod
-    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, softmax_scale):
-        o, lse = flash_attn_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal, softmax_scale)
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, softmax_scale, window,
+                block_index):
+        o, lse = flash_attn_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal, softmax_scale,
+                                       window, block_index)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.args = (cu_seqlens, max_seqlen, causal, softmax_scale)
+        ctx.args = (cu_seqlens, max_seqlen, causal, softmax_scale, window, block_index)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
         dq, dk, dv = flash_attn_varlen_bwd(q, k, v, o, lse, do.contiguous(), *ctx.args)
-        return dq, dk, dv, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None
 
 
 def flash_attention_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=False,
-                           softmax_scale=None):
+                           softmax_scale=None, window=None, block_index=None):
     """Packed variable-length attention with autograd support."""
     return FlashAttentionVarlenFunction.apply(q, k, v, cu_seqlens, max_seqlen, causal,
-                                              softmax_scale)
+                                              softmax_scale, window, block_index)

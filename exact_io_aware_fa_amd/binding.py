@@ -28,12 +28,28 @@ FA_E_LAUNCH = 6
 FA_E_ALIGN = 7
 
 # Every symbol include/fa.h declares.
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_varlen", "fa_bwd", "fa_bwd_gqa",
-            "fa_bwd_varlen", "fa_bwd_timed", "fa_bwd_workspace_bytes", "fa_status_str",
-            "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_varlen", "fa_bwd",
+            "fa_bwd_gqa", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_timed",
+            "fa_bwd_workspace_bytes", "fa_block_index_bytes", "fa_block_index_build",
+            "fa_status_str", "fa_abi_version")
 
 # The FA_ABI_VERSION this binding was written against.
-ABI_VERSION = 3
+ABI_VERSION = 4
+
+FA_BLOCK = 128
+
+
+class FaMask(ctypes.Structure):
+    """fa_mask: window sides (-1 = unbounded) and a block index address."""
+    _fields_ = [("window_left", ctypes.c_int64), ("window_right", ctypes.c_int64),
+                ("block_index", ctypes.c_void_p)]
+
+
+def mask_arg(window=(-1, -1), block_index=None):
+    """A FaMask for ctypes calls, or None when no extra mask is asked for."""
+    if tuple(window) == (-1, -1) and not block_index:
+        return None
+    return FaMask(int(window[0]), int(window[1]), block_index or None)
 
 _lock = threading.Lock()
 _lib = None
@@ -68,10 +84,19 @@ def lib() -> ctypes.CDLL:
         # scale, dtype, then the tensors and the stream.
         _vl = [_i64, _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_int, ctypes.c_float,
                ctypes.c_int]
+        _mp = ctypes.POINTER(FaMask)
         L.fa_fwd_varlen.restype = ctypes.c_int
-        L.fa_fwd_varlen.argtypes = _vl + [_vp, _vp, _vp, _vp, _vp, _vp]
+        L.fa_fwd_varlen.argtypes = _vl + [_vp, _vp, _vp, _mp, _vp, _vp, _vp]
         L.fa_bwd_varlen.restype = ctypes.c_int
-        L.fa_bwd_varlen.argtypes = _vl + [_vp] * 9 + [_vp, ctypes.c_size_t, _vp]
+        L.fa_bwd_varlen.argtypes = _vl + [_vp] * 6 + [_mp] + [_vp] * 4 + [ctypes.c_size_t, _vp]
+        L.fa_fwd_masked.restype = ctypes.c_int
+        L.fa_fwd_masked.argtypes = L.fa_fwd_gqa.argtypes[:12] + [_mp] + L.fa_fwd_gqa.argtypes[12:]
+        L.fa_bwd_masked.restype = ctypes.c_int
+        L.fa_bwd_masked.argtypes = L.fa_bwd_gqa.argtypes[:15] + [_mp] + L.fa_bwd_gqa.argtypes[15:]
+        L.fa_block_index_bytes.restype = ctypes.c_size_t
+        L.fa_block_index_bytes.argtypes = [_i64]
+        L.fa_block_index_build.restype = ctypes.c_int
+        L.fa_block_index_build.argtypes = [_i64, _vp, _vp, _vp]
         L.fa_bwd_timed.restype = ctypes.c_int
         L.fa_bwd_timed.argtypes = L.fa_bwd_gqa.argtypes + [ctypes.POINTER(_vp)]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -101,20 +126,49 @@ def fa_fwd_gqa(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k,
                             lse, stream)
 
 
+def _mref(mask):
+    return None if mask is None else ctypes.byref(mask)
+
+
+def fa_fwd_masked(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k, v,
+                  kv_len, mask, o, lse, stream) -> int:
+    """``mask``: a FaMask (see ``mask_arg``) or None."""
+    return lib().fa_fwd_masked(batch, heads, heads_kv, n, d, int(causal),
+                               float(softmax_scale), int(dtype), q, k, v, kv_len,
+                               _mref(mask), o, lse, stream)
+
+
+def fa_bwd_masked(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k, v, o,
+                  d_o, lse, kv_len, mask, dq, dk, dv, workspace, workspace_bytes,
+                  stream) -> int:
+    return lib().fa_bwd_masked(batch, heads, heads_kv, n, d, int(causal),
+                               float(softmax_scale), int(dtype), q, k, v, o, d_o, lse, kv_len,
+                               _mref(mask), dq, dk, dv, workspace, int(workspace_bytes),
+                               stream)
+
+
 def fa_fwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens, causal,
-                  softmax_scale, dtype, q, k, v, o, lse, stream) -> int:
+                  softmax_scale, dtype, q, k, v, mask, o, lse, stream) -> int:
     return lib().fa_fwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens,
-                               int(causal), float(softmax_scale), int(dtype), q, k, v, o,
-                               lse, stream)
+                               int(causal), float(softmax_scale), int(dtype), q, k, v,
+                               _mref(mask), o, lse, stream)
 
 
 def fa_bwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens, causal,
-                  softmax_scale, dtype, q, k, v, o, d_o, lse, dq, dk, dv, workspace,
+                  softmax_scale, dtype, q, k, v, o, d_o, lse, mask, dq, dk, dv, workspace,
                   workspace_bytes, stream) -> int:
     return lib().fa_bwd_varlen(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens,
                                int(causal), float(softmax_scale), int(dtype), q, k, v, o,
-                               d_o, lse, dq, dk, dv, workspace, int(workspace_bytes),
-                               stream)
+                               d_o, lse, _mref(mask), dq, dk, dv, workspace,
+                               int(workspace_bytes), stream)
+
+
+def fa_block_index_bytes(n) -> int:
+    return int(lib().fa_block_index_bytes(n))
+
+
+def fa_block_index_build(n, block_mask, index, stream) -> int:
+    return lib().fa_block_index_build(n, block_mask, index, stream)
 
 
 def fa_bwd(batch, heads, n, d, causal, softmax_scale, dtype, q, k, v, o, d_o,

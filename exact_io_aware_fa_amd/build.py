@@ -35,6 +35,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fa_bwd_dq_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_aux.hip"),
     os.path.join(CSRC, "kernels", "fa_fp32.hip"),
+    os.path.join(CSRC, "kernels", "fa_block_index.hip"),
 ]
 
 ARCH = "gfx950"

@@ -85,8 +85,17 @@ size_t lse_bytes(const Shape& s) {
   return size_t(s.mem_batch) * size_t(s.heads) * size_t(s.rows) * sizeof(float);
 }
 
+int64_t mask_blocks(int64_t n) { return (n + 127) / 128; }
+
+size_t block_index_bytes(int64_t n) {
+  const int64_t nb = mask_blocks(n);
+  return size_t(2 * (nb + 1) + 2 * nb * nb) * sizeof(int32_t);
+}
+
 fa::Params base_params(const Shape& s, int causal, float scale) {
   fa::Params p{};
+  p.win_left = -1;
+  p.win_right = -1;
   p.cu_seqlens = s.cu_seqlens;
   p.batch = int(s.entries);
   p.heads = int(s.heads);
@@ -103,6 +112,27 @@ fa::Params base_params(const Shape& s, int causal, float scale) {
   return p;
 }
 
+// Checks the optional masks and records them in p. Window sides beyond the
+// sequence length act as unbounded, so they are stored clamped to n.
+fa_status check_mask(const Shape& sh, const fa_mask* mask, fa::Params& p) {
+  if (mask == nullptr) return FA_OK;
+  if (mask->window_left < -1 || mask->window_right < -1) return FA_E_SHAPE;
+  p.win_left = int(mask->window_left < sh.n ? mask->window_left : sh.n);
+  p.win_right = int(mask->window_right < sh.n ? mask->window_right : sh.n);
+  if (mask->block_index != nullptr) {
+    if (mask_blocks(sh.n) > 1024) return FA_E_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(mask->block_index) & 3u) return FA_E_ALIGN;
+    p.blk = mask->block_index;
+    p.nb = int(mask_blocks(sh.n));
+  }
+  return FA_OK;
+}
+
+Range index_range(const Shape& sh, const fa_mask* mask) {
+  if (mask == nullptr || mask->block_index == nullptr) return Range{0, 0};
+  return range_of(mask->block_index, block_index_bytes(sh.n));
+}
+
 // The small device array an entry point reads besides the tensors: the key
 // lengths (padded batches) or the sequence offsets (packed batches).
 Range aux_range(const Shape& sh, const int32_t* kv_len) {
@@ -113,8 +143,11 @@ Range aux_range(const Shape& sh, const int32_t* kv_len) {
 
 fa_status fwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dtype,
                    const void* q, const void* k, const void* v, const int32_t* kv_len,
-                   void* o, float* lse, void* stream) {
+                   const fa_mask* mask, void* o, float* lse, void* stream) {
   fa_status st = check_shape(sh, softmax_scale, dtype);
+  if (st != FA_OK) return st;
+  fa::Params p = base_params(sh, causal, softmax_scale);
+  st = check_mask(sh, mask, p);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !lse) return FA_E_NULLPTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -129,8 +162,9 @@ fa_status fwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dt
   for (const Range& r : ins)
     if (overlaps(r, ro) || overlaps(r, rl)) return FA_E_ALIAS;
   if (overlaps(ra, ro) || overlaps(ra, rl)) return FA_E_ALIAS;
+  const Range ri = index_range(sh, mask);
+  if (overlaps(ri, ro) || overlaps(ri, rl)) return FA_E_ALIAS;
 
-  fa::Params p = base_params(sh, causal, softmax_scale);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -145,10 +179,13 @@ fa_status fwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dt
 
 fa_status bwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dtype,
                    const void* q, const void* k, const void* v, const void* o,
-                   const void* d_o, const float* lse, const int32_t* kv_len, void* dq,
-                   void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                   void* stream, void* const events[4]) {
+                   const void* d_o, const float* lse, const int32_t* kv_len,
+                   const fa_mask* mask, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const events[4]) {
   fa_status st = check_shape(sh, softmax_scale, dtype);
+  if (st != FA_OK) return st;
+  fa::Params p = base_params(sh, causal, softmax_scale);
+  st = check_mask(sh, mask, p);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return FA_E_NULLPTR;
   if (!workspace) return FA_E_WORKSPACE;
@@ -163,19 +200,18 @@ fa_status bwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dt
 
   const size_t tb = tensor_bytes(sh, sh.heads, dtype);
   const size_t kb = tensor_bytes(sh, sh.heads_kv, dtype);
-  const Range ins[7] = {range_of(q, tb), range_of(k, kb),  range_of(v, kb),
+  const Range ins[8] = {range_of(q, tb), range_of(k, kb),  range_of(v, kb),
                         range_of(o, tb), range_of(d_o, tb), range_of(lse, lse_bytes(sh)),
-                        ra};
+                        ra,              index_range(sh, mask)};
   const Range outs[4] = {range_of(dq, tb), range_of(dk, kb), range_of(dv, kb),
                          range_of(workspace, need)};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 7; ++j)
+    for (int j = 0; j < 8; ++j)
       if (overlaps(outs[i], ins[j])) return FA_E_ALIAS;
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], outs[j])) return FA_E_ALIAS;
   }
 
-  fa::Params p = base_params(sh, causal, softmax_scale);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -243,7 +279,7 @@ fa_status fa_fwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                  const void* v, const int32_t* kv_len, void* o, float* lse,
                  void* stream) {
   return fwd_impl(padded_shape(batch, heads, heads, n, d), causal, softmax_scale, dtype, q, k,
-                  v, kv_len, o, lse, stream);
+                  v, kv_len, nullptr, o, lse, stream);
 }
 
 fa_status fa_fwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
@@ -251,16 +287,25 @@ fa_status fa_fwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, 
                      const void* k, const void* v, const int32_t* kv_len, void* o,
                      float* lse, void* stream) {
   return fwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
-                  k, v, kv_len, o, lse, stream);
+                  k, v, kv_len, nullptr, o, lse, stream);
+}
+
+fa_status fa_fwd_masked(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
+                        int causal, float softmax_scale, fa_dtype dtype, const void* q,
+                        const void* k, const void* v, const int32_t* kv_len,
+                        const fa_mask* mask, void* o, float* lse, void* stream) {
+  return fwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
+                  k, v, kv_len, mask, o, lse, stream);
 }
 
 fa_status fa_fwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv, int64_t total,
                         int64_t max_seqlen, int64_t d, const int32_t* cu_seqlens, int causal,
                         float softmax_scale, fa_dtype dtype, const void* q, const void* k,
-                        const void* v, void* o, float* lse, void* stream) {
+                        const void* v, const fa_mask* mask, void* o, float* lse,
+                        void* stream) {
   if (!cu_seqlens) return FA_E_NULLPTR;
   return fwd_impl(packed_shape(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens),
-                  causal, softmax_scale, dtype, q, k, v, nullptr, o, lse, stream);
+                  causal, softmax_scale, dtype, q, k, v, nullptr, mask, o, lse, stream);
 }
 
 fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
@@ -269,8 +314,8 @@ fa_status fa_bwd(int64_t batch, int64_t heads, int64_t n, int64_t d, int causal,
                  const int32_t* kv_len, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, void* stream) {
   return bwd_impl(padded_shape(batch, heads, heads, n, d), causal, softmax_scale, dtype, q, k,
-                  v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
-                  nullptr);
+                  v, o, d_o, lse, kv_len, nullptr, dq, dk, dv, workspace, workspace_bytes,
+                  stream, nullptr);
 }
 
 fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
@@ -279,20 +324,31 @@ fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, 
                      const float* lse, const int32_t* kv_len, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
-                  k, v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
-                  nullptr);
+                  k, v, o, d_o, lse, kv_len, nullptr, dq, dk, dv, workspace, workspace_bytes,
+                  stream, nullptr);
+}
+
+fa_status fa_bwd_masked(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
+                        int causal, float softmax_scale, fa_dtype dtype, const void* q,
+                        const void* k, const void* v, const void* o, const void* d_o,
+                        const float* lse, const int32_t* kv_len, const fa_mask* mask, void* dq,
+                        void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return bwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
+                  k, v, o, d_o, lse, kv_len, mask, dq, dk, dv, workspace, workspace_bytes,
+                  stream, nullptr);
 }
 
 fa_status fa_bwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv, int64_t total,
                         int64_t max_seqlen, int64_t d, const int32_t* cu_seqlens, int causal,
                         float softmax_scale, fa_dtype dtype, const void* q, const void* k,
                         const void* v, const void* o, const void* d_o, const float* lse,
-                        void* dq, void* dk, void* dv, void* workspace,
+                        const fa_mask* mask, void* dq, void* dk, void* dv, void* workspace,
                         size_t workspace_bytes, void* stream) {
   if (!cu_seqlens) return FA_E_NULLPTR;
   return bwd_impl(packed_shape(num_seqs, heads, heads_kv, total, max_seqlen, d, cu_seqlens),
-                  causal, softmax_scale, dtype, q, k, v, o, d_o, lse, nullptr, dq, dk, dv,
-                  workspace, workspace_bytes, stream, nullptr);
+                  causal, softmax_scale, dtype, q, k, v, o, d_o, lse, nullptr, mask, dq, dk,
+                  dv, workspace, workspace_bytes, stream, nullptr);
 }
 
 fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
@@ -302,8 +358,27 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n
                        void* workspace, size_t workspace_bytes, void* stream,
                        void* const events[4]) {
   return bwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
-                  k, v, o, d_o, lse, kv_len, dq, dk, dv, workspace, workspace_bytes, stream,
-                  events);
+                  k, v, o, d_o, lse, kv_len, nullptr, dq, dk, dv, workspace, workspace_bytes,
+                  stream, events);
+}
+
+size_t fa_block_index_bytes(int64_t n) {
+  if (n < 1 || mask_blocks(n) > 1024) return 0;
+  return block_index_bytes(n);
+}
+
+fa_status fa_block_index_build(int64_t n, const uint8_t* block_mask, int32_t* index,
+                               void* stream) {
+  if (n < 1 || n > kMaxN) return FA_E_SHAPE;
+  if (mask_blocks(n) > 1024) return FA_E_UNSUPPORTED;
+  if (!block_mask || !index) return FA_E_NULLPTR;
+  if (reinterpret_cast<uintptr_t>(index) & 3u) return FA_E_ALIGN;
+  const int64_t nb = mask_blocks(n);
+  if (overlaps(range_of(block_mask, size_t(nb * nb)), range_of(index, block_index_bytes(n))))
+    return FA_E_ALIAS;
+  const hipError_t e =
+      fa::launch_block_index(block_mask, int(nb), index, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
 }
 
 }  // extern "C"

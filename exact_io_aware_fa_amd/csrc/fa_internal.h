@@ -41,6 +41,10 @@ struct Params {
   int rows;             // rows per head in memory (n, or the packed total)
   int n_pad;            // n rounded up to a multiple of 64 (workspace rows)
   int causal;
+  int win_left;         // sliding window: keys j >= i - win_left (-1: unbounded)
+  int win_right;        // sliding window: keys j <= i + win_right (-1: unbounded)
+  const int32_t* blk;   // nullable: block-sparse index (see fa_device.h)
+  int nb;               // blocks per side of the block mask
   // Scores enter exp2 as s * c where c = |scale| * log2(e), raised to at
   // least FLT_MIN so that c > 0 and hidden entries (-inf) stay -inf; a
   // negative scale is applied by negating Q (exact), flagged by q_neg.
@@ -59,5 +63,6 @@ hipError_t launch_bwd_dkdv_bf16_staged(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dq_bf16_staged(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_fp32(const Params& p, int d, hipStream_t s);
+hipError_t launch_block_index(const uint8_t* mask, int nb, int32_t* out, hipStream_t s);
 
 }  // namespace fa

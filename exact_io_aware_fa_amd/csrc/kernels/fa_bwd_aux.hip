@@ -67,7 +67,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Params p, long long 
   for (int m = 1; m < G; m <<= 1) s += __shfl_xor(s, m);
   if (sub == 0) {
     p.dvec[row] = s;
-    p.l2vec[row] = p.lse[qrow] * kLog2e;
+    // A row with no visible key (LSE = -inf) gets +inf, so every rebuilt
+    // probability exp2(s c - L log2 e) of it is exactly 0.
+    const float lse = p.lse[qrow];
+    p.l2vec[row] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
   }
   if (p.dq_acc != nullptr) {
     *reinterpret_cast<f32x4*>(p.dq_acc + off) = f32x4{};

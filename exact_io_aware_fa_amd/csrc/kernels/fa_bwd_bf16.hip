@@ -44,7 +44,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
 
-template <int D, int NQB, bool CAUSAL>
+template <int D, int NQB, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
   constexpr int BQ = 32 * NQB;           // queries per tile
   constexpr int ND = D / 16;             // reduction steps of S and dP
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) float sv0[2 * BQ];
   __shared__ __attribute__((aligned(16))) float sv1[2 * BQ];
   __shared__ __attribute__((aligned(16))) float sv2[2 * BQ];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -139,14 +140,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       __syncthreads();  // the zeros land before any wave's tile loads
     }
 
-    const int n_qt = (n + BQ - 1) / BQ;
-    const int it0 = CAUSAL ? (k0 / BQ) : 0;
     const int qsw = p.group;
     // The mask, applied branch-free on the masked steps (see below): a pair
-    // (query q, key) is hidden iff q < lo or q >= n, with lo = the key itself
-    // when causal, 0 otherwise, and lo = n for keys at or past the key limit
-    // (all hidden).
-    const int qlo = mykey >= kv_lim ? n : (CAUSAL ? mykey : 0);
+    // (query q, key) is hidden iff q < qlo or q >= qhi, the queries that see
+    // this lane's key (qlo = n for keys at or past the key limit). Query
+    // tiles [tb, te) hold every query some key of the workgroup is seen by,
+    // tiles [iu0, iu1) only queries that see all of its keys (the bounds are
+    // non-decreasing in the key); rows past n are always masked.
+    const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+    const int qlo = band.qlo(mykey), qhi = band.qhi(mykey);
+    const int k_last = min(k0 + kBKV, kv_lim) - 1;
+    const int tb = band.qlo(k0) / BQ;
+    const int te = (band.qhi(k_last) + BQ - 1) / BQ;
+    const int iu0 = (band.qlo(k0 + kBKV - 1) + BQ - 1) / BQ;
+    const int iu1 = band.qhi(k0) / BQ;
 
     // Loads of query tile it into a stage (sm: Q and dO, sv: L and D). Wave
     // w fills rows
@@ -179,6 +186,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       }
     }
 
+    auto sweep = [&](const auto& tiles) FA_INLINE {
+    const int ns = tiles.count;
+    if (ns == 0) return;
     for (int gq = 0; gq < qsw; ++gq) {
       // Query head gq of the group: its Q, dO and row vectors.
       // Work entry of query head hk * group + gq (workspace rows).
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
                       auto mask_tag) FA_INLINE {
         const int qh = it * BQ + h * 4;
         const int lo = qlo - qh;
-        const int hi = n - qh;
+        const int hi = qhi - qh;
         f32x4 l4[NQB][4], d4[NQB][4];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
@@ -339,38 +349,44 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
                       auto mask_tag) FA_INLINE {
         wait_global_loads();
         __syncthreads();
-        if (it + 2 < n_qt) issue(it + 2, mC, vC);
-        body(it, mA, vA, mB, mask_tag);
+        if (it + 2 < ns) issue(tiles.tile(it + 2), mC, vC);
+        body(tiles.tile(it), mA, vA, mB, mask_tag);
       };
 
-      // Masked steps: the causal diagonal band (the first kBKV / BQ tiles of
-      // the sweep, rounded up to a multiple of three so the unmasked loop
-      // starts with the same stage rotation), every step when the workgroup
-      // straddles the key limit, and the last tile (always masked: it may be
-      // partial). The unmasked steps skip the mask arithmetic.
-      constexpr int HEAD = (kBKV / BQ + 2) / 3 * 3;
-      const int last = n_qt - 1;
-      const bool straddle = k0 + kBKV > kv_lim;
-      const int head = straddle ? last : (CAUSAL ? min(it0 + HEAD, last) : it0);
+      // Steps (it counts steps; tiles.tile(it) is the query tile): masked
+      // steps up to the first that holds only fully visible queries (the
+      // causal diagonal band, or everything when the workgroup straddles the
+      // key limit), rounded up to a multiple of three so the unmasked loop
+      // starts with the same stage rotation; unmasked steps; masked steps
+      // again (the window's far edge), the last step always among them (its
+      // tile may be partial). The unmasked steps skip the mask arithmetic.
+      const int last = ns - 1;
+      const int su0 = tiles.first_at_least(iu0);
+      const int su1 = tiles.first_at_least(iu1);
+      const int head = min((su0 + 2) / 3 * 3, last);
 
-      issue(it0, sm0, sv0);
-      if (it0 + 1 < n_qt) issue(it0 + 1, sm1, sv1);
+      issue(tiles.tile(0), sm0, sv0);
+      if (1 < ns) issue(tiles.tile(1), sm1, sv1);
       wait_global_loads();
       __syncthreads();
       sdp(sm0, s, g);
-      int it = it0;
+      int it = 0;
       for (; it + 3 <= head; it += 3) {
         step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
         step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
         step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
       }
-      // Here either it == head with (it - it0) % 3 == 0, or head == last and
-      // fewer than three steps remain before it, so the unmasked loop below
-      // does not run.
-      for (; it + 3 <= last; it += 3) {
+      // Here either it == head with it % 3 == 0, or head == last and fewer
+      // than three steps remain before it, so the loops below do not run.
+      for (; it + 3 <= min(su1, last); it += 3) {
         step(it, sm0, sv0, sm1, sm2, sv2, std::false_type{});
         step(it + 1, sm1, sv1, sm2, sm0, sv0, std::false_type{});
         step(it + 2, sm2, sv2, sm0, sm1, sv1, std::false_type{});
+      }
+      for (; it + 3 <= last; it += 3) {
+        step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
+        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
+        step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
       }
       // last - it is 0, 1 or 2 here: one masked step per remaining tile. The
       // step of the last tile also computes S and dP of a successor that does
@@ -383,6 +399,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         if (it + 2 <= last) step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
       }
     }  // query heads of the group
+    };
+    if constexpr (SPARSE) {
+      // The workgroup's 128 keys are one block column of the mask.
+      const int nl = stage_blocks(col_blocks(p, k0 / kBlock), sblk, tid, kThreads, p.nb);
+      sweep(sparse_tiles<kBlock / BQ>(sblk, nl, tb, te));
+    } else {
+      sweep(dense_tiles(tb, te));
+    }
   }
 
   // dK = scale * (dS^T Q), dV as accumulated.
@@ -409,11 +433,11 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_c = (p.n + kBKV - 1) / kBKV;
   const long long total = (long long)t_c * p.batch * p.heads_kv;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NQB, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NQB, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return dispatch_mask(p, [&](auto causal, auto sparse) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NQB, decltype(causal)::value, decltype(sparse)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace

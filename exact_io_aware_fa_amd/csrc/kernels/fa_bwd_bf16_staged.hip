@@ -22,7 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
 
-template <int D, int BQ, int NBUF, bool CAUSAL>
+template <int D, int BQ, int NBUF, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) {
   constexpr int ND = D / 16;
   constexpr int NMB = D / 32;
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
   __shared__ __attribute__((aligned(16))) bf16 sdOt[NBUF][D * TSTR];
   __shared__ __attribute__((aligned(16))) float sL[NBUF][BQ];
   __shared__ __attribute__((aligned(16))) float sDv[NBUF][BQ];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -100,15 +101,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
         vf[kd] = as_bf16x8(kok ? bb : z);
       }
     }
-    const int n_qt = (n + BQ - 1) / BQ;
-    const int it0 = CAUSAL ? (k0 / BQ) : 0;
-    // Tiles that need masking: the causal diagonal band (some key of this
-    // workgroup lies above some query of the tile), every tile when the
-    // workgroup straddles the key limit, and a partial last tile.
-    int a_end = it0;
-    if (k0 + kBKV > kv_lim) a_end = n_qt;
-    else if (CAUSAL) a_end = min(n_qt, (k0 + kBKV - 2) / BQ + 1);
-    const int b_end = max(a_end, (n % BQ) ? n_qt - 1 : n_qt);
+    // Queries that see this lane's key: [qlo, qhi) (qlo = n for keys at or
+    // past the key limit). Query tiles [tb, te) hold every query some key of
+    // the workgroup is seen by, tiles [iu0, iu1) only queries that see all
+    // of its keys (the bounds are non-decreasing in the key); rows past n
+    // are always masked.
+    const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+    const int qlo = band.qlo(mykey), qhi = band.qhi(mykey);
+    const int k_last = min(k0 + kBKV, kv_lim) - 1;
+    const int tb = band.qlo(k0) / BQ;
+    const int te = (band.qhi(k_last) + BQ - 1) / BQ;
+    const int iu0 = (band.qlo(k0 + kBKV - 1) + BQ - 1) / BQ;
+    const int iu1 = band.qhi(k0) / BQ;
 
     // Register staging of the next Q / dO tile: unit u < UPT is a Q unit,
     // else a dO unit; a unit is 4 rows x 8 dims. Rows past n are read
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
             float pr = __builtin_amdgcn_exp2f(fmaf(sv[qb][r], cs, -l4[i]));
             if (MASK) {
               const int q = q0 + qb * 32 + g * 8 + h * 4 + i;
-              const bool hidden = q >= n || mykey >= kv_lim || (CAUSAL && mykey > q);
+              const bool hidden = q < qlo || q >= qhi;
               pr = hidden ? 0.f : pr;
             }
             sv[qb][r] = pr;
@@ -232,28 +236,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
         }
     };
 
-    auto run = [&](int it, int buf, auto mask_tag) {
+    auto sweep = [&](const auto& tiles) FA_INLINE {
+    const int ns = tiles.count;
+    // Steps [su0, su1) hold only queries that see every key of the workgroup.
+    const int su0 = tiles.first_at_least(iu0);
+    const int su1 = max(tiles.first_at_least(iu1), su0);
+    auto run = [&](int it, int buf, auto mask_tag) FA_INLINE {
+      // it counts steps; tiles.tile(it) is the query tile of step it.
+      const int t = tiles.tile(it);
       if constexpr (NBUF == 2) {
-        // Buffer `buf` holds tile it. Tile it+1 goes to buf^1 while it is
+        // Buffer `buf` holds tile t. The next tile goes to buf^1 while t is
         // processed: buf^1 was last read before the previous barrier.
-        compute(it, buf, mask_tag);
-        if (it + 1 < n_qt) {
-          swrite(it + 1, buf ^ 1);
-          gload(min(it + 2, n_qt - 1));
+        compute(t, buf, mask_tag);
+        if (it + 1 < ns) {
+          swrite(tiles.tile(it + 1), buf ^ 1);
+          gload(tiles.tile(min(it + 2, ns - 1)));
         }
-        __syncthreads();  // tile it+1 complete; buf free for tile it+2
+        __syncthreads();  // next tile complete; buf free for the one after
       } else {
         __syncthreads();  // previous tile's LDS contents are no longer read
-        swrite(it, 0);
+        swrite(t, 0);
         __syncthreads();
-        gload(min(it + 1, n_qt - 1));
-        compute(it, 0, mask_tag);
+        gload(tiles.tile(min(it + 1, ns - 1)));
+        compute(t, 0, mask_tag);
       }
     };
 
     // One sweep per query head of the group. A sweep's first LDS write is
     // safe: with two buffers every step ends on a barrier, with one every
     // step starts on one.
+    if (ns > 0)
     for (int gq = 0; gq < p.group; ++gq) {
       // Work entry of query head hk * group + gq (workspace rows).
       const int bh = b * p.heads + hk * p.group + gq;
@@ -262,16 +274,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
       dO = static_cast<const bf16*>(p.d_o) + base;
       l2v = p.l2vec + (size_t)bh * p.n_pad;
       dvec = p.dvec + (size_t)bh * p.n_pad;
-      gload(it0);
+      gload(tiles.tile(0));
       if constexpr (NBUF == 2) {
-        swrite(it0, 0);
-        gload(min(it0 + 1, n_qt - 1));
+        swrite(tiles.tile(0), 0);
+        gload(tiles.tile(min(1, ns - 1)));
         __syncthreads();
       }
-      int it = it0;
-      for (; it < a_end; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
-      for (; it < b_end; ++it) run(it, (it - it0) & (NBUF - 1), std::false_type{});
-      for (; it < n_qt; ++it) run(it, (it - it0) & (NBUF - 1), std::true_type{});
+      // Masked steps, unmasked steps (only fully visible queries), masked
+      // steps again.
+      int it = 0;
+      for (; it < su0; ++it) run(it, it & (NBUF - 1), std::true_type{});
+      for (; it < su1; ++it) run(it, it & (NBUF - 1), std::false_type{});
+      for (; it < ns; ++it) run(it, it & (NBUF - 1), std::true_type{});
+    }
+    };
+    if constexpr (SPARSE) {
+      // The workgroup's keys lie in one block column of the mask.
+      const int nl = stage_blocks(col_blocks(p, k0 / kBlock), sblk, tid, kThreads, p.nb);
+      sweep(sparse_tiles<kBlock / BQ>(sblk, nl, tb, te));
+    } else {
+      sweep(dense_tiles(tb, te));
     }
   }
 
@@ -299,11 +321,12 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_c = (p.n + kBKV - 1) / kBKV;
   const long long total = (long long)t_c * p.batch * p.heads_kv;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((bwd_dkdv_staged_kernel<D, BQ, NBUF, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_staged_kernel<D, BQ, NBUF, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return dispatch_mask(p, [&](auto causal, auto sparse) {
+    hipLaunchKernelGGL((bwd_dkdv_staged_kernel<D, BQ, NBUF, decltype(causal)::value,
+                                               decltype(sparse)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace

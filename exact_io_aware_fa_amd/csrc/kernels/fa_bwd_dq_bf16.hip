@@ -36,7 +36,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
 
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL, bool SPARSE, bool WIN>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;           // bytes per row
@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) bf16 sK1[BC * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV0[BC * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV1[BC * D];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,14 +101,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   const float l2 = p.l2vec[(size_t)bh * p.n_pad + qr];
   const float dd = p.dvec[(size_t)bh * p.n_pad + qr];
 
-  int kend = kv_lim;
-  if (CAUSAL) kend = min(kend, q0 + kBR);
-  const int ntiles = (kend + BC - 1) / BC;
-  // Tiles [0, j_unmasked) have every key visible to every query of the
-  // workgroup; the rest go through the masked path.
-  int j_unmasked = kv_lim / BC;
-  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
-  j_unmasked = min(j_unmasked, ntiles);
+  // Keys of this lane's row: [band.lo(qi), band.hi(qi)); key tiles [tb, te) hold every key
+  // some row of the workgroup sees, tiles [ju_lo, ju_hi) only keys that all
+  // of them see (the bounds are non-decreasing in the row); keys
+  // [wlo, whi) are the ones some row of this wave sees.
+  const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+  const int q_last = min(q0 + kBR, n) - 1;
+  const int tb = band.lo(q0) / BC;
+  const int te = (band.hi(q_last) + BC - 1) / BC;
+  const int ju_lo = (band.lo(q_last) + BC - 1) / BC;
+  const int ju_hi = band.hi(q0) / BC;
+  const int wlo = band.lo(qw0);
+  const int whi = band.hi(min(qw0 + 31, n - 1));
 
   f32x16 acc[NMB];
 #pragma unroll
@@ -125,9 +130,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
     ld_koff[i] = (row * D + ((lane % CH) ^ swz_both<D>(row)) * 8) * 2;
     ld_voff[i] = (row * D + ((lane % CH) ^ swz_row<D>(row)) * 8) * 2;
   }
-  auto issue = [&](int j, bf16* dk, bf16* dv) {
+  auto issue = [&](int j, bf16* dk, bf16* dv) FA_INLINE {
     const int kb0 = j * BC;
-    const int bytes = min(kv_lim - kb0, BC) * ROWB;
+    const int bytes = max(min(kv_lim - kb0, BC), 0) * ROWB;
     const auto rk = buffer_rsrc(K + (size_t)kb0 * D, bytes);
     const auto rv = buffer_rsrc(V + (size_t)kb0 * D, bytes);
 #pragma unroll
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   // P^T = exp2(S^T c - L log2 e), dS^T = P^T (dP^T - D) as bf16 B fragments
   // (chunk (kb, kc) holds keys kb*32 + kc*16 + {h*4 + 0..3, 8 + h*4 + 0..3}),
   // then dQ^T += K^T dS^T.
-  auto compute = [&](int j, const bf16* sk, const bf16* sv, auto mask_tag) {
+  auto compute = [&](int j, const bf16* sk, const bf16* sv, auto mask_tag) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kb0 = j * BC;
     f32x16 s[NKB], g[NKB];
@@ -192,6 +197,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
       }
     }
     bf16x8 sf[NKB * 2];
+    // Row bounds of masked tiles, recomputed per tile from an opaque copy
+    // of the row index (so they need no registers across the sweep).
+    int lo_i = 0, hi_i = 0;
+    if (MASK) {
+      int qv = qi;
+      asm volatile("" : "+v"(qv));
+      lo_i = band.lo(qv);
+      hi_i = band.hi(qv);
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float ds[16];
@@ -200,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
         float x = s[kb][r];
         if (MASK) {
           const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+          const bool hidden = key < lo_i || key >= hi_i;
           x = hidden ? kNegInf : x;
         }
         const float pr = __builtin_amdgcn_exp2f(fmaf(x, cs, -l2));
@@ -225,30 +239,53 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   };
 
   // Two LDS stages, one barrier per tile (as in the forward): at the top of
-  // iteration j this wave waits for its own loads of tile j, the barrier
+  // step m this wave waits for its own loads of the step's tile, the barrier
   // makes every wave's loads visible and guarantees every wave has finished
-  // tile j-1, whose stage is then refilled with tile j+1. Waves wholly below
-  // the causal diagonal of a tile skip it.
-  auto iter = [&](int j, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    wait_global_loads();
-    __syncthreads();
-    if (j + 1 < ntiles) issue(j + 1, nk, nv);
-    if (MASK && CAUSAL && j * BC > qw0 + 31) return;
-    compute(j, sk, sv, mask_tag);
+  // step m-1, whose stage is then refilled with the next tile. A wave none of
+  // whose rows sees a masked tile skips it.
+  auto sweep = [&](const auto& tiles) FA_INLINE {
+    const int ns = tiles.count;
+    // Steps [su0, su1) hold the tiles every row sees in full.
+    const int su0 = WIN ? tiles.first_at_least(ju_lo) : 0;
+    const int su1 = max(tiles.first_at_least(ju_hi), su0);
+    auto iter = [&](int m, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv,
+                    auto mask_tag) FA_INLINE {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int j = tiles.tile(m);
+      wait_global_loads();
+      __syncthreads();
+      if (m + 1 < ns) issue(tiles.tile(m + 1), nk, nv);
+      if (MASK && (j * BC >= whi || j * BC + BC <= wlo)) return;
+      compute(j, sk, sv, mask_tag);
+    };
+    auto gen = [&](int m, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv) FA_INLINE {
+      if (m >= su0 && m < su1) iter(m, sk, sv, nk, nv, std::false_type{});
+      else iter(m, sk, sv, nk, nv, std::true_type{});
+    };
+    if (ns > 0) issue(tiles.tile(0), sK0, sV0);
+    // Whole pairs before the unmasked steps, unmasked pairs, then the rest
+    // (a last single step only in the final loop).
+    int m = 0;
+    for (; m < su0 && m + 1 < ns; m += 2) {
+      gen(m, sK0, sV0, sK1, sV1);
+      gen(m + 1, sK1, sV1, sK0, sV0);
+    }
+    for (; m + 1 < su1; m += 2) {
+      iter(m, sK0, sV0, sK1, sV1, std::false_type{});
+      iter(m + 1, sK1, sV1, sK0, sV0, std::false_type{});
+    }
+    for (; m < ns; m += 2) {
+      gen(m, sK0, sV0, sK1, sV1);
+      if (m + 1 >= ns) break;
+      gen(m + 1, sK1, sV1, sK0, sV0);
+    }
   };
-
-  if (ntiles > 0) issue(0, sK0, sV0);
-  int j = 0;
-  for (; j + 1 < j_unmasked; j += 2) {
-    iter(j, sK0, sV0, sK1, sV1, std::false_type{});
-    iter(j + 1, sK1, sV1, sK0, sV0, std::false_type{});
-  }
-  for (; j < ntiles; j += 2) {
-    if (j < j_unmasked) iter(j, sK0, sV0, sK1, sV1, std::false_type{});
-    else iter(j, sK0, sV0, sK1, sV1, std::true_type{});
-    if (j + 1 >= ntiles) break;
-    iter(j + 1, sK1, sV1, sK0, sV0, std::true_type{});
+  if constexpr (SPARSE) {
+    // The workgroup's 128 rows are one block row of the mask.
+    const int nl = stage_blocks(row_blocks(p, q0 / kBlock), sblk, tid, kThreads, p.nb);
+    sweep(sparse_tiles<kBlock / BC>(sblk, nl, tb, te));
+  } else {
+    sweep(dense_tiles(tb, te));
   }
 
   // dQ = scale * (dS K): the scores used Q' = sign(scale) Q with |scale|, the
@@ -273,11 +310,12 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BC, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BC, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return dispatch_mask_win(p, [&](auto causal, auto sparse, auto win) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BC, decltype(causal)::value, decltype(sparse)::value,
+                                      decltype(win)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace

@@ -20,7 +20,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
 
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL, bool SPARSE, bool WIN>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
   constexpr int KSTR = D + 8;    // row-major K / V tiles (bf16 elements)
   constexpr int TSTR = BC + 4;   // transposed K tile [d][key]
@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
   __shared__ __attribute__((aligned(16))) bf16 sV[BC * KSTR];
   __shared__ __attribute__((aligned(16))) bf16 sKt[D * TSTR];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -82,12 +83,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
   const float l2 = p.l2vec[(size_t)bh * p.n_pad + qr];
   const float dd = p.dvec[(size_t)bh * p.n_pad + qr];
 
-  int kend = kv_lim;
-  if (CAUSAL) kend = min(kend, q0 + kBR);
-  const int ntiles = (kend + BC - 1) / BC;
-  int j_unmasked = kv_lim / BC;
-  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
-  j_unmasked = min(j_unmasked, ntiles);
+  // Keys of this lane's row: [band.lo(qi), band.hi(qi)); key tiles [tb, te) hold every key
+  // some row of the workgroup sees, tiles [ju_lo, ju_hi) only keys that all
+  // of them see; keys [wlo, whi) are the ones some row of this wave sees.
+  const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+  const int q_last = min(q0 + kBR, n) - 1;
+  const int tb = band.lo(q0) / BC;
+  const int te = (band.hi(q_last) + BC - 1) / BC;
+  const int ju_lo = (band.lo(q_last) + BC - 1) / BC;
+  const int ju_hi = band.hi(q0) / BC;
+  const int wlo = band.lo(qw0);
+  const int whi = band.hi(min(qw0 + 31, n - 1));
 
   f32x16 acc[NMB];
 #pragma unroll
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
 
   // Key rows at or past the key limit are read clamped to the last visible
   // row; their probabilities are masked to exactly 0.
-  auto gload = [&](int j) {
+  auto gload = [&](int j) FA_INLINE {
     const int kb0 = j * BC;
 #pragma unroll
     for (int i = 0; i < KUPT; ++i) {
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
     }
   };
 
-  auto swrite = [&]() {
+  auto swrite = [&]() FA_INLINE {
 #pragma unroll
     for (int i = 0; i < KUPT; ++i) {
       const int u = tid + i * kThreads;
@@ -141,15 +147,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
     }
   };
 
-  auto step = [&](int j, auto mask_tag) {
+  // Step on key tile j (registers hold it); the loads of tile jn, the next
+  // one (or j again at the end), go out before the compute.
+  auto step = [&](int j, int jn, auto mask_tag) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     __syncthreads();  // every wave is done reading the previous tile
     swrite();
     __syncthreads();
-    gload(min(j + 1, ntiles - 1));
+    gload(jn);
 
     const int kb0 = j * BC;
-    if (MASK && CAUSAL && kb0 > qw0 + 31) return;  // tile above this wave's diagonal
+    if (MASK && (kb0 >= whi || kb0 + BC <= wlo)) return;  // no row of this wave sees it
 
     // S^T = K Q^T and dP^T = V dO^T (keys x queries).
     f32x16 sv[NKB], dp[NKB];
@@ -169,6 +177,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
     // fragments: chunk (kb, kc) holds keys kb*32 + kc*16 + {h*4 + 0..3,
     // 8 + h*4 + 0..3}.
     bf16x8 sf[NKB * 2];
+    // Row bounds of masked tiles, recomputed per tile from an opaque copy
+    // of the row index (so they need no registers across the sweep).
+    int lo_i = 0, hi_i = 0;
+    if (MASK) {
+      int qv = qi;
+      asm volatile("" : "+v"(qv));
+      lo_i = band.lo(qv);
+      hi_i = band.hi(qv);
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float ds[16];
@@ -177,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
         float pr = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], cs, -l2));
         if (MASK) {
           const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+          const bool hidden = key < lo_i || key >= hi_i;
           pr = hidden ? 0.f : pr;
         }
         ds[r] = pr * (dp[kb][r] - dd);
@@ -203,10 +220,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
     }
   };
 
-  if (ntiles > 0) gload(0);
-  int j = 0;
-  for (; j < j_unmasked; ++j) step(j, std::false_type{});
-  for (; j < ntiles; ++j) step(j, std::true_type{});
+  auto sweep = [&](const auto& tiles) FA_INLINE {
+    const int ns = tiles.count;
+    // Steps [su0, su1) hold the tiles every row sees in full.
+    const int su0 = WIN ? tiles.first_at_least(ju_lo) : 0;
+    const int su1 = max(tiles.first_at_least(ju_hi), su0);
+    auto next = [&](int m) FA_INLINE { return tiles.tile(min(m + 1, ns - 1)); };
+    if (ns > 0) gload(tiles.tile(0));
+    int m = 0;
+#pragma unroll 1
+    for (; m < su0; ++m) step(tiles.tile(m), next(m), std::true_type{});
+#pragma unroll 1
+    for (; m < su1; ++m) step(tiles.tile(m), next(m), std::false_type{});
+#pragma unroll 1
+    for (; m < ns; ++m) step(tiles.tile(m), next(m), std::true_type{});
+  };
+  if constexpr (SPARSE) {
+    // The workgroup's rows lie in one block row of the mask.
+    const int nl = stage_blocks(row_blocks(p, q0 / kBlock), sblk, tid, kThreads, p.nb);
+    sweep(sparse_tiles<kBlock / BC>(sblk, nl, tb, te));
+  } else {
+    sweep(dense_tiles(tb, te));
+  }
 
   // dQ = scale * (dS K): the scores used Q' = sign(scale) Q with |scale|, the
   // accumulated sum is dS K with the true dS, so the signed scale applies.
@@ -230,11 +265,12 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((bwd_dq_staged_kernel<D, BC, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_dq_staged_kernel<D, BC, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return dispatch_mask_win(p, [&](auto causal, auto sparse, auto win) {
+    hipLaunchKernelGGL((bwd_dq_staged_kernel<D, BC, decltype(causal)::value,
+                                             decltype(sparse)::value, decltype(win)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace

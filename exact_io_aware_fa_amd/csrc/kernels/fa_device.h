@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../fa_internal.h"
 
 namespace fa {
@@ -86,8 +88,12 @@ __device__ __forceinline__ void gload_lds16(const void* g, void* lds_base) {
 // format word of the gfx9 family). base and bytes must be wave-uniform, so the
 // descriptor lives in scalar registers. Loads through it at byte offsets at or
 // past `bytes` are out of range: they read no memory and return zero.
+// (The size goes through readfirstlane: a clamp such as max(min(x, a), 0)
+// becomes a vector instruction, and a descriptor word in a vector register
+// makes the compiler wrap every load in a loop over the lanes.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // bload_lds16: 16 bytes at byte offset voff (per lane) of a buffer into LDS
@@ -210,6 +216,146 @@ __device__ __forceinline__ int kv_limit(const Params& p, int b, int n) {
   int v = p.kv_len[b];
   v = v < 0 ? 0 : v;
   return v > n ? n : v;
+}
+
+// Interval masks -- causal, key padding and the sliding window -- of one
+// batch entry of length n. Query row i (0-based in its entry) sees keys
+// [lo(i), hi(i)); key j is seen by queries [qlo(j), qhi(j)). All four bounds
+// are non-decreasing, so the first and last row (key) of a tile bound the
+// whole tile. A window side of -1 is unbounded.
+template <bool CAUSAL>
+struct Band {
+  int n, kv_lim, wl, wr;
+  __device__ __forceinline__ int lo(int i) const { return wl >= 0 ? max(i - wl, 0) : 0; }
+  __device__ __forceinline__ int hi(int i) const {
+    int h = kv_lim;
+    if (CAUSAL) h = min(h, i + 1);
+    if (wr >= 0) h = min(h, i + wr + 1);
+    return h;
+  }
+  __device__ __forceinline__ int qlo(int j) const {
+    if (j >= kv_lim) return n;
+    int l = CAUSAL ? j : 0;
+    if (wr >= 0) l = max(l, j - wr);
+    return l;
+  }
+  __device__ __forceinline__ int qhi(int j) const { return wl >= 0 ? min(n, j + wl + 1) : n; }
+};
+template <bool CAUSAL>
+__device__ __forceinline__ Band<CAUSAL> make_band(const Params& p, int n, int kv_lim) {
+  return Band<CAUSAL>{n, kv_lim, p.win_left, p.win_right};
+}
+
+// Block-sparse index (built by the index kernel from a block mask over
+// kBlock x kBlock blocks, nb per side): row_ptr[nb + 1], col_idx[nb * nb],
+// col_ptr[nb + 1], row_idx[nb * nb] -- for query block r the visible key
+// blocks col_idx[row_ptr[r] .. row_ptr[r + 1]), for key block c the query
+// blocks row_idx[col_ptr[c] .. col_ptr[c + 1]), both ascending.
+constexpr int kBlock = 128;
+constexpr int kMaxBlocks = 1024;  // nb limit: the list of one row fits LDS
+struct BlockList {
+  const int32_t* idx;
+  int count;
+};
+// The list of row r (column c). Offsets and counts are clamped to the index's
+// extent, so a malformed index cannot send a kernel out of bounds.
+__device__ __forceinline__ BlockList clamp_list(const int32_t* ptr, const int32_t* idx, int i,
+                                                int nb) {
+  const int a = min(max(ptr[i], 0), nb * nb);
+  const int e = min(max(ptr[i + 1], a), nb * nb);
+  return BlockList{idx + a, min(e - a, nb)};
+}
+__device__ __forceinline__ BlockList row_blocks(const Params& p, int r) {
+  return clamp_list(p.blk, p.blk + (p.nb + 1), r, p.nb);
+}
+__device__ __forceinline__ BlockList col_blocks(const Params& p, int c) {
+  const int32_t* cp = p.blk + (p.nb + 1) + p.nb * p.nb;
+  return clamp_list(cp, cp + (p.nb + 1), c, p.nb);
+}
+// Copies a block list into LDS (every thread of the workgroup takes part; a
+// barrier follows) and returns its length. Entries are clamped to [0, nb).
+__device__ __forceinline__ int stage_blocks(BlockList l, int* lds, int tid, int nthreads, int nb) {
+  for (int i = tid; i < l.count; i += nthreads) lds[i] = min(max(l.idx[i], 0), nb - 1);
+  __syncthreads();
+  return l.count;
+}
+
+// The tiles a workgroup visits, in ascending order, as a function of the
+// step number m in [0, count). Dense: the tiles [tb, te). Sparse: the tiles
+// of the listed blocks (TPB tiles each) that fall inside [tb, te).
+struct DenseTiles {
+  int t0, count;
+  // (readfirstlane: the value is wave-uniform anyway, and an opaque step
+  // keeps the compiler from strength-reducing every address derived from the
+  // tile into a register of its own across the loop.)
+  __device__ __forceinline__ int tile(int m) const {
+    return __builtin_amdgcn_readfirstlane(t0 + m);
+  }
+  // First step whose tile is >= x (count if none).
+  __device__ __forceinline__ int first_at_least(int x) const { return min(max(x - t0, 0), count); }
+};
+__device__ __forceinline__ DenseTiles dense_tiles(int tb, int te) {
+  return DenseTiles{tb, max(te - tb, 0)};
+}
+template <int TPB>
+struct SparseTiles {
+  const int* lst;  // LDS: ascending block indices
+  int nent;        // entries in lst
+  int s;           // tiles of the first block before tb (skipped)
+  int count;
+  __device__ __forceinline__ int tile(int m) const {
+    const int k = m + s;
+    return lst[k / TPB] * TPB + k % TPB;
+  }
+  __device__ __forceinline__ int first_at_least(int x) const {
+    int a = 0, e = nent;  // first entry whose last tile is >= x
+    while (a < e) {
+      const int mid = (a + e) >> 1;
+      if (lst[mid] * TPB + TPB - 1 >= x) e = mid; else a = mid + 1;
+    }
+    if (a == nent) return count;
+    const int m = a * TPB + max(x - lst[a] * TPB, 0) - s;
+    return min(max(m, 0), count);
+  }
+};
+// The listed blocks (already in LDS, ascending, n entries) trimmed to the
+// tile range [tb, te).
+template <int TPB>
+__device__ __forceinline__ SparseTiles<TPB> sparse_tiles(const int* lst, int n, int tb, int te) {
+  // a: first block not wholly before tb; e: first block wholly at or past te.
+  int a = 0, hi = n;
+  while (a < hi) {
+    const int mid = (a + hi) >> 1;
+    if (lst[mid] * TPB + TPB > tb) hi = mid; else a = mid + 1;
+  }
+  int e = a;
+  hi = n;
+  while (e < hi) {
+    const int mid = (e + hi) >> 1;
+    if (lst[mid] * TPB >= te) hi = mid; else e = mid + 1;
+  }
+  if (a >= e || te <= tb) return SparseTiles<TPB>{lst + a, 0, 0, 0};
+  const int s = max(tb - lst[a] * TPB, 0);
+  const int tail = max((lst[e - 1] + 1) * TPB - te, 0);
+  return SparseTiles<TPB>{lst + a, e - a, s, (e - a) * TPB - s - tail};
+}
+
+// Calls f(causal_tag, sparse_tag) with the compile-time flags of the call's
+// masks (host side, for the launchers).
+template <typename F>
+hipError_t dispatch_mask(const Params& p, F&& f) {
+  if (p.blk != nullptr)
+    return p.causal ? f(std::true_type{}, std::true_type{}) : f(std::false_type{}, std::true_type{});
+  return p.causal ? f(std::true_type{}, std::false_type{}) : f(std::false_type{}, std::false_type{});
+}
+// The same with a third flag, set when the window has a lower edge: only
+// then can masked tiles come before the unmasked ones in a query-outer
+// sweep, and kernels without that case keep a shorter loop structure.
+template <typename F>
+hipError_t dispatch_mask_win(const Params& p, F&& f) {
+  if (p.win_left >= 0)
+    return dispatch_mask(p, [&](auto c, auto s) { return f(c, s, std::true_type{}); });
+  return dispatch_mask(p, [&](auto c, auto s) { return f(c, s, std::false_type{}); });
 }
 
 }  // namespace fa

@@ -32,7 +32,7 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
   return fmaf(a[0], b[0], fmaf(a[1], b[1], fmaf(a[2], b[2], a[3] * b[3])));
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
   constexpr int BR = 64;
   constexpr int BC = 32;
@@ -40,6 +40,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
   constexpr int NV = D / 16;    // chunks per lane (chunk index sub + 4 i)
   __shared__ f32x4 sK[BC][C4];
   __shared__ f32x4 sV[BC][C4];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int row = tid >> 2;
@@ -73,10 +74,17 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
     acc[i] = f32x4{};
   }
   float m2 = kNegInf, l = 0.f;
-  int kend = kv_lim;
-  if (CAUSAL) kend = min(kend, q0 + BR);
+  // Keys of this row, [lo_i, hi_i), and the key tiles any row of the
+  // workgroup needs (the bounds are non-decreasing in the row).
+  const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+  const int lo_i = band.lo(qi), hi_i = band.hi(qi);
+  const int q_last = min(q0 + BR, n) - 1;
+  const int tb = band.lo(q0) / BC;
+  const int te = (band.hi(q_last) + BC - 1) / BC;
 
-  for (int k0 = 0; k0 < kend; k0 += BC) {
+  auto sweep = [&](const auto& tiles) {
+  for (int m = 0; m < tiles.count; ++m) {
+    const int k0 = tiles.tile(m) * BC;
     __syncthreads();
     for (int x = tid; x < BC * C4; x += kThreads) {
       const int kr = x / C4, ch = x % C4;
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
       for (int i = 0; i < NV; ++i) part += dot4(q4[i], sK[t][sub + 4 * i]);
       part = quad_sum(part);
       const int key = k0 + t;
-      const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+      const bool hidden = key < lo_i || key >= hi_i;
       sc[t] = hidden ? kNegInf : part;
       mt = fmaxf(mt, sc[t]);
     }
@@ -124,6 +132,14 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
       acc[i] = a;
     }
   }
+  };
+  if constexpr (SPARSE) {
+    // One block row of the mask covers the workgroup's rows (BR <= kBlock).
+    const int nl = stage_blocks(row_blocks(p, q0 / kBlock), sblk, tid, kThreads, p.nb);
+    sweep(sparse_tiles<kBlock / BC>(sblk, nl, tb, te));
+  } else {
+    sweep(dense_tiles(tb, te));
+  }
 
   if (qi < n) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -135,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
   constexpr int BK = 64;
   constexpr int BQ = 16;
@@ -146,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
   __shared__ f32x4 sK[BK][C4];
   __shared__ float sL[BQ], sDv[BQ];
   __shared__ float sdS[BQ][BK + 1];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int kr = tid >> 2;
@@ -185,7 +202,14 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
       sK[r][ch] = (k0 + r < kv_lim) ? *reinterpret_cast<const f32x4*>(K + (size_t)(k0 + r) * D + ch * 4)
                                     : f32x4{};
     }
-    const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
+    // Queries of this key, [qlo_k, qhi_k), and the query tiles any key of the
+    // workgroup needs (the bounds are non-decreasing in the key).
+    const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+    const int qlo_k = band.qlo(key), qhi_k = band.qhi(key);
+    const int k_last = min(k0 + BK, kv_lim) - 1;
+    const int tb = band.qlo(k0) / BQ;
+    const int te = (band.qhi(k_last) + BQ - 1) / BQ;
+    auto sweep = [&](const auto& tiles) {
     for (int gq = 0; gq < p.group; ++gq) {
       // Work entry of query head hk * group + gq (workspace rows).
       const int bh = b * p.heads + hk * p.group + gq;
@@ -197,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
       float* __restrict__ dQ = static_cast<float*>(p.dq) + base;
       // Each query tile starts on a barrier, so the LDS tiles of the previous
       // head are no longer read when this head's first tile is stored.
-      for (int q0 = qstart; q0 < n; q0 += BQ) {
+      for (int m = 0; m < tiles.count; ++m) {
+        const int q0 = tiles.tile(m) * BQ;
         __syncthreads();
         for (int x = tid; x < BQ * C4; x += kThreads) {
           const int r = x / C4, ch = x % C4;
@@ -228,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
           }
           sp = quad_sum(sp);
           dpp = quad_sum(dpp);
-          const bool hidden = q >= n || key >= kv_lim || (CAUSAL && key > q);
+          const bool hidden = q < qlo_k || q >= qhi_k;
           const float pr = hidden ? 0.f : __builtin_amdgcn_exp2f(fmaf(sp, cs, -sL[t]));
           const float ds = pr * (dpp - sDv[t]);
 #pragma unroll
@@ -256,6 +281,14 @@ __global__ __launch_bounds__(kThreads) void bwd_fp32_kernel(Params p) {
         }
       }
     }  // query heads of the group
+    };
+    if constexpr (SPARSE) {
+      // One block column of the mask covers the workgroup's keys (BK <= kBlock).
+      const int nl = stage_blocks(col_blocks(p, k0 / kBlock), sblk, tid, kThreads, p.nb);
+      sweep(sparse_tiles<kBlock / BQ>(sblk, nl, tb, te));
+    } else {
+      sweep(dense_tiles(tb, te));
+    }
   }
 
   if (key < n) {
@@ -272,10 +305,16 @@ template <int D>
 hipError_t launch_fwd_d(const Params& p, hipStream_t s) {
   const long long total = (long long)((p.n + 63) / 64) * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((fwd_fp32_kernel<D, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fwd_fp32_kernel<D, false>), grid, block, 0, s, p);
+  if (p.blk != nullptr) {
+    if (p.causal)
+      hipLaunchKernelGGL((fwd_fp32_kernel<D, true, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_fp32_kernel<D, false, true>), grid, block, 0, s, p);
+  } else if (p.causal) {
+    hipLaunchKernelGGL((fwd_fp32_kernel<D, true, false>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((fwd_fp32_kernel<D, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -283,10 +322,16 @@ template <int D>
 hipError_t launch_bwd_d(const Params& p, hipStream_t s) {
   const long long total = (long long)((p.n + 63) / 64) * p.batch * p.heads_kv;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((bwd_fp32_kernel<D, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_fp32_kernel<D, false>), grid, block, 0, s, p);
+  if (p.blk != nullptr) {
+    if (p.causal)
+      hipLaunchKernelGGL((bwd_fp32_kernel<D, true, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_fp32_kernel<D, false, true>), grid, block, 0, s, p);
+  } else if (p.causal) {
+    hipLaunchKernelGGL((bwd_fp32_kernel<D, true, false>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_fp32_kernel<D, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

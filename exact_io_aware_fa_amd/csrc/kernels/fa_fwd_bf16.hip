@@ -61,7 +61,7 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;           // bytes per row
@@ -125,16 +125,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     }
   }
 
-  int kend = kv_lim;
-  if (CAUSAL) kend = min(kend, q0 + kBR);
-  const int ntiles = (kend + BC - 1) / BC;
-  // This wave's tiles: [0, jlast]; tiles [0, junm) have every key visible to
-  // every query of the wave (below the key limit and, if causal, at or below
-  // the wave's first query), the rest are masked.
-  int jlast = ntiles - 1;
-  if (CAUSAL) jlast = min(jlast, (qw0 + 31) / BC);
-  int junm = kv_lim / BC;
-  if (CAUSAL) junm = min(junm, (qw0 + 1) / BC);
+  // Keys of this lane's row: [band.lo(qi), band.hi(qi)). Step m of the sweep handles key
+  // tile tb + m; the workgroup's rows need tiles [tb, tb + ntiles). This
+  // wave's rows need steps [s_first, s_last], and steps [su_lo, su_hi) hold
+  // only keys every row of the wave sees (the bounds are non-decreasing in
+  // the row); the other steps of the wave are masked.
+  const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+  const int tb = band.lo(q0) / BC;
+  const int ntiles = max((band.hi(min(q0 + kBR, n) - 1) + BC - 1) / BC - tb, 0);
+  const int qw_last = min(qw0 + 31, n - 1);
+  const int s_first = band.lo(qw0) / BC - tb;
+  const int s_last = (band.hi(qw_last) - 1) / BC - tb;
+  const int su_lo = (band.lo(qw_last) + BC - 1) / BC - tb;
+  const int su_hi = band.hi(qw0) / BC - tb;
 
   f32x16 acc[NMB];
 #pragma unroll
@@ -160,8 +163,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     ld_voff[i] = (row * D + ((lane % CH) ^ swz_tr<D>(row)) * 8) * 2;
   }
   auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) FA_INLINE {
-    const int kb0 = j * BC;
-    const auto r = buffer_rsrc(src + (size_t)kb0 * D, min(kv_lim - kb0, BC) * ROWB);
+    const int kb0 = (tb + j) * BC;
+    const auto r = buffer_rsrc(src + (size_t)kb0 * D, max(min(kv_lim - kb0, BC), 0) * ROWB);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) bload_lds16(r, off[i], dst + (w * LPW + i) * RPL * D);
   };
@@ -260,13 +263,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   // P^T as bf16 B fragments in pf (chunk kk holds keys kk*16 + {h*4 + 0..3,
   // 8 + h*4 + 0..3}).
   auto apply_mask = [&](int j) FA_INLINE {
-    const int kb0 = j * BC;
+    const int kb0 = (tb + j) * BC;
+    // Row bounds, recomputed per masked tile from an opaque copy of the
+    // row index (so they need no registers across the sweep).
+    int qv = qi;
+    asm volatile("" : "+v"(qv));
+    const int lo_i = band.lo(qv), hi_i = band.hi(qv);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+        const bool hidden = key < lo_i || key >= hi_i;
         sc[kb][r] = hidden ? kNegInf : sc[kb][r];
       }
   };
@@ -319,13 +327,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     for (int kk = 0; kk < NKB * 2; ++kk) asm volatile("" : "+v"(pf[kk]));
     asm volatile("" : "+v"(lpart));
   };
-  // General softmax phase of tile j: tiles this wave does not own (before
-  // the first, past its causal diagonal or the last) leave P^T zero, so the
-  // next matrix phase, which always runs both products, adds exactly 0.
-  // Masking only edits the scores ahead of the common softmax body.
+  // General softmax phase of step j: tiles this wave does not need (before
+  // the first step, outside its rows' keys or past the last) leave P^T zero,
+  // so the next matrix phase, which always runs both products, adds exactly
+  // 0. Masking only edits the scores ahead of the common softmax body.
   auto valu_phase = [&](int j) FA_INLINE {
-    if (j >= 0 && j < ntiles && j <= jlast) {
-      if (j >= junm) apply_mask(j);
+    if (j >= 0 && j < ntiles && j >= s_first && j <= s_last) {
+      if (j < su_lo || j >= su_hi) apply_mask(j);
       softmax(j);
     } else {
 #pragma unroll
@@ -393,17 +401,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     slots(sk, sv, std::true_type{}, std::true_type{});
   };
 
-  // Steps [1, hot_end) are hot for this wave: tile m exists and is this
-  // wave's (S^T of tile m), and the softmax tile (m for group A, m-1 for
-  // group B) is unmasked. Step 0 and the steps from the first non-hot one
-  // on take the general path. The hot loop runs pairs of steps starting at
-  // an odd step, so every loop keeps a fixed stage assignment.
-  const int hot_end = min(min(ntiles, jlast + 1), grp == 0 ? junm : junm + 1);
+  // Steps [hot_begin, hot_end) are hot for this wave: tile m exists and is
+  // needed by the wave (S^T of tile m), and the softmax tile (m for group A,
+  // m-1 for group B) is unmasked. Step 0 and the other steps take the
+  // general path. Steps run in pairs starting at an odd step, so every loop
+  // keeps a fixed stage assignment; all waves run steps 0 .. ntiles, so
+  // they pass the same barriers.
+  const int hot_begin = WIN ? max(1, su_lo + grp) : 1;
+  const int hot_end = min(min(ntiles, s_last + 1), su_hi + grp);
   if (ntiles > 0) issue(K, ld_koff, 0, sK0);
   wait_global_loads();
+  // The first loop takes whole pairs only, so a last single step is left to
+  // the final loop. (Each group has loops of its own: one shared generic
+  // loop makes the compiler spill.)
   if (grp == 0) {
     step_a(0, sK0, sK1, sV0, sV1);
     int m = 1;
+    for (; m < hot_begin && m + 1 <= ntiles; m += 2) {
+      step_a(m, sK1, sK0, sV1, sV0);
+      step_a(m + 1, sK0, sK1, sV0, sV1);
+    }
     for (; m + 1 < hot_end; m += 2) {
       hot_a(m, sK1, sK0, sV1, sV0);
       hot_a(m + 1, sK0, sK1, sV0, sV1);
@@ -416,6 +433,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   } else {
     step_b(0, sK0, sK1, sV0, sV1);
     int m = 1;
+    for (; m < hot_begin && m + 1 <= ntiles; m += 2) {
+      step_b(m, sK1, sK0, sV1, sV0);
+      step_b(m + 1, sK0, sK1, sV0, sV1);
+    }
     for (; m + 1 < hot_end; m += 2) {
       hot_b(m, sK1, sK0, sV1, sV0);
       hot_b(m + 1, sK0, sK1, sV0, sV1);
@@ -451,11 +472,12 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  // (Block-sparse masks never reach this kernel.)
+  return dispatch_mask_win(p, [&](auto causal, auto, auto win) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, decltype(causal)::value, decltype(win)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace
@@ -463,7 +485,9 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s) {
   switch (d) {
     case 64: return launch_fwd_bf16_d64(p, d, s);
-    case 128: return launch_d<128, 64>(p, s);
+    // Block-sparse masks take the 4-wave kernel: its 128-row workgroups lie
+    // in one block row of the mask.
+    case 128: return p.blk != nullptr ? launch_fwd_bf16_d64(p, d, s) : launch_d<128, 64>(p, s);
     case 256: return launch_fwd_bf16_staged(p, d, s);
     default: return hipErrorInvalidValue;
   }

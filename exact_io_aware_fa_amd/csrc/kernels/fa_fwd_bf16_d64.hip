@@ -36,7 +36,7 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, int MINW, bool CAUSAL>
+template <int D, int BC, int MINW, bool CAUSAL, bool SPARSE, bool WIN>
 __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) {
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;           // bytes per row
@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
   __shared__ __attribute__((aligned(1024))) bf16 sK1[BC * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV0[BC * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV1[BC * D];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -95,15 +96,18 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
     }
   }
 
-  int kend = kv_lim;
-  if (CAUSAL) kend = min(kend, q0 + kBR);
-  const int ntiles = (kend + BC - 1) / BC;
-  // Tiles [0, j_unmasked) have every key visible to every query of the
-  // workgroup: wholly below the key limit and, if causal, at or below the
-  // workgroup's first query. The rest go through the masked path.
-  int j_unmasked = kv_lim / BC;
-  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
-  j_unmasked = min(j_unmasked, ntiles);
+  // Keys of this lane's row: [band.lo(qi), band.hi(qi)); key tiles [tb, te) hold every key
+  // some row of the workgroup sees, tiles [ju_lo, ju_hi) only keys that all
+  // of them see (the bounds are non-decreasing in the row); keys [wlo, whi)
+  // are the ones some row of this wave sees.
+  const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+  const int q_last = min(q0 + kBR, n) - 1;
+  const int tb = band.lo(q0) / BC;
+  const int te = (band.hi(q_last) + BC - 1) / BC;
+  const int ju_lo = (band.lo(q_last) + BC - 1) / BC;
+  const int ju_hi = band.hi(q0) / BC;
+  const int wlo = band.lo(qw0);
+  const int whi = band.hi(min(qw0 + 31, n - 1));
 
   f32x16 acc[NMB];
 #pragma unroll
@@ -125,9 +129,9 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
     ld_koff[i] = (row * D + ((lane % CH) ^ swz_row<D>(row)) * 8) * 2;
     ld_voff[i] = (row * D + ((lane % CH) ^ swz_tr<D>(row)) * 8) * 2;
   }
-  auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) {
+  auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) FA_INLINE {
     const int kb0 = j * BC;
-    const auto r = buffer_rsrc(src + (size_t)kb0 * D, min(kv_lim - kb0, BC) * ROWB);
+    const auto r = buffer_rsrc(src + (size_t)kb0 * D, max(min(kv_lim - kb0, BC), 0) * ROWB);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) bload_lds16(r, off[i], dst + (w * LPW + i) * RPL * D);
   };
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
   }
 
   // S^T (keys x queries) = K Q^T for the tile in sk, raw dot products.
-  auto scores = [&](const bf16* sk, f32x16 (&s)[NKB]) {
+  auto scores = [&](const bf16* sk, f32x16 (&s)[NKB]) FA_INLINE {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16{};
@@ -178,16 +182,25 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
   };
 
   // Online-softmax update with the scores of tile j, then O^T += V^T P^T.
-  auto softmax_pv = [&](int j, f32x16 (&s)[NKB], const bf16* sv, auto mask_tag) {
+  auto softmax_pv = [&](int j, f32x16 (&s)[NKB], const bf16* sv, auto mask_tag) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kb0 = j * BC;
     if (MASK) {
+      // Row bounds of masked tiles, recomputed per tile from an opaque copy
+      // of the row index (so they need no registers across the sweep).
+      int lo_i = 0, hi_i = 0;
+      if (MASK) {
+        int qv = qi;
+        asm volatile("" : "+v"(qv));
+        lo_i = band.lo(qv);
+        hi_i = band.hi(qv);
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+          const bool hidden = key < lo_i || key >= hi_i;
           s[kb][r] = hidden ? kNegInf : s[kb][r];
         }
     }
@@ -250,41 +263,64 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
       }
   };
 
-  // Two LDS stages: at the top of iteration j this wave waits for its own
-  // loads of tile j, then the barrier makes every wave's loads of tile j
-  // visible and guarantees every wave has finished tile j-1, whose stage is
-  // refilled with tile j+1 right after. Waves above the causal diagonal of a
-  // tile skip it.
-  auto iter = [&](int j, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    wait_global_loads();
-    __syncthreads();
-    if (j + 1 < ntiles) {
-      issue(K, ld_koff, j + 1, nk);
-      issue(V, ld_voff, j + 1, nv);
+  // Two LDS stages: at the top of step m this wave waits for its own loads
+  // of the step's tile, then the barrier makes every wave's loads visible and
+  // guarantees every wave has finished step m-1, whose stage is refilled
+  // with the next tile right after. A wave none of whose rows sees a masked
+  // tile skips it. Even steps use stage 0, odd steps stage 1.
+  auto sweep = [&](const auto& tiles) FA_INLINE {
+    const int ns = tiles.count;
+    // Steps [su0, su1) hold the tiles every row sees in full.
+    const int su0 = WIN ? tiles.first_at_least(ju_lo) : 0;
+    const int su1 = max(tiles.first_at_least(ju_hi), su0);
+    auto iter = [&](int m, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv,
+                    auto mask_tag) FA_INLINE {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int j = tiles.tile(m);
+      wait_global_loads();
+      __syncthreads();
+      if (m + 1 < ns) {
+        const int jn = tiles.tile(m + 1);
+        issue(K, ld_koff, jn, nk);
+        issue(V, ld_voff, jn, nv);
+      }
+      if (MASK && (j * BC >= whi || j * BC + BC <= wlo)) return;
+      f32x16 sc[NKB];
+      scores(sk, sc);
+      softmax_pv(j, sc, sv, mask_tag);
+    };
+    auto gen = [&](int m, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv) FA_INLINE {
+      if (m >= su0 && m < su1) iter(m, sk, sv, nk, nv, std::false_type{});
+      else iter(m, sk, sv, nk, nv, std::true_type{});
+    };
+    if (ns > 0) {
+      const int j0 = tiles.tile(0);
+      issue(K, ld_koff, j0, sK0);
+      issue(V, ld_voff, j0, sV0);
     }
-    if (MASK && CAUSAL && j * BC > qw0 + 31) return;
-    f32x16 sc[NKB];
-    scores(sk, sc);
-    softmax_pv(j, sc, sv, mask_tag);
+    // Whole pairs before the unmasked steps, unmasked pairs, then the rest
+    // (a last single step only in the final loop).
+    int m = 0;
+    for (; m < su0 && m + 1 < ns; m += 2) {
+      gen(m, sK0, sV0, sK1, sV1);
+      gen(m + 1, sK1, sV1, sK0, sV0);
+    }
+    for (; m + 1 < su1; m += 2) {
+      iter(m, sK0, sV0, sK1, sV1, std::false_type{});
+      iter(m + 1, sK1, sV1, sK0, sV0, std::false_type{});
+    }
+    for (; m < ns; m += 2) {
+      gen(m, sK0, sV0, sK1, sV1);
+      if (m + 1 >= ns) break;
+      gen(m + 1, sK1, sV1, sK0, sV0);
+    }
   };
-
-  if (ntiles > 0) {
-    issue(K, ld_koff, 0, sK0);
-    issue(V, ld_voff, 0, sV0);
-  }
-  // Pairs of unmasked tiles (even tiles use stage 0, odd tiles stage 1),
-  // then the remaining tiles: at most one unmasked, the rest masked.
-  int j = 0;
-  for (; j + 1 < j_unmasked; j += 2) {
-    iter(j, sK0, sV0, sK1, sV1, std::false_type{});
-    iter(j + 1, sK1, sV1, sK0, sV0, std::false_type{});
-  }
-  for (; j < ntiles; j += 2) {
-    if (j < j_unmasked) iter(j, sK0, sV0, sK1, sV1, std::false_type{});
-    else iter(j, sK0, sV0, sK1, sV1, std::true_type{});
-    if (j + 1 >= ntiles) break;
-    iter(j + 1, sK1, sV1, sK0, sV0, std::true_type{});
+  if constexpr (SPARSE) {
+    // The workgroup's 128 rows are one block row of the mask.
+    const int nl = stage_blocks(row_blocks(p, q0 / kBlock), sblk, tid, kThreads, p.nb);
+    sweep(sparse_tiles<kBlock / BC>(sblk, nl, tb, te));
+  } else {
+    sweep(dense_tiles(tb, te));
   }
 
   // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
@@ -311,11 +347,12 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((fwd_bf16_d64_kernel<D, BC, MINW, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fwd_bf16_d64_kernel<D, BC, MINW, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return dispatch_mask_win(p, [&](auto causal, auto sparse, auto win) {
+    hipLaunchKernelGGL((fwd_bf16_d64_kernel<D, BC, MINW, decltype(causal)::value,
+                                            decltype(sparse)::value, decltype(win)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace
@@ -323,6 +360,9 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 hipError_t launch_fwd_bf16_d64(const Params& p, int d, hipStream_t s) {
   switch (d) {
     case 64: return launch_d<64, 64, 2>(p, s);
+    // d = 128 with a block-sparse mask: 128-row workgroups lie in one block
+    // row of the mask (the 256-row ping-pong workgroups would span two).
+    case 128: return launch_d<128, 64, 2>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

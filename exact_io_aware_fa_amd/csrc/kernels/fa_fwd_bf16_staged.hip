@@ -22,7 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
 
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL, bool SPARSE, bool WIN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) {
   constexpr int KSTR = D + 8;    // K row stride in LDS (bf16 elements)
   constexpr int VSTR = BC + 4;   // V^T row stride in LDS (bf16 elements)
@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) 
 
   __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
   __shared__ __attribute__((aligned(16))) bf16 sVt[D * VSTR];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -79,15 +80,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) 
     }
   }
 
-  int kend = kv_lim;
-  if (CAUSAL) kend = min(kend, q0 + kBR);
-  const int ntiles = (kend + BC - 1) / BC;
-  // Tiles [0, j_unmasked) have every key visible to every query of the
-  // workgroup: wholly below the key limit and, if causal, at or below the
-  // workgroup's first query. The rest go through the masked path.
-  int j_unmasked = kv_lim / BC;
-  if (CAUSAL) j_unmasked = min(j_unmasked, (q0 + 1) / BC);
-  j_unmasked = min(j_unmasked, ntiles);
+  // Keys of this lane's row: [band.lo(qi), band.hi(qi)); key tiles [tb, te) hold every key
+  // some row of the workgroup sees, tiles [ju_lo, ju_hi) only keys that all
+  // of them see (the bounds are non-decreasing in the row); keys [wlo, whi)
+  // are the ones some row of this wave sees.
+  const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
+  const int q_last = min(q0 + kBR, n) - 1;
+  const int tb = band.lo(q0) / BC;
+  const int te = (band.hi(q_last) + BC - 1) / BC;
+  const int ju_lo = (band.lo(q_last) + BC - 1) / BC;
+  const int ju_hi = band.hi(q0) / BC;
+  const int wlo = band.lo(qw0);
+  const int whi = band.hi(min(qw0 + 31, n - 1));
 
   f32x16 acc[NMB];
 #pragma unroll
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) 
   // Fetch key/value tile j into registers. Rows at or past the key limit are
   // read clamped to the last visible row: their scores are masked to -inf,
   // so they contribute exactly 0, and padded rows are never read.
-  auto gload = [&](int j) {
+  auto gload = [&](int j) FA_INLINE {
     const int kb0 = j * BC;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) 
     }
   };
 
-  auto swrite = [&]() {
+  auto swrite = [&]() FA_INLINE {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + i * kThreads;
@@ -146,15 +150,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) 
     }
   };
 
-  auto step = [&](int j, auto mask_tag) {
+  // Step on key tile j (registers hold it); the loads of tile jn, the next
+  // one (or j again at the end), go out before the compute.
+  auto step = [&](int j, int jn, auto mask_tag) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     __syncthreads();  // every wave is done reading the previous tile
     swrite();
     __syncthreads();  // tile j is in LDS
-    gload(min(j + 1, ntiles - 1));
+    gload(jn);
 
     const int kb0 = j * BC;
-    if (MASK && CAUSAL && kb0 > qw0 + 31) return;  // tile above this wave's diagonal
+    if (MASK && (kb0 >= whi || kb0 + BC <= wlo)) return;  // no row of this wave sees it
 
     // S^T (keys x queries) = K Q^T, raw dot products.
     f32x16 s[NKB];
@@ -168,12 +174,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) 
       }
     }
     if (MASK) {
+      // Row bounds of masked tiles, recomputed per tile from an opaque copy
+      // of the row index (so they need no registers across the sweep).
+      int lo_i = 0, hi_i = 0;
+      if (MASK) {
+        int qv = qi;
+        asm volatile("" : "+v"(qv));
+        lo_i = band.lo(qv);
+        hi_i = band.hi(qv);
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool hidden = key >= kv_lim || (CAUSAL && key > qi);
+          const bool hidden = key < lo_i || key >= hi_i;
           s[kb][r] = hidden ? kNegInf : s[kb][r];
         }
     }
@@ -235,10 +250,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_staged_kernel(Params p) 
       }
   };
 
-  if (ntiles > 0) gload(0);
-  int j = 0;
-  for (; j < j_unmasked; ++j) step(j, std::false_type{});
-  for (; j < ntiles; ++j) step(j, std::true_type{});
+  auto sweep = [&](const auto& tiles) FA_INLINE {
+    const int ns = tiles.count;
+    // Steps [su0, su1) hold the tiles every row sees in full.
+    const int su0 = WIN ? tiles.first_at_least(ju_lo) : 0;
+    const int su1 = max(tiles.first_at_least(ju_hi), su0);
+    auto next = [&](int m) FA_INLINE { return tiles.tile(min(m + 1, ns - 1)); };
+    if (ns > 0) gload(tiles.tile(0));
+    int m = 0;
+#pragma unroll 1
+    for (; m < su0; ++m) step(tiles.tile(m), next(m), std::true_type{});
+#pragma unroll 1
+    for (; m < su1; ++m) step(tiles.tile(m), next(m), std::false_type{});
+#pragma unroll 1
+    for (; m < ns; ++m) step(tiles.tile(m), next(m), std::true_type{});
+  };
+  if constexpr (SPARSE) {
+    // The workgroup's rows lie in one block row of the mask.
+    const int nl = stage_blocks(row_blocks(p, q0 / kBlock), sblk, tid, kThreads, p.nb);
+    sweep(sparse_tiles<kBlock / BC>(sblk, nl, tb, te));
+  } else {
+    sweep(dense_tiles(tb, te));
+  }
 
   // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
   const float l = lpart + __shfl_xor(lpart, 32);
@@ -264,11 +297,12 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
-  if (p.causal)
-    hipLaunchKernelGGL((fwd_bf16_staged_kernel<D, BC, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fwd_bf16_staged_kernel<D, BC, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return dispatch_mask_win(p, [&](auto causal, auto sparse, auto win) {
+    hipLaunchKernelGGL((fwd_bf16_staged_kernel<D, BC, decltype(causal)::value,
+                                               decltype(sparse)::value, decltype(win)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace

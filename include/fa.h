@@ -74,6 +74,21 @@
  *            out-of-bounds access, and rows outside every sequence are left
  *            unwritten. (Variable-length batches without padding: page 2,
  *            "4. FlashAttention 深度剖析", 4.7.2 and 4.7.4.)
+ * Windows and block-sparse masks (*_masked, *_varlen: the fa_mask
+ *            argument, NULL for none): a window (window_left, window_right)
+ *            hides key j from query i when j < i - window_left or
+ *            j > i + window_right (a side of -1 is unbounded; positions
+ *            count within each sequence). A block mask is a boolean matrix
+ *            over FA_BLOCK x FA_BLOCK blocks (query block i / FA_BLOCK, key
+ *            block j / FA_BLOCK) that hides every key of a block that is not
+ *            set; it is passed as an index built once per mask by
+ *            fa_block_index_build, and blocks that are not set are skipped
+ *            entirely. All masks combine by AND; a query row left with no
+ *            visible key gets O = 0, LSE = -inf and zero gradients. (The
+ *            window_size argument of the flash-attn call: page 4,
+ *            "FlashAttention 原理深入剖析（下篇）", section 六, and page 2,
+ *            4.8.1; the block-level mask: page 3, "深入浅出 FlashAttention",
+ *            第八部分.)
  * Threads:   entry points are reentrant; concurrent calls on different
  *            streams may share inputs but must not share outputs.
  */
@@ -87,9 +102,24 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+
+/* Side of a block of the block-sparse mask, in rows and in keys. */
+#define FA_BLOCK 128
+
+/*
+ * Optional masks beyond causal and key padding (see the conventions above).
+ * block_index: NULL, or a device array written by fa_block_index_build for
+ * the same sequence length n (packed batches: max_seqlen); it must stay
+ * unchanged while calls that use it are in flight.
+ */
+typedef struct {
+  int64_t window_left;   /* -1: unbounded */
+  int64_t window_right;  /* -1: unbounded */
+  const int32_t* block_index;
+} fa_mask;
 
 typedef enum {
   FA_OK = 0,
@@ -138,16 +168,33 @@ fa_status fa_fwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv,
                      void* stream);
 
 /*
+ * fa_fwd_masked -- fa_fwd_gqa with the optional window and block-sparse
+ * masks (mask may be NULL). Window sides below -1 return FA_E_SHAPE; a
+ * block index for n > 1024 * FA_BLOCK returns FA_E_UNSUPPORTED; the index
+ * must be 4-byte aligned and must not overlap an output.
+ */
+fa_status fa_fwd_masked(int64_t batch, int64_t heads, int64_t heads_kv,
+                        int64_t n, int64_t d,
+                        int causal, float softmax_scale, fa_dtype dtype,
+                        const void* q, const void* k, const void* v,
+                        const int32_t* kv_len, const fa_mask* mask,
+                        void* o, float* lse,
+                        void* stream);
+
+/*
  * fa_fwd_varlen -- forward over a packed variable-length batch (layout and
  * offsets as described above). total >= max_seqlen >= 1; q, o: [heads,
  * total, d]; k, v: [heads_kv, total, d]; lse: float32 [heads, total]. No key
- * padding argument: each sequence's keys are exactly its rows.
+ * padding argument: each sequence's keys are exactly its rows. mask: as for
+ * fa_fwd_masked (NULL for none), positions and blocks counted within each
+ * sequence, the block index built for n = max_seqlen.
  */
 fa_status fa_fwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv,
                         int64_t total, int64_t max_seqlen, int64_t d,
                         const int32_t* cu_seqlens,
                         int causal, float softmax_scale, fa_dtype dtype,
                         const void* q, const void* k, const void* v,
+                        const fa_mask* mask,
                         void* o, float* lse,
                         void* stream);
 
@@ -214,9 +261,24 @@ fa_status fa_bwd_gqa(int64_t batch, int64_t heads, int64_t heads_kv,
                      void* stream);
 
 /*
+ * fa_bwd_masked -- fa_bwd_gqa with the optional masks of fa_fwd_masked
+ * (the same mask as the forward call).
+ */
+fa_status fa_bwd_masked(int64_t batch, int64_t heads, int64_t heads_kv,
+                        int64_t n, int64_t d,
+                        int causal, float softmax_scale, fa_dtype dtype,
+                        const void* q, const void* k, const void* v,
+                        const void* o, const void* d_o, const float* lse,
+                        const int32_t* kv_len, const fa_mask* mask,
+                        void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * fa_bwd_varlen -- backward over a packed variable-length batch: the
  * gradients of fa_bwd for each sequence on its own, with the layouts of
- * fa_fwd_varlen (dq like q; dk, dv like k, v). workspace: at least
+ * fa_fwd_varlen (dq like q; dk, dv like k, v) and the mask of the forward
+ * call. workspace: at least
  * fa_bwd_workspace_bytes(num_seqs, heads, max_seqlen, d, dtype) bytes. Rows
  * outside every sequence are left unwritten.
  */
@@ -226,9 +288,30 @@ fa_status fa_bwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv,
                         int causal, float softmax_scale, fa_dtype dtype,
                         const void* q, const void* k, const void* v,
                         const void* o, const void* d_o, const float* lse,
+                        const fa_mask* mask,
                         void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * fa_block_index_bytes -- size of the block-sparse index for sequence
+ * length n: 4 * (2 (nb + 1) + 2 nb^2) bytes with nb = ceil(n / FA_BLOCK).
+ * Returns 0 unless 1 <= n and nb <= 1024.
+ */
+size_t fa_block_index_bytes(int64_t n);
+
+/*
+ * fa_block_index_build -- builds the index of a block mask for sequence
+ * length n. block_mask: device uint8 [nb][nb] (row = query block, column =
+ * key block; nonzero = visible). index: device int32 output of
+ * fa_block_index_bytes(n) bytes, 4-byte aligned, not overlapping the mask:
+ * for every query block the ascending list of its visible key blocks and
+ * for every key block the ascending list of the query blocks that see it.
+ * Enqueued on `stream` (one small kernel); reuse the index for every call
+ * with that mask.
+ */
+fa_status fa_block_index_build(int64_t n, const uint8_t* block_mask,
+                               int32_t* index, void* stream);
 
 /*
  * fa_bwd_timed -- fa_bwd_gqa, additionally recording caller-owned HIP events on

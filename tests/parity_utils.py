@@ -41,13 +41,14 @@ def to_gpu(inp: dict) -> dict:
     return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
 
-def run_gpu(w, inp, backward=True):
+def run_gpu(w, inp, backward=True, window=None, block_index=None):
     g = to_gpu(inp)
-    o, lse = fa.flash_attn_fwd(g["q"], g["k"], g["v"], w.causal, w.softmax_scale, g["kv_len"])
+    o, lse = fa.flash_attn_fwd(g["q"], g["k"], g["v"], w.causal, w.softmax_scale, g["kv_len"],
+                               window, block_index)
     out = {"o": o, "lse": lse}
     if backward:
         dq, dk, dv = fa.flash_attn_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], w.causal,
-                                       w.softmax_scale, g["kv_len"])
+                                       w.softmax_scale, g["kv_len"], window, block_index)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return out
@@ -62,29 +63,42 @@ def group_of(inp) -> int:
     return inp["q"].shape[1] // inp["k"].shape[1]
 
 
-def check_forward_head(w, inp, gpu, b, h, rows=None, peaky=False):
+def _lse_close(got, ref, tol_abs=None, tol_rel=None):
+    """LSE comparison: rows with no visible key must be -inf on both sides,
+    the others within the tolerance."""
+    empty = ref == -np.inf
+    assert np.array_equal(got == -np.inf, empty), "rows without visible keys differ"
+    g, r = got[~empty], ref[~empty]
+    if tol_rel is not None:
+        return bool(np.all(np.abs(g - r) <= tol_rel * np.maximum(1.0, np.abs(r))))
+    return bool(np.all(np.abs(g - r) <= tol_abs))
+
+
+def check_forward_head(w, inp, gpu, b, h, rows=None, peaky=False, window=(-1, -1),
+                       block_mask=None):
     """Compare O and LSE of query head (b, h) (optionally only query
     ``rows``); K and V come from the K/V head that query head uses."""
     j = h // group_of(inp)
     q = f64(inp["q"][b, h])
     k, v = (f64(inp[x][b, j]) for x in ("k", "v"))
-    ref = oracle.head_forward(q, k, v, w.softmax_scale, w.causal, kv_len_of(inp, b), rows=rows)
+    ref = oracle.head_forward(q, k, v, w.softmax_scale, w.causal, kv_len_of(inp, b), rows=rows,
+                              window=window, block_mask=block_mask)
     go = f64(gpu["o"][b, h])
     gl = gpu["lse"][b, h].cpu().double().numpy()
     if rows is not None:
         go, gl = go[rows], gl[rows]
     if w.dtype == "fp32":
         assert normwise_rel(go, ref["o"]) <= FP32_REL, (b, h, normwise_rel(go, ref["o"]))
-        assert np.all(np.abs(gl - ref["lse"]) <= FP32_REL * np.maximum(1.0, np.abs(ref["lse"])))
+        assert _lse_close(gl, ref["lse"], tol_rel=FP32_REL), (b, h)
     else:
         err = np.abs(go - ref["o"])
         bound = BF16_O_ABS + (2.0 ** -8) * np.abs(ref["o"]) if peaky else BF16_O_ABS
         assert np.all(err <= bound), (b, h, float(err.max()))
-        assert np.abs(gl - ref["lse"]).max() <= BF16_LSE_ABS, (b, h, float(np.abs(gl - ref["lse"]).max()))
+        assert _lse_close(gl, ref["lse"], tol_abs=BF16_LSE_ABS), (b, h)
     return ref
 
 
-def check_backward_head(w, inp, gpu, b, h):
+def check_backward_head(w, inp, gpu, b, h, window=(-1, -1), block_mask=None):
     """Compare dQ of query head (b, h) and dK, dV of the K/V head it uses.
     With grouped K/V heads the oracle runs every query head of that group
     and sums their dK and dV (the gradient of a shared head), and the dQ of
@@ -97,7 +111,8 @@ def check_backward_head(w, inp, gpu, b, h):
     dk = dv = 0.0
     for hh in range(j * grp, (j + 1) * grp):
         q, do = (f64(inp[x][b, hh]) for x in ("q", "do"))
-        ref = oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal, kv_len_of(inp, b))
+        ref = oracle.head_backward(q, k, v, do, w.softmax_scale, w.causal, kv_len_of(inp, b),
+                                   window, block_mask)
         errs[f"dq{hh}"] = normwise_rel(f64(gpu["dq"][b, hh]), ref["dq"])
         dk = dk + ref["dk"]
         dv = dv + ref["dv"]

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.fa_abi_version() == B.ABI_VERSION == 3
+    assert B.fa_abi_version() == B.ABI_VERSION == 4
     for code, tag in ((0, "FA_OK"), (1, "FA_E_NULLPTR"), (2, "FA_E_SHAPE"),
                       (3, "FA_E_UNSUPPORTED"), (4, "FA_E_WORKSPACE"), (5, "FA_E_ALIAS"),
                       (6, "FA_E_LAUNCH"), (7, "FA_E_ALIGN")):
@@ -180,7 +180,8 @@ def fwd_varlen(**kw):
     a.update(kw)
     return B.fa_fwd_varlen(a["num_seqs"], a["heads"], a["heads_kv"], a["total"],
                            a["max_seqlen"], a["d"], a["cu"], a["causal"], a["softmax_scale"],
-                           a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["stream"])
+                           a["dtype"], a["q"], a["k"], a["v"], a.get("mask"), a["o"], a["lse"],
+                           a["stream"])
 
 
 def bwd_varlen(**kw):
@@ -194,8 +195,8 @@ def bwd_varlen(**kw):
     return B.fa_bwd_varlen(a["num_seqs"], a["heads"], a["heads_kv"], a["total"],
                            a["max_seqlen"], a["d"], a["cu"], a["causal"], a["softmax_scale"],
                            a["dtype"], a["q"], a["k"], a["v"], a["o"], a["d_o"], a["lse"],
-                           a["dq"], a["dk"], a["dv"], a["workspace"], a["workspace_bytes"],
-                           a["stream"])
+                           a.get("mask"), a["dq"], a["dk"], a["dv"], a["workspace"],
+                           a["workspace_bytes"], a["stream"])
 
 
 # One head of PACKED is 200 * 64 * 2 = 25600 bytes; its LSE 800 bytes per head.

@@ -131,14 +131,14 @@ def test_rows_outside_every_sequence_are_not_written(dtype):
     lse = torch.full((heads, total), 7.0, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
     B.check(B.fa_fwd_varlen(2, heads, heads, total, 163, d, cu.data_ptr(), 1, 0.125, dt,
-                            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            q.data_ptr(), k.data_ptr(), v.data_ptr(), None, o.data_ptr(),
                             lse.data_ptr(), s))
     grads = [torch.full_like(q, 7.0) for _ in range(3)]
     wsb = B.fa_bwd_workspace_bytes(2, heads, 163, d, dt)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     B.check(B.fa_bwd_varlen(2, heads, heads, total, 163, d, cu.data_ptr(), 1, 0.125, dt,
                             q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            do.data_ptr(), lse.data_ptr(), *(t.data_ptr() for t in grads),
+                            do.data_ptr(), lse.data_ptr(), None, *(t.data_ptr() for t in grads),
                             ws.data_ptr(), wsb, s))
     torch.cuda.synchronize()
     for t in [o, lse] + grads:
