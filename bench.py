@@ -245,6 +245,41 @@ def _gpu_clocks() -> str:
     return "; ".join(keep) if keep else "rocm-smi printed no clock lines"
 
 
+def visible_pairs(w) -> float:
+    """(query, key) pairs a masked workload computes, per (batch, head): the
+    exact count under its causal, window and block masks (FLOP accounting)."""
+    import numpy as np
+
+    from exact_io_aware_fa_amd.inputs import block_mask
+
+    n = w.n
+    i = np.arange(n)
+    lo = np.zeros(n, dtype=np.int64) if w.window[0] < 0 else np.maximum(i - w.window[0], 0)
+    hi = np.full(n, n, dtype=np.int64)
+    if w.causal:
+        hi = np.minimum(hi, i + 1)
+    if w.window[1] >= 0:
+        hi = np.minimum(hi, i + w.window[1] + 1)
+    bm = block_mask(w)
+    if bm is None:
+        return float(np.maximum(hi - lo, 0).sum())
+    total = 0
+    for kb in range(bm.shape[1]):
+        a, e = kb * 128, min(kb * 128 + 128, n)
+        rows = bm[i // 128, kb]
+        total += int(np.maximum(np.minimum(hi, e) - np.maximum(lo, a), 0)[rows].sum())
+    return float(total)
+
+
+def masked_flops(w):
+    """(fwd, bwd) FLOPs of a workload: 4 d per visible pair forward, 2.5x
+    that backward; the unmasked conventions for the others."""
+    if w.window == (-1, -1) and w.blocks is None:
+        return w.flops_fwd(), w.flops_bwd()
+    f = 4.0 * w.batch * w.heads * w.d * visible_pairs(w)
+    return f, 2.5 * f
+
+
 def _sweep_calls(name, dev, stream):
     """(fwd, bwd, tensors, flops_fwd, flops_bwd, bytes_fwd, bytes_bwd) of one
     sweep workload: a padded batch (with grouped heads when k has fewer) or a
@@ -286,6 +321,8 @@ def _sweep_calls(name, dev, stream):
         tensors = (q, k, v, o, do, dq, dk, dv, lse, ws, cu)
         return fwd, bwd, tensors, w.flops_fwd(), w.flops_bwd(), bf, bb
 
+    from exact_io_aware_fa_amd.inputs import block_mask
+
     w = WORKLOADS[name]
     inp = make_inputs(w)
     q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
@@ -293,6 +330,13 @@ def _sweep_calls(name, dev, stream):
     kv_ptr = None if kvl is None else kvl.data_ptr()
     bsz, hh, n, d = q.shape
     hkv = k.shape[1]
+    bm = block_mask(w)
+    idx = None
+    if bm is not None:
+        idx = torch.empty(B.fa_block_index_bytes(n) // 4, dtype=torch.int32, device=dev)
+        bmd = torch.from_numpy(bm).to(device=dev, dtype=torch.uint8)
+        B.check(B.fa_block_index_build(n, bmd.data_ptr(), idx.data_ptr(), stream))
+    mask = B.mask_arg(w.window, None if idx is None else idx.data_ptr())
     dt = B.FA_BF16 if q.dtype == torch.bfloat16 else B.FA_FP32
     scale = w.softmax_scale
     o = torch.empty_like(q)
@@ -302,18 +346,19 @@ def _sweep_calls(name, dev, stream):
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
     def fwd():
-        B.check(B.fa_fwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
-                             k.data_ptr(), v.data_ptr(), kv_ptr, o.data_ptr(),
-                             lse.data_ptr(), stream))
+        B.check(B.fa_fwd_masked(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), kv_ptr, mask, o.data_ptr(),
+                                lse.data_ptr(), stream))
 
     def bwd():
-        B.check(B.fa_bwd_gqa(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
-                             k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                             lse.data_ptr(), kv_ptr, dq.data_ptr(), dk.data_ptr(),
-                             dv.data_ptr(), ws.data_ptr(), wsb, stream))
+        B.check(B.fa_bwd_masked(bsz, hh, hkv, n, d, w.causal, scale, dt, q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), kv_ptr, mask, dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), ws.data_ptr(), wsb, stream))
     bf, bb = comp_bytes(w)
-    tensors = (q, k, v, o, do, dq, dk, dv, lse, ws)
-    return fwd, bwd, tensors, w.flops_fwd(), w.flops_bwd(), bf, bb
+    tensors = (q, k, v, o, do, dq, dk, dv, lse, ws) + (() if idx is None else (idx,))
+    ff, fb = masked_flops(w)
+    return fwd, bwd, tensors, ff, fb, bf, bb
 
 
 def run_sweep(out_path: str | None, only=None) -> int:
@@ -332,7 +377,8 @@ def run_sweep(out_path: str | None, only=None) -> int:
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
     names = [n for n, w in WORKLOADS.items()
-             if w.backward and n.startswith(("bert", "gpt2", "gqa", "sweep"))] + list(PACKED)
+             if w.backward and n.startswith(("bert", "gpt2", "gqa", "window", "blocksparse",
+                                              "sweep"))] + list(PACKED)
     if only:
         names = [n for n in names if any(n.startswith(o) for o in only)]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -386,7 +432,8 @@ def run_sweep(out_path: str | None, only=None) -> int:
              "MFMA %.0f TFLOP/s; roof = min(peak, compulsory-byte AI x %.0f GB/s); GB/s = "
              "compulsory bytes / time. FLOPs: 4BHN^2d forward (x2.5 backward), halved when "
              "causal; the padded workload counts nominal FLOPs; packed (varlen) workloads "
-             "count 4Hd sum_s L_s^2." % (PEAK_BF16_TFLOPS, PEAK_HBM_GBS), "",
+             "count 4Hd sum_s L_s^2; window and block-sparse workloads count 4d per visible "
+             "(query, key) pair." % (PEAK_BF16_TFLOPS, PEAK_HBM_GBS), "",
              "| workload | fwd ms | fwd TFLOP/s | fwd % peak | fwd % roof | fwd GB/s | bwd ms | "
              "bwd TFLOP/s | bwd % peak | bwd % roof | bwd GB/s | fwd+bwd TFLOP/s | cold fwd / bwd ms |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]

@@ -32,6 +32,8 @@ class Workload:
     backward: bool = True
     scale: float | None = None  # default 1/sqrt(d)
     heads_kv: int | None = None  # K/V heads (divides heads); default heads
+    window: tuple = (-1, -1)     # sliding window (left, right), -1 unbounded
+    blocks: tuple | None = None  # block-sparse pattern: ("local_global", local, glob)
 
     @property
     def kv_heads(self) -> int:
@@ -159,6 +161,12 @@ WORKLOADS = {w.name: w for w in [
     # long-sequence causal attention with peaky rows (Q, K ~ N(0, 3^2))
     Workload("long_causal_b1_h32_n16384_d128", 1, 32, 16384, 128, "bf16", True,
              seed=4, qk_sigma=3.0),
+    # sliding-window causal attention (4096-key window, Mistral style)
+    Workload("window_causal_b1_h32_n16384_d128_w4096", 1, 32, 16384, 128, "bf16", True,
+             seed=8, window=(4095, -1)),
+    # block-sparse causal attention: 4 local blocks of 128 plus 2 global ones
+    Workload("blocksparse_causal_b1_h32_n16384_d128_l4g2", 1, 32, 16384, 128, "bf16", True,
+             seed=9, blocks=("local_global", 4, 2)),
     # grouped-query attention: 32 query heads sharing 8 K/V heads (groups of 4)
     Workload("gqa_causal_b1_h32_hkv8_n16384_d128", 1, 32, 16384, 128, "bf16", True,
              seed=5, qk_sigma=3.0, heads_kv=8),
@@ -175,6 +183,23 @@ PACKED = {w.name: w for w in [
 ]}
 
 HEADLINE = "long_causal_b1_h32_n16384_d128"
+
+
+def block_mask(w) -> "np.ndarray | None":
+    """The workload's boolean block mask over 128 x 128 blocks, or None.
+    ("local_global", L, G): query block i keeps key blocks i-L+1 .. i and the
+    first G blocks (a banded pattern with global tokens)."""
+    if w.blocks is None:
+        return None
+    import numpy as np
+    kind, local, glob = w.blocks
+    assert kind == "local_global"
+    nb = (w.n + 127) // 128
+    bm = np.zeros((nb, nb), dtype=bool)
+    for i in range(nb):
+        bm[i, max(0, i - local + 1):i + 1] = True
+        bm[i, :glob] = True
+    return bm
 
 
 def make_inputs(w: Workload, with_grad_out: bool = True) -> dict:

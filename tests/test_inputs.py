@@ -64,3 +64,17 @@ def test_causal_halves_and_backward_is_two_and_a_half():
     assert w.flops_bwd() == pytest.approx(5.498e12, rel=1e-3)
     full = custom("f", 1, 32, 16384, 128, "bf16", False)
     assert full.flops_fwd() == 2 * w.flops_fwd()
+
+
+def test_masked_flop_count_matches_brute_force():
+    # bench.visible_pairs counts the (query, key) pairs a masked workload
+    # computes; brute force over the oracle's element mask must agree.
+    import bench
+    import oracle
+    from exact_io_aware_fa_amd.inputs import Workload, block_mask
+    for window, blocks, causal in (((37, 5), None, False), ((100, -1), None, True),
+                                   ((-1, -1), ("local_global", 2, 1), True),
+                                   ((150, 20), ("local_global", 3, 1), False)):
+        w = Workload("t", 1, 1, 700, 64, "bf16", causal, 0, window=window, blocks=blocks)
+        vis = oracle.visible_mask(w.n, causal, None, None, window, block_mask(w))
+        assert bench.visible_pairs(w) == float(vis.sum())
