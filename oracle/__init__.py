@@ -29,8 +29,13 @@ Modules:
 * ``online``    -- the pages' online-softmax algebra (three-, two- and
   one-pass forms, per-block update, associative block merge), used to pin
   ``attention`` and as the reading of the tiled recurrence.
+* ``fp8``       -- the FP8 forward of page 2 4.5.4: E4M3 rounding, per-block
+  power-of-two scales, the optional random Hadamard rotation of Q and K,
+  both products on E4M3 operands with the probabilities quantised in an
+  integer row frame (pinned by ``tests/test_oracle_fp8.py``).
 
-Parity status: every function here is pinned by ``tests/test_oracle.py``
+Parity status: every function here is pinned by ``tests/test_oracle.py`` or
+``tests/test_oracle_fp8.py``
 (worked examples, closed forms, invariants, brute force, finite differences
 and a library cross-check); none is "parity unpinned".
 """
@@ -46,3 +51,4 @@ from .attention import (  # noqa: F401
     default_scale,
 )
 from . import online  # noqa: F401
+from . import fp8  # noqa: F401

@@ -1,0 +1,432 @@
+"""Pins for the FP8 (E4M3) forward oracle, oracle/fp8.py (runs without a GPU).
+
+The oracle is checked against things other than itself:
+
+* the format figures page 2 prints (exercise 3: largest magnitude 448,
+  smallest normal 2^-6; tests/golden/fp8_format.json);
+* a library cross-check of the E4M3 rounding against torch's float8_e4m3fn
+  cast, and the round trip of every finite code;
+* scipy's Hadamard matrix, orthogonality, and the page's identity
+  (Q H)(K H)^T = Q K^T;
+* brute force for the block exponent (smallest e with amax <= 448 * 2^e);
+* closed forms: equal keys give P^ / u times the mean value row; the LSE is
+  scipy's logsumexp of the dequantised scores;
+* the tiled online forward with running integer frames, written here
+  independently (library E4M3 rounding, any tile width, either tile order),
+  agrees with the one-shot definition, exactly when every probability is in
+  E4M3's normal range and within the subnormal bound otherwise;
+* the error against exact attention stays inside E4M3's relative rounding
+  bound, and the rotation lowers the score error on inputs with outlier
+  channels (the page's reason for it);
+* planted mistakes in the oracle are each rejected by one of the pins.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+import torch
+
+import oracle
+from oracle import fp8 as of
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fp8_format.json")
+LOG2E = 1.0 / math.log(2.0)
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _torch_e4m3(x):
+    """Library E4M3 rounding: torch's float8_e4m3fn cast (in range)."""
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32).copy())
+    return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _inputs(seed, b=1, h=2, n=300, d=64, hkv=None, outliers=0):
+    rng = np.random.default_rng(seed)
+    hkv = h if hkv is None else hkv
+    q = rng.standard_normal((b, h, n, d))
+    k = rng.standard_normal((b, hkv, n, d))
+    v = rng.standard_normal((b, hkv, n, d))
+    if outliers:
+        ch = rng.choice(d, outliers, replace=False)
+        q[..., ch] *= 30.0
+        k[..., ch] *= 30.0
+    return q, k, v
+
+
+# --------------------------------------------------------------------------
+# The E4M3 format
+# --------------------------------------------------------------------------
+
+def test_page2_format_figures():
+    g = _golden()["e4m3_range"]
+    vals = of.e4m3_decode(np.arange(256))
+    finite = vals[np.isfinite(vals)]
+    assert np.max(np.abs(finite)) == g["max_magnitude"] == of.E4M3_MAX
+    normals = np.abs(finite)[np.abs(finite) >= g["min_normal"]]
+    assert np.min(normals) == g["min_normal"] == 2.0 ** g["min_normal_as_power_of_two"]
+    assert of.e4m3_encode(448.0) == 0x7E and of.e4m3_encode(-448.0) == 0xFE
+    assert of.e4m3_encode(2.0 ** -6) == 0x08
+    assert of.e4m3_encode(2.0 ** -9) == 0x01
+    assert of.e4m3_encode(1.0) == 0x38
+    # Only S.1111.111 is NaN: 254 finite codes, no infinities.
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF]) and finite.size == 254
+
+
+def test_e4m3_round_matches_library_cast():
+    rng = np.random.default_rng(1)
+    mags = 2.0 ** rng.uniform(-13, math.log2(448.0), 200_000)
+    x = (mags * rng.choice([-1.0, 1.0], mags.size)).astype(np.float32).astype(np.float64)
+    grid = np.unique(np.abs(of.e4m3_decode(np.arange(127))))
+    mids = (grid[1:] + grid[:-1]) / 2  # exact ties: the even neighbour wins
+    x = np.concatenate([x, mids, -mids, grid, [0.0, 448.0, 2.0 ** -10, 3 * 2.0 ** -11]])
+    np.testing.assert_array_equal(of.e4m3_round(x), _torch_e4m3(x))
+    # Ties to even: 1 + 2^-4 lies halfway between 1 (mantissa 0) and 1.125.
+    assert of.e4m3_round(1.0625) == 1.0 and of.e4m3_round(1.1875) == 1.25
+    # Saturation past the largest value.
+    assert of.e4m3_round(1000.0) == 448.0 and of.e4m3_round(-460.0) == -448.0
+
+
+def test_e4m3_encode_decode_round_trip():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    np.testing.assert_array_equal(of.e4m3_encode(of.e4m3_decode(codes)), codes)
+    torch_codes = torch.from_numpy(of.e4m3_decode(codes).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(torch_codes, codes)
+    # Rounding is monotone and idempotent.
+    x = np.sort(np.random.default_rng(2).uniform(-448, 448, 10_000))
+    r = of.e4m3_round(x)
+    assert np.all(np.diff(r) >= 0)
+    np.testing.assert_array_equal(of.e4m3_round(r), r)
+
+
+# --------------------------------------------------------------------------
+# Hadamard rotation and block scales
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [1, 2, 8, 64, 128, 256])
+def test_hadamard_is_sylvester_and_orthogonal(d):
+    h = of.hadamard(d)
+    np.testing.assert_array_equal(h, scipy.linalg.hadamard(d))
+    np.testing.assert_array_equal(h @ h.T, d * np.eye(d))
+
+
+def test_rotation_keeps_scores():
+    rng = np.random.default_rng(3)
+    d = 128
+    s = rng.choice([-1.0, 1.0], d)
+    r = of.rotation(s)
+    np.testing.assert_array_equal(r, np.diag(s) @ scipy.linalg.hadamard(d))
+    hm = r / math.sqrt(d)  # the page's H: entries +-1/sqrt(d), H H^T = I
+    np.testing.assert_allclose(hm @ hm.T, np.eye(d), atol=1e-15)
+    q, k = rng.standard_normal((50, d)), rng.standard_normal((60, d))
+    np.testing.assert_allclose((q @ hm) @ (k @ hm).T, q @ k.T, atol=1e-12)
+    with pytest.raises(ValueError):
+        of.rotation(np.full(d, 0.5))
+    with pytest.raises(ValueError):
+        of.hadamard(96)
+
+
+def test_block_exponent_is_the_smallest():
+    rng = np.random.default_rng(4)
+    amax = np.concatenate([2.0 ** rng.uniform(-30, 30, 5000),
+                           448.0 * 2.0 ** np.arange(-20, 20),
+                           np.nextafter(448.0 * 2.0 ** np.arange(-20, 20), np.inf)])
+    e = of.block_exponent(amax)
+    for a, ei in zip(amax, e):
+        assert a <= 448.0 * 2.0 ** ei
+        assert a > 448.0 * 2.0 ** (ei - 1)
+    assert of.block_exponent(0.0) == 0
+
+
+def test_quantize_blocks_and_bounds():
+    q, _, _ = _inputs(5, b=2, h=3, n=300, d=64)
+    q[1, 2, 128:256] *= 1e-3  # a block with its own, much smaller scale
+    codes, scales = of.quantize(q)
+    assert codes.shape == (2, 3, 384, 64) and scales.shape == (2, 3, 3)
+    assert np.all(codes[:, :, 300:] == 0)  # padding rows
+    e = np.log2(scales)
+    np.testing.assert_array_equal(e, np.round(e))  # powers of two
+    for b in range(2):
+        for h in range(3):
+            x = q[b, h]
+            xd = of.dequantize(codes[b, h], scales[b, h], 300)
+            sc = scales[b, h][np.arange(300) // 128][:, None]
+            # Block maxima land in (224, 448] once scaled (tight scaling).
+            for blk in range(3):
+                seg = np.abs(x[blk * 128:(blk + 1) * 128]) / scales[b, h, blk]
+                assert 224.0 < seg.max() <= 448.0
+            # Half an E4M3 step: 2^-4 relative in the normal range, 2^-10
+            # absolute (in scaled units) below it.
+            err = np.abs(xd - x)
+            bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sc)
+            assert np.all(err <= bound * (1 + 1e-12))
+
+
+def test_rotated_quantize_represents_x_times_h():
+    rng = np.random.default_rng(6)
+    d = 64
+    s = rng.choice([-1.0, 1.0], d)
+    x, _, _ = _inputs(7, n=200, d=d)
+    codes, scales = of.quantize(x, s)
+    xh = x[0, 0] @ (np.diag(s) @ scipy.linalg.hadamard(d)) / math.sqrt(d)
+    xd = of.dequantize(codes[0, 0], scales[0, 0], 200)
+    sc = scales[0, 0][np.arange(200) // 128][:, None]
+    assert np.all(np.abs(xd - xh) <= np.maximum(2.0 ** -4 * np.abs(xh), 2.0 ** -10 * sc) + 1e-15)
+    # The scale carries the 1/sqrt(d): scale * sqrt(d) is a power of two.
+    e = np.log2(scales * math.sqrt(d))
+    np.testing.assert_allclose(e, np.round(e), atol=1e-12)
+
+
+def test_rotation_flattens_outlier_channels():
+    """Page 2 4.5.4: the rotation spreads outliers and lowers the FP8 error."""
+    d = 128
+    q, k, _ = _inputs(8, n=256, d=d, outliers=3)
+    s = np.random.default_rng(9).choice([-1.0, 1.0], d)
+    exact = q[0, 0] @ k[0, 0].T
+
+    def score_err(signs):
+        qc, qs = of.quantize(q, signs)
+        kc, ks = of.quantize(k, signs)
+        sq = of.dequantize(qc[0, 0], qs[0, 0], 256) @ of.dequantize(kc[0, 0], ks[0, 0], 256).T
+        return np.linalg.norm(sq - exact) / np.linalg.norm(exact)
+
+    plain, rotated = score_err(None), score_err(s)
+    assert rotated < 0.5 * plain
+    # The rotated tensor's peak-to-rms ratio drops.
+    qr = q[0, 0] @ of.rotation(s)
+    ratio = lambda a: np.abs(a).max() / np.sqrt((a ** 2).mean())  # noqa: E731
+    assert ratio(qr) < 0.5 * ratio(q[0, 0])
+
+
+# --------------------------------------------------------------------------
+# The forward
+# --------------------------------------------------------------------------
+
+def _head(qc, qs, kc, ks, vc, vs, n, scale, causal=False, kvb=None):
+    return of.fp8_head_forward(qc[0, 0], qs[0, 0], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0],
+                               n, scale, causal, kvb, parts=True)
+
+
+def test_equal_keys_closed_form():
+    """All keys equal: every score of a row is the same t, so u = 2^(t - ceil t
+    + 8) for every key, P^ = E4M3(u) and O = (P^ / u) * mean of the values."""
+    rng = np.random.default_rng(10)
+    n, d = 200, 64
+    q = rng.standard_normal((1, 1, n, d))
+    k = np.repeat(rng.standard_normal((1, 1, 1, d)), n, axis=2)
+    v = rng.standard_normal((1, 1, n, d))
+    qc, qs = of.quantize(q)
+    kc, ks = of.quantize(k)
+    vc, vs = of.quantize(v)
+    scale = 0.37
+    r = _head(qc, qs, kc, ks, vc, vs, n, scale)
+    qd = of.dequantize(qc[0, 0], qs[0, 0], n)
+    kd = of.dequantize(kc[0, 0], ks[0, 0], n)
+    vd = of.dequantize(vc[0, 0], vs[0, 0], n)
+    t = scale * (qd @ kd[0]) * LOG2E
+    u = 2.0 ** (t - np.ceil(t) + 8)
+    ratio = _torch_e4m3(u) / u
+    assert np.any(np.abs(ratio - 1) > 1e-3)  # the rounding of P is visible
+    np.testing.assert_allclose(r["o"], ratio[:, None] * vd.mean(axis=0)[None, :], rtol=1e-12,
+                               atol=1e-14)
+    # Largest u of a row in (128, 256]: the frame is the ceiling.
+    assert np.all((u > 128) & (u <= 256))
+
+
+def test_lse_is_logsumexp_of_quantised_scores():
+    q, k, v = _inputs(11, n=300, d=64)
+    qc, qs = of.quantize(q)
+    kc, ks = of.quantize(k)
+    vc, vs = of.quantize(v)
+    for causal, kvb in [(False, None), (True, None), (False, 170), (True, 170)]:
+        r = _head(qc, qs, kc, ks, vc, vs, 300, 0.125, causal, kvb)
+        qd = of.dequantize(qc[0, 0], qs[0, 0], 300)
+        kd = of.dequantize(kc[0, 0], ks[0, 0], 300)
+        s = 0.125 * qd @ kd.T
+        vis = oracle.visible_mask(300, causal, kvb)
+        ref = scipy.special.logsumexp(np.where(vis, s, -np.inf), axis=1)
+        np.testing.assert_allclose(r["lse"], ref, rtol=0, atol=1e-12)
+
+
+def _tiled_forward(qd, kd, vd, scale, bc, causal, kvb, reverse=False):
+    """The online forward tile by tile with running integer frames (page 1
+    section 六 / page 2 4.3.2 update, with the frame ceil of the running
+    max), E4M3 rounding from the library."""
+    n = qd.shape[0]
+    f = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros_like(qd[:, :1] * vd[:1, :])
+    starts = list(range(0, n, bc))
+    if reverse:
+        starts = starts[::-1]
+    vis_all = oracle.visible_mask(n, causal, kvb)
+    for j0 in starts:
+        j1 = min(j0 + bc, n)
+        vis = vis_all[:, j0:j1]
+        t = np.where(vis, scale * (qd @ kd[j0:j1].T) * LOG2E, -np.inf)
+        tmax = t.max(axis=1)
+        fnew = np.where(np.isfinite(tmax), np.maximum(f, np.ceil(np.where(np.isfinite(tmax), tmax, 0))), f)
+        alpha = np.where(np.isfinite(f), np.exp2(f - np.where(np.isfinite(fnew), fnew, 0)), 0.0)
+        fr = np.where(np.isfinite(fnew), fnew, 0.0)
+        u = np.where(vis, np.exp2(t - fr[:, None] + 8), 0.0)
+        acc = acc * alpha[:, None] + _torch_e4m3(u) @ vd[j0:j1]
+        l = l * alpha + u.sum(axis=1)
+        f = fnew
+    has = np.isfinite(f)
+    o = np.where(has[:, None], acc / np.where(has, l, 1.0)[:, None], 0.0)
+    return o
+
+
+@pytest.mark.parametrize("causal,kvb", [(False, None), (True, None), (True, 333)])
+def test_tiled_online_forward_agrees(causal, kvb):
+    q, k, v = _inputs(12, n=400, d=64)
+    # Small scores: every u is in E4M3's normal range, so any tiling and any
+    # tile order must reproduce the one-shot result exactly (up to fp64 sums).
+    q *= 0.1
+    qc, qs = of.quantize(q)
+    kc, ks = of.quantize(k)
+    vc, vs = of.quantize(v)
+    r = _head(qc, qs, kc, ks, vc, vs, 400, 0.3, causal, kvb)
+    assert np.all((r["u"] >= 2.0 ** -6) | ~r["vis"])
+    qd, kd = of.dequantize(qc[0, 0], qs[0, 0], 400), of.dequantize(kc[0, 0], ks[0, 0], 400)
+    vd = of.dequantize(vc[0, 0], vs[0, 0], 400)
+    for bc in (64, 128, 37):
+        for rev in (False, True):
+            o = _tiled_forward(qd, kd, vd, 0.3, bc, causal, kvb, rev)
+            np.testing.assert_allclose(o, r["o"], rtol=0, atol=1e-12)
+
+
+def test_tiled_online_forward_subnormal_bound():
+    """With peaky rows some u fall below 2^-6 in the final frame; a tiled run
+    may round them in a finer running frame. Each such u moves by at most
+    2^-9 (half a subnormal step on either side), so |dO| <= 2^-9 sum|v| / l."""
+    q, k, v = _inputs(13, n=384, d=64)
+    qc, qs = of.quantize(q * 3.0)
+    kc, ks = of.quantize(k)
+    vc, vs = of.quantize(v)
+    r = _head(qc, qs, kc, ks, vc, vs, 384, 0.25, True)
+    small = (r["u"] < 2.0 ** -6) & r["vis"]
+    assert small.sum() > 1000
+    qd, kd = of.dequantize(qc[0, 0], qs[0, 0], 384), of.dequantize(kc[0, 0], ks[0, 0], 384)
+    vd = of.dequantize(vc[0, 0], vs[0, 0], 384)
+    bound = 2.0 ** -9 * (small.astype(float) @ np.abs(vd)) / r["l"][:, None] + 1e-12
+    for bc in (64, 128):
+        o = _tiled_forward(qd, kd, vd, 0.25, bc, True, None, reverse=True)
+        assert np.all(np.abs(o - r["o"]) <= bound)
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_close_to_exact_attention(rotate):
+    """Against exact attention on the unquantised inputs. Each of the three
+    roundings (Q and K through the scores, V, and P) has a relative error
+    of at most half an E4M3 step, 2^-4, and about 2^-4 / sqrt(3) in RMS;
+    three independent ones add to about 6% in RMS, so the normwise error of
+    O stays below 2^-3. It is far from zero because P is rounded too."""
+    q, k, v = _inputs(14, b=2, h=4, n=260, d=64, hkv=2)
+    s = np.random.default_rng(15).choice([-1.0, 1.0], 64) if rotate else None
+    for causal in (False, True):
+        got_o, got_lse = of.fp8_attention_fwd(q, k, v, causal=causal, signs=s, kv_len=[260, 201])
+        ref_o, ref_lse = oracle.attention_fwd(q, k, v, causal=causal, kv_len=[260, 201])
+        err = np.linalg.norm(got_o - ref_o) / np.linalg.norm(ref_o)
+        assert 1e-4 < err < 2.0 ** -3
+        np.testing.assert_allclose(got_lse, ref_lse, atol=0.1)
+
+
+def test_padded_keys_do_not_matter():
+    """Hidden keys enter only through their block's scale: new values of the
+    same magnitudes (here, the negated ones) leave the result unchanged."""
+    q, k, v = _inputs(16, n=300, d=64)
+    a = of.fp8_attention_fwd(q, k, v, causal=False, kv_len=[230])
+    k2, v2 = k.copy(), v.copy()
+    k2[..., 230:, :] *= -1.0
+    v2[..., 230:, :] *= -1.0
+    b = of.fp8_attention_fwd(q, k2, v2, causal=False, kv_len=[230])
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    # ... whereas a larger hidden value changes the block's scale.
+    k2[0, 0, 240, 0] = 1e3  # hidden, but in the block of visible keys 128..229
+    c = of.fp8_attention_fwd(q, k2, v2, causal=False, kv_len=[230])
+    assert not np.array_equal(a[0], c[0])
+
+
+def test_grouped_heads_use_their_kv_head():
+    q, k, v = _inputs(18, b=1, h=4, n=140, d=64, hkv=2)
+    full = of.fp8_attention_fwd(q, k, v, causal=True)
+    for h in range(4):
+        one = of.fp8_attention_fwd(q[:, h:h + 1], k[:, h // 2:h // 2 + 1], v[:, h // 2:h // 2 + 1],
+                                   causal=True)
+        np.testing.assert_array_equal(full[0][:, h], one[0][:, 0])
+    with pytest.raises(ValueError):
+        of.fp8_attention_fwd(q[:, :3], k, v)
+
+
+def test_empty_rows_and_negative_scale():
+    q, k, v = _inputs(19, n=130, d=64)
+    o, lse = of.fp8_attention_fwd(q, k, v, kv_len=[0])
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+    # A negative scale is the same as negating Q (exact in E4M3).
+    a = of.fp8_attention_fwd(q, k, v, scale=-0.125)
+    b = of.fp8_attention_fwd(-q, k, v, scale=0.125)
+    np.testing.assert_array_equal(a[0], b[0])
+
+
+# --------------------------------------------------------------------------
+# Planted mistakes
+# --------------------------------------------------------------------------
+
+def _runs_clean(tests):
+    for t in tests:
+        try:
+            t()
+        except AssertionError:
+            return False
+    return True
+
+
+def test_fp8_planted_mistakes_are_rejected(monkeypatch):
+    pins = [test_equal_keys_closed_form,
+            lambda: test_close_to_exact_attention(True),
+            lambda: test_close_to_exact_attention(False),
+            test_quantize_blocks_and_bounds,
+            test_rotated_quantize_represents_x_times_h,
+            test_rotation_keeps_scores,
+            lambda: test_tiled_online_forward_agrees(True, None),
+            test_lse_is_logsumexp_of_quantised_scores,
+            test_e4m3_round_matches_library_cast]
+    assert _runs_clean(pins)
+    good_round, good_exp = of.e4m3_round, of.block_exponent
+    good_frame, good_rot, good_deq = of._frame, of.rotation, of.dequantize
+    mistakes = {
+        "P not rounded": ("_quantize_p", lambda u: u),
+        "floor frame (u up to 512 saturates)": ("_frame", np.floor),
+        "frame one too low": ("_frame", lambda t: good_frame(t) - 1),
+        "block exponent one too high": ("block_exponent", lambda a: good_exp(a) + 1),
+        "block exponent one too low": ("block_exponent", lambda a: good_exp(a) - 1),
+        "ties away from zero": ("e4m3_round", lambda x: np.copysign(
+            np.minimum(np.floor(np.abs(np.asarray(x, float)) / np.ldexp(1.0, np.maximum(
+                np.frexp(np.abs(np.asarray(x, float)))[1] - 1, -6) - 3) + 0.5) * np.ldexp(
+                1.0, np.maximum(np.frexp(np.abs(np.asarray(x, float)))[1] - 1, -6) - 3), 448.0), x)),
+        "rotation without signs": ("rotation", lambda s: of.hadamard(np.asarray(s).size)),
+        "scales ignored": ("dequantize", lambda c, s, n: of.e4m3_decode(np.asarray(c)[:n])),
+        "block scale of the wrong block": ("dequantize", lambda c, s, n: of.e4m3_decode(
+            np.asarray(c)[:n]) * np.asarray(s, float)[::-1][np.arange(n) // 128][:, None]),
+    }
+    for name, (attr, fn) in mistakes.items():
+        monkeypatch.setattr(of, attr, fn)
+        assert not _runs_clean(pins), name
+        monkeypatch.setattr(of, "_quantize_p", lambda u: good_round(u))
+        monkeypatch.setattr(of, "_frame", good_frame)
+        monkeypatch.setattr(of, "block_exponent", good_exp)
+        monkeypatch.setattr(of, "e4m3_round", good_round)
+        monkeypatch.setattr(of, "rotation", good_rot)
+        monkeypatch.setattr(of, "dequantize", good_deq)
+    assert _runs_clean(pins)
