@@ -29,6 +29,7 @@ on a bounded sample of the same workload -- whole heads, fwd+bwd, until about
 10 s of CPU work -- and scales it to the same TFLOP/s convention.
 
     python bench.py --sweep [--out FILE] [--only PREFIX ...]
+    python bench.py --fp8 [--out FILE] [--only PREFIX ...]
 
 times fa_fwd and fa_bwd separately on every parity workload with a backward
 (the BERT- and GPT-2-shaped ones, the grouped-head one, the 18-point
@@ -450,6 +451,122 @@ def run_sweep(out_path: str | None, only=None) -> int:
     return 0
 
 
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 matrix-core peak (published)
+
+
+def run_fp8(out_path: str | None, only=None) -> int:
+    """FP8 forward timings: the three block encodings (Q, K with the Hadamard
+    rotation; V transposed) and the E4M3 attention kernel, next to the bf16
+    forward on the same inputs."""
+    import statistics
+
+    import torch
+
+    from exact_io_aware_fa_amd import attention as fa
+    from exact_io_aware_fa_amd import binding as B
+    from exact_io_aware_fa_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py --fp8 needs a GPU", file=sys.stderr)
+        return 1
+    B.lib()
+    dev = torch.device("cuda:0")
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    names = [n for n, w in WORKLOADS.items()
+             if w.d == 128 and w.window == (-1, -1) and w.blocks is None and w.dtype == "bf16"]
+    if only:
+        names = [n for n in names if any(n.startswith(o) for o in only)]
+    ev = [hip.create() for _ in range(4)]
+    clocks_before = _gpu_clocks()
+    rows = []
+    for name in names:
+        w = WORKLOADS[name]
+        inp = make_inputs(w, with_grad_out=False)
+        q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+        kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)
+        bsz, hh, n, d = q.shape
+        hkv = k.shape[1]
+        signs = fa.hadamard_signs(d, torch.Generator().manual_seed(w.seed), dev)
+        q8, qs = fa.fp8_quantize(q, signs)
+        k8, ks = fa.fp8_quantize(k, signs)
+        v8, vs = fa.fp8_quantize(v, layout="vt")
+        o = torch.empty_like(q)
+        lse = torch.empty((bsz, hh, n), dtype=torch.float32, device=dev)
+        kp = None if kvl is None else kvl.data_ptr()
+        sc = w.softmax_scale
+
+        def quant():
+            for x, c, s_, sg, lay in ((q, q8, qs, signs, B.FA_FP8_ROWS),
+                                      (k, k8, ks, signs, B.FA_FP8_ROWS),
+                                      (v, v8, vs, None, B.FA_FP8_VT)):
+                B.check(B.fa_fp8_quantize(bsz, x.shape[1], n, d, lay, x.data_ptr(),
+                                          None if sg is None else sg.data_ptr(), c.data_ptr(),
+                                          s_.data_ptr(), stream))
+
+        def attn():
+            B.check(B.fa_fwd_fp8(bsz, hh, hkv, n, d, w.causal, sc, q8.data_ptr(), qs.data_ptr(),
+                                 k8.data_ptr(), ks.data_ptr(), v8.data_ptr(), vs.data_ptr(), kp,
+                                 o.data_ptr(), lse.data_ptr(), stream))
+
+        def bf16():
+            B.check(B.fa_fwd_gqa(bsz, hh, hkv, n, d, w.causal, sc, B.FA_BF16, q.data_ptr(),
+                                 k.data_ptr(), v.data_ptr(), kp, o.data_ptr(), lse.data_ptr(),
+                                 stream))
+
+        def timed(fn):
+            hip.record(ev[0], stream)
+            fn()
+            hip.record(ev[1], stream)
+            return hip.elapsed_ms(ev[0], ev[1])
+
+        for _ in range(10):
+            quant()
+            attn()
+            bf16()
+        torch.cuda.synchronize()
+        tq, ta, tb, spent = [], [], [], 0.0
+        while len(ta) < 50 or spent < 200.0:
+            tq.append(timed(quant))
+            ta.append(timed(attn))
+            tb.append(timed(bf16))
+            spent += tq[-1] + ta[-1] + tb[-1]
+        mq, ma, mb = statistics.median(tq), statistics.median(ta), statistics.median(tb)
+        ff = w.flops_fwd()
+        rows.append((name, mq, ma, min(ta), ff / ma / 1e9, ff / (ma + mq) / 1e9, mb,
+                     ff / mb / 1e9))
+        print(json.dumps({"workload": name, "fp8_quantize_ms": round(mq, 4),
+                          "fp8_attn_ms": round(ma, 4), "bf16_fwd_ms": round(mb, 4),
+                          "fp8_attn_tflops": round(ff / ma / 1e9, 1)}), flush=True)
+        del q, k, v, q8, k8, v8, o, lse
+        torch.cuda.empty_cache()
+    for e_ in ev:
+        hip.destroy(e_)
+    lines = ["# FP8 (E4M3) forward on one MI355X", "",
+             "Command: `python bench.py --fp8 --out <this file>` (from the repository root).", "",
+             "Clocks before (rocm-smi): " + clocks_before,
+             "Clocks after (rocm-smi): " + _gpu_clocks(), "",
+             "Medians (min in parentheses) over >= 50 calls and >= 200 ms, warm cache. "
+             "`encode` = the three block encodings (Q and K rotated by the Hadamard matrix, "
+             "V transposed); `attention` = fa_fwd_fp8 on the codes; `bf16` = fa_fwd on the "
+             "same bf16 inputs. FLOPs 4BHN^2d, halved when causal (nominal for padded "
+             "batches); fp8 peak %.0f TFLOP/s, bf16 peak %.0f." % (PEAK_FP8_TFLOPS,
+                                                                   PEAK_BF16_TFLOPS), "",
+             "| workload | encode ms | attention ms | attention TFLOP/s | % fp8 peak | "
+             "encode+attention TFLOP/s | bf16 fwd ms | bf16 fwd TFLOP/s | speed-up vs bf16 |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| %s | %.4f | %.4f (%.4f) | %.1f | %.1f | %.1f | %.4f | %.1f | %.2fx |"
+                     % (r[0], r[1], r[2], r[3], r[4], 100 * r[4] / PEAK_FP8_TFLOPS, r[5], r[6],
+                        r[7], r[6] / r[2]))
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
+
+
 def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "summarize":
         sp = argparse.ArgumentParser(prog="bench.py summarize")
@@ -472,7 +589,10 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="time fwd and bwd on every sweep workload and print a table")
-    ap.add_argument("--out", default=None, help="with --sweep: also write the table here")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward (encode + E4M3 attention) against the bf16 "
+                         "forward on the d=128 workloads and print a table")
+    ap.add_argument("--out", default=None, help="with --sweep / --fp8: also write the table here")
     ap.add_argument("--only", nargs="*", default=None, metavar="PREFIX",
                     help="with --sweep: only the workloads whose names start so")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -482,6 +602,8 @@ def main() -> int:
 
     if args.sweep:
         return run_sweep(args.out, args.only)
+    if args.fp8:
+        return run_fp8(args.out, args.only)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the work shards by (batch, head) with no exchange; see the design notes). "

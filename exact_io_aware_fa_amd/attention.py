@@ -258,3 +258,84 @@ def flash_attention_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=False,
     """Packed variable-length attention with autograd support."""
     return FlashAttentionVarlenFunction.apply(q, k, v, cu_seqlens, max_seqlen, causal,
                                               softmax_scale, window, block_index)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) forward: encode Q, K, V per 128-row block, then attend on the
+# codes (page 2, "4. FlashAttention 深度剖析", 4.5.4).
+
+def _fp8_rows(n):
+    return (n + _b.FA_BLOCK - 1) // _b.FA_BLOCK * _b.FA_BLOCK
+
+
+def hadamard_signs(d, generator=None, device="cuda"):
+    """Random +-1 signs (int8 GPU tensor of length d) for the rotation
+    diag(signs) H_d of Q and K; draw one vector per model and reuse it."""
+    bits = torch.randint(0, 2, (d,), generator=generator, dtype=torch.int8)
+    return (2 * bits - 1).to(torch.int8).to(device)
+
+
+def fp8_quantize(x, signs=None, layout="rows"):
+    """E4M3 codes and per-block scales of a bf16 tensor x [batch, heads, n, d].
+
+    layout "rows": codes [batch, heads, np, d]; "vt": codes
+    [batch, heads, np / 128, d, 128] (each block transposed, the V layout).
+    scales: float32 [batch, heads, np / 128]. With ``signs`` (int8 [d]) the
+    rows are rotated by diag(signs) H_d first (Q and K only)."""
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 GPU tensor [batch, heads, n, d]")
+    b, h, n, d = x.shape
+    np_ = _fp8_rows(n)
+    vt = layout == "vt"
+    if layout not in ("rows", "vt"):
+        raise ValueError("layout must be 'rows' or 'vt'")
+    shape = (b, h, np_ // _b.FA_BLOCK, d, _b.FA_BLOCK) if vt else (b, h, np_, d)
+    codes = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty((b, h, np_ // _b.FA_BLOCK), dtype=torch.float32, device=x.device)
+    if signs is not None:
+        if signs.dtype != torch.int8 or signs.numel() != d or not signs.is_cuda:
+            raise ValueError(f"signs must be an int8 GPU tensor of {d} entries")
+        signs = signs.contiguous()
+    _b.check(_b.fa_fp8_quantize(b, h, n, d, _b.FA_FP8_VT if vt else _b.FA_FP8_ROWS,
+                                x.data_ptr(), signs.data_ptr() if signs is not None else None,
+                                codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
+
+
+def flash_attn_fp8_fwd_codes(q8, q_scales, k8, k_scales, v8, v_scales, n, causal=False,
+                             softmax_scale=None, kv_len=None):
+    """FP8 forward on encoded operands (``fp8_quantize`` layouts: q8, k8
+    "rows", v8 "vt"). Returns (o bf16 [batch, heads, n, d], lse float32)."""
+    b, h, np_, d = q8.shape
+    hkv = k8.shape[1]
+    if np_ != _fp8_rows(n) or k8.shape != (b, hkv, np_, d) or \
+            v8.shape != (b, hkv, np_ // _b.FA_BLOCK, d, _b.FA_BLOCK):
+        raise ValueError("codes do not match the fp8_quantize layouts for this n")
+    for t in (q8, k8, v8, q_scales, k_scales, v_scales):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous GPU tensors")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty((b, h, n, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=q8.device)
+    kl = _kv_len_arg(kv_len, b, n, q8.device)
+    _b.check(_b.fa_fwd_fp8(b, h, hkv, n, d, causal, scale, q8.data_ptr(), q_scales.data_ptr(),
+                           k8.data_ptr(), k_scales.data_ptr(), v8.data_ptr(),
+                           v_scales.data_ptr(), kl.data_ptr() if kl is not None else None,
+                           o.data_ptr(), lse.data_ptr(), _stream()))
+    return o, lse
+
+
+def flash_attn_fp8_fwd(q, k, v, causal=False, softmax_scale=None, kv_len=None, signs=None):
+    """FP8 attention forward from bf16 q [batch, heads, n, d] and k, v
+    [batch, heads_kv, n, d]: Q and K are encoded per block (rotated by
+    diag(signs) H_d when ``signs`` is given), V per block in the transposed
+    layout, then both products run on the E4M3 matrix cores. Returns
+    (o bf16, lse float32)."""
+    _check_qkv(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the FP8 forward takes bfloat16 inputs")
+    q8, qs = fp8_quantize(q, signs)
+    k8, ks = fp8_quantize(k, signs)
+    v8, vs = fp8_quantize(v, layout="vt")
+    return flash_attn_fp8_fwd_codes(q8, qs, k8, ks, v8, vs, q.shape[2], causal, softmax_scale,
+                                    kv_len)

@@ -31,12 +31,17 @@ FA_E_ALIGN = 7
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_varlen", "fa_bwd",
             "fa_bwd_gqa", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_timed",
             "fa_bwd_workspace_bytes", "fa_block_index_bytes", "fa_block_index_build",
+            "fa_fp8_codes_bytes", "fa_fp8_scales_bytes", "fa_fp8_quantize", "fa_fwd_fp8",
             "fa_status_str", "fa_abi_version")
 
 # The FA_ABI_VERSION this binding was written against.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 FA_BLOCK = 128
+
+# Layouts of encoded FP8 tensors.
+FA_FP8_ROWS = 0
+FA_FP8_VT = 1
 
 
 class FaMask(ctypes.Structure):
@@ -101,6 +106,16 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_timed.argtypes = L.fa_bwd_gqa.argtypes + [ctypes.POINTER(_vp)]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+        L.fa_fp8_codes_bytes.restype = ctypes.c_size_t
+        L.fa_fp8_codes_bytes.argtypes = [_i64, _i64, _i64, _i64]
+        L.fa_fp8_scales_bytes.restype = ctypes.c_size_t
+        L.fa_fp8_scales_bytes.argtypes = [_i64, _i64, _i64]
+        L.fa_fp8_quantize.restype = ctypes.c_int
+        L.fa_fp8_quantize.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                      _vp]
+        L.fa_fwd_fp8.restype = ctypes.c_int
+        L.fa_fwd_fp8.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.fa_status_str.restype = ctypes.c_char_p
         L.fa_status_str.argtypes = [ctypes.c_int]
         L.fa_abi_version.restype = ctypes.c_int
@@ -202,6 +217,25 @@ def fa_bwd_timed(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, 
 
 def fa_bwd_workspace_bytes(batch, heads, n, d, dtype) -> int:
     return int(lib().fa_bwd_workspace_bytes(batch, heads, n, d, int(dtype)))
+
+
+def fa_fp8_codes_bytes(batch, heads, n, d) -> int:
+    return int(lib().fa_fp8_codes_bytes(batch, heads, n, d))
+
+
+def fa_fp8_scales_bytes(batch, heads, n) -> int:
+    return int(lib().fa_fp8_scales_bytes(batch, heads, n))
+
+
+def fa_fp8_quantize(batch, heads, n, d, layout, x, signs, codes, scales, stream) -> int:
+    return lib().fa_fp8_quantize(batch, heads, n, d, int(layout), x, signs, codes, scales,
+                                 stream)
+
+
+def fa_fwd_fp8(batch, heads, heads_kv, n, d, causal, softmax_scale, q8, q_scales, k8,
+               k_scales, v8, v_scales, kv_len, o, lse, stream) -> int:
+    return lib().fa_fwd_fp8(batch, heads, heads_kv, n, d, int(causal), float(softmax_scale),
+                            q8, q_scales, k8, k_scales, v8, v_scales, kv_len, o, lse, stream)
 
 
 def fa_status_str(status: int) -> str:

@@ -36,6 +36,8 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fa_bwd_aux.hip"),
     os.path.join(CSRC, "kernels", "fa_fp32.hip"),
     os.path.join(CSRC, "kernels", "fa_block_index.hip"),
+    os.path.join(CSRC, "kernels", "fa_fp8_quant.hip"),
+    os.path.join(CSRC, "kernels", "fa_fwd_fp8.hip"),
 ]
 
 ARCH = "gfx950"

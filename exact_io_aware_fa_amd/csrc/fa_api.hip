@@ -246,11 +246,126 @@ fa_status bwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dt
   return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
 }
 
+// FP8 encoded tensors: np rows per head (n rounded up to a block), one
+// scale per block.
+int64_t fp8_rows(int64_t n) { return (n + 127) / 128 * 128; }
+size_t fp8_codes_bytes(int64_t bh, int64_t n, int64_t d) { return size_t(bh * fp8_rows(n) * d); }
+size_t fp8_scales_bytes(int64_t bh, int64_t n) { return size_t(bh * (fp8_rows(n) / 128)) * 4; }
+
+fa_status check_fp8_shape(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n) {
+  if (batch < 1 || heads < 1 || n < 1 || n > kMaxN) return FA_E_SHAPE;
+  if (batch > INT32_MAX - 1 || heads > INT32_MAX) return FA_E_SHAPE;
+  if (heads_kv < 1 || heads_kv > heads || heads % heads_kv != 0) return FA_E_SHAPE;
+  if (batch * heads * ((n + 127) / 128) >= (int64_t(1) << 31)) return FA_E_SHAPE;
+  return FA_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 }  // namespace
 
 extern "C" {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+size_t fa_fp8_codes_bytes(int64_t batch, int64_t heads, int64_t n, int64_t d) {
+  if (check_fp8_shape(batch, heads, heads, n) != FA_OK || d < 1 || d > 256) return 0;
+  return fp8_codes_bytes(batch * heads, n, d);
+}
+
+size_t fa_fp8_scales_bytes(int64_t batch, int64_t heads, int64_t n) {
+  if (check_fp8_shape(batch, heads, heads, n) != FA_OK) return 0;
+  return fp8_scales_bytes(batch * heads, n);
+}
+
+fa_status fa_fp8_quantize(int64_t batch, int64_t heads, int64_t n, int64_t d, int layout,
+                          const void* x, const int8_t* signs, uint8_t* codes, float* scales,
+                          void* stream) {
+  fa_status st = check_fp8_shape(batch, heads, heads, n);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (layout != FA_FP8_ROWS && layout != FA_FP8_VT) return FA_E_UNSUPPORTED;
+  if (layout == FA_FP8_VT && signs != nullptr) return FA_E_UNSUPPORTED;
+  if (n * d * 2 >= (int64_t(1) << 31)) return FA_E_SHAPE;
+  if (!x || !codes || !scales) return FA_E_NULLPTR;
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(scales)) return FA_E_ALIGN;
+  if (signs && !aligned16(signs)) return FA_E_ALIGN;
+  const int64_t bh = batch * heads;
+  const Range rx = range_of(x, size_t(bh * n * d) * 2);
+  const Range rs = signs ? range_of(signs, size_t(d)) : Range{0, 0};
+  const Range rc = range_of(codes, fp8_codes_bytes(bh, n, d));
+  const Range rk = range_of(scales, fp8_scales_bytes(bh, n));
+  if (overlaps(rc, rk) || overlaps(rc, rx) || overlaps(rc, rs) || overlaps(rk, rx) ||
+      overlaps(rk, rs))
+    return FA_E_ALIAS;
+  fa::Fp8QuantParams p{};
+  p.x = x;
+  p.signs = signs;
+  p.codes = codes;
+  p.scales = scales;
+  p.bh = int(bh);
+  p.n = int(n);
+  p.np = int(fp8_rows(n));
+  p.nb = p.np / 128;
+  p.vt = layout == FA_FP8_VT ? 1 : 0;
+  p.post = signs ? float(1.0 / sqrt(double(d))) : 1.f;
+  const hipError_t e = fa::launch_fp8_quantize(p, int(d), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
+}
+
+fa_status fa_fwd_fp8(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
+                     int causal, float softmax_scale, const uint8_t* q8, const float* q_scales,
+                     const uint8_t* k8, const float* k_scales, const uint8_t* v8,
+                     const float* v_scales, const int32_t* kv_len, void* o, float* lse,
+                     void* stream) {
+  fa_status st = check_fp8_shape(batch, heads, heads_kv, n);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_E_UNSUPPORTED;
+  if (!isfinite(softmax_scale)) return FA_E_UNSUPPORTED;
+  if (n * d * 2 >= (int64_t(1) << 31)) return FA_E_SHAPE;
+  if (!q8 || !q_scales || !k8 || !k_scales || !v8 || !v_scales || !o || !lse)
+    return FA_E_NULLPTR;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o)) return FA_E_ALIGN;
+  if (!aligned4(q_scales) || !aligned4(k_scales) || !aligned4(v_scales) || !aligned4(lse) ||
+      !aligned4(kv_len))
+    return FA_E_ALIGN;
+  const int64_t bq = batch * heads, bk = batch * heads_kv;
+  const Range ins[7] = {range_of(q8, fp8_codes_bytes(bq, n, d)),
+                        range_of(k8, fp8_codes_bytes(bk, n, d)),
+                        range_of(v8, fp8_codes_bytes(bk, n, d)),
+                        range_of(q_scales, fp8_scales_bytes(bq, n)),
+                        range_of(k_scales, fp8_scales_bytes(bk, n)),
+                        range_of(v_scales, fp8_scales_bytes(bk, n)),
+                        kv_len ? range_of(kv_len, size_t(batch) * 4) : Range{0, 0}};
+  const Range ro = range_of(o, size_t(bq * n * d) * 2);
+  const Range rl = range_of(lse, size_t(bq * n) * 4);
+  if (overlaps(ro, rl)) return FA_E_ALIAS;
+  for (const Range& r : ins)
+    if (overlaps(r, ro) || overlaps(r, rl)) return FA_E_ALIAS;
+  fa::Fp8Params p{};
+  p.q8 = q8;
+  p.k8 = k8;
+  p.v8 = v8;
+  p.q_scale = q_scales;
+  p.k_scale = k_scales;
+  p.v_scale = v_scales;
+  p.kv_len = kv_len;
+  p.o = o;
+  p.lse = lse;
+  p.batch = int(batch);
+  p.heads = int(heads);
+  p.heads_kv = int(heads_kv);
+  p.group = int(heads / heads_kv);
+  p.n = int(n);
+  p.np = int(fp8_rows(n));
+  p.nb = p.np / 128;
+  p.causal = causal ? 1 : 0;
+  const float c = fabsf(softmax_scale) * 1.4426950408889634f;
+  p.c = c < FLT_MIN ? FLT_MIN : c;
+  p.q_neg = softmax_scale < 0.f ? 1 : 0;
+  const hipError_t e = fa::launch_fwd_fp8(p, int(d), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
+}
 
 const char* fa_status_str(fa_status s) {
   switch (s) {

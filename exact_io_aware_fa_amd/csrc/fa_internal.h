@@ -53,6 +53,49 @@ struct Params {
   int q_neg;
 };
 
+// FP8 (E4M3) forward. Codes of Q and K are [batch*heads][np][d] bytes, V's
+// [batch*heads_kv][nb][d][128] (each 128-key block transposed); rows past n
+// hold zero codes. One float scale per (head, 128-row block); V's scales
+// are powers of two.
+struct Fp8Params {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* q_scale;   // [batch*heads][nb]
+  const float* k_scale;   // [batch*heads_kv][nb]
+  const float* v_scale;   // [batch*heads_kv][nb]
+  const int32_t* kv_len;  // nullable, device int32[batch]
+  void* o;                // bf16 [batch, heads, n, d]
+  float* lse;             // [batch, heads, n]
+  int batch;
+  int heads;
+  int heads_kv;
+  int group;
+  int n;
+  int np;                 // n rounded up to a multiple of 128
+  int nb;                 // np / 128
+  int causal;
+  float c;                // |scale| * log2(e), at least FLT_MIN
+  int q_neg;              // negative scale: Q codes are negated (sign bit)
+};
+
+// Blockwise E4M3 encoding of one bf16 tensor [bh][n][d].
+struct Fp8QuantParams {
+  const void* x;          // bf16
+  const int8_t* signs;    // nullable: rotate by diag(signs) H_d first
+  uint8_t* codes;
+  float* scales;
+  int bh;                 // batch * heads
+  int n;
+  int np;
+  int nb;
+  int vt;                 // 1: V layout (blocks transposed), 0: rows
+  float post;             // factor folded into the stored scales (1/sqrt(d) if rotated)
+};
+
+hipError_t launch_fp8_quantize(const Fp8QuantParams& p, int d, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s);
+
 hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s);
 hipError_t launch_fwd_bf16_staged(const Params& p, int d, hipStream_t s);
 hipError_t launch_fwd_bf16_d64(const Params& p, int d, hipStream_t s);

@@ -1,0 +1,180 @@
+// Blockwise E4M3 encoding of Q, K or V for the FP8 forward, for gfx950.
+//
+// Method: page 2 ("4. FlashAttention 深度剖析"), 4.5.4 (FP8 support): every
+// block is scaled once and its scale kept; Q and K may first be rotated by a
+// random Hadamard matrix. E4M3's range (largest magnitude 448, smallest
+// normal 2^-6) is the page's exercise 3.
+//
+// A block is 128 rows of one head. Its scale is the power of two 2^e with e
+// the smallest integer such that max |x| <= 448 * 2^e, so x * 2^-e is exact
+// and the only rounding is the conversion to E4M3 (v_cvt_pk_fp8_f32: round to
+// nearest even, with subnormals). With a rotation the block is x R, R =
+// diag(signs) H_d (entries +-1, fast Walsh-Hadamard butterflies in fp32),
+// and the stored scale is 2^e / sqrt(d), so scale * codes approximates
+// x R / sqrt(d), the page's x H.
+//
+// Layouts written: rows -- codes [bh][np][d], as the attention kernel's Q
+// and K operands want them; V -- codes [bh][nb][d][128], each block
+// transposed (channel-major), so that the kernel's V^T operand reads are
+// plain row reads. Rows past n are zero codes.
+//
+// One workgroup (256 threads) per block: thread t holds half a row (row
+// t / 2, channels (t % 2) * d/2 ...) in fp32 registers.
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int D, bool ROT, bool VT>
+__global__ __launch_bounds__(kQThreads) void fp8_quant_kernel(Fp8QuantParams p) {
+  constexpr int HD = D / 2;  // channels per thread
+  static_assert(HD % 16 == 0, "row split");
+  __shared__ float red[kQThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? 128 * D : 16];
+
+  const int blk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int r = t >> 1;
+  const int hh = t & 1;
+  const int row = blk * 128 + r;
+
+  float x[HD];
+  if (row < p.n) {
+    const bf16* src = static_cast<const bf16*>(p.x) + ((size_t)bh * p.n + row) * D + hh * HD;
+#pragma unroll
+    for (int i = 0; i < HD / 8; ++i) {
+      const u32x4 v = ld16(src + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * i + 2 * j] = bf16_lo(v[j]);
+        x[8 * i + 2 * j + 1] = bf16_hi(v[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < HD; ++i) x[i] = 0.f;
+  }
+
+  if (ROT) {
+    // x <- x diag(signs) H_d. H_d is the product of one +-butterfly per
+    // index bit; bits below log2(d/2) are inside the thread, the top bit
+    // pairs the two halves of the row (lanes t and t ^ 1).
+#pragma unroll
+    for (int i = 0; i < HD / 16; ++i) {
+      const u32x4 sv = ld16(p.signs + hh * HD + 16 * i);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int8_t sg = (int8_t)((sv[j >> 2] >> (8 * (j & 3))) & 0xFF);
+        x[16 * i + j] = sg < 0 ? -x[16 * i + j] : x[16 * i + j];
+      }
+    }
+#pragma unroll
+    for (int h = 1; h < HD; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < HD; ++i)
+        if (!(i & h)) {
+          const float a = x[i], b = x[i + h];
+          x[i] = a + b;
+          x[i + h] = a - b;
+        }
+#pragma unroll
+    for (int i = 0; i < HD; ++i) {
+      const float y = __shfl_xor(x[i], 1);
+      x[i] = hh ? (y - x[i]) : (x[i] + y);
+    }
+  }
+
+  // Block maximum of |x|.
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < HD; ++i) am = fmaxf(am, fabsf(x[i]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+  if ((t & 63) == 0) red[t >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  // Smallest e with am <= 448 * 2^e: am = m 2^E, m in [0.5, 1), and
+  // 448 = 0.875 * 2^9.
+  int E;
+  const float m = frexpf(am, &E);
+  const int e = am == 0.f ? 0 : (m <= 0.875f ? E - 9 : E - 8);
+  if (t == 0) p.scales[(size_t)bh * p.nb + blk] = ldexpf(1.f, e) * p.post;
+
+  uint32_t w[HD / 4];
+#pragma unroll
+  for (int i = 0; i < HD / 4; ++i) {
+    uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * i], -e), ldexpf(x[4 * i + 1], -e),
+                                                 0u, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * i + 2], -e), ldexpf(x[4 * i + 3], -e), c,
+                                        true);
+    w[i] = c;
+  }
+
+  if (!VT) {
+    uint8_t* dst = p.codes + ((size_t)bh * p.np + row) * D + hh * HD;
+#pragma unroll
+    for (int i = 0; i < HD / 16; ++i)
+      *reinterpret_cast<u32x4*>(dst + 16 * i) =
+          u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < HD / 16; ++i)
+      *reinterpret_cast<u32x4*>(tile + r * D + hh * HD + 16 * i) =
+          u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    __syncthreads();
+    // Transposed block: output row c (channel) holds the block's 128 keys.
+    constexpr int TPC = kQThreads / D;  // threads per output row
+    constexpr int KPT = 128 / TPC;      // keys per thread
+    const int c = t / TPC;
+    const int k0 = (t % TPC) * KPT;
+    uint8_t* dst = p.codes + ((size_t)bh * p.nb + blk) * (size_t)(D * 128) + c * 128 + k0;
+#pragma unroll
+    for (int ch = 0; ch < KPT / 16; ++ch) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          v |= (uint32_t)tile[(k0 + 16 * ch + 4 * q + b) * D + c] << (8 * b);
+        o[q] = v;
+      }
+      *reinterpret_cast<u32x4*>(dst + 16 * ch) = o;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const Fp8QuantParams& p, hipStream_t s) {
+  dim3 grid((unsigned)p.nb, (unsigned)p.bh), block(kQThreads);
+  const bool rot = p.signs != nullptr;
+  if (p.vt) {
+    if (rot) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fp8_quant_kernel<D, false, true>), grid, block, 0, s, p);
+  } else if (rot) {
+    hipLaunchKernelGGL((fp8_quant_kernel<D, true, false>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((fp8_quant_kernel<D, false, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8_quantize(const Fp8QuantParams& p, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_d<64>(p, s);
+    case 128: return launch_d<128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,494 @@
+// Attention forward on FP8 (E4M3) operands with fp32 accumulation, for
+// gfx950 (d = 128).
+//
+// Method: page 2 ("4. FlashAttention 深度剖析"), 4.5.4 (FP8 support): both
+// products of the forward take E4M3 operands, every block carries the scale
+// it was encoded with, and the products accumulate in fp32. The tiling and
+// the (m, l, O) update are those of the bf16 forward (page 2 4.3.2; page 1,
+// "注意力为什么受限于显存带宽：用算术强度与分块把 FlashAttention 推导清楚",
+// section 六), with two changes the format asks for:
+// * the running row reference is an integer frame f = ceil(max t) in base-2
+//   units (t = s * c), so every rescale factor 2^(f_old - f_new) is a power
+//   of two: a probability rounded in an earlier, lower frame is the same
+//   E4M3 value as if it had been rounded in the final frame (in the normal
+//   range), whatever the tile order;
+// * probabilities enter the P V product as E4M3(2^(t - f + 8)), in (0, 256]:
+//   the factor 2^8 moves the largest probabilities of a row to the top of the
+//   format's normal range (<= 448); l sums the unrounded values and the 2^8
+//   cancels in O = O~ / l.
+//
+// Operands (written by the quantiser kernel):
+// * Q, K codes row-major [rows][128] bytes; the scores of a tile are
+//   (Q K^T codes) * sigma_q * sigma_k, the two block scales folded into the
+//   exp2 factor (c_j = |scale| log2(e) sigma_q sigma_k,j);
+// * V codes stored per 128-key block transposed ([128 channels][128 keys]);
+//   the V block scale is a power of two and enters the P V product through
+//   the matrix core's own E8M0 operand scale, so O~ needs no rescale when
+//   the V block changes.
+//
+// Mapping onto CDNA4 (as the bf16 forward): 8 wave64s per workgroup, 256
+// query rows, 32 per wave for the whole key sweep; ping-pong between the
+// two waves of a SIMD (matrix phase of one, softmax phase of the other);
+// K and V^T tiles straight from HBM into LDS (two stages each). The score
+// product is S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4: lane l supplies
+// query l % 32 as B and key row sigma(l % 32) as A, with
+// sigma(8a + 4b + i) = 16b + 4a + i, so that the result register r of lane
+// (c, h) holds key 16h + r of its 32-key block: each lane then owns 16
+// consecutive keys per block, and its rounded probabilities are directly
+// the B operand of O^T += V^T P^T, whose A operand (V^T) is read as two
+// 16-byte runs of one channel row.
+#include <float.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kBR = 256;  // query rows per workgroup (8 waves x 32)
+constexpr int kD = 128;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// acc[32x32] += A[32x64] B[64x32] on the E4M3 matrix cores, fp32 accumulate.
+// Lane l supplies row l % 32 of A and column l % 32 of B, each with 32 of
+// the 64 reduction indices (chosen by l / 32); byte k of an A lane pairs
+// with byte k of the B lane of the same half, so any assignment of
+// reduction indices to bytes works as long as A and B use it alike. Result
+// layout as mma32. With `sa`, A is scaled by 2^(sa - 127) (E8M0).
+__device__ __forceinline__ f32x16 mma_f8(i32x8 a, i32x8 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_f8_sa(i32x8 a, i32x8 b, f32x16 acc, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, 127);
+}
+
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Key row read by A lane c of a 32-key block (see the header).
+__device__ __forceinline__ int key_of_lane(int c) {
+  return 16 * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
+}
+// XOR swizzles of the 16-byte chunk index. K rows (128 bytes): the 16
+// lanes of a read phase touch rows {0..7, 16..23} (or {8..15, 24..31}) of a
+// block at one logical chunk; the swizzle is a bijection on each parity
+// class of those rows, so they hit 16 different bank groups. V^T rows
+// (BC bytes): 16 consecutive rows at one logical chunk.
+__device__ __forceinline__ int swz_k(int row) { return ((row >> 1) & 3) | ((row >> 2) & 4); }
+template <int BC>
+__device__ __forceinline__ int swz_v(int row) {
+  return BC == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+}
+
+// A wave-uniform float loaded by every lane with a vector load (so that it
+// is counted by vmcnt, like the tile loads, and not by lgkmcnt, like the LDS
+// reads of the matrix phase).
+__device__ __forceinline__ float vload_uniform(const float* a, int i) {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return a[i + z];
+}
+
+template <int BC, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
+  constexpr int D = kD;
+  constexpr int TILEB = BC * D;          // bytes of a K or V^T tile
+  constexpr int NW = kThreads / 64;      // waves per workgroup
+  constexpr int LPW = TILEB / 1024 / NW;  // 1 KB loads per tensor per wave
+  constexpr int KRPL = 1024 / D;         // K rows per 1 KB load
+  constexpr int VCH = BC / 16;           // 16-byte chunks per V^T row
+  constexpr int VRPL = 1024 / BC;        // V^T rows per 1 KB load
+  constexpr int NKB = BC / 32;           // 32-key blocks of S^T
+  constexpr int NKK = BC / 64;           // 64-key reduction chunks of O^T
+  constexpr int NMB = D / 32;            // 32-channel blocks of O^T
+  static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "tile split");
+  static_assert(BC == 64 || BC == 128, "tile width");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[TILEB];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+
+  const int n = p.n;
+  const int t_r = (n + kBR - 1) / kBR;
+  int b, hq, qb;
+  remap_workgroup(blockIdx.x, gridDim.x, t_r, CAUSAL, p.batch, b, hq, qb);
+  const size_t bhq = (size_t)b * p.heads + hq;
+  const size_t bhk = (size_t)b * p.heads_kv + hq / p.group;
+  const uint8_t* __restrict__ Q8 = p.q8 + bhq * (size_t)p.np * D;
+  const uint8_t* __restrict__ K8 = p.k8 + bhk * (size_t)p.np * D;
+  const uint8_t* __restrict__ V8 = p.v8 + bhk * (size_t)p.np * D;
+  const float* __restrict__ ksc = p.k_scale + bhk * p.nb;
+  const float* __restrict__ vsc = p.v_scale + bhk * p.nb;
+  bf16* __restrict__ O = static_cast<bf16*>(p.o) + bhq * (size_t)n * D;
+
+  int kv_lim = n;
+  if (p.kv_len != nullptr) kv_lim = min(max(p.kv_len[b], 0), n);
+  const int q0 = qb * kBR;
+  const int qw0 = q0 + 32 * (2 * (w & 3) + grp);
+  const int qi = qw0 + c;
+  // exp2 factor of this wave's rows: |scale| log2(e) sigma_q (one block).
+  const float cq = p.c * p.q_scale[bhq * p.nb + min(qw0 / 128, p.nb - 1)];
+
+  // Q codes of this wave's rows as B fragments: lane (c, h) holds bytes
+  // 64 kd + 32 h .. + 31 of row qi. A negative scale negates the codes
+  // (sign bit, exact); rows past n are zero.
+  i32x8 qf[2];
+  {
+    const uint32_t flip = p.q_neg ? 0x80808080u : 0u;
+    const int qr = min(qi, n - 1);
+#pragma unroll
+    for (int kd = 0; kd < 2; ++kd) {
+      const uint8_t* src = Q8 + (size_t)qr * D + kd * 64 + h * 32;
+      const u32x4 lo = ld16(src) ^ flip, hi = ld16(src + 16) ^ flip;
+      const bool in = qi < n;
+      qf[kd] = i32x8{(int)(in ? lo[0] : 0u), (int)(in ? lo[1] : 0u), (int)(in ? lo[2] : 0u),
+                     (int)(in ? lo[3] : 0u), (int)(in ? hi[0] : 0u), (int)(in ? hi[1] : 0u),
+                     (int)(in ? hi[2] : 0u), (int)(in ? hi[3] : 0u)};
+    }
+  }
+
+  // Key ranges as in the bf16 forward (no window: every row starts at key
+  // 0, so the masked steps of a wave are the last ones).
+  const Band<CAUSAL> band{n, kv_lim, -1, -1};
+  const int ntiles = max((band.hi(min(q0 + kBR, n) - 1) + BC - 1) / BC, 0);
+  const int qw_last = min(qw0 + 31, n - 1);
+  const int s_first = 0;
+  const int s_last = (band.hi(qw_last) - 1) / BC;
+  const int su_hi = band.hi(qw0) / BC;
+
+  f32x16 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+  float f = kNegInf;   // integer frame of the running row max (base-2 units)
+  float lpart = 0.f;   // this half-wave's share of the row sum (in 2^(t - f + 8))
+  f32x16 sc[NKB];
+  i32x8 pf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) pf[kk] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+
+  // DMA offsets (tile-invariant). K: lane l of load i writes physical chunk
+  // l % 8 of row (w LPW + i) 8 + l / 8, fetching logical chunk
+  // (l % 8) ^ swz_k(row). V^T: row (w LPW + i) VRPL + l / VCH, chunk l % VCH.
+  int ld_koff[LPW], ld_voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int kr = (w * LPW + i) * KRPL + lane / 8;
+    ld_koff[i] = kr * D + (((lane & 7) ^ swz_k(kr)) << 4);
+    const int vr = (w * LPW + i) * VRPL + lane / VCH;
+    ld_voff[i] = vr * 128 + (((lane % VCH) ^ swz_v<BC>(vr)) << 4);
+  }
+  auto issue_k = [&](int j, uint8_t* dst) FA_INLINE {
+    const auto r = buffer_rsrc(K8 + (size_t)j * BC * D, TILEB);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) bload_lds16(r, ld_koff[i], dst + (w * LPW + i) * 1024);
+  };
+  auto issue_v = [&](int j, uint8_t* dst) FA_INLINE {
+    const int kb0 = j * BC;
+    const auto r =
+        buffer_rsrc(V8 + (size_t)(kb0 >> 7) * (D * 128) + (kb0 & 127), D * 128 - (kb0 & 127));
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) bload_lds16(r, ld_voff[i], dst + (w * LPW + i) * 1024);
+  };
+
+  // Operand read offsets (tile-invariant): K row key_of_lane(c) of each
+  // 32-key block, logical chunks 4 kd + 2 h + {0, 1}; V^T row c of each
+  // 32-channel block, logical chunks 4 kk + h and 4 kk + 2 + h.
+  int koff[2][2], voff[NKK][2];
+  {
+    const int kr = key_of_lane(c);
+#pragma unroll
+    for (int kd = 0; kd < 2; ++kd)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) koff[kd][e] = kr * D + (((4 * kd + 2 * h + e) ^ swz_k(kr)) << 4);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        voff[kk][e] = c * BC + (((4 * kk + 2 * e + h) ^ swz_v<BC>(c)) << 4);
+  }
+
+  // Matrix phase: S^T slots (NKB blocks x 2 halves of d), then O^T slots
+  // (NMB channel blocks x NKK key chunks), operands read PF slots ahead.
+  constexpr int NS = NKB * 2;
+  constexpr int NPV = NMB * NKK;
+  constexpr int PF = 3;
+  auto rd = [&](const uint8_t* sk, const uint8_t* sv, int k) FA_INLINE {
+    u32x4 lo, hi;
+    if (k < NS) {
+      const int kb = k % NKB, kd = k / NKB;
+      const uint8_t* base = sk + kb * 32 * D;
+      lo = ld16(base + koff[kd][0]);
+      hi = ld16(base + koff[kd][1]);
+    } else {
+      const int mb = (k - NS) % NMB, kk = (k - NS) / NMB;
+      const uint8_t* base = sv + mb * 32 * BC;
+      lo = ld16(base + voff[kk][0]);
+      hi = ld16(base + voff[kk][1]);
+    }
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto slots = [&](const uint8_t* sk, const uint8_t* sv, int ve) FA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sc[kb] = f32x16{};
+    i32x8 fr[PF + 1];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) fr[k] = rd(sk, sv, k);
+#pragma unroll
+    for (int k = 0; k < NS + NPV; ++k) {
+      if (k + PF < NS + NPV) fr[(k + PF) % (PF + 1)] = rd(sk, sv, k + PF);
+      if (k < NS) {
+        const int kb = k % NKB, kd = k / NKB;
+        sc[kb] = mma_f8(fr[k % (PF + 1)], qf[kd], sc[kb]);
+      } else {
+        const int mb = (k - NS) % NMB, kk = (k - NS) / NMB;
+        acc[mb] = mma_f8_sa(fr[k % (PF + 1)], pf[kk], acc[mb], ve);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Keep the products in this half-period: otherwise the compiler sinks
+    // the O^T products past the next barrier, next to their first use.
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(acc[mb]));
+  };
+
+  // Softmax phase of tile j with exp2 factor cj.
+  auto apply_mask = [&](int j) FA_INLINE {
+    const int kb0 = j * BC;
+    int qv = qi;
+    asm volatile("" : "+v"(qv));
+    const int hi_i = band.hi(qv);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb0 + kb * 32 + 16 * h + r;
+        sc[kb][r] = key >= hi_i ? kNegInf : sc[kb][r];
+      }
+  };
+  auto softmax = [&](float cj) FA_INLINE {
+    float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sc[kb][r]);
+    const float mt = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+    // New integer frame: ceil of the running max of t = s * cj (cj > 0, so
+    // -inf stays -inf).
+    const float fnew = fmaxf(f, ceilf(mt * cj));
+    const float fref = (fnew == kNegInf) ? 0.f : fnew;
+    const float alpha = __builtin_amdgcn_exp2f(f - fref);  // 2^k; 1 if unchanged, 0 while empty
+    f = fnew;
+    const float off = 8.f - fref;
+    float rp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], cj, off));
+        sc[kb][r] = e;
+        rp[r & 3] += e;
+      }
+    lpart = fmaf(lpart, alpha, (rp[0] + rp[1]) + (rp[2] + rp[3]));
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    }
+    // P^T fragments: bytes 0-15 from block 2 kk, 16-31 from block 2 kk + 1,
+    // four probabilities per dword (RNE to E4M3).
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x16& s = sc[2 * kk + (q >> 2)];
+        const int r = 4 * (q & 3);
+        uint32_t v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r], s[r + 1], 0u, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r + 2], s[r + 3], v, true);
+        pf[kk][q] = (int)v;
+      }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(pf[kk]));
+    asm volatile("" : "+v"(lpart));
+  };
+  auto valu_phase = [&](int j, float cj) FA_INLINE {
+    if (j >= 0 && j < ntiles && j >= s_first && j <= s_last) {
+      if (j >= su_hi) apply_mask(j);
+      softmax(cj);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) pf[kk] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  };
+
+  // Per-tile scales, loaded one step ahead with the tiles: at step m the
+  // softmax of tile m (group A) uses cj_m, that of tile m - 1 (group B)
+  // cj_m1, and the P V product of tile m - 1 uses V exponent ve_m1.
+  auto kfactor = [&](int j) FA_INLINE {
+    return vload_uniform(ksc, min(j * BC / 128, p.nb - 1));
+  };
+  auto vexp = [&](int j) FA_INLINE {
+    return vload_uniform(vsc, min(j * BC / 128, p.nb - 1));
+  };
+  float k_nx = kfactor(0);  // sigma_k of tile m + 1 (in flight)
+  float v_nx = 1.f;         // sigma_v of tile m (in flight); tile -1: P is 0
+  float cj_m = 0.f, cj_m1 = 0.f;
+  int ve_m1 = 127;
+
+  auto phase_barrier = [&]() FA_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mid_barrier = [&]() FA_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto open_step = [&](int m, uint8_t* nk, uint8_t* nv) FA_INLINE {
+    wait_global_loads();
+    // The scale loads of the previous step have landed: take them over
+    // before this step's loads are issued.
+    asm volatile("" : "+v"(k_nx), "+v"(v_nx));
+    cj_m1 = cj_m;
+    cj_m = fmaxf(cq * k_nx, FLT_MIN);
+    ve_m1 = (int)((__float_as_uint(v_nx) >> 23) & 0xFF);
+    phase_barrier();
+    if (m + 1 < ntiles) {
+      issue_k(m + 1, nk);
+      k_nx = kfactor(m + 1);
+    }
+    if (m < ntiles) {
+      issue_v(m, nv);
+      v_nx = vexp(m);
+    }
+  };
+  auto step_a = [&](int m, const uint8_t* sk, uint8_t* nk, uint8_t* nv, const uint8_t* sv)
+      FA_INLINE {
+    open_step(m, nk, nv);
+    slots(sk, sv, ve_m1);
+    mid_barrier();
+    valu_phase(m, cj_m);
+  };
+  auto step_b = [&](int m, const uint8_t* sk, uint8_t* nk, uint8_t* nv, const uint8_t* sv)
+      FA_INLINE {
+    open_step(m, nk, nv);
+    valu_phase(m - 1, cj_m1);
+    mid_barrier();
+    slots(sk, sv, ve_m1);
+  };
+  auto hot_a = [&](int m, const uint8_t* sk, uint8_t* nk, uint8_t* nv, const uint8_t* sv)
+      FA_INLINE {
+    open_step(m, nk, nv);
+    slots(sk, sv, ve_m1);
+    mid_barrier();
+    softmax(cj_m);
+  };
+  auto hot_b = [&](int m, const uint8_t* sk, uint8_t* nk, uint8_t* nv, const uint8_t* sv)
+      FA_INLINE {
+    open_step(m, nk, nv);
+    softmax(cj_m1);
+    mid_barrier();
+    slots(sk, sv, ve_m1);
+  };
+
+  // All stages start zeroed (finite data under masked or unused rows).
+  {
+    constexpr int NZ = TILEB / 16 / kThreads;
+    static_assert(NZ * 16 * kThreads == TILEB, "zero fill");
+#pragma unroll
+    for (int t = 0; t < NZ; ++t) {
+      const int e = (t * kThreads + tid) * 16;
+      *reinterpret_cast<u32x4*>(sK0 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sK1 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sV0 + e) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sV1 + e) = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  }
+
+  // Steps as in the bf16 forward: whole pairs from step 1 with fixed stage
+  // assignments; steps [1, hot_end) take the straight-line steps.
+  const int hot_end = min(min(ntiles, s_last + 1), su_hi + grp);
+  if (ntiles > 0) issue_k(0, sK0);
+  if (grp == 0) {
+    step_a(0, sK0, sK1, sV0, sV1);
+    int m = 1;
+    for (; m + 1 < hot_end; m += 2) {
+      hot_a(m, sK1, sK0, sV1, sV0);
+      hot_a(m + 1, sK0, sK1, sV0, sV1);
+    }
+    for (; m <= ntiles; m += 2) {
+      step_a(m, sK1, sK0, sV1, sV0);
+      if (m + 1 > ntiles) break;
+      step_a(m + 1, sK0, sK1, sV0, sV1);
+    }
+  } else {
+    step_b(0, sK0, sK1, sV0, sV1);
+    int m = 1;
+    for (; m + 1 < hot_end; m += 2) {
+      hot_b(m, sK1, sK0, sV1, sV0);
+      hot_b(m + 1, sK0, sK1, sV0, sV1);
+    }
+    for (; m <= ntiles; m += 2) {
+      step_b(m, sK1, sK0, sV1, sV0);
+      if (m + 1 > ntiles) break;
+      step_b(m + 1, sK0, sK1, sV0, sV1);
+    }
+  }
+
+  // Epilogue: O = O~ / l (bf16), LSE = ln 2 (f - 8 + log2 l).
+  const float l = halves_sum(lpart);
+  if (qi < n) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* orow = O + (size_t)qi * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 u;
+        u[0] = pack_bf16x2(acc[mb][g * 4 + 0] * inv, acc[mb][g * 4 + 1] * inv);
+        u[1] = pack_bf16x2(acc[mb][g * 4 + 2] * inv, acc[mb][g * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + mb * 32 + g * 8 + h * 4) = u;
+      }
+    if (h == 0) p.lse[bhq * n + qi] = l > 0.f ? (f - 8.f + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s) {
+  if (d != kD) return hipErrorInvalidValue;
+  const int t_r = (p.n + kBR - 1) / kBR;
+  const long long total = (long long)t_r * p.batch * p.heads;
+  dim3 grid((unsigned)total), block(kThreads);
+  // 128-key tiles: half the per-tile overhead of 64 (barriers, row max
+  // exchange, frame update) for the same matrix work.
+  constexpr int BC = 128;
+  if (p.causal)
+    hipLaunchKernelGGL((fwd_fp8_kernel<BC, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<BC, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa

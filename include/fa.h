@@ -102,7 +102,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
 
@@ -334,6 +334,85 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t heads_kv,
                        void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes,
                        void* stream, void* const events[4]);
+
+/*
+ * FP8 forward (page 2, "4. FlashAttention 深度剖析", 4.5.4: E4M3 operands in
+ * the forward, one scale per block recorded when the block is encoded, FP32
+ * accumulation, optional random Hadamard rotation of Q and K; exercise 3:
+ * E4M3's largest magnitude is 448 and its smallest normal 2^-6).
+ *
+ * E4M3 here is the 1-4-3 format with exponent bias 7, subnormals, no
+ * infinities and S.1111.111 as NaN. A tensor [batch, heads, n, d] is encoded
+ * in blocks of FA_BLOCK rows of one head (np = n rounded up to a multiple of
+ * FA_BLOCK, nb = np / FA_BLOCK blocks per head):
+ *   codes  -- uint8, batch * heads * np * d bytes, in one of two layouts:
+ *             FA_FP8_ROWS  [batch, heads, np, d] (Q and K),
+ *             FA_FP8_VT    [batch, heads, nb, d, FA_BLOCK]: every block
+ *                          transposed, channel-major (V);
+ *             codes of rows n .. np - 1 are zero;
+ *   scales -- float32 [batch, heads, nb]; block b stands for
+ *             scales[b] * decode(codes of b).
+ * The scale of a block is 2^e with e the smallest integer such that the
+ * block's largest magnitude is at most 448 * 2^e (e = 0 for an all-zero
+ * block), so x * 2^-e is exact and the only rounding is E4M3's own (to
+ * nearest, ties to even). With a rotation the encoded block is x R with
+ * R = diag(signs) H_d (H_d the Sylvester Hadamard matrix, entries +-1) and
+ * the stored scale is 2^e / sqrt(d): scale * codes approximates x R / sqrt(d),
+ * the page's x H. Rotating Q and K with the same signs leaves Q K^T
+ * unchanged.
+ */
+#define FA_FP8_ROWS 0
+#define FA_FP8_VT 1
+
+/* Bytes of the codes and of the scales of a [batch, heads, n, d] tensor;
+ * 0 for invalid sizes. */
+size_t fa_fp8_codes_bytes(int64_t batch, int64_t heads, int64_t n, int64_t d);
+size_t fa_fp8_scales_bytes(int64_t batch, int64_t heads, int64_t n);
+
+/*
+ * fa_fp8_quantize -- encodes the bf16 tensor x [batch, heads, n, d]
+ * (d = 64 or 128, else FA_E_UNSUPPORTED) into `codes` (layout FA_FP8_ROWS or
+ * FA_FP8_VT, else FA_E_UNSUPPORTED) and `scales`, as described above.
+ * signs: NULL (no rotation) or a device int8[d] of +1 / -1 entries (any
+ * negative value counts as -1), 16-byte aligned; a rotation with the
+ * FA_FP8_VT layout returns FA_E_UNSUPPORTED (V is not rotated). Outputs
+ * must not overlap x, signs or each other. Sizes as for fa_fwd; x, codes
+ * 16-byte aligned, scales 4-byte aligned. Blocks whose largest magnitude
+ * lies below 2^-100 or above 2^120 are outside the supported range.
+ */
+fa_status fa_fp8_quantize(int64_t batch, int64_t heads, int64_t n, int64_t d,
+                          int layout, const void* x, const int8_t* signs,
+                          uint8_t* codes, float* scales, void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward on encoded operands: q8 (FA_FP8_ROWS,
+ * [batch, heads, np, d]), k8 (FA_FP8_ROWS, [batch, heads_kv, np, d]), v8
+ * (FA_FP8_VT, [batch, heads_kv, nb, d, FA_BLOCK]) with their scales; d = 128
+ * (else FA_E_UNSUPPORTED); grouped heads, causal, kv_len and softmax_scale
+ * as for fa_fwd_gqa. Both products run on the E4M3 matrix cores with FP32
+ * accumulation. With t_ij = softmax_scale * log2(e) * (sq q^_i . sk k^_j)
+ * and the integer row frame f_i = ceil(max_j t_ij) over the visible keys,
+ * the probabilities enter the P V product as E4M3(2^(t_ij - f_i + 8)) and
+ *     O_i   = sum_j E4M3(2^(t_ij - f_i + 8)) sv v^_j / l_i,
+ *     l_i   = sum_j 2^(t_ij - f_i + 8),
+ *     LSE_i = ln 2 * (f_i - 8 + log2 l_i)   (natural log of the row's sum
+ *             of exp(scores)),
+ * up to the matrix cores' fp32 accumulation. The frame is an integer, so the
+ * rounding of a probability does not depend on the order in which the key
+ * tiles are visited. o: bf16 [batch, heads, n, d]; lse: float32 [batch,
+ * heads, n]; hidden keys and empty rows as for fa_fwd. The V scales must be
+ * powers of two (as fa_fp8_quantize writes them; only each entry's
+ * exponent is used); Q and K scales are any positive floats. Code pointers
+ * and o 16-byte aligned; scales, lse and kv_len 4-byte aligned; outputs
+ * must not overlap any input or each other.
+ */
+fa_status fa_fwd_fp8(int64_t batch, int64_t heads, int64_t heads_kv,
+                     int64_t n, int64_t d, int causal, float softmax_scale,
+                     const uint8_t* q8, const float* q_scales,
+                     const uint8_t* k8, const float* k_scales,
+                     const uint8_t* v8, const float* v_scales,
+                     const int32_t* kv_len,
+                     void* o, float* lse, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_str(fa_status s);

@@ -183,17 +183,20 @@ def _quantize_p(u: np.ndarray) -> np.ndarray:
 
 
 def fp8_head_forward(qc, qs, kc, ks, vc, vs, n: int, scale: float, causal: bool,
-                     kv_len_b: int | None = None, parts: bool = False) -> dict:
+                     kv_len_b: int | None = None, parts: bool = False, rows=None) -> dict:
     """Forward of one head from codes and scales (see the module docstring).
 
-    qc, kc, vc: [np, d] codes; qs, ks, vs: [nb] scales. Returns dict(o, lse)
-    and, with ``parts``, the intermediate arrays (t, f, u, pq, l, vv, tabs,
-    vis) a parity check needs.
+    qc, kc, vc: [np, d] codes; qs, ks, vs: [nb] scales. ``rows`` selects
+    query rows (each output row depends on its own query row and all keys
+    only). Returns dict(o, lse) and, with ``parts``, the intermediate arrays
+    (t, f, u, pq, l, vv, tabs, vis) a parity check needs.
     """
     q = dequantize(qc, qs, n)
+    if rows is not None:
+        q = q[np.asarray(rows, dtype=np.int64)]
     k = dequantize(kc, ks, n)
     vv = dequantize(vc, vs, n)
-    vis = visible_mask(n, causal, kv_len_b)
+    vis = visible_mask(n, causal, kv_len_b, rows)
     log2e = 1.0 / math.log(2.0)
     t = np.where(vis, scale * (q @ k.T) * log2e, -np.inf)
     tmax = t.max(axis=1)

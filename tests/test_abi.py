@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.fa_abi_version() == B.ABI_VERSION == 4
+    assert B.fa_abi_version() == B.ABI_VERSION == 5
     for code, tag in ((0, "FA_OK"), (1, "FA_E_NULLPTR"), (2, "FA_E_SHAPE"),
                       (3, "FA_E_UNSUPPORTED"), (4, "FA_E_WORKSPACE"), (5, "FA_E_ALIAS"),
                       (6, "FA_E_LAUNCH"), (7, "FA_E_ALIGN")):
@@ -246,3 +246,70 @@ def test_loader_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+# ---------------------------------------------------------------------------
+# FP8 entry points
+
+def test_fp8_sizes_closed_form(lib):
+    # np = n rounded up to 128; codes batch*heads*np*d bytes, scales 4 per block.
+    assert B.fa_fp8_codes_bytes(2, 3, 300, 128) == 2 * 3 * 384 * 128
+    assert B.fa_fp8_scales_bytes(2, 3, 300) == 2 * 3 * 3 * 4
+    assert B.fa_fp8_codes_bytes(1, 1, 128, 64) == 128 * 64
+    assert B.fa_fp8_codes_bytes(0, 1, 128, 64) == 0
+    assert B.fa_fp8_scales_bytes(1, 1, 0) == 0
+
+
+X8, C8, S8, SG = (0x2_0000_0000 * (i + 1) for i in range(4))
+
+
+def quant(**kw):
+    a = dict(batch=2, heads=3, n=300, d=128, layout=B.FA_FP8_ROWS, x=X8, signs=None,
+             codes=C8, scales=S8, stream=None)
+    a.update(kw)
+    return B.fa_fp8_quantize(a["batch"], a["heads"], a["n"], a["d"], a["layout"], a["x"],
+                             a["signs"], a["codes"], a["scales"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=256), B.FA_E_UNSUPPORTED), (dict(d=96), B.FA_E_UNSUPPORTED),
+    (dict(layout=2), B.FA_E_UNSUPPORTED),
+    (dict(layout=B.FA_FP8_VT, signs=SG), B.FA_E_UNSUPPORTED),
+    (dict(n=0), B.FA_E_SHAPE), (dict(batch=0), B.FA_E_SHAPE),
+    (dict(x=None), B.FA_E_NULLPTR), (dict(codes=None), B.FA_E_NULLPTR),
+    (dict(scales=None), B.FA_E_NULLPTR),
+    (dict(x=X8 + 2), B.FA_E_ALIGN), (dict(codes=C8 + 8), B.FA_E_ALIGN),
+    (dict(scales=S8 + 2), B.FA_E_ALIGN), (dict(signs=SG + 4), B.FA_E_ALIGN),
+    (dict(codes=X8 + 4096), B.FA_E_ALIAS), (dict(scales=C8 + 64), B.FA_E_ALIAS),
+    (dict(scales=X8), B.FA_E_ALIAS), (dict(signs=C8 + 16), B.FA_E_ALIAS),
+])
+def test_fp8_quantize_validation(lib, kw, code):
+    assert quant(**kw) == code
+
+
+Q8, K8, V8, QS, KS, VS, O8, L8, KL8 = (0x3_0000_0000 * (i + 1) for i in range(9))
+
+
+def fwd8(**kw):
+    a = dict(batch=2, heads=4, heads_kv=2, n=300, d=128, causal=1, softmax_scale=0.125,
+             q8=Q8, qs=QS, k8=K8, ks=KS, v8=V8, vs=VS, kv_len=None, o=O8, lse=L8, stream=None)
+    a.update(kw)
+    return B.fa_fwd_fp8(a["batch"], a["heads"], a["heads_kv"], a["n"], a["d"], a["causal"],
+                        a["softmax_scale"], a["q8"], a["qs"], a["k8"], a["ks"], a["v8"],
+                        a["vs"], a["kv_len"], a["o"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), B.FA_E_UNSUPPORTED), (dict(softmax_scale=float("nan")), B.FA_E_UNSUPPORTED),
+    (dict(heads_kv=3), B.FA_E_SHAPE), (dict(heads_kv=0), B.FA_E_SHAPE),
+    (dict(heads_kv=8), B.FA_E_SHAPE), (dict(n=0), B.FA_E_SHAPE),
+    (dict(n=(1 << 22) + 1), B.FA_E_SHAPE),
+    (dict(q8=None), B.FA_E_NULLPTR), (dict(vs=None), B.FA_E_NULLPTR),
+    (dict(o=None), B.FA_E_NULLPTR), (dict(lse=None), B.FA_E_NULLPTR),
+    (dict(k8=K8 + 8), B.FA_E_ALIGN), (dict(o=O8 + 4), B.FA_E_ALIGN),
+    (dict(ks=KS + 2), B.FA_E_ALIGN), (dict(kv_len=KL8 + 1), B.FA_E_ALIGN),
+    (dict(o=Q8 + 1024), B.FA_E_ALIAS), (dict(lse=O8 + 16), B.FA_E_ALIAS),
+    (dict(lse=VS), B.FA_E_ALIAS), (dict(o=KL8 - 16, kv_len=KL8), B.FA_E_ALIAS),
+])
+def test_fwd_fp8_validation(lib, kw, code):
+    assert fwd8(**kw) == code
