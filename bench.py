@@ -162,7 +162,8 @@ def load_traffic(src_hash: str, workload: str):
 
 def _short(name: str) -> str:
     for key in ("fwd_bf16_kernel", "fwd_bf16_staged_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
-                "bwd_prep_kernel", "fwd_fp32_kernel", "bwd_fp32_kernel", "copyBuffer"):
+                "bwd_prep_kernel", "fwd_fp32_kernel", "bwd_fp32_kernel", "fwd_fp8_kernel",
+                "fp8_quant_kernel", "copyBuffer"):
         if key in name:
             if key == "copyBuffer":
                 return name
@@ -454,7 +455,21 @@ def run_sweep(out_path: str | None, only=None) -> int:
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 matrix-core peak (published)
 
 
-def run_fp8(out_path: str | None, only=None) -> int:
+def calibrate_copy(mib: int, dev) -> None:
+    """Copy `mib` MiB device-to-device three times: a plain copy kernel of
+    known size, against which rocprofv3's HBM byte counters are scaled."""
+    if not mib:
+        return
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def run_fp8(out_path: str | None, only=None, copy_mib: int = 0) -> int:
     """FP8 forward timings: the three block encodings (Q, K with the Hadamard
     rotation; V transposed) and the E4M3 attention kernel, next to the bf16
     forward on the same inputs."""
@@ -471,6 +486,7 @@ def run_fp8(out_path: str | None, only=None) -> int:
         return 1
     B.lib()
     dev = torch.device("cuda:0")
+    calibrate_copy(copy_mib, dev)
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
     names = [n for n, w in WORKLOADS.items()
@@ -603,7 +619,7 @@ def main() -> int:
     if args.sweep:
         return run_sweep(args.out, args.only)
     if args.fp8:
-        return run_fp8(args.out, args.only)
+        return run_fp8(args.out, args.only, args.calibrate_copy)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the work shards by (batch, head) with no exchange; see the design notes). "
@@ -621,14 +637,7 @@ def main() -> int:
         return 1
     B.lib()  # fail loudly if the library is missing
     dev = torch.device("cuda:0")
-    if args.calibrate_copy:
-        nbytes = args.calibrate_copy << 20
-        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibrate_copy(args.calibrate_copy, dev)
     inp = make_inputs(w)
     q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
     kvl = None if inp["kv_len"] is None else inp["kv_len"].to(dev)

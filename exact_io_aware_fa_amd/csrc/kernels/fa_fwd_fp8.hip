@@ -58,12 +58,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // the 64 reduction indices (chosen by l / 32); byte k of an A lane pairs
 // with byte k of the B lane of the same half, so any assignment of
 // reduction indices to bytes works as long as A and B use it alike. Result
-// layout as mma32. With `sa`, A is scaled by 2^(sa - 127) (E8M0).
+// layout as mma32. mma_f8_s scales A by 2^(sa - 127) and B by 2^(sb - 127)
+// (E8M0 bytes, per lane: lane l's scale applies to the 32 reduction indices
+// it supplies of row / column l % 32).
 __device__ __forceinline__ f32x16 mma_f8(i32x8 a, i32x8 b, f32x16 acc) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16 mma_f8_sa(i32x8 a, i32x8 b, f32x16 acc, int sa) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, 127);
+__device__ __forceinline__ f32x16 mma_f8_s(i32x8 a, i32x8 b, f32x16 acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 }
 
 __device__ __forceinline__ float halves_max(float x) {
@@ -180,9 +182,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
   float f = kNegInf;   // integer frame of the running row max (base-2 units)
-  float lpart = 0.f;   // this half-wave's share of the row sum (in 2^(t - f + 8))
+  float fo = kNegInf;  // frame of the accumulators O~ and l: the row's first frame
+  float lpart = 0.f;   // this half-wave's share of the row sum (in 2^(t - fo + 8))
   f32x16 sc[NKB];
   i32x8 pf[NKK];
+  int sb = 127;        // E8M0 scale 2^(f - fo) of the pending P^T fragments
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) pf[kk] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
         sc[kb] = mma_f8(fr[k % (PF + 1)], qf[kd], sc[kb]);
       } else {
         const int mb = (k - NS) % NMB, kk = (k - NS) / NMB;
-        acc[mb] = mma_f8_sa(fr[k % (PF + 1)], pf[kk], acc[mb], ve);
+        acc[mb] = mma_f8_s(fr[k % (PF + 1)], pf[kk], acc[mb], ve, sb);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -294,11 +298,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
       for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sc[kb][r]);
     const float mt = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
     // New integer frame: ceil of the running max of t = s * cj (cj > 0, so
-    // -inf stays -inf).
+    // -inf stays -inf). Probabilities are rounded in this frame.
     const float fnew = fmaxf(f, ceilf(mt * cj));
-    const float fref = (fnew == kNegInf) ? 0.f : fnew;
-    const float alpha = __builtin_amdgcn_exp2f(f - fref);  // 2^k; 1 if unchanged, 0 while empty
     f = fnew;
+    const float fref = (fnew == kNegInf) ? 0.f : fnew;
     const float off = 8.f - fref;
     float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -309,26 +312,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
         sc[kb][r] = e;
         rp[r & 3] += e;
       }
-    lpart = fmaf(lpart, alpha, (rp[0] + rp[1]) + (rp[2] + rp[3]));
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+    // O~ and l stay in the row's first frame fo: this tile's contribution
+    // enters scaled by 2^(f - fo), a power of two that the P V product applies
+    // through its B-operand scale, so O~ itself is never rescaled. Only when
+    // the gap would leave the safe exponent range (scores spread over more
+    // than 2^64) is the accumulator moved to the current frame.
+    fo = (fo == kNegInf) ? fnew : fo;
+    if (__builtin_amdgcn_ballot_w64(fnew - fo > 64.f)) {
+      const float alpha = __builtin_amdgcn_exp2f(fo - fref);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+      lpart *= alpha;
+      fo = fnew;
     }
+    const int gap = (fnew == kNegInf) ? 0 : (int)(fnew - fo);
+    lpart += ldexpf((rp[0] + rp[1]) + (rp[2] + rp[3]), gap);
+    sb = 127 + gap;
     // P^T fragments: bytes 0-15 from block 2 kk, 16-31 from block 2 kk + 1,
     // four probabilities per dword (RNE to E4M3).
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const f32x16& s = sc[2 * kk + (q >> 2)];
+        const f32x16& v = sc[2 * kk + (q >> 2)];
         const int r = 4 * (q & 3);
-        uint32_t v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r], s[r + 1], 0u, false);
-        v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r + 2], s[r + 3], v, true);
-        pf[kk][q] = (int)v;
+        uint32_t w8 = __builtin_amdgcn_cvt_pk_fp8_f32(v[r], v[r + 1], 0u, false);
+        w8 = __builtin_amdgcn_cvt_pk_fp8_f32(v[r + 2], v[r + 3], w8, true);
+        pf[kk][q] = (int)w8;
       }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(pf[kk]));
-    asm volatile("" : "+v"(lpart));
+    asm volatile("" : "+v"(lpart), "+v"(sb));
   };
   auto valu_phase = [&](int j, float cj) FA_INLINE {
     if (j >= 0 && j < ntiles && j >= s_first && j <= s_last) {
@@ -337,6 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
     } else {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) pf[kk] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      sb = 127;
     }
   };
 
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
     }
   }
 
-  // Epilogue: O = O~ / l (bf16), LSE = ln 2 (f - 8 + log2 l).
+  // Epilogue: O = O~ / l (bf16), LSE = ln 2 (fo - 8 + log2 l).
   const float l = halves_sum(lpart);
   if (qi < n) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -470,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
         u[1] = pack_bf16x2(acc[mb][g * 4 + 2] * inv, acc[mb][g * 4 + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + mb * 32 + g * 8 + h * 4) = u;
       }
-    if (h == 0) p.lse[bhq * n + qi] = l > 0.f ? (f - 8.f + __log2f(l)) * kLn2 : kNegInf;
+    if (h == 0) p.lse[bhq * n + qi] = l > 0.f ? (fo - 8.f + __log2f(l)) * kLn2 : kNegInf;
   }
 }
 

@@ -358,6 +358,22 @@ def test_padded_keys_do_not_matter():
     assert not np.array_equal(a[0], c[0])
 
 
+def test_row_subsets_are_the_same_rows():
+    """Each output row depends on its own query row and the keys only, so the
+    rows= evaluation is the same definition on fewer rows."""
+    q, k, v = _inputs(20, n=400, d=64)
+    qc, qs = of.quantize(q)
+    kc, ks = of.quantize(k)
+    vc, vs = of.quantize(v)
+    full = _head(qc, qs, kc, ks, vc, vs, 400, 0.2, True, 350)
+    rows = np.array([0, 1, 127, 128, 255, 399])
+    part = of.fp8_head_forward(qc[0, 0], qs[0, 0], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0], 400,
+                               0.2, True, 350, parts=True, rows=rows)
+    np.testing.assert_array_equal(part["o"], full["o"][rows])
+    np.testing.assert_array_equal(part["lse"], full["lse"][rows])
+    np.testing.assert_array_equal(part["u"], full["u"][rows])
+
+
 def test_grouped_heads_use_their_kv_head():
     q, k, v = _inputs(18, b=1, h=4, n=140, d=64, hkv=2)
     full = of.fp8_attention_fwd(q, k, v, causal=True)
