@@ -35,10 +35,12 @@ Readings (where the page is silent):
   so that a tiled kernel, whose running frames only differ from the final
   one by powers of two, rounds every normal-range u exactly as here, in any
   tile order. The factor 2^8 is the largest power of two that keeps u <= 448.
-* The row sum is taken on the unrounded u: l_i = sum_j u_ij. Then
-  O_i = sum_j P^_ij v^_j / l_i with v^ the dequantised V rows, and
+* The row sum is taken on the rounded probabilities: l_i = sum_j P^_ij, so
+  O_i = sum_j P^_ij v^_j / l_i (v^ the dequantised V rows) is a convex
+  combination of V rows whose weights sum to exactly 1, and
   LSE_i = ln 2 * (f_i - 8 + log2 l_i), the log-sum-exp of the quantised
-  scores (the probabilities' rounding does not enter it).
+  scores up to the rounding of the probabilities (a factor within
+  1 +- 2^-4 inside the log).
 
 Masks as in ``attention``: causal (j > i hidden) and key padding
 (j >= kv_len[b] hidden); a row with no visible key gives O = 0,
@@ -182,6 +184,11 @@ def _quantize_p(u: np.ndarray) -> np.ndarray:
     return e4m3_round(u)
 
 
+def _row_sum(u: np.ndarray, pq: np.ndarray) -> np.ndarray:
+    """l_i: the sum of the row's rounded probabilities."""
+    return pq.sum(axis=1)
+
+
 def fp8_head_forward(qc, qs, kc, ks, vc, vs, n: int, scale: float, causal: bool,
                      kv_len_b: int | None = None, parts: bool = False, rows=None) -> dict:
     """Forward of one head from codes and scales (see the module docstring).
@@ -203,8 +210,9 @@ def fp8_head_forward(qc, qs, kc, ks, vc, vs, n: int, scale: float, causal: bool,
     has = np.isfinite(tmax)
     f = np.where(has, _frame(np.where(has, tmax, 0.0)), 0.0)
     u = np.where(vis, np.exp2(t - f[:, None] + P_SHIFT), 0.0)
-    l = u.sum(axis=1)
     pq = _quantize_p(u)
+    l = _row_sum(u, pq)
+    has = has & (l > 0)
     l_safe = np.where(has, l, 1.0)
     o = np.where(has[:, None], (pq @ vv) / l_safe[:, None], 0.0)
     lse = np.where(has, (f - P_SHIFT + np.log2(l_safe)) * math.log(2.0), -np.inf)

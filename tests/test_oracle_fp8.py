@@ -9,8 +9,10 @@ The oracle is checked against things other than itself:
 * scipy's Hadamard matrix, orthogonality, and the page's identity
   (Q H)(K H)^T = Q K^T;
 * brute force for the block exponent (smallest e with amax <= 448 * 2^e);
-* closed forms: equal keys give P^ / u times the mean value row; the LSE is
-  scipy's logsumexp of the dequantised scores;
+* closed forms: two groups of equal keys give the library-rounded weights'
+  average of the two groups' mean value rows; constant V gives exactly that
+  constant; the LSE lies within ln(1 + 2^-4) of scipy's logsumexp of the
+  dequantised scores;
 * the tiled online forward with running integer frames, written here
   independently (library E4M3 rounding, any tile width, either tile order),
   agrees with the one-shot definition, exactly when every probability is in
@@ -216,33 +218,54 @@ def _head(qc, qs, kc, ks, vc, vs, n, scale, causal=False, kvb=None):
                                n, scale, causal, kvb, parts=True)
 
 
-def test_equal_keys_closed_form():
-    """All keys equal: every score of a row is the same t, so u = 2^(t - ceil t
-    + 8) for every key, P^ = E4M3(u) and O = (P^ / u) * mean of the values."""
+def test_two_key_groups_closed_form():
+    """Keys equal within each of two groups: a row's scores take two values
+    t_A, t_B, so with f = ceil(max(t_A, t_B)), u = 2^(t - f + 8) and
+    P^ = E4M3(u) (library rounding) the output is
+    (n_A P^_A vbar_A + n_B P^_B vbar_B) / (n_A P^_A + n_B P^_B)."""
     rng = np.random.default_rng(10)
-    n, d = 200, 64
+    n, d, na = 200, 64, 77
     q = rng.standard_normal((1, 1, n, d))
-    k = np.repeat(rng.standard_normal((1, 1, 1, d)), n, axis=2)
+    k = np.empty((1, 1, n, d))
+    k[0, 0, :na] = rng.standard_normal(d)
+    k[0, 0, na:] = rng.standard_normal(d)
     v = rng.standard_normal((1, 1, n, d))
     qc, qs = of.quantize(q)
     kc, ks = of.quantize(k)
     vc, vs = of.quantize(v)
-    scale = 0.37
+    scale = 0.61
     r = _head(qc, qs, kc, ks, vc, vs, n, scale)
     qd = of.dequantize(qc[0, 0], qs[0, 0], n)
     kd = of.dequantize(kc[0, 0], ks[0, 0], n)
     vd = of.dequantize(vc[0, 0], vs[0, 0], n)
-    t = scale * (qd @ kd[0]) * LOG2E
-    u = 2.0 ** (t - np.ceil(t) + 8)
-    ratio = _torch_e4m3(u) / u
-    assert np.any(np.abs(ratio - 1) > 1e-3)  # the rounding of P is visible
-    np.testing.assert_allclose(r["o"], ratio[:, None] * vd.mean(axis=0)[None, :], rtol=1e-12,
-                               atol=1e-14)
-    # Largest u of a row in (128, 256]: the frame is the ceiling.
-    assert np.all((u > 128) & (u <= 256))
+    ta = scale * (qd @ kd[0]) * LOG2E
+    tb = scale * (qd @ kd[na]) * LOG2E
+    f = np.ceil(np.maximum(ta, tb))
+    pa, pb = _torch_e4m3(2.0 ** (ta - f + 8)), _torch_e4m3(2.0 ** (tb - f + 8))
+    va, vb = vd[:na].mean(axis=0), vd[na:].mean(axis=0)
+    want = (na * pa[:, None] * va + (n - na) * pb[:, None] * vb) / (na * pa + (n - na) * pb)[:, None]
+    np.testing.assert_allclose(r["o"], want, rtol=1e-12, atol=1e-14)
+    # The rounding of P is visible: unrounded weights give another result.
+    ua, ub = 2.0 ** (ta - f + 8), 2.0 ** (tb - f + 8)
+    plain = (na * ua[:, None] * va + (n - na) * ub[:, None] * vb) / (na * ua + (n - na) * ub)[:, None]
+    assert np.abs(plain - want).max() > 1e-3
+    # The larger group's u lies in (128, 256]: the frame is the ceiling.
+    top = np.maximum(2.0 ** (ta - f + 8), 2.0 ** (tb - f + 8))
+    assert np.all((top > 128) & (top <= 256))
 
 
-def test_lse_is_logsumexp_of_quantised_scores():
+def test_constant_values_give_exactly_that_value():
+    """O is a convex combination of V rows (the weights are the rounded
+    probabilities over their own sum): V = 1 everywhere gives O = 1 exactly,
+    for any scores and masks."""
+    q, k, _ = _inputs(21, n=300, d=64)
+    v = np.ones((1, 2, 300, 64))
+    for causal, kvl in ((False, None), (True, [250])):
+        o, _ = of.fp8_attention_fwd(q * 2.5, k, v, causal=causal, kv_len=kvl)
+        np.testing.assert_array_equal(o, np.ones_like(o))
+
+
+def test_lse_is_near_logsumexp_of_quantised_scores():
     q, k, v = _inputs(11, n=300, d=64)
     qc, qs = of.quantize(q)
     kc, ks = of.quantize(k)
@@ -254,7 +277,11 @@ def test_lse_is_logsumexp_of_quantised_scores():
         s = 0.125 * qd @ kd.T
         vis = oracle.visible_mask(300, causal, kvb)
         ref = scipy.special.logsumexp(np.where(vis, s, -np.inf), axis=1)
-        np.testing.assert_allclose(r["lse"], ref, rtol=0, atol=1e-12)
+        # The rounded probabilities are each within 2^-4 of the exact ones,
+        # so their sum is too: |LSE - logsumexp| <= ln(1 + 2^-4).
+        err = np.abs(r["lse"] - ref)
+        assert np.all(err <= math.log1p(2.0 ** -4) + 1e-12)
+        assert err.max() > 1e-6
 
 
 def _tiled_forward(qd, kd, vd, scale, bc, causal, kvb, reverse=False):
@@ -278,8 +305,9 @@ def _tiled_forward(qd, kd, vd, scale, bc, causal, kvb, reverse=False):
         alpha = np.where(np.isfinite(f), np.exp2(f - np.where(np.isfinite(fnew), fnew, 0)), 0.0)
         fr = np.where(np.isfinite(fnew), fnew, 0.0)
         u = np.where(vis, np.exp2(t - fr[:, None] + 8), 0.0)
-        acc = acc * alpha[:, None] + _torch_e4m3(u) @ vd[j0:j1]
-        l = l * alpha + u.sum(axis=1)
+        pq = _torch_e4m3(u)
+        acc = acc * alpha[:, None] + pq @ vd[j0:j1]
+        l = l * alpha + pq.sum(axis=1)
         f = fnew
     has = np.isfinite(f)
     o = np.where(has[:, None], acc / np.where(has, l, 1.0)[:, None], 0.0)
@@ -307,8 +335,10 @@ def test_tiled_online_forward_agrees(causal, kvb):
 
 def test_tiled_online_forward_subnormal_bound():
     """With peaky rows some u fall below 2^-6 in the final frame; a tiled run
-    may round them in a finer running frame. Each such u moves by at most
-    2^-9 (half a subnormal step on either side), so |dO| <= 2^-9 sum|v| / l."""
+    may round them in a finer running frame. Each such P^ moves by at most
+    2^-9 (half a subnormal step on either side), in the numerator and in l
+    alike, so |dO| <= 2^-9 (sum|v| + m |O|) / (l - 2^-9 m) over the m small
+    entries of the row."""
     q, k, v = _inputs(13, n=384, d=64)
     qc, qs = of.quantize(q * 3.0)
     kc, ks = of.quantize(k)
@@ -318,7 +348,9 @@ def test_tiled_online_forward_subnormal_bound():
     assert small.sum() > 1000
     qd, kd = of.dequantize(qc[0, 0], qs[0, 0], 384), of.dequantize(kc[0, 0], ks[0, 0], 384)
     vd = of.dequantize(vc[0, 0], vs[0, 0], 384)
-    bound = 2.0 ** -9 * (small.astype(float) @ np.abs(vd)) / r["l"][:, None] + 1e-12
+    m = small.sum(axis=1)[:, None]
+    bound = 2.0 ** -9 * ((small.astype(float) @ np.abs(vd)) + m * np.abs(r["o"])) / (
+        r["l"][:, None] - 2.0 ** -9 * m) + 1e-12
     for bc in (64, 128):
         o = _tiled_forward(qd, kd, vd, 0.25, bc, True, None, reverse=True)
         assert np.all(np.abs(o - r["o"]) <= bound)
@@ -338,7 +370,23 @@ def test_close_to_exact_attention(rotate):
         ref_o, ref_lse = oracle.attention_fwd(q, k, v, causal=causal, kv_len=[260, 201])
         err = np.linalg.norm(got_o - ref_o) / np.linalg.norm(ref_o)
         assert 1e-4 < err < 2.0 ** -3
-        np.testing.assert_allclose(got_lse, ref_lse, atol=0.1)
+        # logsumexp is 1-Lipschitz in the scores: |dLSE_i| <= max_j |dS_ij|
+        # + ln(1 + 2^-4) (the rounding of P inside the sum). Every encoded
+        # entry x (of Q H and K H, or Q and K) is within 2^-4 |x| + 2^-10 s
+        # of its value (s its block scale), which bounds dS_ij.
+        rot = np.eye(64) if s is None else of.rotation(s) / 8.0
+        for b in range(2):
+            for h in range(4):
+                qr, kr = q[b, h] @ rot, k[b, h // 2] @ rot
+                _, qs_ = of.quantize(q[b:b + 1, h:h + 1], s)
+                _, ks_ = of.quantize(k[b:b + 1, h // 2:h // 2 + 1], s)
+                rows = np.arange(260) // 128
+                eq = 2.0 ** -4 * np.abs(qr) + 2.0 ** -10 * qs_[0, 0][rows][:, None]
+                ek = 2.0 ** -4 * np.abs(kr) + 2.0 ** -10 * ks_[0, 0][rows][:, None]
+                ds = (eq @ np.abs(kr).T + np.abs(qr) @ ek.T + eq @ ek.T) / 8.0
+                vis = oracle.visible_mask(260, causal, [260, 201][b])
+                bound = np.where(vis, ds, 0.0).max(axis=1) + math.log1p(2.0 ** -4) + 1e-9
+                assert np.all(np.abs(got_lse[b, h] - ref_lse[b, h]) <= bound)
 
 
 def test_padded_keys_do_not_matter():
@@ -409,20 +457,23 @@ def _runs_clean(tests):
 
 
 def test_fp8_planted_mistakes_are_rejected(monkeypatch):
-    pins = [test_equal_keys_closed_form,
+    pins = [test_two_key_groups_closed_form,
             lambda: test_close_to_exact_attention(True),
             lambda: test_close_to_exact_attention(False),
             test_quantize_blocks_and_bounds,
             test_rotated_quantize_represents_x_times_h,
             test_rotation_keeps_scores,
             lambda: test_tiled_online_forward_agrees(True, None),
-            test_lse_is_logsumexp_of_quantised_scores,
+            test_lse_is_near_logsumexp_of_quantised_scores,
+            test_constant_values_give_exactly_that_value,
             test_e4m3_round_matches_library_cast]
     assert _runs_clean(pins)
     good_round, good_exp = of.e4m3_round, of.block_exponent
     good_frame, good_rot, good_deq = of._frame, of.rotation, of.dequantize
+    good_sum = of._row_sum
     mistakes = {
         "P not rounded": ("_quantize_p", lambda u: u),
+        "row sum of the unrounded u": ("_row_sum", lambda u, pq: u.sum(axis=1)),
         "floor frame (u up to 512 saturates)": ("_frame", np.floor),
         "frame one too low": ("_frame", lambda t: good_frame(t) - 1),
         "block exponent one too high": ("block_exponent", lambda a: good_exp(a) + 1),
@@ -445,4 +496,5 @@ def test_fp8_planted_mistakes_are_rejected(monkeypatch):
         monkeypatch.setattr(of, "e4m3_round", good_round)
         monkeypatch.setattr(of, "rotation", good_rot)
         monkeypatch.setattr(of, "dequantize", good_deq)
+        monkeypatch.setattr(of, "_row_sum", good_sum)
     assert _runs_clean(pins)
