@@ -14,8 +14,9 @@
 //   range), whatever the tile order;
 // * probabilities enter the P V product as E4M3(2^(t - f + 8)), in (0, 256]:
 //   the factor 2^8 moves the largest probabilities of a row to the top of the
-//   format's normal range (<= 448); l sums the unrounded values and the 2^8
-//   cancels in O = O~ / l.
+//   format's normal range (<= 448); l is the sum of the rounded values, so
+//   O = O~ / l weights the V rows by exactly the probabilities the product
+//   used, and the 2^8 cancels.
 //
 // Operands (written by the quantiser kernel):
 // * Q, K codes row-major [rows][128] bytes; the scores of a tile are
@@ -72,11 +73,6 @@ __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Key row read by A lane c of a 32-key block (see the header).
@@ -181,9 +177,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   f32x16 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+  // Row sums l = sum_j P^_j on the matrix cores: the product of an all-ones
+  // A operand with the P^T fragments gives every row of this block the sum
+  // over the tile's keys (both reduction halves), in the same frame as O~.
+  f32x16 accl = f32x16{};
   float f = kNegInf;   // integer frame of the running row max (base-2 units)
   float fo = kNegInf;  // frame of the accumulators O~ and l: the row's first frame
-  float lpart = 0.f;   // this half-wave's share of the row sum (in 2^(t - fo + 8))
   f32x16 sc[NKB];
   i32x8 pf[NKK];
   int sb = 127;        // E8M0 scale 2^(f - fo) of the pending P^T fragments
@@ -270,10 +269,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    constexpr int kOnes = 0x38383838;  // four E4M3 1.0
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      accl = mma_f8_s(i32x8{kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes}, pf[kk],
+                      accl, 127, sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // Keep the products in this half-period: otherwise the compiler sinks
     // the O^T products past the next barrier, next to their first use.
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(acc[mb]));
+    asm volatile("" : "+v"(accl));
   };
 
   // Softmax phase of tile j with exp2 factor cj.
@@ -303,31 +310,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
     f = fnew;
     const float fref = (fnew == kNegInf) ? 0.f : fnew;
     const float off = 8.f - fref;
-    float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], cj, off));
-        sc[kb][r] = e;
-        rp[r & 3] += e;
-      }
+      for (int r = 0; r < 16; ++r) sc[kb][r] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], cj, off));
     // O~ and l stay in the row's first frame fo: this tile's contribution
-    // enters scaled by 2^(f - fo), a power of two that the P V product applies
-    // through its B-operand scale, so O~ itself is never rescaled. Only when
-    // the gap would leave the safe exponent range (scores spread over more
-    // than 2^64) is the accumulator moved to the current frame.
+    // enters scaled by 2^(f - fo), a power of two that the P V product (and
+    // the row-sum product) applies through its B-operand scale, so the
+    // accumulators are never rescaled. Only when the gap would leave the
+    // safe exponent range (scores spread over more than 2^64) are they moved
+    // to the current frame.
     fo = (fo == kNegInf) ? fnew : fo;
     if (__builtin_amdgcn_ballot_w64(fnew - fo > 64.f)) {
       const float alpha = __builtin_amdgcn_exp2f(fo - fref);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
-      lpart *= alpha;
+      accl *= alpha;
       fo = fnew;
     }
-    const int gap = (fnew == kNegInf) ? 0 : (int)(fnew - fo);
-    lpart += ldexpf((rp[0] + rp[1]) + (rp[2] + rp[3]), gap);
-    sb = 127 + gap;
+    sb = 127 + ((fnew == kNegInf) ? 0 : (int)(fnew - fo));
     // P^T fragments: bytes 0-15 from block 2 kk, 16-31 from block 2 kk + 1,
     // four probabilities per dword (RNE to E4M3).
 #pragma unroll
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
       }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(pf[kk]));
-    asm volatile("" : "+v"(lpart), "+v"(sb));
+    asm volatile("" : "+v"(sb));
   };
   auto valu_phase = [&](int j, float cj) FA_INLINE {
     if (j >= 0 && j < ntiles && j >= s_first && j <= s_last) {
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   }
 
   // Epilogue: O = O~ / l (bf16), LSE = ln 2 (fo - 8 + log2 l).
-  const float l = halves_sum(lpart);
+  const float l = accl[0];
   if (qi < n) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16* orow = O + (size_t)qi * D;

@@ -22,10 +22,11 @@ and fp32 rounding). Where E4M3(u (1 - delta)) != E4M3(u (1 + delta)) the
 GPU may legitimately round u to the neighbouring code: that element may move
 O_i by the code step times |v_j| / l_i. Probabilities below 2^-5 of the row
 frame may be rounded in a finer running frame (or the frame itself may
-differ by one): at most 2^-9 each. The row sum l (fp32, unrounded u) is off
-by at most sum_j u_ij delta_ij relative, which scales all of O_i, and the
-O product itself by eps * sum_j P^_ij |v_j|. On top: the bf16 rounding of O
-(2^-9 relative; 2^-8 is allowed) and 1e-5 absolute.
+differ by one): at most 2^-9 each. The row sum l is the sum of the same
+rounded values (taken on the matrix cores): it moves by those steps and by
+eps * l, and the O product by eps * sum_j P^_ij |v_j|; with numerator error
+a and row-sum error b, |dO_i| <= (a + |O_i| b) / (l_i - b). On top: the
+bf16 rounding of O (2^-9 relative; 2^-8 is allowed) and 1e-5 absolute.
 
 That envelope holds for any accumulation order the hardware may use, so it
 is wide (often a tenth of |O|). Each head must also meet a normwise bound,
@@ -80,7 +81,8 @@ def _dev(a):
 
 def _allowance(parts):
     """Per-element bound on |O_gpu - O_oracle| beyond bf16 rounding (see the
-    module docstring) and the relative bound on l."""
+    module docstring): the numerator's error over l, and the row sum's
+    relative error."""
     vis, u, l, vv = parts["vis"], parts["u"], parts["l"], parts["vv"]
     t = np.where(vis, parts["t"], 0.0)
     dt = EPS_MMA * parts["tabs"] + 2.0 ** -22 * np.abs(t)
@@ -92,7 +94,7 @@ def _allowance(parts):
     ls = np.where(has, l, 1.0)
     av = np.abs(vv)
     num = (band @ av + EPS_MMA * (parts["pq"] @ av)) / ls[:, None]
-    l_rel = np.where(has, (np.where(vis, u * delta, 0.0)).sum(axis=1) / ls, 0.0)
+    l_rel = np.where(has, band.sum(axis=1) / ls + EPS_MMA, 0.0)
     return num, l_rel
 
 
@@ -102,7 +104,8 @@ def _check_head(o_gpu, lse_gpu, qc, qs, kc, ks, vc, vs, n, scale, causal, kvb, r
     num, l_rel = _allowance(r)
     ref = r["o"]
     got = o_gpu.astype(np.float64)
-    tol = (2.0 ** -8 + l_rel[:, None]) * np.abs(ref) + num * (1 + l_rel[:, None]) + 1e-5
+    lr = np.minimum(l_rel, 0.5)[:, None]
+    tol = 2.0 ** -8 * np.abs(ref) + (num + np.abs(ref) * lr) / (1 - lr) + 1e-5
     err = np.abs(got - ref)
     bad = err > tol
     assert not bad.any(), (f"{bad.sum()} elements out of tolerance; worst excess "
@@ -261,7 +264,11 @@ def test_end_to_end_against_oracle(rotate):
                                   signs=None if signs is None else signs.astype(np.float64))
     err = np.linalg.norm(o - ro) / np.linalg.norm(ro)
     assert err < 4e-3, err
-    np.testing.assert_allclose(lse, rl, atol=2e-3, rtol=0)
+    # LSE: one neighbouring-code rounding of a row's dominant probability
+    # moves it by at most ln(1 + 2^-4); such roundings are rare, so the mean
+    # deviation stays small.
+    dl = np.abs(lse - rl)
+    assert dl.max() <= math.log1p(2.0 ** -4) and dl.mean() < 1e-3, (dl.max(), dl.mean())
 
 
 # --------------------------------------------------------------------------
