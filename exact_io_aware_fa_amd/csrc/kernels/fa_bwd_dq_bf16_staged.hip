@@ -21,7 +21,11 @@ constexpr int kThreads = 256;
 constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
 
 template <int D, int BC, bool CAUSAL, bool SPARSE, bool WIN>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_staged_kernel(Params p) {
+// One workgroup per CU (one wave per SIMD): the dQ accumulator and the Q
+// and dO fragments then fit the 512 registers of a lone wave (with AGPRs);
+// at two per CU they spilled 150-700 registers per lane, which cost more
+// than the halved occupancy (d = 256 backward 340 -> 490 TFLOP/s).
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_staged_kernel(Params p) {
   constexpr int KSTR = D + 8;    // row-major K / V tiles (bf16 elements)
   constexpr int TSTR = BC + 4;   // transposed K tile [d][key]
   constexpr int ND = D / 16;
