@@ -255,6 +255,12 @@ def comp_bytes(w) -> tuple[float, float]:
 
 def _gpu_clocks() -> str:
     import subprocess
+    # Under a profiler that preloads its library into every process, the
+    # rocm-smi child (a script started through env) would initialise the GPU
+    # and then exec its interpreter; clocks are not needed there.
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(
+            k.startswith("ROCPROF") for k in os.environ):
+        return "not queried under the profiler"
     try:
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
     except (OSError, subprocess.SubprocessError) as exc:
