@@ -44,8 +44,8 @@ also timed cold: a 512 MB buffer is written between calls.
 
     python bench.py --fp8 [--out FILE] [--only PREFIX ...] [--calibrate-copy MIB]
 
-times the FP8 forward on every d = 128 padded workload without a window or
-block mask: the three block encodings (fa_fp8_quantize for Q and K with the
+times the FP8 forward on every d = 64 or 128 padded workload without a
+window or block mask: the three block encodings (fa_fp8_quantize for Q and K with the
 Hadamard rotation, for V in the transposed layout), fa_fwd_fp8 on the codes,
 and the bf16 fa_fwd on the same inputs, with the same iteration rule; it
 reports TFLOP/s against the fp8 dense peak (5.0 PFLOP/s) and the speed-up
@@ -152,6 +152,49 @@ def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
                    f"(materialised S, P, dP, dS; no causal skipping), "
                    f"{per_head:.2f} s per head; FLOPs counted as for the GPU"),
     }
+
+
+def cpu_baseline_fp8(w, inp, signs, budget_s: float = 10.0, rows: int = 1024) -> dict:
+    """Time the FP8 oracle (fp64 NumPy) on one head after another until
+    ~budget_s: the encoding of the head's Q, K, V, then the forward on codes
+    for `rows` evenly spaced query rows (the oracle's row subset). FLOPs:
+    4 d per visible (query, key) pair of the sampled rows, as for the GPU."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import fp8 as of
+    from oracle.attention import visible_mask
+
+    group = w.heads // w.kv_heads
+    spent, flops, done = 0.0, 0.0, 0
+    sg = signs.cpu().numpy().astype(np.float64)
+    sel = np.linspace(0, w.n - 1, min(rows, w.n)).astype(np.int64)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            q = inp["q"][b:b + 1, h:h + 1].float().double().numpy()
+            k = inp["k"][b:b + 1, h // group:h // group + 1].float().double().numpy()
+            v = inp["v"][b:b + 1, h // group:h // group + 1].float().double().numpy()
+            kv = None if inp["kv_len"] is None else int(inp["kv_len"][b])
+            t0 = time.perf_counter()
+            qc, qs = of.quantize(q, sg)
+            kc, ks = of.quantize(k, sg)
+            vc, vs = of.quantize(v)
+            of.fp8_head_forward(qc[0, 0], qs[0, 0], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0], w.n,
+                                w.softmax_scale, w.causal, kv, rows=sel)
+            spent += time.perf_counter() - t0
+            flops += 4.0 * w.d * visible_mask(w.n, w.causal, kv, sel).sum()
+            done += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} head(s): encode Q, K, V of the head, then the forward of "
+                      f"{len(sel)} evenly spaced query rows against all keys, fp64 NumPy, "
+                      f"{spent / done:.2f} s per head"}
 
 
 def load_traffic(src_hash: str, workload: str):
@@ -512,12 +555,14 @@ def run_fp8(out_path: str | None, only=None, copy_mib: int = 0) -> int:
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
     names = [n for n, w in WORKLOADS.items()
-             if w.d == 128 and w.window == (-1, -1) and w.blocks is None and w.dtype == "bf16"]
+             if w.d in (64, 128) and w.window == (-1, -1) and w.blocks is None
+             and w.dtype == "bf16"]
     if only:
         names = [n for n in names if any(n.startswith(o) for o in only)]
     ev = [hip.create() for _ in range(4)]
     clocks_before = _gpu_clocks()
     rows = []
+    cpu = None  # (workload, CPU oracle timing) for the long causal workload
     for name in names:
         w = WORKLOADS[name]
         inp = make_inputs(w, with_grad_out=False)
@@ -571,6 +616,8 @@ def run_fp8(out_path: str | None, only=None, copy_mib: int = 0) -> int:
             spent += tq[-1] + ta[-1] + tb[-1]
         mq, ma, mb = statistics.median(tq), statistics.median(ta), statistics.median(tb)
         ff = w.flops_fwd()
+        if cpu is None and name.startswith("long_causal"):
+            cpu = (name, cpu_baseline_fp8(w, inp, signs))
         rows.append((name, mq, ma, min(ta), ff / ma / 1e9, ff / (ma + mq) / 1e9, mb,
                      ff / mb / 1e9))
         print(json.dumps({"workload": name, "fp8_quantize_ms": round(mq, 4),
@@ -597,6 +644,9 @@ def run_fp8(out_path: str | None, only=None, copy_mib: int = 0) -> int:
         lines.append("| %s | %.4f | %.4f (%.4f) | %.1f | %.1f | %.1f | %.4f | %.1f | %.2fx |"
                      % (r[0], r[1], r[2], r[3], r[4], 100 * r[4] / PEAK_FP8_TFLOPS, r[5], r[6],
                         r[7], r[6] / r[2]))
+    if cpu is not None:
+        lines += ["", "CPU oracle beside it (%s): %.4f TFLOP/s on %d threads; %s." % (
+            cpu[0], cpu[1]["value"], cpu[1]["cores"], cpu[1]["sample"])]
     text = "\n".join(lines) + "\n"
     if out_path:
         with open(out_path, "w") as f:
@@ -629,7 +679,7 @@ def main() -> int:
                     help="time fwd and bwd on every sweep workload and print a table")
     ap.add_argument("--fp8", action="store_true",
                     help="time the FP8 forward (encode + E4M3 attention) against the bf16 "
-                         "forward on the d=128 workloads and print a table")
+                         "forward on the d=64 and d=128 workloads and print a table")
     ap.add_argument("--out", default=None, help="with --sweep / --fp8: also write the table here")
     ap.add_argument("--only", nargs="*", default=None, metavar="PREFIX",
                     help="with --sweep: only the workloads whose names start so")

@@ -320,7 +320,7 @@ fa_status fa_fwd_fp8(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, 
                      void* stream) {
   fa_status st = check_fp8_shape(batch, heads, heads_kv, n);
   if (st != FA_OK) return st;
-  if (d != 128) return FA_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return FA_E_UNSUPPORTED;
   if (n * d * 2 >= (int64_t(1) << 31)) return FA_E_SHAPE;
   if (!q8 || !q_scales || !k8 || !k_scales || !v8 || !v_scales || !o || !lse)

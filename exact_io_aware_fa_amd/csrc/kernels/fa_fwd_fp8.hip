@@ -1,5 +1,5 @@
 // Attention forward on FP8 (E4M3) operands with fp32 accumulation, for
-// gfx950 (d = 128).
+// gfx950 (d = 64 and 128).
 //
 // Method: page 2 ("4. FlashAttention 深度剖析"), 4.5.4 (FP8 support): both
 // products of the forward take E4M3 operands, every block carries the scale
@@ -19,10 +19,10 @@
 //   used, and the 2^8 cancels.
 //
 // Operands (written by the quantiser kernel):
-// * Q, K codes row-major [rows][128] bytes; the scores of a tile are
+// * Q, K codes row-major [rows][d] bytes; the scores of a tile are
 //   (Q K^T codes) * sigma_q * sigma_k, the two block scales folded into the
 //   exp2 factor (c_j = |scale| log2(e) sigma_q sigma_k,j);
-// * V codes stored per 128-key block transposed ([128 channels][128 keys]);
+// * V codes stored per 128-key block transposed ([d channels][128 keys]);
 //   the V block scale is a power of two and enters the P V product through
 //   the matrix core's own E8M0 operand scale, so O~ needs no rescale when
 //   the V block changes.
@@ -50,7 +50,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kBR = 256;  // query rows per workgroup (8 waves x 32)
-constexpr int kD = 128;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -79,12 +78,16 @@ __device__ __forceinline__ float halves_max(float x) {
 __device__ __forceinline__ int key_of_lane(int c) {
   return 16 * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
 }
-// XOR swizzles of the 16-byte chunk index. K rows (128 bytes): the 16
-// lanes of a read phase touch rows {0..7, 16..23} (or {8..15, 24..31}) of a
-// block at one logical chunk; the swizzle is a bijection on each parity
-// class of those rows, so they hit 16 different bank groups. V^T rows
-// (BC bytes): 16 consecutive rows at one logical chunk.
-__device__ __forceinline__ int swz_k(int row) { return ((row >> 1) & 3) | ((row >> 2) & 4); }
+// XOR swizzles of the 16-byte chunk index. K rows (d bytes): the 16 lanes
+// of a read phase touch rows {0..7, 16..23} (or {8..15, 24..31}) of a block
+// at one logical chunk; rows that share bank groups (same parity for
+// 128-byte rows, same row % 4 for 64-byte rows) must land on different
+// chunks, which these swizzles do. V^T rows (BC bytes): 16 consecutive rows
+// at one logical chunk.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (((row >> 1) & 3) | ((row >> 2) & 4)) : (((row >> 2) & 1) | ((row >> 3) & 2));
+}
 template <int BC>
 __device__ __forceinline__ int swz_v(int row) {
   return BC == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
@@ -99,9 +102,10 @@ __device__ __forceinline__ float vload_uniform(const float* a, int i) {
   return a[i + z];
 }
 
-template <int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
-  constexpr int D = kD;
+  constexpr int NQF = D / 64;            // 64-channel halves of a score product
+  constexpr int CPR = D / 16;            // 16-byte chunks per K row
   constexpr int TILEB = BC * D;          // bytes of a K or V^T tile
   constexpr int NW = kThreads / 64;      // waves per workgroup
   constexpr int LPW = TILEB / 1024 / NW;  // 1 KB loads per tensor per wave
@@ -113,6 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   constexpr int NMB = D / 32;            // 32-channel blocks of O^T
   static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "tile split");
   static_assert(BC == 64 || BC == 128, "tile width");
+  static_assert(D == 64 || D == 128, "head dim");
 
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILEB];
@@ -150,12 +155,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   // Q codes of this wave's rows as B fragments: lane (c, h) holds bytes
   // 64 kd + 32 h .. + 31 of row qi. A negative scale negates the codes
   // (sign bit, exact); rows past n are zero.
-  i32x8 qf[2];
+  i32x8 qf[NQF];
   {
     const uint32_t flip = p.q_neg ? 0x80808080u : 0u;
     const int qr = min(qi, n - 1);
 #pragma unroll
-    for (int kd = 0; kd < 2; ++kd) {
+    for (int kd = 0; kd < NQF; ++kd) {
       const uint8_t* src = Q8 + (size_t)qr * D + kd * 64 + h * 32;
       const u32x4 lo = ld16(src) ^ flip, hi = ld16(src + 16) ^ flip;
       const bool in = qi < n;
@@ -191,12 +196,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
 
   // DMA offsets (tile-invariant). K: lane l of load i writes physical chunk
   // l % 8 of row (w LPW + i) 8 + l / 8, fetching logical chunk
-  // (l % 8) ^ swz_k(row). V^T: row (w LPW + i) VRPL + l / VCH, chunk l % VCH.
+  // (l % CPR) ^ swz_k(row). V^T: row (w LPW + i) VRPL + l / VCH, chunk l % VCH.
   int ld_koff[LPW], ld_voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int kr = (w * LPW + i) * KRPL + lane / 8;
-    ld_koff[i] = kr * D + (((lane & 7) ^ swz_k(kr)) << 4);
+    const int kr = (w * LPW + i) * KRPL + lane / CPR;
+    ld_koff[i] = kr * D + (((lane % CPR) ^ swz_k<D>(kr)) << 4);
     const int vr = (w * LPW + i) * VRPL + lane / VCH;
     ld_voff[i] = vr * 128 + (((lane % VCH) ^ swz_v<BC>(vr)) << 4);
   }
@@ -216,13 +221,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   // Operand read offsets (tile-invariant): K row key_of_lane(c) of each
   // 32-key block, logical chunks 4 kd + 2 h + {0, 1}; V^T row c of each
   // 32-channel block, logical chunks 4 kk + h and 4 kk + 2 + h.
-  int koff[2][2], voff[NKK][2];
+  int koff[NQF][2], voff[NKK][2];
   {
     const int kr = key_of_lane(c);
 #pragma unroll
-    for (int kd = 0; kd < 2; ++kd)
+    for (int kd = 0; kd < NQF; ++kd)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) koff[kd][e] = kr * D + (((4 * kd + 2 * h + e) ^ swz_k(kr)) << 4);
+      for (int e = 0; e < 2; ++e)
+        koff[kd][e] = kr * D + (((4 * kd + 2 * h + e) ^ swz_k<D>(kr)) << 4);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
 
   // Matrix phase: S^T slots (NKB blocks x 2 halves of d), then O^T slots
   // (NMB channel blocks x NKK key chunks), operands read PF slots ahead.
-  constexpr int NS = NKB * 2;
+  constexpr int NS = NKB * NQF;
   constexpr int NPV = NMB * NKK;
   constexpr int PF = 3;
   auto rd = [&](const uint8_t* sk, const uint8_t* sv, int k) FA_INLINE {
@@ -490,10 +496,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s) {
-  if (d != kD) return hipErrorInvalidValue;
+template <int D>
+hipError_t launch_d(const Fp8Params& p, hipStream_t s) {
   const int t_r = (p.n + kBR - 1) / kBR;
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(kThreads);
@@ -501,10 +505,20 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s) {
   // exchange, frame update) for the same matrix work.
   constexpr int BC = 128;
   if (p.causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<BC, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, BC, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<BC, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, BC, false>), grid, block, 0, s, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_d<64>(p, s);
+    case 128: return launch_d<128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fa

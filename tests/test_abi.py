@@ -300,7 +300,8 @@ def fwd8(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=64), B.FA_E_UNSUPPORTED), (dict(softmax_scale=float("nan")), B.FA_E_UNSUPPORTED),
+    (dict(d=256), B.FA_E_UNSUPPORTED), (dict(d=96), B.FA_E_UNSUPPORTED),
+    (dict(softmax_scale=float("nan")), B.FA_E_UNSUPPORTED),
     (dict(heads_kv=3), B.FA_E_SHAPE), (dict(heads_kv=0), B.FA_E_SHAPE),
     (dict(heads_kv=8), B.FA_E_SHAPE), (dict(n=0), B.FA_E_SHAPE),
     (dict(n=(1 << 22) + 1), B.FA_E_SHAPE),

@@ -180,16 +180,20 @@ def test_quantize_matches_oracle(batch, heads, n, d, layout, rotate):
 # --------------------------------------------------------------------------
 
 FWD = [
-    # (batch, heads, heads_kv, n, causal, padded, qk_sigma, scale)
-    (2, 4, 2, 300, True, False, 1.0, None),
-    (2, 4, 2, 300, False, True, 1.0, None),
-    (1, 2, 2, 1000, True, False, 3.0, None),     # peaky rows: frames move
-    (1, 2, 1, 1000, False, False, 1.0, None),    # multi-query
-    (2, 2, 2, 257, True, True, 1.0, -0.07),      # negative scale
-    (1, 2, 2, 200, False, False, 1.0, 0.0),      # zero scale: uniform weights
-    (1, 1, 1, 1, True, False, 1.0, None),
-    (1, 2, 2, 64, False, False, 1.0, None),
-    (1, 2, 2, 513, True, False, 2.0, None),
+    # (batch, heads, heads_kv, n, causal, padded, qk_sigma, scale, d)
+    (2, 4, 2, 300, True, False, 1.0, None, 128),
+    (2, 4, 2, 300, False, True, 1.0, None, 128),
+    (1, 2, 2, 1000, True, False, 3.0, None, 128),     # peaky rows: frames move
+    (1, 2, 1, 1000, False, False, 1.0, None, 128),    # multi-query
+    (2, 2, 2, 257, True, True, 1.0, -0.07, 128),      # negative scale
+    (1, 2, 2, 200, False, False, 1.0, 0.0, 128),      # zero scale: uniform weights
+    (1, 1, 1, 1, True, False, 1.0, None, 128),
+    (1, 2, 2, 64, False, False, 1.0, None, 128),
+    (1, 2, 2, 513, True, False, 2.0, None, 128),
+    (2, 4, 2, 300, True, True, 1.0, None, 64),
+    (1, 2, 1, 1000, False, False, 3.0, None, 64),     # peaky, multi-query
+    (1, 2, 2, 129, True, False, 1.0, -0.2, 64),
+    (1, 1, 1, 1, False, False, 1.0, None, 64),
 ]
 
 
@@ -204,12 +208,12 @@ def _run_codes(q, k, v, n, causal, scale, kv_len, signs=None):
     return (qc, qs, kc, ks, vc, vs), o.float().cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("batch,heads,heads_kv,n,causal,padded,sigma,scale", FWD)
-def test_forward_on_oracle_codes(batch, heads, heads_kv, n, causal, padded, sigma, scale):
-    w = custom(f"fp8_b{batch}_h{heads}_kv{heads_kv}_n{n}", batch, heads, n, 128, "bf16", causal,
-               seed=n * 13 + heads, qk_sigma=sigma, padded=padded, heads_kv=heads_kv)
+@pytest.mark.parametrize("batch,heads,heads_kv,n,causal,padded,sigma,scale,d", FWD)
+def test_forward_on_oracle_codes(batch, heads, heads_kv, n, causal, padded, sigma, scale, d):
+    w = custom(f"fp8_b{batch}_h{heads}_kv{heads_kv}_n{n}", batch, heads, n, d, "bf16", causal,
+               seed=n * 13 + heads + d, qk_sigma=sigma, padded=padded, heads_kv=heads_kv)
     inp = make_inputs(w, with_grad_out=False)
-    print(f"[fp8] forward b={batch} h={heads} kv={heads_kv} n={n} causal={causal} "
+    print(f"[fp8] forward b={batch} h={heads} kv={heads_kv} n={n} d={d} causal={causal} "
           f"padded={padded} sigma={sigma} scale={scale}", flush=True)
     sc = w.softmax_scale if scale is None else scale
     (qc, qs, kc, ks, vc, vs), o, lse = _run_codes(inp["q"], inp["k"], inp["v"], n, causal, sc,
@@ -237,12 +241,12 @@ def test_rotated_codes_forward():
 # The whole recipe
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("rotate", [False, True])
-def test_end_to_end_against_oracle(rotate):
-    w = custom("fp8_e2e", 2, 4, 600, 128, "bf16", True, seed=91, padded=True, heads_kv=2)
+@pytest.mark.parametrize("rotate,d", [(False, 128), (True, 128), (False, 64), (True, 64)])
+def test_end_to_end_against_oracle(rotate, d):
+    w = custom("fp8_e2e", 2, 4, 600, d, "bf16", True, seed=91 + d, padded=True, heads_kv=2)
     inp = make_inputs(w, with_grad_out=False)
-    signs = _signs(128, 9) if rotate else None
-    print(f"[fp8] end to end rotate={rotate}", flush=True)
+    signs = _signs(d, 9) if rotate else None
+    print(f"[fp8] end to end rotate={rotate} d={d}", flush=True)
     o, lse = fa.flash_attn_fp8_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), True,
                                    kv_len=inp["kv_len"].cuda(),
                                    signs=None if signs is None else _dev(signs))
@@ -307,9 +311,9 @@ def test_fp8_rejects_unsupported_head_dim():
     x = torch.zeros(1, 1, 64, 256, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError, match="FA_E_UNSUPPORTED"):
         fa.fp8_quantize(x)
-    q8 = torch.zeros(1, 1, 128, 64, dtype=torch.uint8, device="cuda")
+    q8 = torch.zeros(1, 1, 128, 256, dtype=torch.uint8, device="cuda")
     s = torch.ones(1, 1, 1, device="cuda")
-    v8 = torch.zeros(1, 1, 1, 64, 128, dtype=torch.uint8, device="cuda")
+    v8 = torch.zeros(1, 1, 1, 256, 128, dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError, match="FA_E_UNSUPPORTED"):
         fa.flash_attn_fp8_fwd_codes(q8, s, q8, s, v8, s, 100)
     assert B.ABI_VERSION == B.fa_abi_version()
