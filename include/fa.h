@@ -377,8 +377,9 @@ size_t fa_fp8_scales_bytes(int64_t batch, int64_t heads, int64_t n);
  * negative value counts as -1), 16-byte aligned; a rotation with the
  * FA_FP8_VT layout returns FA_E_UNSUPPORTED (V is not rotated). Outputs
  * must not overlap x, signs or each other. Sizes as for fa_fwd; x, codes
- * 16-byte aligned, scales 4-byte aligned. Blocks whose largest magnitude
- * lies below 2^-100 or above 2^120 are outside the supported range.
+ * 16-byte aligned, scales 4-byte aligned. x must be finite; blocks whose
+ * largest magnitude lies below 2^-100 or above 2^120 are outside the
+ * supported range.
  */
 fa_status fa_fp8_quantize(int64_t batch, int64_t heads, int64_t n, int64_t d,
                           int layout, const void* x, const int8_t* signs,
