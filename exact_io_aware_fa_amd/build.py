@@ -79,7 +79,10 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     objs = [o for o, _ in results]
     logs = "".join(l for _, l in results)
     tmp = LIB_PATH + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # --no-undefined: a kernel whose host stub failed to compile must stop the
+    # build, not surface as an unresolved symbol when the library is loaded.
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+           "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")

@@ -26,13 +26,18 @@
 //   straight into LDS through buffer descriptors, row-major with one XOR
 //   swizzle that makes both the row reads (A operands of S and dP) and the
 //   transposing reads (A operands of dV^T and dK^T, ds_read_b64_tr_b16)
-//   conflict-free. Three stages: tile i+2 streams in while tile i+1 is read
+//   conflict-free. Four stages: tile i+2 streams in while tile i+1 is read
 //   row-wise and tile i transposed; one barrier per tile.
 // * Software pipeline: iteration i computes S and dP of tile i+1 on the
 //   matrix cores while the vector units turn S and dP of tile i into P and
 //   dS, then accumulates dV and dK of tile i. With one wave per SIMD (the
 //   accumulators and K/V fragments need more than half the register file)
 //   the overlap has to come from within the wave.
+// * The S and dP products write ordinary VGPRs (mma32_v below), and the
+//   results of consecutive tiles alternate between two register sets (the
+//   loop is unrolled by four, the period of both the stages and the sets):
+//   the vector units read them where they land, with no copy out of the
+//   accumulation registers that the dK, dV products use.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -43,6 +48,35 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
+
+// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs. The compiler
+// selects the AGPR form for every matrix builtin of a kernel that may use
+// more than 256 registers per lane, after which the vector units could only
+// read S and dP through one v_accvgpr_read per value. Written as assembly,
+// the product is invisible to the compiler's hazard tracking; it is safe
+// here because every result is first read, and its registers first
+// reused, by code of the next pipeline step (hundreds of instructions and
+// 16 products later, beyond any required wait states; the step keeps its
+// results live to its end, see body), and each accumulation chain
+// alternates with another, so two products of one chain are never
+// adjacent. mma32_v0 starts a chain (C = 0).
+// The result may not overlap the A or B registers (the product still reads
+// them while it writes), hence the early-clobber output of mma32_v0; in
+// mma32_v the accumulator is live on entry, so it cannot share them either.
+__device__ __forceinline__ f32x16 mma32_v(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+// An empty use of two results in VGPRs (keeps them, and their registers,
+// live up to this point).
+__device__ __forceinline__ void keep_live(const f32x16& x, const f32x16& y) {
+  asm volatile("" ::"v"(x), "v"(y));
+}
+__device__ __forceinline__ f32x16 mma32_v0(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
 
 template <int D, int NQB, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
@@ -66,9 +100,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) bf16 sm0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) bf16 sm1[2 * TILE];
   __shared__ __attribute__((aligned(1024))) bf16 sm2[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 sm3[2 * TILE];
   __shared__ __attribute__((aligned(16))) float sv0[2 * BQ];
   __shared__ __attribute__((aligned(16))) float sv1[2 * BQ];
   __shared__ __attribute__((aligned(16))) float sv2[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float sv3[2 * BQ];
   __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
@@ -136,6 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         *reinterpret_cast<u32x4*>(sm0 + e) = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(sm1 + e) = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(sm2 + e) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm3 + e) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();  // the zeros land before any wave's tile loads
     }
@@ -219,12 +256,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       auto sdp = [&](const bf16* sm, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) FA_INLINE {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          s[qb] = f32x16{};
-          g[qb] = f32x16{};
+          s[qb] = mma32_v0(as_bf16x8(ld16(sm + qb * 32 * D + qoff[0])), kf[0]);
+          g[qb] = mma32_v0(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[0])), vf[0]);
 #pragma unroll
-          for (int kd = 0; kd < ND; ++kd) {
-            s[qb] = mma32(as_bf16x8(ld16(sm + qb * 32 * D + qoff[kd])), kf[kd], s[qb]);
-            g[qb] = mma32(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[kd])), vf[kd], g[qb]);
+          for (int kd = 1; kd < ND; ++kd) {
+            s[qb] = mma32_v(as_bf16x8(ld16(sm + qb * 32 * D + qoff[kd])), kf[kd], s[qb]);
+            g[qb] = mma32_v(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[kd])), vf[kd], g[qb]);
           }
         }
       };
@@ -259,16 +296,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
       // One query tile, software-pipelined and issued in a fixed order (the
       // sched_barrier fences pin it): phase 1 computes S and dP of tile it+1
-      // (stage mB, row reads two products ahead) while the vector units turn
-      // S and dP of tile it (in s, g; L and D in vA) into P and dS, 16/ND
-      // values per product pair; phase 2 accumulates dV^T and dK^T of tile it
-      // from stage mA (transposing reads one pair ahead).
+      // (stage mB, row reads two products ahead) into sn, gn while the vector
+      // units turn S and dP of tile it (in s, g; L and D in vA) into P and
+      // dS, 16/ND values per product pair; phase 2 accumulates dV^T and dK^T
+      // of tile it from stage mA (transposing reads one pair ahead). The
+      // next step takes sn, gn as its s, g.
       constexpr int NS = NQB * ND;        // phase-1 slots (2 products each)
       constexpr int EPS = 16 / ND;        // P/dS values per phase-1 slot
       constexpr int NP = NQB * 2 * NMB;   // phase-2 slots (2 products each)
-      f32x16 s[NQB], g[NQB];
+      f32x16 sa[NQB], ga[NQB], sb[NQB], gb[NQB];
       auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB,
-                      auto mask_tag) FA_INLINE {
+                      f32x16 (&s)[NQB], f32x16 (&g)[NQB], f32x16 (&sn)[NQB],
+                      f32x16 (&gn)[NQB], auto mask_tag) FA_INLINE {
         const int qh = it * BQ + h * 4;
         const int lo = qlo - qh;
         const int hi = qhi - qh;
@@ -280,13 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
             l4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[qb * 32 + gi * 8 + h * 4]);
             d4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[BQ + qb * 32 + gi * 8 + h * 4]);
           }
-        f32x16 s2[NQB], g2[NQB];
         bf16x8 rq[3], rg[3];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          s2[qb] = f32x16{};
-          g2[qb] = f32x16{};
-        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           rq[j] = as_bf16x8(ld16(mB + (j / ND) * 32 * D + qoff[j % ND]));
@@ -297,8 +330,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         for (int j = 0; j < NS; ++j) {
           {
             const int qb = j / ND, kd = j % ND;
-            s2[qb] = mma32(rq[j % 3], kf[kd], s2[qb]);
-            g2[qb] = mma32(rg[j % 3], vf[kd], g2[qb]);
+            if (kd == 0) {
+              sn[qb] = mma32_v0(rq[j % 3], kf[kd]);
+              gn[qb] = mma32_v0(rg[j % 3], vf[kd]);
+            } else {
+              sn[qb] = mma32_v(rq[j % 3], kf[kd], sn[qb]);
+              gn[qb] = mma32_v(rg[j % 3], vf[kd], gn[qb]);
+            }
             if (j + 2 < NS) {
               const int j2 = j + 2;
               rq[j2 % 3] = as_bf16x8(ld16(mB + (j2 / ND) * 32 * D + qoff[j2 % ND]));
@@ -333,70 +371,77 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
           dk[mb] = mma32(fq[k % 2], sfr, dk[mb]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        // sn, gn stay live to here even where nothing reads them (the last
+        // tile's successor): otherwise the compiler may hand their registers
+        // to other values while those products are still writing them.
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          s[qb] = s2[qb];
-          g[qb] = g2[qb];
-        }
+        for (int qb = 0; qb < NQB; ++qb) keep_live(sn[qb], gn[qb]);
       };
 
-      // Stages: tile it in A, tile it+1 in B, tile it+2 goes to C (rotating
-      // with the loop unrolled by three). At the top of an iteration each wave
-      // waits for its own loads of tile it+1; the barrier then makes every
-      // wave's loads visible and guarantees that every wave has finished the
-      // previous iteration, the last reader of stage C (tile it-1).
-      auto step = [&](int it, bf16* mA, float* vA, bf16* mB, bf16* mC, float* vC,
-                      auto mask_tag) FA_INLINE {
+      // Step it uses stage it % 4 for tile it (A), stage (it + 1) % 4 for
+      // tile it+1 (B) and sends tile it+2 to stage (it + 2) % 4 (C); the
+      // scores of tile it are in register set it % 2. At the top of a step
+      // each wave waits for its own loads of tile it+1; the barrier then
+      // makes every wave's loads visible and guarantees that every wave has
+      // finished the previous step, the last reader of stage C (tile it-2).
+      auto step = [&](int it, auto stage_tag, auto mask_tag) FA_INLINE {
+        constexpr int K = decltype(stage_tag)::value;
+        bf16* const sms[4] = {sm0, sm1, sm2, sm3};
+        float* const svs[4] = {sv0, sv1, sv2, sv3};
         wait_global_loads();
         __syncthreads();
-        if (it + 2 < ns) issue(tiles.tile(it + 2), mC, vC);
-        body(tiles.tile(it), mA, vA, mB, mask_tag);
+        if (it + 2 < ns) issue(tiles.tile(it + 2), sms[(K + 2) % 4], svs[(K + 2) % 4]);
+        if constexpr (K % 2 == 0)
+          body(tiles.tile(it), sms[K], svs[K], sms[(K + 1) % 4], sa, ga, sb, gb, mask_tag);
+        else
+          body(tiles.tile(it), sms[K], svs[K], sms[(K + 1) % 4], sb, gb, sa, ga, mask_tag);
+      };
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, 3>;
+      auto quad = [&](int it, auto mask_tag) FA_INLINE {
+        step(it, S0{}, mask_tag);
+        step(it + 1, S1{}, mask_tag);
+        step(it + 2, S2{}, mask_tag);
+        step(it + 3, S3{}, mask_tag);
       };
 
       // Steps (it counts steps; tiles.tile(it) is the query tile): masked
       // steps up to the first that holds only fully visible queries (the
       // causal diagonal band, or everything when the workgroup straddles the
-      // key limit), rounded up to a multiple of three so the unmasked loop
+      // key limit), rounded up to a multiple of four so the unmasked loop
       // starts with the same stage rotation; unmasked steps; masked steps
       // again (the window's far edge), the last step always among them (its
       // tile may be partial). The unmasked steps skip the mask arithmetic.
       const int last = ns - 1;
       const int su0 = tiles.first_at_least(iu0);
       const int su1 = tiles.first_at_least(iu1);
-      const int head = min((su0 + 2) / 3 * 3, last);
+      const int head = min((su0 + 3) / 4 * 4, last);
 
       issue(tiles.tile(0), sm0, sv0);
       if (1 < ns) issue(tiles.tile(1), sm1, sv1);
       wait_global_loads();
       __syncthreads();
-      sdp(sm0, s, g);
+      sdp(sm0, sa, ga);
       int it = 0;
-      for (; it + 3 <= head; it += 3) {
-        step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
-        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
-        step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
-      }
-      // Here either it == head with it % 3 == 0, or head == last and fewer
-      // than three steps remain before it, so the loops below do not run.
-      for (; it + 3 <= min(su1, last); it += 3) {
-        step(it, sm0, sv0, sm1, sm2, sv2, std::false_type{});
-        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::false_type{});
-        step(it + 2, sm2, sv2, sm0, sm1, sv1, std::false_type{});
-      }
-      for (; it + 3 <= last; it += 3) {
-        step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
-        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
-        step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
-      }
-      // last - it is 0, 1 or 2 here: one masked step per remaining tile. The
+      for (; it + 4 <= head; it += 4) quad(it, std::true_type{});
+      // Here either it == head with it % 4 == 0, or head == last and fewer
+      // than four steps remain before it, so the loops below do not run.
+      for (; it + 4 <= min(su1, last); it += 4) quad(it, std::false_type{});
+      for (; it + 4 <= last; it += 4) quad(it, std::true_type{});
+      // last - it is 0 to 3 here: one masked step per remaining tile. The
       // step of the last tile also computes S and dP of a successor that does
       // not exist, from the finite data left in its stage, and drops them
       // (one tile's two products per sweep): a separate finishing body needs
       // registers of its own and made the compiler spill the accumulators.
-      step(it, sm0, sv0, sm1, sm2, sv2, std::true_type{});
+      step(it, S0{}, std::true_type{});
       if (it + 1 <= last) {
-        step(it + 1, sm1, sv1, sm2, sm0, sv0, std::true_type{});
-        if (it + 2 <= last) step(it + 2, sm2, sv2, sm0, sm1, sv1, std::true_type{});
+        step(it + 1, S1{}, std::true_type{});
+        if (it + 2 <= last) {
+          step(it + 2, S2{}, std::true_type{});
+          if (it + 3 <= last) step(it + 3, S3{}, std::true_type{});
+        }
       }
     }  // query heads of the group
     };

@@ -1,0 +1,84 @@
+"""Static check of the dK/dV kernel's matrix products that write VGPRs.
+
+The S and dP products of the backward's dK/dV kernel are inline assembly
+(v_mfma_f32_32x32x16_bf16 with a VGPR accumulator), which the compiler's
+hazard tracking does not see. The kernel is only correct if no other
+instruction reads or writes a product's result registers until the product
+has finished (an 8-pass product needs about a dozen wait states). This test
+compiles the kernel for gfx950 and checks, in the generated assembly, that
+within WINDOW instructions after each such product nothing but the next
+product of the same accumulation chain (same registers as destination and
+accumulator) touches those registers, and that no result overlaps the
+product's A or B operands. Runs on the CPU (hipcc cross-compiles).
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "exact_io_aware_fa_amd", "csrc", "kernels", "fa_bwd_bf16.hip")
+WINDOW = 24  # instructions; well above the wait states of an 8-pass product
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def _vgprs(text):
+    out = set()
+    for m in re.finditer(r"\bv\[(\d+):(\d+)\]", text):
+        out |= set(range(int(m.group(1)), int(m.group(2)) + 1))
+    for m in re.finditer(r"\bv(\d+)\b", text):
+        out.add(int(m.group(1)))
+    return out
+
+
+@pytest.fixture(scope="module")
+def assembly(tmp_path_factory):
+    hipcc = _hipcc()
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "dkdv.s"
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-munsafe-fp-atomics",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = [l.strip() for l in out.read_text().split("\n")]
+    # Instructions only (no labels, directives or comments).
+    return [l for l in lines
+            if l and not l.startswith((";", ".")) and not l.endswith(":") and "//" not in l[:2]]
+
+
+def test_vgpr_products_exist(assembly):
+    n = sum(1 for l in assembly if l.startswith("v_mfma_f32_32x32x16_bf16 v["))
+    assert n > 0, "no VGPR-accumulator products found: the check below would be vacuous"
+
+
+def test_no_access_to_vgpr_product_results_in_flight(assembly):
+    bad = []
+    for i, line in enumerate(assembly):
+        if not line.startswith("v_mfma_f32_32x32x16_bf16 v["):
+            continue
+        ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
+        dst = _vgprs(ops[0])
+        if dst & (_vgprs(ops[1]) | _vgprs(ops[2])):
+            bad.append(("result overlaps A/B", line, ""))
+        for nxt in assembly[i + 1:i + 1 + WINDOW]:
+            if nxt.startswith("s_"):
+                continue  # scalar instructions touch no VGPRs
+            nops = [o.strip() for o in nxt.split(None, 1)[1].split(",")] if " " in nxt else []
+            if nxt.startswith("v_mfma") and len(nops) == 4 and \
+                    _vgprs(nops[0]) == dst and _vgprs(nops[3]) == dst:
+                break  # the chain's next product: accumulates in place
+            if _vgprs(" ".join(nops)) & dst:
+                bad.append(("touched while in flight", line, nxt))
+                break
+    assert not bad, bad[:5]
