@@ -9,6 +9,9 @@
 // print no formula):
 //     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = <dO_i, O_i>,
 //     dK = scale dS^T Q.
+// The kernel forms G = D - dP on the matrix cores (dO (-V)^T accumulated
+// onto D) and accumulates P * G = -dS, so dK comes out negated and is
+// scaled by -scale at the end: the subtraction costs no vector instruction.
 // dQ = scale dS K is computed by the query-outer kernel in
 // fa_bwd_dq_bf16.hip.
 //
@@ -67,6 +70,14 @@ __device__ __forceinline__ f32x16 mma32_v(bf16x8 a, bf16x8 b, f32x16 c) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
   return c;
 }
+// Product with a separate accumulator input: d = a b + c (d must not
+// overlap a, b or c). Starts a chain at c instead of zero.
+__device__ __forceinline__ f32x16 mma32_vc(bf16x8 a, bf16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // An empty use of two results in VGPRs (keeps them, and their registers,
 // live up to this point).
 __device__ __forceinline__ void keep_live(const f32x16& x, const f32x16& y) {
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         const u32x4 a = ld16(K + (size_t)kr * D + kd * 16 + h * 8);
         const u32x4 bb = ld16(V + (size_t)kr * D + kd * 16 + h * 8);
         kf[kd] = as_bf16x8(kok ? (a ^ kflip) : z);
-        vf[kd] = as_bf16x8(kok ? bb : z);
+        vf[kd] = as_bf16x8(kok ? (bb ^ 0x80008000u) : z);  // -V (see G above)
       }
     }
 
@@ -253,32 +264,50 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
       // S = Q K^T and dP = dO V^T of the tile in stage sm (lane = key, 16
       // queries per 32-query block); used once, before the loop.
-      auto sdp = [&](const bf16* sm, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) FA_INLINE {
+      // D of the tile in stage v in the accumulator layout of G: element
+      // (gi, i) of block qb is query qb*32 + gi*8 + 4h + i.
+      auto read_d = [&](const float* v, f32x16 (&dd)[NQB]) FA_INLINE {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&v[BQ + qb * 32 + gi * 8 + h * 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dd[qb][gi * 4 + i] = x[i];
+          }
+      };
+
+      auto sdp = [&](const bf16* sm, const float* sv, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) FA_INLINE {
+        f32x16 dd[NQB];
+        read_d(sv, dd);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           s[qb] = mma32_v0(as_bf16x8(ld16(sm + qb * 32 * D + qoff[0])), kf[0]);
-          g[qb] = mma32_v0(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[0])), vf[0]);
+          g[qb] = mma32_vc(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[0])), vf[0], dd[qb]);
 #pragma unroll
           for (int kd = 1; kd < ND; ++kd) {
             s[qb] = mma32_v(as_bf16x8(ld16(sm + qb * 32 * D + qoff[kd])), kf[kd], s[qb]);
             g[qb] = mma32_v(as_bf16x8(ld16(sm + TILE + qb * 32 * D + qoff[kd])), vf[kd], g[qb]);
           }
         }
+        // dd stays live until every chain has moved past its first product.
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) keep_live(dd[qb], dd[qb]);
       };
 
-      // P = exp2(S c - L log2 e) and dS = P (dP - D) for element e of the
-      // lane's 16 NQB values, in place in s and g. Query of element
+      // P = exp2(S c - L log2 e) and -dS = P (D - dP) = P G for element e of
+      // the lane's 16 NQB values, in place in s and g. Query of element
       // (qb, gi, i) is q0 + 4h + (qb*32 + gi*8 + i); the pair is hidden iff
       // that offset is < lo or >= hi, and a hidden pair gets P = 0, dS = 0.
-      auto pds1 = [&](int e, int lo, int hi, const f32x4 (&l4)[NQB][4], const f32x4 (&d4)[NQB][4],
-                      f32x16 (&s)[NQB], f32x16 (&g)[NQB], auto mask_tag) FA_INLINE {
+      auto pds1 = [&](int e, int lo, int hi, const f32x4 (&l4)[NQB][4], f32x16 (&s)[NQB],
+                      f32x16 (&g)[NQB], auto mask_tag) FA_INLINE {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int qb = e / 16, r = e % 16, gi = r / 4, i = r % 4;
         const int off = qb * 32 + gi * 8 + i;
         const float x = (MASK && (off < lo || off >= hi)) ? kNegInf : s[qb][r];
         const float pr = __builtin_amdgcn_exp2f(fmaf(x, cs, -l4[qb][gi][i]));
         s[qb][r] = pr;
-        g[qb][r] = pr * (g[qb][r] - d4[qb][gi][i]);
+        g[qb][r] = pr * g[qb][r];
       };
 
       // A fragments of the transposing reads for (qb, qc, mb): dO^T and Q^T of
@@ -295,30 +324,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       };
 
       // One query tile, software-pipelined and issued in a fixed order (the
-      // sched_barrier fences pin it): phase 1 computes S and dP of tile it+1
-      // (stage mB, row reads two products ahead) into sn, gn while the vector
-      // units turn S and dP of tile it (in s, g; L and D in vA) into P and
-      // dS, 16/ND values per product pair; phase 2 accumulates dV^T and dK^T
-      // of tile it from stage mA (transposing reads one pair ahead). The
-      // next step takes sn, gn as its s, g.
+      // sched_barrier fences pin it): phase 1 computes S and G = D - dP of
+      // tile it+1 (stage mB, row reads two products ahead; D from vB) into
+      // sn, gn while the vector units turn S and G of tile it (in s, g; L
+      // from vA) into P and -dS, 16/ND values per product pair; phase 2
+      // accumulates dV^T and -dK^T of tile it from stage mA (transposing
+      // reads one pair ahead). The next step takes sn, gn as its s, g.
       constexpr int NS = NQB * ND;        // phase-1 slots (2 products each)
       constexpr int EPS = 16 / ND;        // P/dS values per phase-1 slot
       constexpr int NP = NQB * 2 * NMB;   // phase-2 slots (2 products each)
       f32x16 sa[NQB], ga[NQB], sb[NQB], gb[NQB];
-      auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB,
+      auto body = [&](int it, const bf16* mA, const float* vA, const bf16* mB, const float* vB,
                       f32x16 (&s)[NQB], f32x16 (&g)[NQB], f32x16 (&sn)[NQB],
                       f32x16 (&gn)[NQB], auto mask_tag) FA_INLINE {
         const int qh = it * BQ + h * 4;
         const int lo = qlo - qh;
         const int hi = qhi - qh;
-        f32x4 l4[NQB][4], d4[NQB][4];
+        f32x4 l4[NQB][4];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int gi = 0; gi < 4; ++gi) {
+          for (int gi = 0; gi < 4; ++gi)
             l4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[qb * 32 + gi * 8 + h * 4]);
-            d4[qb][gi] = *reinterpret_cast<const f32x4*>(&vA[BQ + qb * 32 + gi * 8 + h * 4]);
-          }
+        f32x16 dn[NQB];  // D of tile it+1: where its G chains start
+        read_d(vB, dn);
         bf16x8 rq[3], rg[3];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -332,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
             const int qb = j / ND, kd = j % ND;
             if (kd == 0) {
               sn[qb] = mma32_v0(rq[j % 3], kf[kd]);
-              gn[qb] = mma32_v0(rg[j % 3], vf[kd]);
+              gn[qb] = mma32_vc(rg[j % 3], vf[kd], dn[qb]);
             } else {
               sn[qb] = mma32_v(rq[j % 3], kf[kd], sn[qb]);
               gn[qb] = mma32_v(rg[j % 3], vf[kd], gn[qb]);
@@ -344,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
             }
           }
 #pragma unroll
-          for (int e = j * EPS; e < (j + 1) * EPS; ++e) pds1(e, lo, hi, l4, d4, s, g, mask_tag);
+          for (int e = j * EPS; e < (j + 1) * EPS; ++e) pds1(e, lo, hi, l4, s, g, mask_tag);
           __builtin_amdgcn_sched_barrier(0);
         }
         bf16x8 fo[2], fq[2];
@@ -372,10 +401,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
           __builtin_amdgcn_sched_barrier(0);
         }
         // sn, gn stay live to here even where nothing reads them (the last
-        // tile's successor): otherwise the compiler may hand their registers
-        // to other values while those products are still writing them.
+        // tile's successor), and so does dn: otherwise the compiler may hand
+        // their registers to other values while those products are still
+        // writing (sn, gn) or reading (dn) them.
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) keep_live(sn[qb], gn[qb]);
+        for (int qb = 0; qb < NQB; ++qb) {
+          keep_live(sn[qb], gn[qb]);
+          keep_live(dn[qb], dn[qb]);
+        }
       };
 
       // Step it uses stage it % 4 for tile it (A), stage (it + 1) % 4 for
@@ -392,9 +425,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         __syncthreads();
         if (it + 2 < ns) issue(tiles.tile(it + 2), sms[(K + 2) % 4], svs[(K + 2) % 4]);
         if constexpr (K % 2 == 0)
-          body(tiles.tile(it), sms[K], svs[K], sms[(K + 1) % 4], sa, ga, sb, gb, mask_tag);
+          body(tiles.tile(it), sms[K], svs[K], sms[(K + 1) % 4], svs[(K + 1) % 4], sa, ga, sb, gb,
+               mask_tag);
         else
-          body(tiles.tile(it), sms[K], svs[K], sms[(K + 1) % 4], sb, gb, sa, ga, mask_tag);
+          body(tiles.tile(it), sms[K], svs[K], sms[(K + 1) % 4], svs[(K + 1) % 4], sb, gb, sa, ga,
+               mask_tag);
       };
       using S0 = std::integral_constant<int, 0>;
       using S1 = std::integral_constant<int, 1>;
@@ -423,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
       if (1 < ns) issue(tiles.tile(1), sm1, sv1);
       wait_global_loads();
       __syncthreads();
-      sdp(sm0, sa, ga);
+      sdp(sm0, sv0, sa, ga);
       int it = 0;
       for (; it + 4 <= head; it += 4) quad(it, std::true_type{});
       // Here either it == head with it % 4 == 0, or head == last and fewer
@@ -456,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
 
   // dK = scale * (dS^T Q), dV as accumulated.
   if (mykey < n) {
-    const float ks = p.scale;
+    const float ks = -p.scale;  // dk holds -dS^T Q
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll

@@ -4,12 +4,14 @@ The S and dP products of the backward's dK/dV kernel are inline assembly
 (v_mfma_f32_32x32x16_bf16 with a VGPR accumulator), which the compiler's
 hazard tracking does not see. The kernel is only correct if no other
 instruction reads or writes a product's result registers until the product
-has finished (an 8-pass product needs about a dozen wait states). This test
-compiles the kernel for gfx950 and checks, in the generated assembly, that
-within WINDOW instructions after each such product nothing but the next
-product of the same accumulation chain (same registers as destination and
-accumulator) touches those registers, and that no result overlaps the
-product's A or B operands. Runs on the CPU (hipcc cross-compiles).
+has finished (an 8-pass product needs about a dozen wait states), and no
+instruction may overwrite a separate accumulator input (C) that the product
+may still be reading. This test compiles the kernel for gfx950 and checks,
+in the generated assembly, that within WINDOW instructions after each such
+product nothing but the next product of the same accumulation chain (same
+registers as destination and accumulator) touches the result registers,
+nothing writes a separate C input, and that no result overlaps the
+product's A, B or C operands. Runs on the CPU (hipcc cross-compiles).
 """
 
 import os
@@ -69,12 +71,19 @@ def test_no_access_to_vgpr_product_results_in_flight(assembly):
             continue
         ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
         dst = _vgprs(ops[0])
+        src_c = _vgprs(ops[3])
         if dst & (_vgprs(ops[1]) | _vgprs(ops[2])):
             bad.append(("result overlaps A/B", line, ""))
+        if src_c and src_c != dst and dst & src_c:
+            bad.append(("result partly overlaps C", line, ""))
+        separate_c = src_c if src_c != dst else set()
         for nxt in assembly[i + 1:i + 1 + WINDOW]:
             if nxt.startswith("s_"):
                 continue  # scalar instructions touch no VGPRs
             nops = [o.strip() for o in nxt.split(None, 1)[1].split(",")] if " " in nxt else []
+            if nops and _vgprs(nops[0]) & separate_c:
+                bad.append(("C input overwritten while read", line, nxt))
+                break
             if nxt.startswith("v_mfma") and len(nops) == 4 and \
                     _vgprs(nops[0]) == dst and _vgprs(nops[3]) == dst:
                 break  # the chain's next product: accumulates in place
