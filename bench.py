@@ -224,9 +224,63 @@ def _short(name: str) -> str:
     return name[:60]
 
 
-def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, out_json):
+XCDS = 8                # MI355X: 8 accelerator dies (GRBM counters add over them)
+SIMDS = 256 * 4         # 256 compute units x 4 SIMDs
+MFMA_FLOP_PER_CLK = 1024  # bf16 32x32x16 product: 32768 FLOP in 32 cycles per SIMD
+
+
+def summarize_sq(sq_db) -> list:
+    """Markdown lines for an SQ counter pass: per kernel, the shader clock
+    the kernel ran at (GRBM_GUI_ACTIVE per die over the dispatch duration),
+    the matrix-core FLOPs counted by the hardware (SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    512 FLOP each) and their rate, matrix-core busy time as a fraction of all
+    SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES), vector instructions per matrix
+    instruction, and LDS bank conflicts (SQ_LDS_BANK_CONFLICT cycles over
+    SQ_LDS_IDX_ACTIVE cycles)."""
+    import sqlite3
+
+    per = {}
+    for kn, ctr, val, dur, did in sqlite3.connect(sq_db).execute(
+            "select kernel_name, counter_name, value, duration, dispatch_id from counters_collection"):
+        d = per.setdefault(_short(kn), {}).setdefault(did, {"dur": dur})
+        d[ctr] = d.get(ctr, 0.0) + val
+    lines = ["", "## Clock, matrix cores and LDS (`--pmc` SQ pass)", "",
+             "Per dispatch, averaged: clock = GRBM_GUI_ACTIVE / %d dies / duration; FLOP = "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x "
+             "cycles); peak at clock = %d SIMDs x %d FLOP/cycle x clock; LDS conflicts = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. Durations are those of the counter pass "
+             "(dispatches serialised by the profiler)." % (XCDS, SIMDS, SIMDS, MFMA_FLOP_PER_CLK), "",
+             "| kernel | dispatches | us | clock GHz | MFMA TFLOP | TFLOP/s | peak at clock TFLOP/s | "
+             "MFMA busy | VALU instr per MFMA instr | LDS bank-conflict cycles / LDS active |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for k, ds in per.items():
+        if k.startswith("__amd") or k.startswith("void at::"):
+            continue
+        n = len(ds)
+
+        def avg(c):
+            return sum(d.get(c, 0.0) for d in ds.values()) / n
+        dur = sum(d["dur"] for d in ds.values()) / n
+        cyc = avg("GRBM_GUI_ACTIVE") / XCDS
+        if dur <= 0 or cyc <= 0:
+            continue
+        clk = cyc / dur
+        flop = avg("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+        mfma_instr = flop / 32768.0
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (SIMDS * cyc)
+        valu = (avg("SQ_INSTS_VALU") - mfma_instr) / mfma_instr if mfma_instr else float("nan")
+        lds_act = avg("SQ_LDS_IDX_ACTIVE")
+        conf = avg("SQ_LDS_BANK_CONFLICT") / lds_act if lds_act else 0.0
+        lines.append("| `%s` | %d | %.1f | %.2f | %.3f | %.0f | %.0f | %.3f | %.2f | %.4f |" % (
+            k, n, dur / 1e3, clk, flop / 1e12, flop / dur / 1e3,
+            SIMDS * MFMA_FLOP_PER_CLK * clk / 1e3, busy, valu, conf))
+    return lines
+
+
+def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, out_json, sq_db=None):
     """Summarise rocprofv3 databases (kernel trace + FETCH_SIZE + WRITE_SIZE
-    passes) into a short markdown file and the traffic JSON this bench reads."""
+    passes, optionally an SQ counter pass) into a short markdown file and the
+    traffic JSON this bench reads."""
     import sqlite3
 
     rows = sqlite3.connect(trace_db).execute(
@@ -272,6 +326,8 @@ def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, o
         traffic[k] = {"read_bytes": rd, "write_bytes": wr}
         lines.append("| `%s` | %d | %.0f | %.0f | %.3f | %.3f |" % (k, len(v["FETCH_SIZE"]), fk, wk,
                                                                    rd / 1e9, wr / 1e9))
+    if sq_db:
+        lines += summarize_sq(sq_db)
     open(out_md, "w").write("\n".join(lines) + "\n")
     bwd = [k for k in traffic if k.startswith("bwd_dkdv_kernel")]
     if bwd and out_json:
@@ -665,8 +721,10 @@ def main() -> int:
         sp.add_argument("--command", required=True)
         sp.add_argument("--out-md", required=True)
         sp.add_argument("--out-json", default=None)
+        sp.add_argument("--sq-db", default=None, help="database of an SQ counter pass")
         a = sp.parse_args(sys.argv[2:])
-        summarize_rocprof(a.trace_db, a.fetch_db, a.write_db, a.copy_mib, a.command, a.out_md, a.out_json)
+        summarize_rocprof(a.trace_db, a.fetch_db, a.write_db, a.copy_mib, a.command, a.out_md, a.out_json,
+                          a.sq_db)
         return 0
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
