@@ -91,3 +91,24 @@ def test_no_access_to_vgpr_product_results_in_flight(assembly):
                 bad.append(("touched while in flight", line, nxt))
                 break
     assert not bad, bad[:5]
+
+
+def test_no_vector_write_of_vgpr_product_operands_just_before(assembly):
+    """A vector instruction that writes a register needs a few wait states
+    before a matrix product may read it as A, B or C; the compiler inserts
+    them for its own products only. Here every operand of an assembly
+    product comes from LDS loads or from products; check that no vector ALU
+    instruction writes one within the WINDOW_BEFORE instructions before it."""
+    WINDOW_BEFORE = 6
+    bad = []
+    for i, line in enumerate(assembly):
+        if not line.startswith("v_mfma_f32_32x32x16_bf16 v["):
+            continue
+        ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
+        srcs = _vgprs(ops[1]) | _vgprs(ops[2]) | (_vgprs(ops[3]) if ops[3] != ops[0] else set())
+        for prev in reversed(assembly[max(i - WINDOW_BEFORE, 0):i]):
+            if prev.startswith("v_") and not prev.startswith("v_mfma") and " " in prev:
+                if _vgprs(prev.split(None, 1)[1].split(",")[0]) & srcs:
+                    bad.append((prev, line))
+                    break
+    assert not bad, bad[:5]
