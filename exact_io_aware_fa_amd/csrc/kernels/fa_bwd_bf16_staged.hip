@@ -169,21 +169,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
       const bf16* tQt = sQt[buf];
       const bf16* tdOt = sdOt[buf];
 
+      // A fragments are read two products ahead through a ring of three (the
+      // sched_barrier fences keep the compiler from hoisting every read to
+      // the top, which would hold all 2 ND fragments in registers at once).
       f32x16 sv[NQB], dp[NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        bf16x8 qa[ND], ga[ND];
-#pragma unroll
-        for (int kd = 0; kd < ND; ++kd) {
-          qa[kd] = as_bf16x8(ld16(&tQ[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-          ga[kd] = as_bf16x8(ld16(&tdO[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
-        }
+        auto rd = [&](const bf16* t, int kd) FA_INLINE {
+          return as_bf16x8(ld16(&t[(qb * 32 + c) * QSTR + kd * 16 + h * 8]));
+        };
+        bf16x8 qa[3], ga[3];
+        qa[0] = rd(tQ, 0);
+        ga[0] = rd(tdO, 0);
+        qa[1] = rd(tQ, 1);
+        ga[1] = rd(tdO, 1);
         sv[qb] = f32x16{};
         dp[qb] = f32x16{};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kd = 0; kd < ND; ++kd) {
-          sv[qb] = mma32(qa[kd], kf[kd], sv[qb]);
-          dp[qb] = mma32(ga[kd], vf[kd], dp[qb]);
+          if (kd + 2 < ND) {
+            qa[(kd + 2) % 3] = rd(tQ, kd + 2);
+            ga[(kd + 2) % 3] = rd(tdO, kd + 2);
+          }
+          sv[qb] = mma32(qa[kd % 3], kf[kd], sv[qb]);
+          dp[qb] = mma32(ga[kd % 3], vf[kd], dp[qb]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
 #pragma unroll
@@ -217,21 +228,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
           }
           const bf16x8 pfr = as_bf16x8(pu);
           const bf16x8 sfr = as_bf16x8(su);
-          bf16x8 oa[NMB], qa[NMB];
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) {
+          // Transposed A fragments one pair ahead, as above.
+          auto rdt = [&](int mb, bf16x8& fo, bf16x8& fq) FA_INLINE {
             const int off = (mb * 32 + c) * TSTR + qb * 32 + qc * 16 + h * 4;
             const u32x2 olo = ld8(&tdOt[off]);
             const u32x2 ohi = ld8(&tdOt[off + 8]);
-            oa[mb] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+            fo = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
             const u32x2 qlo = ld8(&tQt[off]);
             const u32x2 qhi = ld8(&tQt[off + 8]);
-            qa[mb] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
-          }
+            fq = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+          };
+          bf16x8 oa[2], qa[2];
+          rdt(0, oa[0], qa[0]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
-            dv[mb] = mma32(oa[mb], pfr, dv[mb]);
-            dk[mb] = mma32(qa[mb], sfr, dk[mb]);
+            if (mb + 1 < NMB) rdt(mb + 1, oa[(mb + 1) % 2], qa[(mb + 1) % 2]);
+            dv[mb] = mma32(oa[mb % 2], pfr, dv[mb]);
+            dk[mb] = mma32(qa[mb % 2], sfr, dk[mb]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
     };
