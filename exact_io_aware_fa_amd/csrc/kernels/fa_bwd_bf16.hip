@@ -36,7 +36,7 @@
 //   dS, then accumulates dV and dK of tile i. With one wave per SIMD (the
 //   accumulators and K/V fragments need more than half the register file)
 //   the overlap has to come from within the wave.
-// * The S and dP products write ordinary VGPRs (mma32_v below), and the
+// * The S and dP products write ordinary VGPRs (mma32_v, in fa_device.h), and the
 //   results of consecutive tiles alternate between two register sets (the
 //   loop is unrolled by four, the period of both the stages and the sets):
 //   the vector units read them where they land, with no copy out of the
@@ -52,42 +52,16 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBKV = 128;  // keys per workgroup (4 waves x 32)
 
-// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs. The compiler
-// selects the AGPR form for every matrix builtin of a kernel that may use
-// more than 256 registers per lane, after which the vector units could only
-// read S and dP through one v_accvgpr_read per value. Written as assembly,
-// the product is invisible to the compiler's hazard tracking; it is safe
-// here because every result is first read, and its registers first
-// reused, by code of the next pipeline step (hundreds of instructions and
-// 16 products later, beyond any required wait states; the step keeps its
-// results live to its end, see body), and each accumulation chain
-// alternates with another, so two products of one chain are never
-// adjacent. mma32_v0 starts a chain (C = 0).
-// The result may not overlap the A or B registers (the product still reads
-// them while it writes), hence the early-clobber output of mma32_v0; in
-// mma32_v the accumulator is live on entry, so it cannot share them either.
-__device__ __forceinline__ f32x16 mma32_v(bf16x8 a, bf16x8 b, f32x16 c) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-  return c;
-}
-// Product with a separate accumulator input: d = a b + c (d must not
-// overlap a, b or c). Starts a chain at c instead of zero.
-__device__ __forceinline__ f32x16 mma32_vc(bf16x8 a, bf16x8 b, const f32x16& c) {
-  f32x16 d;
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
-
-// An empty use of two results in VGPRs (keeps them, and their registers,
-// live up to this point).
-__device__ __forceinline__ void keep_live(const f32x16& x, const f32x16& y) {
-  asm volatile("" ::"v"(x), "v"(y));
-}
-__device__ __forceinline__ f32x16 mma32_v0(bf16x8 a, bf16x8 b) {
-  f32x16 d;
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-  return d;
-}
+// S and dP accumulate in VGPRs (mma32_v, mma32_v0, mma32_vc in fa_device.h):
+// this kernel may use more than 256 registers per lane, so the compiler
+// gives every matrix builtin the AGPR form, after which the vector units
+// could read S and dP only through one v_accvgpr_read per value. The
+// assembly products are safe here because every result is first read, and
+// its registers first reused, by code of the next pipeline step (hundreds
+// of instructions and 16 products later, beyond any required wait states;
+// the step keeps its results and accumulator inputs live to its end, see
+// body), and each accumulation chain alternates with another, so two
+// products of one chain are never adjacent.
 
 template <int D, int NQB, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {

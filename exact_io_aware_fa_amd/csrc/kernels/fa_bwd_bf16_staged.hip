@@ -11,6 +11,10 @@
 // ([d][query], rows padded by 8 bytes, built with byte permutes), one tile
 // at a time. At d = 256 the dK and dV accumulators alone take 256 registers,
 // which leaves no room for the software pipeline of the d <= 128 kernel.
+// S and dP accumulate in VGPRs (mma32_v, mma32_v0 in fa_device.h; the
+// compiler would give the AGPR form to every product of a kernel this size,
+// and the vector units would then move each value out of and back into
+// AGPRs); mfma_drain waits for the last of them before S and dP are read.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -183,8 +187,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
         ga[0] = rd(tdO, 0);
         qa[1] = rd(tQ, 1);
         ga[1] = rd(tdO, 1);
-        sv[qb] = f32x16{};
-        dp[qb] = f32x16{};
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kd = 0; kd < ND; ++kd) {
@@ -192,11 +194,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
             qa[(kd + 2) % 3] = rd(tQ, kd + 2);
             ga[(kd + 2) % 3] = rd(tdO, kd + 2);
           }
-          sv[qb] = mma32(qa[kd % 3], kf[kd], sv[qb]);
-          dp[qb] = mma32(ga[kd % 3], vf[kd], dp[qb]);
+          if (kd == 0) {
+            sv[qb] = mma32_v0(qa[0], kf[0]);
+            dp[qb] = mma32_v0(ga[0], vf[0]);
+          } else {
+            sv[qb] = mma32_v(qa[kd % 3], kf[kd], sv[qb]);
+            dp[qb] = mma32_v(ga[kd % 3], vf[kd], dp[qb]);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // S and dP are read right below: let the last products finish.
+      mfma_drain();
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll

@@ -38,6 +38,46 @@ __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 acc) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs, as inline
+// assembly: for kernels where the compiler would give its matrix builtins
+// the AGPR form (more than 256 registers per lane in play), so that vector
+// code can read the results without a v_accvgpr_read each. The compiler's
+// hazard tracking does not see these products; the caller must keep every
+// result and accumulator input untouched until the product is done (about
+// a dozen wait states for this 8-pass product: mfma_drain, or enough other
+// instructions) and must not place two products of one chain back to back
+// unless the second accumulates onto exactly the first's result.
+// mma32_v accumulates onto c in place; mma32_v0 starts a chain at zero;
+// mma32_vc starts one at c, into new registers. A result may not overlap
+// the A, B or C registers (they are still read while it is written): hence
+// the early-clobber outputs.
+__device__ __forceinline__ f32x16 mma32_v(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ f32x16 mma32_v0(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ f32x16 mma32_vc(bf16x8 a, bf16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+// An empty use of two values in VGPRs (keeps them, and their registers,
+// live up to this point).
+__device__ __forceinline__ void keep_live(const f32x16& x, const f32x16& y) {
+  asm volatile("" ::"v"(x), "v"(y));
+}
+// 20 wait states: enough for any result of the products above to be
+// written before the next instruction reads it.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }

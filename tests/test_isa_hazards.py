@@ -1,17 +1,20 @@
-"""Static check of the dK/dV kernel's matrix products that write VGPRs.
+"""Static check of the matrix products that accumulate in VGPRs.
 
-The S and dP products of the backward's dK/dV kernel are inline assembly
+The S and dP products of the backward's dK/dV kernels (d <= 128 and the
+register-staged d = 256 kernel) are inline assembly
 (v_mfma_f32_32x32x16_bf16 with a VGPR accumulator), which the compiler's
-hazard tracking does not see. The kernel is only correct if no other
+hazard tracking does not see. A kernel is only correct if no other
 instruction reads or writes a product's result registers until the product
 has finished (an 8-pass product needs about a dozen wait states), and no
-instruction may overwrite a separate accumulator input (C) that the product
-may still be reading. This test compiles the kernel for gfx950 and checks,
-in the generated assembly, that within WINDOW instructions after each such
-product nothing but the next product of the same accumulation chain (same
-registers as destination and accumulator) touches the result registers,
-nothing writes a separate C input, and that no result overlaps the
-product's A, B or C operands. Runs on the CPU (hipcc cross-compiles).
+instruction overwrites a separate accumulator input (C) that the product
+may still be reading. This test compiles each kernel for gfx950 and checks,
+in the generated assembly, that for WAIT_STATES wait states after each such
+product (an instruction counts one, s_nop N counts N + 1) nothing but the
+next product of the same accumulation chain (same registers as destination
+and accumulator) touches the result registers, nothing writes a separate C
+input, that no result overlaps the product's A, B or C operands, and that
+no vector instruction writes an operand just before a product reads it.
+Runs on the CPU (hipcc cross-compiles).
 """
 
 import os
@@ -22,8 +25,9 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "exact_io_aware_fa_amd", "csrc", "kernels", "fa_bwd_bf16.hip")
-WINDOW = 24  # instructions; well above the wait states of an 8-pass product
+KERNELS = os.path.join(ROOT, "exact_io_aware_fa_amd", "csrc", "kernels")
+SOURCES = ("fa_bwd_bf16.hip", "fa_bwd_bf16_staged.hip")
+WAIT_STATES = 20  # well above what an 8-pass product needs before its result is read
 
 
 def _hipcc():
@@ -42,15 +46,21 @@ def _vgprs(text):
     return out
 
 
-@pytest.fixture(scope="module")
-def assembly(tmp_path_factory):
+def _wait_states(inst):
+    m = re.match(r"s_nop\s+(\d+)", inst)
+    return int(m.group(1)) + 1 if m else 1
+
+
+@pytest.fixture(scope="module", params=SOURCES)
+def assembly(request, tmp_path_factory):
     hipcc = _hipcc()
     if hipcc is None:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "dkdv.s"
+    out = tmp_path_factory.mktemp("isa") / (request.param + ".s")
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-munsafe-fp-atomics",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", SRC, "-o", str(out)]
+           "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(KERNELS, request.param), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     lines = [l.strip() for l in out.read_text().split("\n")]
@@ -77,7 +87,11 @@ def test_no_access_to_vgpr_product_results_in_flight(assembly):
         if src_c and src_c != dst and dst & src_c:
             bad.append(("result partly overlaps C", line, ""))
         separate_c = src_c if src_c != dst else set()
-        for nxt in assembly[i + 1:i + 1 + WINDOW]:
+        waited = 0
+        for nxt in assembly[i + 1:]:
+            if waited >= WAIT_STATES:
+                break
+            waited += _wait_states(nxt)
             if nxt.startswith("s_"):
                 continue  # scalar instructions touch no VGPRs
             nops = [o.strip() for o in nxt.split(None, 1)[1].split(",")] if " " in nxt else []
