@@ -110,19 +110,30 @@ def test_no_access_to_vgpr_product_results_in_flight(assembly):
 def test_no_vector_write_of_vgpr_product_operands_just_before(assembly):
     """A vector instruction that writes a register needs a few wait states
     before a matrix product may read it as A, B or C; the compiler inserts
-    them for its own products only. Here every operand of an assembly
-    product comes from LDS loads or from products; check that no vector ALU
-    instruction writes one within the WINDOW_BEFORE instructions before it."""
+    them for its own products only. For each operand register of an
+    assembly product, the nearest earlier instruction that writes it (within
+    WINDOW_BEFORE instructions) must not be a vector ALU instruction: the
+    operands come from LDS loads or from other products."""
     WINDOW_BEFORE = 6
     bad = []
     for i, line in enumerate(assembly):
         if not line.startswith("v_mfma_f32_32x32x16_bf16 v["):
             continue
         ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
-        srcs = _vgprs(ops[1]) | _vgprs(ops[2]) | (_vgprs(ops[3]) if ops[3] != ops[0] else set())
+        pending = _vgprs(ops[1]) | _vgprs(ops[2]) | (_vgprs(ops[3]) if ops[3] != ops[0] else set())
         for prev in reversed(assembly[max(i - WINDOW_BEFORE, 0):i]):
-            if prev.startswith("v_") and not prev.startswith("v_mfma") and " " in prev:
-                if _vgprs(prev.split(None, 1)[1].split(",")[0]) & srcs:
+            if not pending:
+                break
+            # Instructions whose first operand is a destination: vector ALU
+            # and matrix instructions and loads (a store's first operand is
+            # an address it reads).
+            if not prev.startswith(("v_", "ds_read", "buffer_load", "global_load", "scratch_load")) \
+                    or " " not in prev:
+                continue
+            written = _vgprs(prev.split(None, 1)[1].split(",")[0]) & pending
+            if written:
+                if prev.startswith("v_") and not prev.startswith("v_mfma"):
                     bad.append((prev, line))
                     break
+                pending -= written
     assert not bad, bad[:5]
