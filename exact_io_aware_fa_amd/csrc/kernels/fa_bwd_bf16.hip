@@ -236,8 +236,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
         }
       };
 
-      // S = Q K^T and dP = dO V^T of the tile in stage sm (lane = key, 16
-      // queries per 32-query block); used once, before the loop.
       // D of the tile in stage v in the accumulator layout of G: element
       // (gi, i) of block qb is query qb*32 + gi*8 + 4h + i.
       auto read_d = [&](const float* v, f32x16 (&dd)[NQB]) FA_INLINE {
@@ -251,6 +249,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(Params p) {
           }
       };
 
+      // S = Q K^T and G = D - dP (dO (-V)^T accumulated onto D) of the tile
+      // in stage sm, D read from stage sv (lane = key, 16 queries per
+      // 32-query block); used once per sweep, before the loop.
       auto sdp = [&](const bf16* sm, const float* sv, f32x16 (&s)[NQB], f32x16 (&g)[NQB]) FA_INLINE {
         f32x16 dd[NQB];
         read_d(sv, dd);
