@@ -1,0 +1,74 @@
+"""Host logic of bench.py's profile summary: the SQ counter section.
+
+summarize_sq derives, per kernel, the shader clock (GRBM_GUI_ACTIVE per die
+over the dispatch duration), the matrix-core FLOPs and their rate, the
+matrix-core busy fraction, vector instructions per matrix instruction and
+the LDS bank-conflict ratio from a rocprofv3 counter database. This test
+builds such a database by hand (the columns rocprofv3 writes that the
+summary reads) with values whose derived figures are known, and checks the
+table row. No GPU is needed.
+"""
+
+import os
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _db(path, rows):
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (kernel_name text, counter_name text, "
+                "value real, duration integer, dispatch_id integer)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_summarize_sq_derives_clock_flops_busy_and_conflicts(tmp_path):
+    name = "void fa::(anonymous namespace)::fwd_bf16_kernel<128, 64, true, false>(fa::Params)"
+    dur_ns = 2_000_000                      # 2 ms
+    clk_ghz = 1.75
+    cycles = clk_ghz * dur_ns               # per die
+    mfma_instr = 1_000_000                  # 32x32x16 products
+    mops = mfma_instr * 32768 / 512         # SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512 FLOP
+    busy = 0.5 * bench.SIMDS * cycles       # half of all SIMD cycles
+    rows = []
+    for did in (1, 2):                      # two identical dispatches
+        rows += [
+            (name, "GRBM_GUI_ACTIVE", cycles * bench.XCDS, dur_ns, did),
+            (name, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops, dur_ns, did),
+            (name, "SQ_VALU_MFMA_BUSY_CYCLES", busy, dur_ns, did),
+            (name, "SQ_INSTS_VALU", 4.0 * mfma_instr, dur_ns, did),  # 3 vector per matrix
+            (name, "SQ_LDS_IDX_ACTIVE", 1000.0, dur_ns, did),
+            (name, "SQ_LDS_BANK_CONFLICT", 25.0, dur_ns, did),
+        ]
+    db = tmp_path / "sq.db"
+    _db(str(db), rows)
+    lines = bench.summarize_sq(str(db))
+    row = [l for l in lines if l.startswith("| `fwd_bf16_kernel")]
+    assert len(row) == 1, lines
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    # kernel, dispatches, us, clock, MFMA TFLOP, TFLOP/s, peak at clock, busy, VALU/MFMA, LDS
+    assert cells[1] == "2"
+    assert float(cells[2]) == 2000.0
+    assert abs(float(cells[3]) - clk_ghz) < 0.01
+    flop = mfma_instr * 32768
+    assert abs(float(cells[4]) - flop / 1e12) < 1e-3
+    assert abs(float(cells[5]) - flop / dur_ns / 1e3) < 1.0
+    assert abs(float(cells[6]) - bench.SIMDS * bench.MFMA_FLOP_PER_CLK * clk_ghz / 1e3) < 1.0
+    assert abs(float(cells[7]) - 0.5) < 1e-3
+    assert abs(float(cells[8]) - 3.0) < 1e-2
+    assert abs(float(cells[9]) - 0.025) < 1e-4
+
+
+def test_summarize_sq_skips_runtime_copies(tmp_path):
+    rows = [("__amd_rocclr_copyBuffer", "GRBM_GUI_ACTIVE", 1e6, 1000, 1)]
+    db = tmp_path / "sq.db"
+    _db(str(db), rows)
+    lines = bench.summarize_sq(str(db))
+    assert not [l for l in lines if "copyBuffer" in l]
