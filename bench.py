@@ -751,8 +751,8 @@ def main() -> int:
     if args.fp8:
         return run_fp8(args.out, args.only, args.calibrate_copy)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the work shards by (batch, head) with no exchange; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the work would shard by (batch, head) with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
