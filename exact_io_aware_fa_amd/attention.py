@@ -17,12 +17,22 @@ from . import binding as _b
 _DTYPES = {torch.bfloat16: _b.FA_BF16, torch.float32: _b.FA_FP32}
 
 
-def _check_qkv(q, k, v):
-    for name, t in (("q", q), ("k", k), ("v", v)):
+def _on_device(ref, named, layout):
+    """Every tensor in ``named`` must be a contiguous GPU tensor on ref's
+    device (the library receives raw device pointers; a host pointer or a
+    pointer into another GPU's memory would be read by the kernels)."""
+    for name, t in named:
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, q on {ref.device}")
         if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [batch, heads, n, d]")
+            raise ValueError(f"{name} must be contiguous {layout}")
+
+
+def _check_qkv(q, k, v, devices=True):
+    # Shapes and dtypes first, then devices: every check runs on the host
+    # before anything is launched.
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
         raise ValueError("q must be [batch, heads, n, d] and k, v one "
                          "[batch, heads_kv, n, d] shape")
@@ -33,7 +43,26 @@ def _check_qkv(q, k, v):
                          "heads_kv that divides q's")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if devices:
+        _on_device(q, (("q", q), ("k", k), ("v", v)), "[batch, heads, n, d]")
     return hkv
+
+
+def _check_saved(q, k, v, o, lse, do, lse_shape):
+    """The backward's extra inputs: o and do shaped and typed like q, lse the
+    forward's float32 logsumexp of shape ``lse_shape``; then every tensor on
+    q's device (after all shape checks, so that a wrong shape is reported
+    before a wrong device)."""
+    if o.shape != q.shape or do.shape != q.shape or o.dtype != q.dtype or do.dtype != q.dtype:
+        raise ValueError("o and do must match q in shape and dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(lse_shape):
+        raise ValueError(f"lse must be float32 of shape {list(lse_shape)} (the forward's)")
+    _on_device(q, (("q", q), ("k", k), ("v", v)), "")
+    for name, t in (("o", o), ("do", do), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
 
 
 def _kv_len_arg(kv_len, batch, n, device):
@@ -110,11 +139,10 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
                    kv_len=None, window=None, block_index=None):
     """Backward from the saved LSE: returns (dq, dk, dv); dk, dv shaped like
     k, v (summed over each K/V head's group of query heads)."""
-    hkv = _check_qkv(q, k, v)
-    if o.shape != q.shape or do.shape != q.shape or o.dtype != q.dtype or do.dtype != q.dtype:
-        raise ValueError("o and do must match q in shape and dtype")
-    o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
+    hkv = _check_qkv(q, k, v, devices=False)
     b, h, n, d = q.shape
+    _check_saved(q, k, v, o, lse, do, (b, h, n))
+    o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     kvl = _kv_len_arg(kv_len, b, n, q.device)
     dt = _DTYPES[q.dtype]
@@ -131,12 +159,7 @@ def flash_attn_bwd(q, k, v, o, lse, do, causal=False, softmax_scale=None,
     return dq, dk, dv
 
 
-def _check_packed(q, k, v):
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [heads, total, d]")
+def _check_packed(q, k, v, devices=True):
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
         raise ValueError("q must be [heads, total, d] and k, v one [heads_kv, total, d] shape")
     h, total, d = q.shape
@@ -146,6 +169,8 @@ def _check_packed(q, k, v):
                          "divides q's")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if devices:
+        _on_device(q, (("q", q), ("k", k), ("v", v)), "[heads, total, d]")
     return hkv
 
 
@@ -189,11 +214,10 @@ def flash_attn_varlen_bwd(q, k, v, o, lse, do, cu_seqlens, max_seqlen=None, caus
                           softmax_scale=None, window=None, block_index=None):
     """Backward of ``flash_attn_varlen_fwd`` from the saved LSE: returns
     (dq, dk, dv) shaped like q, k, v."""
-    hkv = _check_packed(q, k, v)
-    if o.shape != q.shape or do.shape != q.shape or o.dtype != q.dtype or do.dtype != q.dtype:
-        raise ValueError("o and do must match q in shape and dtype")
-    o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
+    hkv = _check_packed(q, k, v, devices=False)
     h, total, d = q.shape
+    _check_saved(q, k, v, o, lse, do, (h, total))
+    o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     cu, nseq, mx = _cu_seqlens_arg(cu_seqlens, total, max_seqlen, q.device)
     dt = _DTYPES[q.dtype]
@@ -306,14 +330,23 @@ def flash_attn_fp8_fwd_codes(q8, q_scales, k8, k_scales, v8, v_scales, n, causal
                              softmax_scale=None, kv_len=None):
     """FP8 forward on encoded operands (``fp8_quantize`` layouts: q8, k8
     "rows", v8 "vt"). Returns (o bf16 [batch, heads, n, d], lse float32)."""
+    if q8.dim() != 4 or k8.dim() != 4:
+        raise ValueError("q8 and k8 must be [batch, heads, np, d] codes")
     b, h, np_, d = q8.shape
     hkv = k8.shape[1]
     if np_ != _fp8_rows(n) or k8.shape != (b, hkv, np_, d) or \
             v8.shape != (b, hkv, np_ // _b.FA_BLOCK, d, _b.FA_BLOCK):
         raise ValueError("codes do not match the fp8_quantize layouts for this n")
-    for t in (q8, k8, v8, q_scales, k_scales, v_scales):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("codes and scales must be contiguous GPU tensors")
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be uint8 E4M3 codes")
+    nb = np_ // _b.FA_BLOCK
+    for name, t, hh in (("q_scales", q_scales, h), ("k_scales", k_scales, hkv),
+                        ("v_scales", v_scales, hkv)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (b, hh, nb):
+            raise ValueError(f"{name} must be float32 of shape {[b, hh, nb]}")
+    _on_device(q8, (("q8", q8), ("k8", k8), ("v8", v8), ("q_scales", q_scales),
+                    ("k_scales", k_scales), ("v_scales", v_scales)), "(fp8_quantize layout)")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     o = torch.empty((b, h, n, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q8.device)

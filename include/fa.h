@@ -393,11 +393,15 @@ fa_status fa_fp8_quantize(int64_t batch, int64_t heads, int64_t n, int64_t d,
  * as for fa_fwd_gqa. Both products run on the E4M3 matrix cores with FP32
  * accumulation. With t_ij = softmax_scale * log2(e) * (sq q^_i . sk k^_j)
  * and the integer row frame f_i = ceil(max_j t_ij) over the visible keys,
- * the probabilities enter the P V product as E4M3(2^(t_ij - f_i + 8)) and
- *     O_i   = sum_j E4M3(2^(t_ij - f_i + 8)) sv v^_j / l_i,
- *     l_i   = sum_j 2^(t_ij - f_i + 8),
+ * the probabilities enter the P V product as P^_ij = E4M3(2^(t_ij - f_i + 8))
+ * and
+ *     O_i   = sum_j P^_ij sv v^_j / l_i,
+ *     l_i   = sum_j P^_ij   (the sum of the ROUNDED probabilities, taken on
+ *             the matrix cores with the same operands as the P V product),
  *     LSE_i = ln 2 * (f_i - 8 + log2 l_i)   (natural log of the row's sum
- *             of exp(scores)),
+ *             of exp(scores), up to the rounding of the probabilities: each
+ *             is within half an E4M3 step, 2^-4 relative, of its exact
+ *             value, so LSE_i is within ln(1 + 2^-4) of the exact one),
  * up to the matrix cores' fp32 accumulation. The frame is an integer, so the
  * rounding of a probability does not depend on the order in which the key
  * tiles are visited. o: bf16 [batch, heads, n, d]; lse: float32 [batch,

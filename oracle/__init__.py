@@ -29,10 +29,13 @@ Modules:
 * ``online``    -- the pages' online-softmax algebra (three-, two- and
   one-pass forms, per-block update, associative block merge), used to pin
   ``attention`` and as the reading of the tiled recurrence.
-* ``fp8``       -- the FP8 forward of page 2 4.5.4: E4M3 rounding, per-block
-  power-of-two scales, the optional random Hadamard rotation of Q and K,
-  both products on E4M3 operands with the probabilities quantised in an
-  integer row frame (pinned by ``tests/test_oracle_fp8.py``).
+* ``fp8``       -- page 2 4.5.4's FP8 recipe: the E4M3 format (rounding,
+  decoding), per-block power-of-two scales and the optional random Hadamard
+  rotation of Q and K are definitions; its forward on codes (probabilities
+  quantised in an integer row frame, row sums of the rounded values) is a
+  model of the GPU kernel's arithmetic, a secondary diagnostic. The FP8
+  forward's parity gate is ``attention.head_forward`` on the dequantised
+  operands (pinned by ``tests/test_oracle_fp8.py``).
 
 Parity status: every function here is pinned by ``tests/test_oracle.py`` or
 ``tests/test_oracle_fp8.py``

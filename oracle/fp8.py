@@ -3,6 +3,21 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
 product path.
 
+Two roles, kept apart:
+
+* The format and the encoder (E4M3 rounding and decoding, block exponents,
+  the Hadamard rotation, ``quantize``) are definitions: they follow the page
+  and the format, and the GPU encoder must match them code for code.
+* The forward on codes (``fp8_head_forward`` and the functions built on it)
+  is a MODEL OF THE KERNEL'S ARITHMETIC, not the definition of what the FP8
+  forward computes: the integer row frame and the row sum of the rounded
+  probabilities below are the kernel's own design choices (readings the page
+  leaves open). It serves as a secondary, tighter diagnostic. The parity
+  gate of the FP8 forward is exact attention (``attention.head_forward``)
+  on the dequantised operands, within a bound that follows from E4M3
+  rounding of the probabilities alone (half an E4M3 step, 2^-4 relative,
+  per weight) and fp32 accumulation.
+
 Page 2 ("4. FlashAttention 深度剖析"), 4.5.4 (FP8 support), fixes the recipe:
 the forward runs its products on E4M3 operands; every block is scaled once,
 when it is loaded, and its scale factor is kept; the FP8 products accumulate

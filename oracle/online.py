@@ -112,15 +112,23 @@ def block_state(x, v):
     return (m, float(w.sum()), w @ v)
 
 
-def merge(a, b):
-    """Merge two block states (page 2, 4.2.4): m = max(m_A, m_B),
-    l = l_A e^(m_A - m) + l_B e^(m_B - m), O~ likewise."""
-    m_a, l_a, o_a = a
-    m_b, l_b, o_b = b
-    m = max(m_a, m_b)
-    e_a = float(_rescale(m_a, m))
-    e_b = float(_rescale(m_b, m))
-    return (m, e_a * l_a + e_b * l_b, e_a * np.asarray(o_a) + e_b * np.asarray(o_b))
+def merge(*states):
+    """Combine any number of block states into the state of their union
+    (page 2, 4.2.4, the merge equation for two blocks, applied to all at
+    once). A state (m, l, O~) stands for l = sum e^(x - m) and O~ = sum
+    e^(x - m) v over its block; re-expressed against a common reference R
+    every sum is multiplied by e^(m - R), after which the sums over disjoint
+    blocks simply add. R is the largest m, so no factor exceeds 1 (empty
+    states, m = -inf, contribute 0)."""
+    if not states:
+        raise ValueError("merge needs at least one state")
+    ref = max(st[0] for st in states)
+    l_tot, o_tot = 0.0, 0.0
+    for m_s, l_s, o_s in states:
+        factor = float(_rescale(m_s, ref))
+        l_tot = l_tot + factor * l_s
+        o_tot = o_tot + factor * np.asarray(o_s, dtype=np.float64)
+    return (ref, l_tot, o_tot)
 
 
 def block_update(state, s_block, v_block):

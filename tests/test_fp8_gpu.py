@@ -1,38 +1,61 @@
 """GPU parity of the FP8 (E4M3) forward (page 2, "4. FlashAttention 深度剖析",
-4.5.4) against the oracle in oracle/fp8.py, through the C ABI.
+4.5.4), through the C ABI.
 
+Primary gate -- exact attention on the operands the kernel sees. The codes
+the GPU encoder wrote are read back and decoded with torch's own E4M3 type
+(float8_e4m3fn), multiplied by their block scales, and the plain fp64
+definition of attention (oracle.head_forward, the same oracle as the bf16
+path) runs on those dequantised (and, with the Hadamard rotation, rotated)
+Q, K, V. The GPU output must lie within a bound derived only from what the
+page fixes for the FP8 forward:
+
+* The probabilities enter the P V product as E4M3 values, so each weight
+  carries at most half an E4M3 step of error: 2^-4 relative in the normal
+  range. The weights of a row are scaled so that its largest lies in the
+  top binade below the format's maximum, (128, 256]; weights that end up
+  below the smallest normal (2^-6) are off by at most half a subnormal
+  step, 2^-10, doubled here to 2^-9 because the kernel's own rounded
+  maximum may put the row's scaling one binade higher.
+* The products accumulate in fp32 (page 2 4.5.4) on the matrix cores,
+  which sum E4M3 products with a truncation of up to 2^-12.5 of the summed
+  magnitudes (measured; bound here by EPS_MMA = 2^-10): a score moves by
+  at most EPS_MMA times its summed magnitudes, which scales its weight by
+  at most ln 2 times that (plus 2^-20 for exp2 and fp32 rounding); the row
+  sum and the P V product move by EPS_MMA of their summed magnitudes.
+* O is rounded to bf16 (2^-9 relative; 2^-8 allowed).
+
+With u_j the exact weights in that scaling, delta_j their allowance,
+numerator error a_c and row-sum error b:
+    |O_gpu - O|_c <= (sum_j delta_j |v_jc - O_c| + a_c + |O_c| b) / (sum_j u_j - b')
+    |LSE_gpu - LSE| <= -ln(1 - b' / sum_j u_j)
+(b' = sum_j delta_j + b). The LSE bound is at most ln(1 + 2^-4)-ish when
+every weight of a row rounds the same way by a full half step; typical
+errors are far smaller and are printed.
+
+Diagnostic -- the kernel against a model of its own arithmetic
+(oracle/fp8.py: probabilities rounded in an integer row frame, row sums of
+the rounded values). With identical codes on both sides the GPU must follow
+that model up to the neighbouring-code roundings its fp32 scores allow:
 * Quantiser: codes and scales of fa_fp8_quantize equal the oracle's bit for
   bit without a rotation (the scaling is exact and both round to nearest
   even); with the Hadamard rotation (fp32 butterflies on the GPU, fp64 in
   the oracle) a code may differ only by one step, and only where the
   oracle's exact value lies within fp32 rounding of a rounding boundary.
-* Forward on the oracle's own codes (so both sides see identical operands):
-  element by element with a tolerance derived from the arithmetic, below.
-* The whole recipe (GPU quantiser + forward) against the oracle's.
-* The full long-sequence size (B=1, H=32, N=16384, d=128, causal) in the
-  launch configuration the benchmark times, on sampled rows.
+* Forward on identical codes: element by element, within the envelope
+  below, and normwise within 1e-2 (the bf16 path's bar for O).
 
-Tolerance of the forward. The matrix cores accumulate fp8 products in fp32
-but not faithfully: a 64-term product was measured off by up to
-2^-12.5 * sum |a_k b_k| on random E4M3 operands, so the bound used here is
-eps = 2^-10 * sum |a_k b_k| (a 5x margin). A score's base-2 value t then
-deviates by at most dt = eps * sum_k |q^_k k^_k| * c + 2^-22 |t|, and a
-probability u = 2^(t - f + 8) by a relative delta = ln 2 * dt + 2^-20 (exp2
-and fp32 rounding). Where E4M3(u (1 - delta)) != E4M3(u (1 + delta)) the
-GPU may legitimately round u to the neighbouring code: that element may move
-O_i by the code step times |v_j| / l_i. Probabilities below 2^-5 of the row
-frame may be rounded in a finer running frame (or the frame itself may
-differ by one): at most 2^-9 each. The row sum l is the sum of the same
-rounded values (taken on the matrix cores): it moves by those steps and by
-eps * l, and the O product by eps * sum_j P^_ij |v_j|; with numerator error
-a and row-sum error b, |dO_i| <= (a + |O_i| b) / (l_i - b). On top: the
-bf16 rounding of O (2^-9 relative; 2^-8 is allowed) and 1e-5 absolute.
-
-That envelope holds for any accumulation order the hardware may use, so it
-is wide (often a tenth of |O|). Each head must also meet a normwise bound,
-|O_gpu - O_oracle| <= 1e-2 |O_oracle|, the bf16 path's bar for O: the bf16
-rounding of O alone gives about 2e-3, and the neighbouring-code roundings
-above are rare; a wrong key, block scale, frame or tile moves O by far more.
+Envelope of the model check. With the same EPS_MMA, a score's base-2 value
+t deviates by at most dt = eps * sum_k |q^_k k^_k| * c + 2^-22 |t|, and a
+probability u = 2^(t - f + 8) by a relative delta = ln 2 * dt + 2^-20.
+Where E4M3(u (1 - delta)) != E4M3(u (1 + delta)) the GPU may legitimately
+round u to the neighbouring code: that element may move O_i by the code
+step times |v_j| / l_i. Probabilities below 2^-5 of the row frame may be
+rounded in a finer running frame (or the frame itself may differ by one):
+at most 2^-9 each. The row sum l is the sum of the same rounded values
+(taken on the matrix cores): it moves by those steps and by eps * l, and the
+O product by eps * sum_j P^_ij |v_j|; with numerator error a and row-sum
+error b, |dO_i| <= (a + |O_i| b) / (l_i - b). On top: the bf16 rounding of
+O (2^-9 relative; 2^-8 is allowed) and 1e-5 absolute.
 """
 
 import math
@@ -121,6 +144,167 @@ def _check_head(o_gpu, lse_gpu, qc, qs, kc, ks, vc, vs, n, scale, causal, kvb, r
           f"median tol/|o| {np.median(tol / np.maximum(np.abs(ref), 1e-30)):.3e}", flush=True)
     assert nw <= NORMWISE_TOL, nw
     return nw
+
+
+# --------------------------------------------------------------------------
+# Primary gate: exact attention on the dequantised operands
+# --------------------------------------------------------------------------
+
+LOG2E = 1.0 / math.log(2.0)
+SUB_ABS = 2.0 ** -9       # subnormal weights: half a step, x2 for a frame one higher
+HALF_STEP_REL = 2.0 ** -4  # normal weights: half an E4M3 step (3 mantissa bits)
+
+
+def _decode(codes, scales):
+    """scale * value of each code of one head: codes [np, d] (uint8, rows
+    layout), scales [nb] -- decoded with torch's float8_e4m3fn type."""
+    c = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn)
+    vals = c.to(torch.float64).numpy()
+    rows = np.arange(vals.shape[0]) // 128
+    return vals * np.asarray(scales, dtype=np.float64)[rows][:, None]
+
+
+def _gpu_codes(x, signs=None, layout="rows"):
+    """GPU encoder output for a bf16 CPU tensor, read back to the host, in
+    the rows layout [B, H, np, d] (V blocks transposed back)."""
+    codes, scales = fa.fp8_quantize(x.cuda(), None if signs is None else _dev(signs),
+                                    layout=layout)
+    torch.cuda.synchronize()
+    c = codes.cpu().numpy()
+    if layout == "vt":
+        b, h, nb, d, blk = c.shape
+        c = np.ascontiguousarray(c.transpose(0, 1, 2, 4, 3).reshape(b, h, nb * blk, d))
+    return c, scales.cpu().numpy()
+
+
+def _check_exact(o_gpu, lse_gpu, qd, kd, vd, scale, causal, kvb, rows=None):
+    """O and LSE of one head (optionally only query ``rows``) against the
+    fp64 definition of attention on dequantised operands qd, kd, vd [n, d],
+    within the E4M3-derived bound of the module docstring."""
+    import oracle
+    from oracle.attention import visible_mask
+
+    n = kd.shape[0]
+    ref = oracle.head_forward(qd, kd, vd, scale, causal, kvb, rows=rows)
+    qr = qd if rows is None else qd[np.asarray(rows, dtype=np.int64)]
+    vis = visible_mask(n, causal, kvb, rows)
+    t = np.where(vis, scale * (qr @ kd.T) * LOG2E, -np.inf)
+    tmax = t.max(axis=1)
+    has = np.isfinite(tmax)
+    frame = np.where(has, np.ceil(np.where(has, tmax, 0.0)), 0.0)
+    u = np.where(vis, np.exp2(t - frame[:, None] + 8.0), 0.0)   # row max in (128, 256]
+    tabs = abs(scale) * LOG2E * (np.abs(qr) @ np.abs(kd).T)
+    rho = math.log(2.0) * (EPS_MMA * tabs + 2.0 ** -22 * np.abs(np.where(vis, t, 0.0))) + 2.0 ** -20
+    delta = np.where(vis, (HALF_STEP_REL * (1 + rho) + rho) * u + SUB_ABS, 0.0)
+    lsum = u.sum(axis=1)
+    pmax = u + delta
+    o = ref["o"]
+    av = np.abs(vd)
+    # numerator: rounded weights, then the P V product's accumulation
+    num = EPS_MMA * (pmax @ av)
+    step = max(1, (1 << 23) // (n * vd.shape[1]))            # rows per chunk (64 MB)
+    for r0 in range(0, o.shape[0], step):
+        r1 = min(r0 + step, o.shape[0])
+        dev = np.abs(vd[None, :, :] - o[r0:r1, None, :])
+        num[r0:r1] += np.einsum("rj,rjc->rc", delta[r0:r1], dev)
+    b_sum = EPS_MMA * pmax.sum(axis=1)                      # row-sum accumulation
+    b_all = delta.sum(axis=1) + b_sum
+    den = np.where(has, lsum - b_all, 1.0)
+    assert np.all(den[has] > 0.5 * lsum[has])
+    tol = (num + np.abs(o) * b_sum[:, None]) / den[:, None]
+    tol = tol + 2.0 ** -8 * (np.abs(o) + tol) + 1e-6          # bf16 rounding of O
+    got = o_gpu.astype(np.float64)
+    err = np.abs(got - o)
+    bad = (err > tol) & has[:, None]
+    assert not bad.any(), (f"{bad.sum()} elements out of the E4M3 bound; worst excess "
+                           f"{(err - tol).max():.3g}")
+    assert np.all(got[~has] == 0.0)
+    lref = ref["lse"]
+    assert np.array_equal(np.isfinite(lse_gpu), has)
+    ltol = -np.log1p(-np.where(has, b_all / np.where(has, lsum, 1.0), 0.0)) \
+        + 2.0 ** -20 * np.abs(np.where(has, lref, 0.0)) + 1e-6
+    lerr = np.abs(np.where(has, lse_gpu - lref, 0.0))
+    assert np.all(lerr <= ltol), float((lerr - ltol).max())
+    nw = float(np.linalg.norm(got - o) / max(np.linalg.norm(o), 1e-30))
+    print(f"[fp8 exact] normwise O err {nw:.3e} (max elem {err.max():.3e}, median bound "
+          f"{np.median(tol[has]):.3e}); LSE err max {lerr.max():.3e} mean "
+          f"{lerr[has].mean() if has.any() else 0.0:.3e}, bound median "
+          f"{np.median(ltol[has]) if has.any() else 0.0:.3e}", flush=True)
+    return nw, float(lerr.max())
+
+
+EXACT = [
+    # (batch, heads, heads_kv, n, d, causal, padded, qk_sigma, scale, rotate)
+    (2, 4, 2, 300, 128, True, False, 1.0, None, False),
+    (2, 4, 2, 300, 128, False, True, 1.0, None, True),
+    (1, 2, 2, 1000, 128, True, False, 3.0, None, True),    # peaky rows: the row max moves
+    (1, 2, 1, 777, 128, False, False, 1.0, None, False),   # multi-query
+    (2, 2, 2, 257, 128, True, True, 1.0, -0.07, False),    # negative scale
+    (1, 2, 2, 200, 128, False, False, 1.0, 0.0, False),    # zero scale: uniform weights
+    (1, 1, 1, 1, 128, True, False, 1.0, None, False),
+    (2, 4, 2, 300, 64, True, True, 1.0, None, True),
+    (1, 2, 1, 1000, 64, False, False, 3.0, None, False),   # peaky, multi-query
+    (1, 2, 2, 129, 64, True, False, 1.0, -0.2, True),
+]
+
+
+@pytest.mark.parametrize("batch,heads,heads_kv,n,d,causal,padded,sigma,scale,rotate", EXACT)
+def test_against_exact_attention_on_dequantised_operands(batch, heads, heads_kv, n, d, causal,
+                                                         padded, sigma, scale, rotate):
+    w = custom(f"fp8x_b{batch}_h{heads}_kv{heads_kv}_n{n}", batch, heads, n, d, "bf16", causal,
+               seed=n * 17 + heads + d, qk_sigma=sigma, padded=padded, heads_kv=heads_kv)
+    inp = make_inputs(w, with_grad_out=False)
+    print(f"[fp8 exact] b={batch} h={heads} kv={heads_kv} n={n} d={d} causal={causal} "
+          f"padded={padded} sigma={sigma} scale={scale} rotate={rotate}", flush=True)
+    sc = w.softmax_scale if scale is None else scale
+    signs = _signs(d, n) if rotate else None
+    kvl = None if inp["kv_len"] is None else inp["kv_len"].cuda()
+    o, lse = fa.flash_attn_fp8_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), causal,
+                                   sc, kvl, None if signs is None else _dev(signs))
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    qc, qs = _gpu_codes(inp["q"], signs)
+    kc, ks = _gpu_codes(inp["k"], signs)
+    vc, vs = _gpu_codes(inp["v"], layout="vt")
+    g = heads // heads_kv
+    for b in range(batch):
+        kvb = None if inp["kv_len"] is None else int(inp["kv_len"][b])
+        for h in range(heads):
+            j = h // g
+            _check_exact(o[b, h], lse[b, h], _decode(qc[b, h], qs[b, h])[:n],
+                         _decode(kc[b, j], ks[b, j])[:n], _decode(vc[b, j], vs[b, j])[:n], sc,
+                         causal, kvb)
+
+
+def test_exact_attention_full_size_sampled_rows():
+    """The long causal size (B=1, H=32, N=16384, d=128, Q, K std 3) in the
+    launch configuration the benchmark times: GPU encoder with the rotation,
+    then the forward; sampled rows of four heads against exact attention on
+    the decoded operands."""
+    w = WORKLOADS["long_causal_b1_h32_n16384_d128"]
+    n, heads = w.n, w.heads
+    g = torch.Generator().manual_seed(w.seed)
+    q = (torch.randn(1, 2, n, 128, generator=g) * w.qk_sigma).to(torch.bfloat16)
+    k = (torch.randn(1, 2, n, 128, generator=g) * w.qk_sigma).to(torch.bfloat16)
+    v = torch.randn(1, 2, n, 128, generator=g).to(torch.bfloat16)
+    rep = lambda t: t.repeat(1, heads // 2, 1, 1).contiguous()  # noqa: E731
+    signs = _signs(128, 44)
+    print(f"[fp8 exact] full size n={n} heads={heads}", flush=True)
+    o, lse = fa.flash_attn_fp8_fwd(rep(q).cuda(), rep(k).cuda(), rep(v).cuda(), True,
+                                   w.softmax_scale, None, _dev(signs))
+    torch.cuda.synchronize()
+    qc, qs = _gpu_codes(q, signs)
+    kc, ks = _gpu_codes(k, signs)
+    vc, vs = _gpu_codes(v, layout="vt")
+    rows = np.unique(np.concatenate([np.arange(0, 24), np.random.default_rng(8).integers(0, n, 40),
+                                     np.arange(n - 24, n)]))
+    ridx = torch.from_numpy(rows).cuda()
+    for h in (0, 1, heads - 2, heads - 1):
+        hs = h % 2
+        og = o[0, h, ridx].float().cpu().numpy()
+        lg = lse[0, h, ridx].cpu().numpy()
+        _check_exact(og, lg, _decode(qc[0, hs], qs[0, hs])[:n], _decode(kc[0, hs], ks[0, hs])[:n],
+                     _decode(vc[0, hs], vs[0, hs])[:n], w.softmax_scale, True, None, rows=rows)
 
 
 # --------------------------------------------------------------------------
@@ -243,6 +427,11 @@ def test_rotated_codes_forward():
 
 @pytest.mark.parametrize("rotate,d", [(False, 128), (True, 128), (False, 64), (True, 64)])
 def test_end_to_end_against_oracle(rotate, d):
+    """The whole recipe (GPU encoder, then the forward): against exact
+    attention on the decoded operands (the primary gate), and against the
+    model of the kernel's arithmetic run on the GPU encoder's own codes
+    (with a rotation these may differ from the oracle encoder's by one step
+    in rare elements, which the quantiser test bounds)."""
     w = custom("fp8_e2e", 2, 4, 600, d, "bf16", True, seed=91 + d, padded=True, heads_kv=2)
     inp = make_inputs(w, with_grad_out=False)
     signs = _signs(d, 9) if rotate else None
@@ -252,27 +441,18 @@ def test_end_to_end_against_oracle(rotate, d):
                                    signs=None if signs is None else _dev(signs))
     torch.cuda.synchronize()
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
-    qc, qs = _oracle_codes(inp["q"], signs)
-    kc, ks = _oracle_codes(inp["k"], signs)
-    vc, vs = _oracle_codes(inp["v"])
-    if not rotate:
-        # Identical codes on both sides (the quantiser is exact here).
-        for b in range(2):
-            for h in range(4):
-                _check_head(o[b, h], lse[b, h], qc[b, h], qs[b, h], kc[b, h // 2],
-                            ks[b, h // 2], vc[b, h // 2], vs[b, h // 2], 600, w.softmax_scale,
-                            True, int(inp["kv_len"][b]))
-    ro, rl = of.fp8_attention_fwd(inp["q"].float().numpy(), inp["k"].float().numpy(),
-                                  inp["v"].float().numpy(), causal=True,
-                                  kv_len=inp["kv_len"].numpy(),
-                                  signs=None if signs is None else signs.astype(np.float64))
-    err = np.linalg.norm(o - ro) / np.linalg.norm(ro)
-    assert err < 4e-3, err
-    # LSE: one neighbouring-code rounding of a row's dominant probability
-    # moves it by at most ln(1 + 2^-4); such roundings are rare, so the mean
-    # deviation stays small.
-    dl = np.abs(lse - rl)
-    assert dl.max() <= math.log1p(2.0 ** -4) and dl.mean() < 1e-3, (dl.max(), dl.mean())
+    qc, qs = _gpu_codes(inp["q"], signs)
+    kc, ks = _gpu_codes(inp["k"], signs)
+    vc, vs = _gpu_codes(inp["v"], layout="vt")
+    for b in range(2):
+        kvb = int(inp["kv_len"][b])
+        for h in range(4):
+            j = h // 2
+            _check_exact(o[b, h], lse[b, h], _decode(qc[b, h], qs[b, h])[:600],
+                         _decode(kc[b, j], ks[b, j])[:600], _decode(vc[b, j], vs[b, j])[:600],
+                         w.softmax_scale, True, kvb)
+            _check_head(o[b, h], lse[b, h], qc[b, h], qs[b, h], kc[b, j], ks[b, j], vc[b, j],
+                        vs[b, j], 600, w.softmax_scale, True, kvb)
 
 
 # --------------------------------------------------------------------------

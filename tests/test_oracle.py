@@ -162,7 +162,8 @@ def test_merge_is_associative_over_partitions_and_trees(trial):
     for s in reversed(parts[:-1]):
         right = online.merge(s, right)
     tree = _tree_merge(rng, parts)
-    for st in (left, right, tree):
+    flat = online.merge(*parts)  # every block state at once
+    for st in (left, right, tree, flat):
         assert st[0] == whole[0]
         assert abs(st[1] - whole[1]) <= 1e-12 * whole[1]
         np.testing.assert_allclose(st[2], whole[2], rtol=1e-12, atol=1e-12)

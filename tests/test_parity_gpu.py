@@ -95,17 +95,23 @@ def test_sweep_n2048_two_heads_in_full(name):
 
 
 @pytest.mark.parametrize("name", SWEEP_ROWS)
-def test_sweep_longer_sampled_rows(name):
+def test_sweep_longer_one_head_in_full(name):
+    """N = 4096 and 8192 (every d, causal and not): one (b, h) head in full,
+    forward and backward, against the fp64 oracle; seeded rows of another
+    head forward; finite gradients everywhere."""
     w = WORKLOADS[name]
     inp = workload_inputs(w)
     print(f"[parity] {name}", flush=True)
     gpu = run_gpu(w, inp)
+    for name_ in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.isfinite(gpu[name_]).all(), name_
     rng = np.random.default_rng(w.seed)
-    for b, h in ((0, 0), (1, 11)):
-        rows = np.sort(rng.choice(w.n, size=16, replace=False))
-        check_forward_head(w, inp, gpu, b, h, rows=rows)
-    for name_ in ("dq", "dk", "dv"):
-        assert torch.isfinite(gpu[name_]).all()
+    rows = np.sort(rng.choice(w.n, size=16, replace=False))
+    check_forward_head(w, inp, gpu, 0, 0, rows=rows)
+    b, h = 1, int(rng.integers(0, w.heads))
+    print(f"[parity] {name}: head ({b}, {h}) in full, fp64 oracle fwd+bwd", flush=True)
+    check_forward_head(w, inp, gpu, b, h)
+    check_backward_head(w, inp, gpu, b, h)
 
 
 EDGE = [
@@ -169,3 +175,12 @@ def test_wrapper_rejects_bad_arguments():
     y = torch.randn(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError, match="FA_E_UNSUPPORTED"):
         flash_attn_fwd(y, y, y)
+    # The backward's saved tensors must be GPU tensors on q's device too.
+    from exact_io_aware_fa_amd.attention import flash_attn_bwd
+    o, lse = flash_attn_fwd(g, g, g)
+    with pytest.raises(ValueError, match="lse must be a GPU tensor"):
+        flash_attn_bwd(g, g, g, o, lse.cpu(), g)
+    with pytest.raises(ValueError, match="do must be a GPU tensor"):
+        flash_attn_bwd(g, g, g, o, lse, x)
+    with pytest.raises(ValueError, match="lse must be float32 of shape"):
+        flash_attn_bwd(g, g, g, o, lse[:, :, :32], g)
