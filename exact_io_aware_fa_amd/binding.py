@@ -26,16 +26,20 @@ FA_E_WORKSPACE = 4
 FA_E_ALIAS = 5
 FA_E_LAUNCH = 6
 FA_E_ALIGN = 7
+FA_E_SCRATCH = 8
+
+# Size of the static scratch fa_bwd_noalloc uses on each device.
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # Every symbol include/fa.h declares.
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_masked", "fa_fwd_varlen", "fa_bwd",
-            "fa_bwd_gqa", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_timed",
+            "fa_bwd_gqa", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_timed", "fa_bwd_noalloc",
             "fa_bwd_workspace_bytes", "fa_block_index_bytes", "fa_block_index_build",
             "fa_fp8_codes_bytes", "fa_fp8_scales_bytes", "fa_fp8_quantize", "fa_fwd_fp8",
             "fa_status_str", "fa_abi_version")
 
 # The FA_ABI_VERSION this binding was written against.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 FA_BLOCK = 128
 
@@ -102,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.fa_block_index_bytes.argtypes = [_i64]
         L.fa_block_index_build.restype = ctypes.c_int
         L.fa_block_index_build.argtypes = [_i64, _vp, _vp, _vp]
+        L.fa_bwd_noalloc.restype = ctypes.c_int
+        L.fa_bwd_noalloc.argtypes = L.fa_bwd_gqa.argtypes[:18] + [_vp]
         L.fa_bwd_timed.restype = ctypes.c_int
         L.fa_bwd_timed.argtypes = L.fa_bwd_gqa.argtypes + [ctypes.POINTER(_vp)]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -200,6 +206,13 @@ def fa_bwd_gqa(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k,
                             float(softmax_scale), int(dtype), q, k, v, o, d_o, lse,
                             kv_len, dq, dk, dv, workspace, int(workspace_bytes),
                             stream)
+
+
+def fa_bwd_noalloc(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k, v, o,
+                   d_o, lse, kv_len, dq, dk, dv, stream) -> int:
+    return lib().fa_bwd_noalloc(batch, heads, heads_kv, n, d, int(causal),
+                                float(softmax_scale), int(dtype), q, k, v, o, d_o, lse,
+                                kv_len, dq, dk, dv, stream)
 
 
 def fa_bwd_timed(batch, heads, heads_kv, n, d, causal, softmax_scale, dtype, q, k,

@@ -7,8 +7,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_internal.h"
+
+// Scratch of fa_bwd_noalloc: the backward workspace (the D and L log2 e
+// vectors) for callers that cannot allocate. One copy per device, at its own
+// device address, held until the process ends. In host code `scratch` names
+// a host-side stand-in, never the device memory: the device address comes
+// from noalloc_scratch() below and is the only one ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -262,6 +271,38 @@ fa_status check_fp8_shape(int64_t batch, int64_t heads, int64_t heads_kv, int64_
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Per-device address of `scratch`, looked up once per device with that device
+// current (hipGetSymbolAddress), under a lock.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0)
+      return hipErrorInvalidSymbol;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,6 +418,9 @@ const char* fa_status_str(fa_status s) {
     case FA_E_ALIAS: return "FA_E_ALIAS: an output overlaps an input or another output";
     case FA_E_LAUNCH: return "FA_E_LAUNCH: kernel launch failed";
     case FA_E_ALIGN: return "FA_E_ALIGN: pointer not 16-byte aligned";
+    case FA_E_SCRATCH:
+      return "FA_E_SCRATCH: the call needs more scratch than fa_bwd_noalloc's static "
+             "FA_NOALLOC_SCRATCH_BYTES buffer; use fa_bwd_gqa with a workspace";
   }
   return "FA_E_UNKNOWN";
 }
@@ -475,6 +519,26 @@ fa_status fa_bwd_timed(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n
   return bwd_impl(padded_shape(batch, heads, heads_kv, n, d), causal, softmax_scale, dtype, q,
                   k, v, o, d_o, lse, kv_len, nullptr, dq, dk, dv, workspace, workspace_bytes,
                   stream, events);
+}
+
+fa_status fa_bwd_noalloc(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, int64_t d,
+                         int causal, float softmax_scale, fa_dtype dtype, const void* q,
+                         const void* k, const void* v, const void* o, const void* d_o,
+                         const float* lse, const int32_t* kv_len, void* dq, void* dk,
+                         void* dv, void* stream) {
+  // Sizes first, on the host only, so that a call too large for the static
+  // buffer is rejected before any HIP call.
+  const Shape sh = padded_shape(batch, heads, heads_kv, n, d);
+  fa_status st = check_shape(sh, softmax_scale, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = 2 * vec_bytes(sh.entries, sh.heads, sh.n);
+  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_E_SCRATCH;
+  void* ws = nullptr;
+  if (noalloc_scratch(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return FA_E_LAUNCH;
+  // The backward's prep kernel writes every element of the workspace the
+  // other kernels read, so nothing left by an earlier call is ever used.
+  return bwd_impl(sh, causal, softmax_scale, dtype, q, k, v, o, d_o, lse, kv_len, nullptr, dq,
+                  dk, dv, ws, FA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 size_t fa_block_index_bytes(int64_t n) {

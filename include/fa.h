@@ -102,7 +102,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
 
@@ -129,7 +129,9 @@ typedef enum {
   FA_E_WORKSPACE = 4,   /* workspace NULL or smaller than required           */
   FA_E_ALIAS = 5,       /* an output overlaps an input or another output     */
   FA_E_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch          */
-  FA_E_ALIGN = 7        /* a pointer is not 16-byte aligned                  */
+  FA_E_ALIGN = 7,       /* a pointer is not 16-byte aligned                  */
+  FA_E_SCRATCH = 8      /* fa_bwd_noalloc: the call needs more scratch than
+                           FA_NOALLOC_SCRATCH_BYTES                          */
 } fa_status;
 
 /*
@@ -292,6 +294,39 @@ fa_status fa_bwd_varlen(int64_t num_seqs, int64_t heads, int64_t heads_kv,
                         void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd_gqa for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments and results as fa_bwd_gqa, without the
+ * workspace: the library uses a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES bytes instead, one copy on each device it runs on,
+ * held until the process ends. The call allocates and frees nothing.
+ *
+ * Limit: calls whose fa_bwd_workspace_bytes(batch, heads, n, d, dtype)
+ * exceeds FA_NOALLOC_SCRATCH_BYTES (16 MiB: batch x heads x n up to about
+ * 2^21 rows, e.g. 32 heads of 65536 or 128 heads of 16384) return
+ * FA_E_SCRATCH before anything is enqueued; use fa_bwd_gqa for them.
+ * Every call on one device shares that device's array, and the array keeps
+ * whatever the last call left in it (each call writes every element it reads
+ * before reading it, so leftovers are never used). Calls that overlap in time
+ * on one device -- on different streams, or from different threads without
+ * ordering -- race on the array and give undefined results; calls ordered on
+ * one stream are safe. The array's device address is looked up on a device's
+ * first call (a HIP runtime query made with the stream's device current);
+ * make that first call outside graph capture. A failed lookup returns
+ * FA_E_LAUNCH.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+fa_status fa_bwd_noalloc(int64_t batch, int64_t heads, int64_t heads_kv,
+                         int64_t n, int64_t d,
+                         int causal, float softmax_scale, fa_dtype dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* o, const void* d_o, const float* lse,
+                         const int32_t* kv_len,
+                         void* dq, void* dk, void* dv,
+                         void* stream);
 
 /*
  * fa_block_index_bytes -- size of the block-sparse index for sequence

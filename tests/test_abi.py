@@ -44,10 +44,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.fa_abi_version() == B.ABI_VERSION == 5
+    assert B.fa_abi_version() == B.ABI_VERSION == 6
     for code, tag in ((0, "FA_OK"), (1, "FA_E_NULLPTR"), (2, "FA_E_SHAPE"),
                       (3, "FA_E_UNSUPPORTED"), (4, "FA_E_WORKSPACE"), (5, "FA_E_ALIAS"),
-                      (6, "FA_E_LAUNCH"), (7, "FA_E_ALIGN")):
+                      (6, "FA_E_LAUNCH"), (7, "FA_E_ALIGN"), (8, "FA_E_SCRATCH")):
         assert B.fa_status_str(code).startswith(tag)
     assert B.fa_status_str(99) == "FA_E_UNKNOWN"
 
@@ -314,3 +314,16 @@ def fwd8(**kw):
 ])
 def test_fwd_fp8_validation(lib, kw, code):
     assert fwd8(**kw) == code
+
+
+def test_bwd_noalloc_rejects_oversize_and_bad_shapes_before_any_hip_call(lib):
+    """fa_bwd_noalloc checks sizes on the host first: a call whose workspace
+    would exceed the static scratch returns FA_E_SCRATCH, bad shapes their
+    usual codes; neither touches the HIP runtime (no GPU here)."""
+    args = [Q, K, V, O, DO, L, None, DQ, DK, DV, None]
+    assert B.fa_bwd_workspace_bytes(1, 80, 32768, 128, B.FA_BF16) > B.FA_NOALLOC_SCRATCH_BYTES
+    assert B.fa_bwd_workspace_bytes(1, 32, 16384, 128, B.FA_BF16) <= B.FA_NOALLOC_SCRATCH_BYTES
+    assert B.fa_bwd_noalloc(1, 80, 80, 32768, 128, 1, 0.1, B.FA_BF16, *args) == B.FA_E_SCRATCH
+    assert B.fa_bwd_noalloc(1, 4, 3, 64, 64, 1, 0.1, B.FA_BF16, *args) == B.FA_E_SHAPE
+    assert B.fa_bwd_noalloc(1, 4, 4, 64, 96, 1, 0.1, B.FA_BF16, *args) == B.FA_E_UNSUPPORTED
+    assert B.fa_bwd_noalloc(0, 4, 4, 64, 64, 1, 0.1, B.FA_BF16, *args) == B.FA_E_SHAPE
