@@ -118,11 +118,87 @@ class HipEvents:
         self.rt.hipEventDestroy(ev)
 
 
-def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
-    """Time the fp64 oracle on whole heads (fwd+bwd) until ~budget_s."""
-    import numpy as np
+def host_info() -> dict:
+    """The host the CPU oracle runs on: CPU model, the cores this process may
+    use, and the BLAS library NumPy calls with its thread count."""
+    import numpy  # noqa: F401  (loads the BLAS threadpoolctl reports)
     from threadpoolctl import threadpool_info
 
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    vendor = ", ".join(sorted({"%s %s" % (i.get("internal_api", "?"), i.get("version", "?"))
+                               for i in blas})) or "none found"
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas": vendor, "blas_threads": int(threads)}
+
+
+class SclkSampler:
+    """Samples the GPU's current shader clock from sysfs (pp_dpm_sclk, the
+    level marked '*') in a background thread while the timed steps run; the
+    main thread waits in a device synchronisation meanwhile. Reports the
+    median, minimum and maximum in MHz and the number of samples."""
+
+    def __init__(self, period_s: float = 0.004):
+        import glob
+        import threading
+
+        cands = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = cands[0] if len(cands) == 1 else None
+        self.note = ("pp_dpm_sclk of %s" % self.path if self.path else
+                     "no unique pp_dpm_sclk (%d found)" % len(cands))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except (OSError, ValueError, IndexError):
+                v = None
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def result(self) -> dict:
+        import statistics
+
+        if not self.samples:
+            return {"source": self.note, "samples": 0}
+        return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
+                "max_mhz": max(self.samples), "samples": len(self.samples),
+                "source": self.note + ", sampled during the timed steps"}
+
+
+def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
+    """Time the fp64 oracle on whole heads (fwd+bwd) until ~budget_s."""
     import oracle
 
     heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
@@ -141,16 +217,18 @@ def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
             break
     per_head = spent / done
     flops_per_head = (w.flops_fwd() + w.flops_bwd()) / (w.batch * w.heads)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                   if i.get("user_api") == "blas"] or [1])
+    host = host_info()
     return {
         "value": flops_per_head / per_head / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": host["blas_threads"],
         "kind": "oracle",
         "sample": (f"{done} of {w.batch * w.heads} heads, fwd+bwd, fp64 NumPy "
                    f"(materialised S, P, dP, dS; no causal skipping), "
                    f"{per_head:.2f} s per head; FLOPs counted as for the GPU"),
+        "cpu_model": host["cpu_model"],
+        "affinity_cores": host["affinity_cores"],
+        "blas": host["blas"],
     }
 
 
@@ -160,7 +238,6 @@ def cpu_baseline_fp8(w, inp, signs, budget_s: float = 10.0, rows: int = 1024) ->
     for `rows` evenly spaced query rows (the oracle's row subset). FLOPs:
     4 d per visible (query, key) pair of the sampled rows, as for the GPU."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from oracle import fp8 as of
     from oracle.attention import visible_mask
@@ -188,13 +265,14 @@ def cpu_baseline_fp8(w, inp, signs, budget_s: float = 10.0, rows: int = 1024) ->
                 break
         if spent >= budget_s:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                   if i.get("user_api") == "blas"] or [1])
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    host = host_info()
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": host["blas_threads"],
             "kind": "oracle",
             "sample": f"{done} head(s): encode Q, K, V of the head, then the forward of "
                       f"{len(sel)} evenly spaced query rows against all keys, fp64 NumPy, "
-                      f"{spent / done:.2f} s per head"}
+                      f"{spent / done:.2f} s per head",
+            "cpu_model": host["cpu_model"], "affinity_cores": host["affinity_cores"],
+            "blas": host["blas"]}
 
 
 def load_traffic(src_hash: str, workload: str):
@@ -277,7 +355,38 @@ def summarize_sq(sq_db) -> list:
     return lines
 
 
-def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, out_json, sq_db=None):
+def summarize_tcc(tcc_db) -> list:
+    """Markdown lines for an L2 pass (TCC_HIT_sum, TCC_MISS_sum): per kernel,
+    the L2 requests per dispatch and the fraction that hit. A miss goes on
+    to the Infinity Cache (MALL) or HBM; FETCH_SIZE counts the bytes those
+    misses read."""
+    import sqlite3
+
+    per = {}
+    for kn, ctr, val, did in sqlite3.connect(tcc_db).execute(
+            "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+        d = per.setdefault(_short(kn), {}).setdefault(did, {})
+        d[ctr] = d.get(ctr, 0.0) + val
+    lines = ["", "## L2 hit rate (`--pmc TCC_HIT_sum TCC_MISS_sum` pass)", "",
+             "Per dispatch, averaged: hit rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum).", "",
+             "| kernel | dispatches | L2 requests (M) | hits (M) | misses (M) | hit rate |",
+             "|---|---|---|---|---|---|"]
+    for k, ds in per.items():
+        if k.startswith("__amd") or k.startswith("void at::"):
+            continue
+        n = len(ds)
+        hit = sum(d.get("TCC_HIT_sum", 0.0) for d in ds.values()) / n
+        miss = sum(d.get("TCC_MISS_sum", 0.0) for d in ds.values()) / n
+        tot = hit + miss
+        if tot <= 0:
+            continue
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.4f |" % (
+            k, n, tot / 1e6, hit / 1e6, miss / 1e6, hit / tot))
+    return lines
+
+
+def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, out_json, sq_db=None,
+                      tcc_db=None):
     """Summarise rocprofv3 databases (kernel trace + FETCH_SIZE + WRITE_SIZE
     passes, optionally an SQ counter pass) into a short markdown file and the
     traffic JSON this bench reads."""
@@ -328,6 +437,8 @@ def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, o
                                                                    rd / 1e9, wr / 1e9))
     if sq_db:
         lines += summarize_sq(sq_db)
+    if tcc_db:
+        lines += summarize_tcc(tcc_db)
     open(out_md, "w").write("\n".join(lines) + "\n")
     bwd = [k for k in traffic if k.startswith("bwd_dkdv_kernel")]
     if bwd and out_json:
@@ -722,9 +833,10 @@ def main() -> int:
         sp.add_argument("--out-md", required=True)
         sp.add_argument("--out-json", default=None)
         sp.add_argument("--sq-db", default=None, help="database of an SQ counter pass")
+        sp.add_argument("--tcc-db", default=None, help="database of an L2 hit/miss pass")
         a = sp.parse_args(sys.argv[2:])
         summarize_rocprof(a.trace_db, a.fetch_db, a.write_db, a.copy_mib, a.command, a.out_md, a.out_json,
-                          a.sq_db)
+                          a.sq_db, a.tcc_db)
         return 0
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -806,11 +918,12 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     fwd_ms = [hip.elapsed_ms(ev_f0[i], ev_f1[i]) for i in range(nev)]
     main_ms = [hip.elapsed_ms(ev_b[i][1], ev_b[i][2]) for i in range(nev)]
@@ -852,6 +965,7 @@ def main() -> int:
                 "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
                 "dkdv_kernel_ms": round(avg(main_ms), 4),
                 "dq_kernel_ms": round(avg(dq_ms), 4)},
+        "sclk": sclk.result(),
         "roofline": {
             "kernel": "bwd_dkdv_kernel (recompute backward, dK and dV, d=%d)" % d,
             "bound": "mfma",

@@ -72,3 +72,18 @@ def test_summarize_sq_skips_runtime_copies(tmp_path):
     _db(str(db), rows)
     lines = bench.summarize_sq(str(db))
     assert not [l for l in lines if "copyBuffer" in l]
+
+
+def test_summarize_tcc_hit_rate(tmp_path):
+    name = "void fa::(anonymous namespace)::bwd_dkdv_kernel<128, 1, true, false>(fa::Params)"
+    rows = []
+    for did in (1, 2):
+        rows += [(name, "TCC_HIT_sum", 9.0e6, 1000, did), (name, "TCC_MISS_sum", 1.0e6, 1000, did)]
+    db = tmp_path / "tcc.db"
+    _db(str(db), rows)
+    lines = bench.summarize_tcc(str(db))
+    row = [l for l in lines if l.startswith("| `bwd_dkdv_kernel")]
+    assert len(row) == 1, lines
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    assert cells[1] == "2" and float(cells[2]) == 10.0 and float(cells[3]) == 9.0
+    assert float(cells[5]) == 0.9
