@@ -46,6 +46,9 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kBR = 256;  // query rows per workgroup (8 waves x 32)
+// The reference of a row's probabilities trails its running max by at most
+// this much (base 2): probabilities stay in [0, 2^kLazy].
+constexpr float kLazy = 64.f;
 
 // Exchange with the other 32-lane half of the wave (v_permlane32_swap): the
 // two results hold the value of lane l % 32 and of lane l % 32 + 32 in some
@@ -142,8 +145,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   f32x16 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
-  float m2 = kNegInf;   // running max in scaled base-2 units (s * cs)
+  // Reference of the row's probabilities, in scaled base-2 units (s * cs):
+  // P = exp2(s * cs - fref). It is the exact running max when set, and is
+  // only moved up (with a rescale of O~, l and lcorr) once the running max
+  // runs more than kLazy above it, so probabilities lie in [0, 2^kLazy].
+  float fref = kNegInf;
   float lpart = 0.f;    // this half-wave's share of the running row sum
+  // Row-sum correction: for every tile, bf16(p_max) - p_max of the tile's
+  // largest probability (the same in both halves of the wave).
+  float lcorr = 0.f;
   f32x16 sc[NKB];       // scores of the tile between the two phases
   bf16x8 pf[NKB * 2];   // P^T fragments of the tile between the two phases
 #pragma unroll
@@ -278,37 +288,33 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
         sc[kb][r] = hidden ? kNegInf : sc[kb][r];
       }
   };
-  auto softmax = [&](int j) FA_INLINE {
-    // Row max and row sum use four independent partial results each, so the
-    // dependent-instruction chains are a quarter as long.
-    float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sc[kb][r]);
-    const float mt = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
-    // The reference is the exact running max, so the row's largest
-    // probability is exactly 1 before its bf16 rounding.
-    const float mt2 = (mt == kNegInf) ? kNegInf : mt * cs;
-    const float m2n = fmaxf(m2, mt2);
-    const float mref = (m2n == kNegInf) ? 0.f : m2n;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);  // 1 if unchanged, 0 while empty
-    m2 = m2n;
-
+  // The online update with a lazy reference (page 1 section 六's running
+  // max is still formed every tile, but O~ and l are rescaled only when it
+  // runs kLazy above the reference). Exactness of the result does not depend
+  // on the reference; what matters for accuracy is that the weights the P V
+  // product uses (bf16-rounded P) and the row sum it is normalised by agree.
+  // l sums the fp32 P (so the LSE is that of the fp32 probabilities), and
+  // lcorr adds, per tile, the rounding bf16(p) - p of the tile's largest
+  // probability: a row dominated by one key is then normalised by exactly
+  // the weight its product used. (With the exact max as reference that
+  // weight is exactly 1 and needs no correction; with a lazy one it is
+  // 2^delta, rounded.)
+  auto finish_tile = [&](float mt) FA_INLINE {
+    // sc holds t = s * cs - fref; mt is the row's largest t (-inf if none).
     float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], cs, -mref));
+        const float e = __builtin_amdgcn_exp2f(sc[kb][r]);
         sc[kb][r] = e;
         rp[r & 3] += e;
       }
-    lpart = fmaf(lpart, alpha, (rp[0] + rp[1]) + (rp[2] + rp[3]));
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
-    }
+    lpart += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+    // The tile's largest probability (exp2 of the same operand as its
+    // element's) and its bf16 rounding error; an empty row adds 0 - 0.
+    const float pm = __builtin_amdgcn_exp2f(mt);
+    lcorr += __uint_as_float(pack_bf16x2(pm, 0.f) << 16) - pm;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -325,7 +331,71 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     // matrix work.
 #pragma unroll
     for (int kk = 0; kk < NKB * 2; ++kk) asm volatile("" : "+v"(pf[kk]));
-    asm volatile("" : "+v"(lpart));
+    asm volatile("" : "+v"(lpart), "+v"(lcorr));
+  };
+  auto rescale = [&](float alpha) FA_INLINE {
+#pragma unroll
+    for (int q = 0; q < NMB; ++q) acc[q] *= alpha;
+    lpart *= alpha;
+    lcorr *= alpha;
+  };
+  // Unmasked tile whose rows all have a finite reference (every row has
+  // seen a visible key in an earlier, general step): the scores are shifted
+  // first, t = s * cs - fref, and the row max is taken over t (results of
+  // arithmetic, so the max needs no NaN quieting of its inputs).
+  auto softmax_hot = [&]() FA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = fmaf(sc[kb][r], cs, -fref);
+    float ma = fmaxf(sc[0][0], sc[0][1]), mb = fmaxf(sc[0][2], sc[0][3]);
+#pragma unroll
+    for (int i = 4; i < 16 * NKB; i += 4) {
+      ma = fmaxf(fmaxf(ma, sc[i / 16][i % 16]), sc[i / 16][i % 16 + 1]);
+      mb = fmaxf(fmaxf(mb, sc[i / 16][i % 16 + 2]), sc[i / 16][i % 16 + 3]);
+    }
+    float mt = halves_max(fmaxf(ma, mb));
+    if (__builtin_amdgcn_ballot_w64(mt > kLazy)) {
+      // Move the reference of each row whose max ran kLazy ahead up to that
+      // max (its largest t becomes exactly 0); the other rows move by 0, an
+      // exact no-op, so every row's result depends on its own scores only.
+      const float delta = mt > kLazy ? mt : 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][r] -= delta;
+      rescale(__builtin_amdgcn_exp2f(-delta));
+      fref += delta;
+      mt -= delta;
+    }
+    finish_tile(mt);
+  };
+  // General tile (masked entries -inf, references possibly unset): the max
+  // is taken over the raw scores first, the reference is set (or moved) to
+  // the running max when it is unset or runs kLazy ahead.
+  auto softmax = [&]() FA_INLINE {
+    float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sc[kb][r]);
+    const float mraw = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+    const float m2 = mraw * cs;  // -inf stays -inf (cs > 0)
+    const bool move = m2 > fref + kLazy;  // also when the reference is unset
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      // Rows that move take their running max as the reference (an unset
+      // one gives alpha = exp2(-inf) = 0, on sums that are 0); the others
+      // keep theirs and are scaled by exactly 1.
+      rescale(move ? __builtin_amdgcn_exp2f(fref - m2) : 1.f);
+      fref = move ? m2 : fref;
+    }
+    // Rows without a visible key so far: every score is -inf, t = -inf.
+    const float ref = fref == kNegInf ? 0.f : fref;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = fmaf(sc[kb][r], cs, -ref);
+    finish_tile(fmaf(mraw, cs, -ref));
   };
   // General softmax phase of step j: tiles this wave does not need (before
   // the first step, outside its rows' keys or past the last) leave P^T zero,
@@ -334,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   auto valu_phase = [&](int j) FA_INLINE {
     if (j >= 0 && j < ntiles && j >= s_first && j <= s_last) {
       if (j < su_lo || j >= su_hi) apply_mask(j);
-      softmax(j);
+      softmax();
     } else {
 #pragma unroll
       for (int kk = 0; kk < NKB * 2; ++kk) pf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
@@ -392,11 +462,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     open_step(m, nk, nv);
     slots(sk, sv, std::true_type{}, std::true_type{});
     mid_barrier();
-    softmax(m);
+    softmax_hot();
   };
   auto hot_b = [&](int m, const bf16* sk, bf16* nk, bf16* nv, const bf16* sv) FA_INLINE {
     open_step(m, nk, nv);
-    softmax(m - 1);
+    softmax_hot();
     mid_barrier();
     slots(sk, sv, std::true_type{}, std::true_type{});
   };
@@ -407,7 +477,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   // general path. Steps run in pairs starting at an odd step, so every loop
   // keeps a fixed stage assignment; all waves run steps 0 .. ntiles, so
   // they pass the same barriers.
-  const int hot_begin = WIN ? max(1, su_lo + grp) : 1;
+  // The hot softmax needs every row's reference set: the first tile every
+  // row of the wave sees (tile 0; with a window's lower edge, tile su_lo) is
+  // handled by a general step, which for group B is the step after it.
+  const int hot_begin = WIN ? max(1, su_lo + 1 + grp) : 1 + grp;
   const int hot_end = min(min(ntiles, s_last + 1), su_hi + grp);
   if (ntiles > 0) issue(K, ld_koff, 0, sK0);
   wait_global_loads();
@@ -448,10 +521,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
     }
   }
 
-  // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
+  // Epilogue: O = O~ / (l + lcorr) (bf16, round to nearest even),
+  // L = ln 2 (fref + log2 l).
   const float l = halves_sum(lpart);
   if (qi < n) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? 1.f / (l + lcorr) : 0.f;
     bf16* orow = O + (size_t)qi * D;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -463,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
         *reinterpret_cast<u32x2*>(orow + mb * 32 + g * 8 + h * 4) = u;
       }
     if (h == 0)
-      p.lse[qrow0 + qi] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+      p.lse[qrow0 + qi] = l > 0.f ? (fref + __log2f(l)) * kLn2 : kNegInf;
   }
 }
 
