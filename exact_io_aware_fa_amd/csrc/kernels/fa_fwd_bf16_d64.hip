@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBR = 128;  // query rows per workgroup (4 waves x 32)
+constexpr float kLazy = 64.f;  // reference lag bound (base 2), as for d = 128
 
 // Exchange with the other 32-lane half of the wave (v_permlane32_swap): the
 // two results hold the value of lane l % 32 and of lane l % 32 + 32 in some
@@ -112,8 +113,12 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
   f32x16 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
-  float m2 = kNegInf;   // running max in scaled base-2 units (s * cs)
+  // Reference of the row's probabilities (P = exp2(s * cs - fref)), moved
+  // only when the running max runs kLazy above it; the row-sum correction
+  // lcorr and the rest of the lazy update are as in fa_fwd_bf16.hip.
+  float fref = kNegInf;
   float lpart = 0.f;    // this half-wave's share of the running row sum
+  float lcorr = 0.f;    // per tile: bf16(p_max) - p_max of its largest probability
 
   // Loads of a key (or value) tile into LDS. Wave w fills rows
   // [w * LPW * RPL, (w + 1) * LPW * RPL); lane l of a 1 KB load writes
@@ -204,36 +209,76 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
           s[kb][r] = hidden ? kNegInf : s[kb][r];
         }
     }
-    // Row max and row sum use four independent partial results each, so the
-    // dependent-instruction chains are a quarter as long.
-    float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    // Lazy online update (see fa_fwd_bf16.hip): t = s * cs - fref, the
+    // reference moving only when a row's max runs kLazy above it.
+    float mt;  // the row's largest t (-inf if it sees no key of the tile)
+    if (MASK) {
+      // General tile: masked entries are -inf and the reference may be unset,
+      // so the max is taken over the raw scores first.
+      float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kb][r]);
-    const float mt = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
-    // The reference is the exact running max, so the row's largest
-    // probability is exactly 1 before its bf16 rounding. The rescale of O~
-    // is skipped (wave-uniform branch) when no row's max changed.
-    const float mt2 = (mt == kNegInf) ? kNegInf : mt * cs;
-    const float m2n = fmaxf(m2, mt2);
-    const float mref = (m2n == kNegInf) ? 0.f : m2n;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mref);  // 1 if unchanged, 0 while empty
-    m2 = m2n;
-
+        for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kb][r]);
+      const float mraw = halves_max(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])));
+      const float m2 = mraw * cs;  // -inf stays -inf (cs > 0)
+      const bool move = m2 > fref + kLazy;  // also when the reference is unset
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(fref - m2) : 1.f;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+        lpart *= alpha;
+        lcorr *= alpha;
+        fref = move ? m2 : fref;
+      }
+      const float ref = fref == kNegInf ? 0.f : fref;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], cs, -ref);
+      mt = fmaf(mraw, cs, -ref);
+    } else {
+      // Unmasked tile, every row's reference set (an earlier general step
+      // covered the first tile each row sees): shift first, then the max.
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], cs, -fref);
+      float ma = fmaxf(s[0][0], s[0][1]), mc = fmaxf(s[0][2], s[0][3]);
+#pragma unroll
+      for (int i = 4; i < 16 * NKB; i += 4) {
+        ma = fmaxf(fmaxf(ma, s[i / 16][i % 16]), s[i / 16][i % 16 + 1]);
+        mc = fmaxf(fmaxf(mc, s[i / 16][i % 16 + 2]), s[i / 16][i % 16 + 3]);
+      }
+      mt = halves_max(fmaxf(ma, mc));
+      if (__builtin_amdgcn_ballot_w64(mt > kLazy)) {
+        const float delta = mt > kLazy ? mt : 0.f;  // per row: others move by 0
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+        lpart *= alpha;
+        lcorr *= alpha;
+        fref += delta;
+        mt -= delta;
+      }
+    }
     float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cs, -mref));
+        const float e = __builtin_amdgcn_exp2f(s[kb][r]);
         s[kb][r] = e;
         rp[r & 3] += e;
       }
-    lpart = fmaf(lpart, alpha, (rp[0] + rp[1]) + (rp[2] + rp[3]));
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    lpart += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+    {
+      const float pm = __builtin_amdgcn_exp2f(mt);
+      lcorr += __uint_as_float(pack_bf16x2(pm, 0.f) << 16) - pm;
     }
 
     // P^T as bf16 B fragments: chunk kk holds keys kk*16 + {h*4 + 0..3,
@@ -270,8 +315,11 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
   // tile skips it. Even steps use stage 0, odd steps stage 1.
   auto sweep = [&](const auto& tiles) FA_INLINE {
     const int ns = tiles.count;
-    // Steps [su0, su1) hold the tiles every row sees in full.
-    const int su0 = WIN ? tiles.first_at_least(ju_lo) : 0;
+    // Steps [su0, su1) hold tiles every row sees in full, after the first
+    // such tile (which takes the general path: a row may see its first key
+    // there, and the unmasked update needs every row's reference set).
+    // (Clamped: with no such tile su0 would lie past the last step.)
+    const int su0 = min((WIN ? tiles.first_at_least(ju_lo) : 0) + 1, ns);
     const int su1 = max(tiles.first_at_least(ju_hi), su0);
     auto iter = [&](int m, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv,
                     auto mask_tag) FA_INLINE {
@@ -323,10 +371,11 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
     sweep(dense_tiles(tb, te));
   }
 
-  // Epilogue: O = O~ / l (bf16, round to nearest even), L = m + ln l.
+  // Epilogue: O = O~ / (l + lcorr) (bf16, round to nearest even),
+  // L = ln 2 (fref + log2 l).
   const float l = halves_sum(lpart);
   if (qi < n) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? 1.f / (l + lcorr) : 0.f;
     bf16* orow = O + (size_t)qi * D;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -338,7 +387,7 @@ __global__ __launch_bounds__(kThreads, MINW) void fwd_bf16_d64_kernel(Params p) 
         *reinterpret_cast<u32x2*>(orow + mb * 32 + g * 8 + h * 4) = u;
       }
     if (h == 0)
-      p.lse[qrow0 + qi] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+      p.lse[qrow0 + qi] = l > 0.f ? (fref + __log2f(l)) * kLn2 : kNegInf;
   }
 }
 
