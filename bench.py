@@ -385,6 +385,61 @@ def summarize_tcc(tcc_db) -> list:
     return lines
 
 
+def summarize_launch_gaps(trace_db) -> list:
+    """Markdown lines splitting each backward call (prep, dK/dV and dQ
+    kernels, launched back to back on one stream) into kernel time and the
+    gaps between its kernels, from a kernel trace: per sequence, span = end
+    of the dQ kernel - start of the prep kernel; gaps = span - the three
+    durations. Forward calls are single kernels (no gap inside a call).
+    Sequences are grouped by the dK/dV kernel's template arguments."""
+    import sqlite3
+
+    rows = sqlite3.connect(trace_db).execute(
+        "select name, start, end from kernels order by start").fetchall()
+    seqs = {}
+    for i in range(len(rows) - 2):
+        names = [_short(rows[i + k][0]) for k in range(3)]
+        if not (names[0].startswith("bwd_prep_kernel") and names[1].startswith("bwd_dkdv")
+                and names[2].startswith("bwd_dq")):
+            continue
+        durs = [rows[i + k][2] - rows[i + k][1] for k in range(3)]
+        span = rows[i + 2][2] - rows[i][1]
+        seqs.setdefault(names[1] + " + " + names[2], []).append((span, sum(durs), durs))
+    lines = ["", "## Backward calls: kernel time and launch gaps (kernel trace)", "",
+             "Per call (three kernels in order on one stream): span = end of the dQ kernel - "
+             "start of the prep kernel; gaps = span - sum of the three kernel durations. "
+             "Averages over the traced calls.", "",
+             "| dK/dV + dQ kernels | calls | prep us | dK/dV us | dQ us | kernels us | span us | gaps us |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k, v in seqs.items():
+        n = len(v)
+        avg = lambda f: sum(f(x) for x in v) / n / 1e3  # noqa: E731
+        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f |" % (
+            k, n, avg(lambda x: x[2][0]), avg(lambda x: x[2][1]), avg(lambda x: x[2][2]),
+            avg(lambda x: x[1]), avg(lambda x: x[0]), avg(lambda x: x[0] - x[1])))
+    return lines
+
+
+def summarize_trace(trace_db, command, out_md) -> None:
+    """A kernel-trace-only summary: per-kernel durations and the launch-gap
+    split of the backward calls."""
+    import sqlite3
+
+    rows = sqlite3.connect(trace_db).execute(
+        "select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+        "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[5] for r in rows)
+    lines = ["# rocprofv3 summary: %s" % os.path.basename(out_md).rsplit(".", 1)[0], "",
+             "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+             "## Kernel trace (`--kernel-trace --stats`)", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, tot in rows:
+        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (_short(name), calls, avg / 1e3,
+                                                                   mn / 1e3, mx / 1e3, 100 * tot / total))
+    lines += summarize_launch_gaps(trace_db)
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, out_json, sq_db=None,
                       tcc_db=None):
     """Summarise rocprofv3 databases (kernel trace + FETCH_SIZE + WRITE_SIZE
@@ -619,6 +674,8 @@ def run_sweep(out_path: str | None, only=None) -> int:
     ev = [hip.create() for _ in range(2)]
     clocks_before = _gpu_clocks()
     rows = []
+    sclk = SclkSampler(period_s=0.02)
+    sclk.__enter__()
     for name in names:
         fwd, bwd, tensors, ff, fb, bf, bb = _sweep_calls(name, dev, stream)
 
@@ -655,12 +712,18 @@ def run_sweep(out_path: str | None, only=None) -> int:
                           "fwd_tflops": round(tff, 1), "bwd_tflops": round(tfb, 1)}), flush=True)
         del fwd, bwd, tensors
         torch.cuda.empty_cache()
+    sclk.__exit__(None, None, None)
     for e_ in ev:
         hip.destroy(e_)
+    sr = sclk.result()
+    sclk_line = ("Shader clock sampled during the sweep (%s): median %.0f MHz, min %.0f, max %.0f "
+                 "(%d samples)" % (sr["source"], sr["median_mhz"], sr["min_mhz"], sr["max_mhz"],
+                                   sr["samples"]) if sr.get("samples") else
+                 "Shader clock: not sampled (%s)" % sr["source"])
     lines = ["# Attention sweep on one MI355X", "",
              "Command: `python bench.py --sweep --out <this file>` (from the repository root).", "",
              "Clocks before the sweep (rocm-smi): " + clocks_before,
-             "Clocks after the sweep (rocm-smi): " + _gpu_clocks(), "",
+             "Clocks after the sweep (rocm-smi): " + _gpu_clocks(), sclk_line, "",
              "Times are medians (min in parentheses) over >= 50 calls and >= 200 ms, warm "
              "cache; `cold` medians write a 512 MB buffer before each call. Peak = bf16 dense "
              "MFMA %.0f TFLOP/s; roof = min(peak, compulsory-byte AI x %.0f GB/s); GB/s = "
@@ -823,6 +886,14 @@ def run_fp8(out_path: str | None, only=None, copy_mib: int = 0) -> int:
 
 
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize-trace":
+        sp = argparse.ArgumentParser(prog="bench.py summarize-trace")
+        sp.add_argument("trace_db")
+        sp.add_argument("--command", required=True)
+        sp.add_argument("--out-md", required=True)
+        a = sp.parse_args(sys.argv[2:])
+        summarize_trace(a.trace_db, a.command, a.out_md)
+        return 0
     if len(sys.argv) > 1 and sys.argv[1] == "summarize":
         sp = argparse.ArgumentParser(prog="bench.py summarize")
         sp.add_argument("trace_db")

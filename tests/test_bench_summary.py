@@ -87,3 +87,30 @@ def test_summarize_tcc_hit_rate(tmp_path):
     cells = [c.strip() for c in row[0].strip("|").split("|")]
     assert cells[1] == "2" and float(cells[2]) == 10.0 and float(cells[3]) == 9.0
     assert float(cells[5]) == 0.9
+
+
+def test_launch_gaps_of_backward_calls(tmp_path):
+    db = tmp_path / "trace.db"
+    con = sqlite3.connect(str(db))
+    con.execute("create table kernels (name text, start integer, end integer)")
+    pre = "void fa::(anonymous namespace)::"
+    rows = []
+    t = 0
+    for _ in range(3):   # a forward, then prep, dK/dV, dQ with 1 us and 2 us gaps
+        rows.append((pre + "fwd_bf16_d64_kernel<64, 64, 2, true, false, false>(fa::Params)", t, t + 30_000))
+        t += 31_000
+        rows.append(("_ZN2fa12_GLOBAL__N_115bwd_prep_kernelILi64EDF16bEEvNS_6ParamsEx", t, t + 6_000))
+        t += 7_000
+        rows.append((pre + "bwd_dkdv_kernel<64, 2, true, false>(fa::Params)", t, t + 50_000))
+        t += 52_000
+        rows.append((pre + "bwd_dq_kernel<64, 64, true, false, false>(fa::Params)", t, t + 30_000))
+        t += 40_000
+    con.executemany("insert into kernels values (?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    lines = bench.summarize_launch_gaps(str(db))
+    row = [l for l in lines if l.startswith("| `bwd_dkdv")]
+    assert len(row) == 1, lines
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    assert cells[1] == "3"
+    assert [float(x) for x in cells[2:8]] == [6.0, 50.0, 30.0, 86.0, 89.0, 3.0]
