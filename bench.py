@@ -44,7 +44,7 @@ also timed cold: a 512 MB buffer is written between calls.
 
     python bench.py --fp8 [--out FILE] [--only PREFIX ...] [--calibrate-copy MIB]
 
-times the FP8 forward on every d = 64 or 128 padded workload without a
+times the FP8 forward on every padded workload (d = 64, 128, 256) without a
 window or block mask: the three block encodings (fa_fp8_quantize for Q and K with the
 Hadamard rotation, for V in the transposed layout), fa_fwd_fp8 on the codes,
 and the bf16 fa_fwd on the same inputs, with the same iteration rule; it
@@ -785,7 +785,7 @@ def run_fp8(out_path: str | None, only=None, copy_mib: int = 0) -> int:
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
     names = [n for n, w in WORKLOADS.items()
-             if w.d in (64, 128) and w.window == (-1, -1) and w.blocks is None
+             if w.window == (-1, -1) and w.blocks is None
              and w.dtype == "bf16"]
     if only:
         names = [n for n in names if any(n.startswith(o) for o in only)]

@@ -324,7 +324,7 @@ fa_status fa_fp8_quantize(int64_t batch, int64_t heads, int64_t n, int64_t d, in
                           void* stream) {
   fa_status st = check_fp8_shape(batch, heads, heads, n);
   if (st != FA_OK) return st;
-  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_E_UNSUPPORTED;
   if (layout != FA_FP8_ROWS && layout != FA_FP8_VT) return FA_E_UNSUPPORTED;
   if (layout == FA_FP8_VT && signs != nullptr) return FA_E_UNSUPPORTED;
   if (n * d * 2 >= (int64_t(1) << 31)) return FA_E_SHAPE;
@@ -361,7 +361,7 @@ fa_status fa_fwd_fp8(int64_t batch, int64_t heads, int64_t heads_kv, int64_t n, 
                      void* stream) {
   fa_status st = check_fp8_shape(batch, heads, heads_kv, n);
   if (st != FA_OK) return st;
-  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_E_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return FA_E_UNSUPPORTED;
   if (n * d * 2 >= (int64_t(1) << 31)) return FA_E_SHAPE;
   if (!q8 || !q_scales || !k8 || !k_scales || !v8 || !v_scales || !o || !lse)

@@ -39,10 +39,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Chunk swizzle of the staged block: a read phase (16 lanes) covers rows
-// 0..7 (or 8..15, ...) at one logical chunk of each half row.
+// 0..7 (or 8..15, ...) at one logical chunk of each half row. (d = 256: a
+// row is two full passes over the banks, so the two halves of a row share a
+// bank group and the reads conflict two ways; this kernel is bound by HBM.)
 template <int D>
 __device__ __forceinline__ int qswz(int row) {
-  return D == 128 ? (row & 7) : ((row >> 1) & 3);
+  return D >= 128 ? (row & 7) : ((row >> 1) & 3);
 }
 
 template <int D, bool ROT, bool VT>
@@ -224,6 +226,7 @@ hipError_t launch_fp8_quantize(const Fp8QuantParams& p, int d, hipStream_t s) {
   switch (d) {
     case 64: return launch_d<64>(p, s);
     case 128: return launch_d<128>(p, s);
+    case 256: return launch_d<256>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,5 +1,5 @@
 // Attention forward on FP8 (E4M3) operands with fp32 accumulation, for
-// gfx950 (d = 64 and 128).
+// gfx950 (d = 64, 128 and 256).
 //
 // Method: page 2 ("4. FlashAttention 深度剖析"), 4.5.4 (FP8 support): both
 // products of the forward take E4M3 operands, every block carries the scale
@@ -29,7 +29,11 @@
 //
 // Mapping onto CDNA4 (as the bf16 forward): 8 wave64s per workgroup, 256
 // query rows, 32 per wave for the whole key sweep; ping-pong between the
-// two waves of a SIMD (matrix phase of one, softmax phase of the other);
+// two waves of a SIMD (matrix phase of one, softmax phase of the other).
+// At d = 256 a wave's O accumulator alone is 128 registers, which with the
+// Q codes and the score tile exceeds the 256 registers a wave may hold when
+// two share a SIMD: there the workgroup is 4 waves (128 rows, one wave per
+// SIMD with up to 512 registers), each running both phases in turn;
 // K and V^T tiles straight from HBM into LDS (two stages each). The score
 // product is S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4: lane l supplies
 // query l % 32 as B and key row sigma(l % 32) as A, with
@@ -47,9 +51,6 @@
 namespace fa {
 
 namespace {
-
-constexpr int kThreads = 512;
-constexpr int kBR = 256;  // query rows per workgroup (8 waves x 32)
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -84,8 +85,11 @@ __device__ __forceinline__ int key_of_lane(int c) {
 // 128-byte rows, same row % 4 for 64-byte rows) must land on different
 // chunks, which these swizzles do. V^T rows (BC bytes): 16 consecutive rows
 // at one logical chunk.
+// (256-byte rows all start at bank 0: the 16 rows of a phase take 16
+// different chunks.)
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
+  if (D == 256) return (row & 7) | ((row >> 1) & 8);
   return D == 128 ? (((row >> 1) & 3) | ((row >> 2) & 4)) : (((row >> 2) & 1) | ((row >> 3) & 2));
 }
 template <int BC>
@@ -102,8 +106,13 @@ __device__ __forceinline__ float vload_uniform(const float* a, int i) {
   return a[i + z];
 }
 
-template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
+template <int D, int BC, bool CAUSAL, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64, 1) void fwd_fp8_kernel(Fp8Params p) {
+  // 8 waves: ping-pong between waves w and w + 4 (groups A and B); 4 waves:
+  // every wave is in group A and runs both phases of each step.
+  constexpr int kThreads = NWAVES * 64;
+  constexpr int kBR = 32 * NWAVES;       // query rows per workgroup
+  static_assert(NWAVES == 8 || NWAVES == 4, "workgroup shape");
   constexpr int NQF = D / 64;            // 64-channel halves of a score product
   constexpr int CPR = D / 16;            // 16-byte chunks per K row
   constexpr int TILEB = BC * D;          // bytes of a K or V^T tile
@@ -117,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   constexpr int NMB = D / 32;            // 32-channel blocks of O^T
   static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "tile split");
   static_assert(BC == 64 || BC == 128, "tile width");
-  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
 
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILEB];
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = w >> 2;
+  const int grp = NWAVES == 8 ? (w >> 2) : 0;
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
   int kv_lim = n;
   if (p.kv_len != nullptr) kv_lim = min(max(p.kv_len[b], 0), n);
   const int q0 = qb * kBR;
-  const int qw0 = q0 + 32 * (2 * (w & 3) + grp);
+  const int qw0 = NWAVES == 8 ? q0 + 32 * (2 * (w & 3) + grp) : q0 + 32 * w;
   const int qi = qw0 + c;
   // exp2 factor of this wave's rows: |scale| log2(e) sigma_q (one block).
   const float cq = p.c * p.q_scale[bhq * p.nb + min(qw0 / 128, p.nb - 1)];
@@ -284,9 +293,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
     }
     // Keep the products in this half-period: otherwise the compiler sinks
     // the O^T products past the next barrier, next to their first use.
+    // (Ping-pong only: with one wave per SIMD there is nothing to overlap,
+    // and the accumulators may live in AGPRs.)
+    if constexpr (NWAVES == 8) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(acc[mb]));
-    asm volatile("" : "+v"(accl));
+      for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(acc[mb]));
+      asm volatile("" : "+v"(accl));
+    }
   };
 
   // Softmax phase of tile j with exp2 factor cj.
@@ -347,9 +360,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
         w8 = __builtin_amdgcn_cvt_pk_fp8_f32(v[r + 2], v[r + 3], w8, true);
         pf[kk][q] = (int)w8;
       }
+    if constexpr (NWAVES == 8) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(pf[kk]));
-    asm volatile("" : "+v"(sb));
+      for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(pf[kk]));
+      asm volatile("" : "+v"(sb));
+    }
   };
   auto valu_phase = [&](int j, float cj) FA_INLINE {
     if (j >= 0 && j < ntiles && j >= s_first && j <= s_last) {
@@ -498,16 +513,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8Params p) {
 
 template <int D>
 hipError_t launch_d(const Fp8Params& p, hipStream_t s) {
-  const int t_r = (p.n + kBR - 1) / kBR;
+  constexpr int NW = D == 256 ? 4 : 8;
+  constexpr int BR = 32 * NW;
+  const int t_r = (p.n + BR - 1) / BR;
   const long long total = (long long)t_r * p.batch * p.heads;
-  dim3 grid((unsigned)total), block(kThreads);
+  dim3 grid((unsigned)total), block(NW * 64);
   // 128-key tiles: half the per-tile overhead of 64 (barriers, row max
   // exchange, frame update) for the same matrix work.
   constexpr int BC = 128;
   if (p.causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, BC, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, BC, true, NW>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, BC, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, BC, false, NW>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -517,6 +534,7 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s) {
   switch (d) {
     case 64: return launch_d<64>(p, s);
     case 128: return launch_d<128>(p, s);
+    case 256: return launch_d<256>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -406,7 +406,7 @@ size_t fa_fp8_scales_bytes(int64_t batch, int64_t heads, int64_t n);
 
 /*
  * fa_fp8_quantize -- encodes the bf16 tensor x [batch, heads, n, d]
- * (d = 64 or 128, else FA_E_UNSUPPORTED) into `codes` (layout FA_FP8_ROWS or
+ * (d = 64, 128 or 256, else FA_E_UNSUPPORTED) into `codes` (layout FA_FP8_ROWS or
  * FA_FP8_VT, else FA_E_UNSUPPORTED) and `scales`, as described above.
  * signs: NULL (no rotation) or a device int8[d] of +1 / -1 entries (any
  * negative value counts as -1), 16-byte aligned; a rotation with the
@@ -423,8 +423,8 @@ fa_status fa_fp8_quantize(int64_t batch, int64_t heads, int64_t n, int64_t d,
 /*
  * fa_fwd_fp8 -- attention forward on encoded operands: q8 (FA_FP8_ROWS,
  * [batch, heads, np, d]), k8 (FA_FP8_ROWS, [batch, heads_kv, np, d]), v8
- * (FA_FP8_VT, [batch, heads_kv, nb, d, FA_BLOCK]) with their scales; d = 64
- * or 128 (else FA_E_UNSUPPORTED); grouped heads, causal, kv_len and softmax_scale
+ * (FA_FP8_VT, [batch, heads_kv, nb, d, FA_BLOCK]) with their scales; d = 64,
+ * 128 or 256 (else FA_E_UNSUPPORTED); grouped heads, causal, kv_len and softmax_scale
  * as for fa_fwd_gqa. Both products run on the E4M3 matrix cores with FP32
  * accumulation. With t_ij = softmax_scale * log2(e) * (sq q^_i . sk k^_j)
  * and the integer row frame f_i = ceil(max_j t_ij) over the visible keys,

@@ -272,8 +272,8 @@ def quant(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=256), B.FA_E_UNSUPPORTED), (dict(d=96), B.FA_E_UNSUPPORTED),
-    (dict(layout=2), B.FA_E_UNSUPPORTED),
+    (dict(d=32), B.FA_E_UNSUPPORTED), (dict(d=96), B.FA_E_UNSUPPORTED),
+    (dict(d=512), B.FA_E_UNSUPPORTED), (dict(layout=2), B.FA_E_UNSUPPORTED),
     (dict(layout=B.FA_FP8_VT, signs=SG), B.FA_E_UNSUPPORTED),
     (dict(n=0), B.FA_E_SHAPE), (dict(batch=0), B.FA_E_SHAPE),
     (dict(x=None), B.FA_E_NULLPTR), (dict(codes=None), B.FA_E_NULLPTR),
@@ -300,8 +300,8 @@ def fwd8(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=256), B.FA_E_UNSUPPORTED), (dict(d=96), B.FA_E_UNSUPPORTED),
-    (dict(softmax_scale=float("nan")), B.FA_E_UNSUPPORTED),
+    (dict(d=32), B.FA_E_UNSUPPORTED), (dict(d=96), B.FA_E_UNSUPPORTED),
+    (dict(d=512), B.FA_E_UNSUPPORTED), (dict(softmax_scale=float("nan")), B.FA_E_UNSUPPORTED),
     (dict(heads_kv=3), B.FA_E_SHAPE), (dict(heads_kv=0), B.FA_E_SHAPE),
     (dict(heads_kv=8), B.FA_E_SHAPE), (dict(n=0), B.FA_E_SHAPE),
     (dict(n=(1 << 22) + 1), B.FA_E_SHAPE),

@@ -245,6 +245,10 @@ EXACT = [
     (2, 4, 2, 300, 64, True, True, 1.0, None, True),
     (1, 2, 1, 1000, 64, False, False, 3.0, None, False),   # peaky, multi-query
     (1, 2, 2, 129, 64, True, False, 1.0, -0.2, True),
+    (2, 4, 2, 300, 256, True, True, 1.0, None, True),    # d = 256: 4-wave workgroups
+    (1, 2, 1, 1000, 256, False, False, 3.0, None, False),
+    (1, 2, 2, 129, 256, True, False, 1.0, -0.2, False),
+    (1, 1, 1, 1, 256, True, False, 1.0, None, False),
 ]
 
 
@@ -321,6 +325,9 @@ QUANT = [
     (1, 3, 129, 64, "rows", True),
     (1, 1, 1, 128, "rows", False),
     (1, 1, 1, 128, "vt", False),
+    (2, 2, 300, 256, "rows", False),
+    (2, 2, 300, 256, "vt", False),
+    (1, 2, 257, 256, "rows", True),
 ]
 
 
@@ -378,6 +385,8 @@ FWD = [
     (1, 2, 1, 1000, False, False, 3.0, None, 64),     # peaky, multi-query
     (1, 2, 2, 129, True, False, 1.0, -0.2, 64),
     (1, 1, 1, 1, False, False, 1.0, None, 64),
+    (2, 4, 2, 300, True, True, 1.0, None, 256),       # d = 256: 4-wave workgroups
+    (1, 2, 1, 1000, False, False, 3.0, None, 256),
 ]
 
 
@@ -425,7 +434,8 @@ def test_rotated_codes_forward():
 # The whole recipe
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("rotate,d", [(False, 128), (True, 128), (False, 64), (True, 64)])
+@pytest.mark.parametrize("rotate,d", [(False, 128), (True, 128), (False, 64), (True, 64),
+                                      (True, 256)])
 def test_end_to_end_against_oracle(rotate, d):
     """The whole recipe (GPU encoder, then the forward): against exact
     attention on the decoded operands (the primary gate), and against the
@@ -488,12 +498,12 @@ def test_full_size_sampled_rows():
 
 
 def test_fp8_rejects_unsupported_head_dim():
-    x = torch.zeros(1, 1, 64, 256, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError, match="FA_E_UNSUPPORTED"):
         fa.fp8_quantize(x)
-    q8 = torch.zeros(1, 1, 128, 256, dtype=torch.uint8, device="cuda")
+    q8 = torch.zeros(1, 1, 128, 96, dtype=torch.uint8, device="cuda")
     s = torch.ones(1, 1, 1, device="cuda")
-    v8 = torch.zeros(1, 1, 1, 256, 128, dtype=torch.uint8, device="cuda")
+    v8 = torch.zeros(1, 1, 1, 96, 128, dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError, match="FA_E_UNSUPPORTED"):
         fa.flash_attn_fp8_fwd_codes(q8, s, q8, s, v8, s, 100)
     assert B.ABI_VERSION == B.fa_abi_version()
