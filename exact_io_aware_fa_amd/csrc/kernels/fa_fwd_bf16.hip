@@ -1,5 +1,6 @@
 // Fused attention forward, bf16 in/out, fp32 accumulate, for gfx950
-// (d = 128; d = 64 uses fa_fwd_bf16_d64.hip, d = 256 fa_fwd_bf16_staged.hip).
+// (d = 128 and 256; d = 64 uses fa_fwd_bf16_d64.hip, block-sparse d = 256
+// fa_fwd_bf16_staged.hip).
 //
 // Method: the tiled forward of page 2 ("4. FlashAttention 深度剖析", 4.3.2)
 // with the per-block (m, l, O) update of page 1 ("注意力为什么受限于显存带宽：
@@ -36,6 +37,10 @@
 //   hit every LDS bank once per 256 bytes.
 // * exp2 with the log2(e) factor folded into the score scale; the max-shift
 //   and scale are one FMA per score.
+// * d = 256: a wave's O accumulator (128 registers) and Q fragments (64)
+//   leave no room for a second wave on the SIMD, so the workgroup is 4
+//   waves (128 rows), one per SIMD with up to 512 registers, each running
+//   both phases of every step in turn (the schedule of group A below).
 #include <type_traits>
 
 #include "fa_device.h"
@@ -44,8 +49,6 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kBR = 256;  // query rows per workgroup (8 waves x 32)
 // The reference of a row's probabilities trails its running max by at most
 // this much (base 2): probabilities stay in [0, 2^kLazy].
 constexpr float kLazy = 64.f;
@@ -64,8 +67,13 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
+template <int D, int BC, bool CAUSAL, bool WIN, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
+  // 8 waves: ping-pong between waves w and w + 4 (groups A and B); 4 waves:
+  // every wave is in group A and runs both phases of each step.
+  constexpr int kThreads = NWAVES * 64;
+  constexpr int kBR = 32 * NWAVES;      // query rows per workgroup
+  static_assert(NWAVES == 8 || NWAVES == 4, "workgroup shape");
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;           // bytes per row
   constexpr int TILEB = BC * ROWB;      // bytes per K or V tile
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = w >> 2;  // 0: group A, 1: group B
+  const int grp = NWAVES == 8 ? (w >> 2) : 0;  // 0: group A, 1: group B
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
   // Rows of wave w: the two waves of a SIMD (w and w + 4) take neighbouring
   // 32-row blocks, so both groups span the workgroup's 256 rows and reach
   // the causal diagonal at about the same step.
-  const int qw0 = q0 + 32 * (2 * (w & 3) + grp);
+  const int qw0 = NWAVES == 8 ? q0 + 32 * (2 * (w & 3) + grp) : q0 + 32 * w;
   const int qi = qw0 + c;
   const float cs = p.c;
 
@@ -543,13 +551,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(Params p) {
 
 template <int D, int BC>
 hipError_t launch_d(const Params& p, hipStream_t s) {
-  const int t_r = (p.n + kBR - 1) / kBR;
+  constexpr int NW = D == 256 ? 4 : 8;
+  const int t_r = (p.n + 32 * NW - 1) / (32 * NW);
   const long long total = (long long)t_r * p.batch * p.heads;
-  dim3 grid((unsigned)total), block(kThreads);
+  dim3 grid((unsigned)total), block(NW * 64);
   // (Block-sparse masks never reach this kernel.)
   return dispatch_mask_win(p, [&](auto causal, auto, auto win) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, decltype(causal)::value, decltype(win)::value>),
-                       grid, block, 0, s, p);
+    hipLaunchKernelGGL(
+        (fwd_bf16_kernel<D, BC, decltype(causal)::value, decltype(win)::value, NW>), grid,
+        block, 0, s, p);
     return hipGetLastError();
   });
 }
@@ -562,7 +572,9 @@ hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s) {
     // Block-sparse masks take the 4-wave kernel: its 128-row workgroups lie
     // in one block row of the mask.
     case 128: return p.blk != nullptr ? launch_fwd_bf16_d64(p, d, s) : launch_d<128, 64>(p, s);
-    case 256: return launch_fwd_bf16_staged(p, d, s);
+    // Block-sparse d = 256 takes the register-staged kernel (128-row
+    // workgroups lie in one block row of the mask; it supports the lists).
+    case 256: return p.blk != nullptr ? launch_fwd_bf16_staged(p, d, s) : launch_d<256, 64>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
