@@ -4,9 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-fa_fwd (O and LSE) followed by fa_bwd (the D_i / L_i log2 e pass, the
-key-outer dK/dV kernel, the query-outer dQ kernel), all on torch's current
-stream, with the inputs
+fa_fwd (O and LSE) followed by fa_bwd (the query-outer dQ kernel, which also
+forms D_i and L_i log2 e, then the key-outer dK/dV kernel), all on torch's
+current stream, with the inputs
 already resident in device memory. W untimed steps, then exactly K timed steps
 between two device synchronisations. One JSON line is printed.
 
@@ -386,37 +386,52 @@ def summarize_tcc(tcc_db) -> list:
 
 
 def summarize_launch_gaps(trace_db) -> list:
-    """Markdown lines splitting each backward call (prep, dK/dV and dQ
-    kernels, launched back to back on one stream) into kernel time and the
-    gaps between its kernels, from a kernel trace: per sequence, span = end
-    of the dQ kernel - start of the prep kernel; gaps = span - the three
+    """Markdown lines splitting each backward call of a kernel trace into
+    kernel time and the gaps between its kernels. A call is a maximal run of
+    consecutive backward kernels (an optional prep kernel, the dQ and the
+    dK/dV kernel, launched back to back on one stream); span = end of its
+    last kernel - start of its first; gaps = span - the sum of its kernel
     durations. Forward calls are single kernels (no gap inside a call).
-    Sequences are grouped by the dK/dV kernel's template arguments."""
+    Calls are grouped by their dK/dV and dQ kernels' template arguments."""
     import sqlite3
 
     rows = sqlite3.connect(trace_db).execute(
         "select name, start, end from kernels order by start").fetchall()
+    runs, cur = [], []
+    for name, start, end in rows:
+        short = _short(name)
+        if short.startswith("bwd_"):
+            cur.append((short, start, end))
+        elif cur:
+            runs.append(cur)
+            cur = []
+    if cur:
+        runs.append(cur)
     seqs = {}
-    for i in range(len(rows) - 2):
-        names = [_short(rows[i + k][0]) for k in range(3)]
-        if not (names[0].startswith("bwd_prep_kernel") and names[1].startswith("bwd_dkdv")
-                and names[2].startswith("bwd_dq")):
+    for run in runs:
+        kinds = {k: (e - s_) for k, s_, e in run}
+        dk = [k for k in kinds if k.startswith("bwd_dkdv")]
+        dq = [k for k in kinds if k.startswith("bwd_dq")]
+        if len(dk) != 1 or len(dq) != 1 or len(run) > 3:
             continue
-        durs = [rows[i + k][2] - rows[i + k][1] for k in range(3)]
-        span = rows[i + 2][2] - rows[i][1]
-        seqs.setdefault(names[1] + " + " + names[2], []).append((span, sum(durs), durs))
+        prep = sum(v for k, v in kinds.items() if k.startswith("bwd_prep"))
+        durs = (prep, kinds[dk[0]], kinds[dq[0]])
+        span = run[-1][2] - run[0][1]
+        seqs.setdefault(dk[0] + " + " + dq[0], []).append((span, sum(durs), durs, len(run)))
     lines = ["", "## Backward calls: kernel time and launch gaps (kernel trace)", "",
-             "Per call (three kernels in order on one stream): span = end of the dQ kernel - "
-             "start of the prep kernel; gaps = span - sum of the three kernel durations. "
-             "Averages over the traced calls.", "",
-             "| dK/dV + dQ kernels | calls | prep us | dK/dV us | dQ us | kernels us | span us | gaps us |",
-             "|---|---|---|---|---|---|---|---|"]
+             "Per call (its kernels in order on one stream): span = end of the last kernel - "
+             "start of the first; gaps = span - sum of the kernel durations. Averages over "
+             "the traced calls.", "",
+             "| dK/dV + dQ kernels | calls | kernels per call | prep us | dK/dV us | dQ us | "
+             "kernels us | span us | gaps us |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for k, v in seqs.items():
         n = len(v)
         avg = lambda f: sum(f(x) for x in v) / n / 1e3  # noqa: E731
-        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f |" % (
-            k, n, avg(lambda x: x[2][0]), avg(lambda x: x[2][1]), avg(lambda x: x[2][2]),
-            avg(lambda x: x[1]), avg(lambda x: x[0]), avg(lambda x: x[0] - x[1])))
+        lines.append("| `%s` | %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f |" % (
+            k, n, v[0][3], avg(lambda x: x[2][0]), avg(lambda x: x[2][1]),
+            avg(lambda x: x[2][2]), avg(lambda x: x[1]), avg(lambda x: x[0]),
+            avg(lambda x: x[0] - x[1])))
     return lines
 
 
@@ -997,8 +1012,10 @@ def main() -> int:
         wall = time.perf_counter() - t0
 
     fwd_ms = [hip.elapsed_ms(ev_f0[i], ev_f1[i]) for i in range(nev)]
+    # bf16: dQ kernel (with D_i, L_i log2 e) between events 0 and 1, the
+    # dK/dV kernel between events 1 and 2.
+    dq_ms = [hip.elapsed_ms(ev_b[i][0], ev_b[i][1]) for i in range(nev)]
     main_ms = [hip.elapsed_ms(ev_b[i][1], ev_b[i][2]) for i in range(nev)]
-    dq_ms = [hip.elapsed_ms(ev_b[i][2], ev_b[i][3]) for i in range(nev)]
     bwd_ms = [hip.elapsed_ms(ev_b[i][0], ev_b[i][3]) for i in range(nev)]
     for e in ev_f0 + ev_f1 + [x for r in ev_b for x in r]:
         hip.destroy(e)

@@ -243,14 +243,22 @@ fa_status bwd_impl(const Shape& sh, int causal, float softmax_scale, fa_dtype dt
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
   };
   const int d = int(sh.d);
-  const bool bf = dtype == FA_BF16;
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = fa::launch_bwd_prep(p, d, bf, s);
-  if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = bf ? fa::launch_bwd_dkdv_bf16(p, d, s) : fa::launch_bwd_fp32(p, d, s);
+  if (dtype == FA_BF16) {
+    // bf16: the query-outer dQ kernel also forms D_i and L_i log2(e) for its
+    // rows and writes them to the workspace, so it runs first and the dK/dV
+    // kernel, which reads them, second (two launches).
+    if (e == hipSuccess) e = fa::launch_bwd_dq_bf16(p, d, s);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = fa::launch_bwd_dkdv_bf16(p, d, s);
+  } else {
+    // fp32: D_i, L_i log2(e) and the zeroed dQ accumulator come from the
+    // prep kernel, then one kernel adds dQ with atomics and writes dK, dV.
+    if (e == hipSuccess) e = fa::launch_bwd_prep(p, d, false, s);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = fa::launch_bwd_fp32(p, d, s);
+  }
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess && bf) e = fa::launch_bwd_dq_bf16(p, d, s);
   if (e == hipSuccess) e = mark(3);
   return e == hipSuccess ? FA_OK : FA_E_LAUNCH;
 }

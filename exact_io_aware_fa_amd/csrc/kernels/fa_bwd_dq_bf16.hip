@@ -90,16 +90,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   // Q (sign-flipped for a negative scale) and dO rows of this wave as B
   // fragments [qi][kd*16 + h*8 + e]; rows past n read row n-1 (never stored).
   bf16x8 qf[ND], gf[ND];
+#pragma unroll
+  for (int kd = 0; kd < ND; ++kd) gf[kd] = as_bf16x8(ld16(dO + (size_t)qr * D + kd * 16 + h * 8));
+  // D_i and L_i log2(e) of this lane's row, also written to the workspace
+  // for the dK/dV kernel (which runs after this one); formed before the Q
+  // fragments are loaded, so the O row and Q never occupy registers at once.
+  float dd, l2;
+  bwd_row_terms<ND>(p, bh, qi, n, static_cast<const bf16*>(p.o_in) + base + (size_t)qr * D, gf,
+                    p.lse[qrow0 + qr], h, dd, l2);
   {
     const uint32_t flip = p.q_neg ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kd = 0; kd < ND; ++kd) {
+    for (int kd = 0; kd < ND; ++kd)
       qf[kd] = as_bf16x8(ld16(Q + (size_t)qr * D + kd * 16 + h * 8) ^ flip);
-      gf[kd] = as_bf16x8(ld16(dO + (size_t)qr * D + kd * 16 + h * 8));
-    }
   }
-  const float l2 = p.l2vec[(size_t)bh * p.n_pad + qr];
-  const float dd = p.dvec[(size_t)bh * p.n_pad + qr];
 
   // Keys of this lane's row: [band.lo(qi), band.hi(qi)); key tiles [tb, te) hold every key
   // some row of the workgroup sees, tiles [ju_lo, ju_hi) only keys that all

@@ -84,8 +84,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_staged_kernel(Params p) {
       gf[kd] = as_bf16x8(ld16(dO + (size_t)qr * D + kd * 16 + h * 8));
     }
   }
-  const float l2 = p.l2vec[(size_t)bh * p.n_pad + qr];
-  const float dd = p.dvec[(size_t)bh * p.n_pad + qr];
+  // D_i and L_i log2(e) of this lane's row, also written to the workspace
+  // for the dK/dV kernel (which runs after this one).
+  float dd, l2;
+  bwd_row_terms<ND>(p, bh, qi, n, static_cast<const bf16*>(p.o_in) + base + (size_t)qr * D, gf,
+                    p.lse[qrow0 + qr], h, dd, l2);
 
   // Keys of this lane's row: [band.lo(qi), band.hi(qi)); key tiles [tb, te) hold every key
   // some row of the workgroup sees, tiles [ju_lo, ju_hi) only keys that all

@@ -249,6 +249,42 @@ __device__ __forceinline__ size_t span_row0(const Params& p, const Span& s, int 
   return ((size_t)s.mb * nh + hh) * (size_t)p.rows + s.start;
 }
 
+// The backward's row terms, formed by the query-outer dQ kernel for its own
+// rows and written to the workspace for the dK/dV kernel, which runs after
+// it: D_i = <dO_i, O_i> in fp32 (the row term of dS = P * (dP - D); softmax
+// calculus gives sum_j P_ij dP_ij = <dO_i, O_i>) and L_i log2(e), the saved
+// row statistic in base-2 units (+inf for a row with no visible key, so that
+// every rebuilt probability of it is exactly 0). Lane (c, h) holds elements
+// kd*16 + h*8 .. +7 of its row's dO as fragments gf[kd] and reads the same
+// elements of O from orow; the two halves of the row are summed with
+// v_permlane32_swap (the same sum on both lanes). Rows [len, n_pad) of the
+// entry get 0 and 0 (they are loaded, never used).
+template <int ND>
+__device__ __forceinline__ void bwd_row_terms(const Params& p, int bh, int qi, int len,
+                                              const bf16* orow, const bf16x8 (&gf)[ND],
+                                              float lse, int h, float& dd, float& l2) {
+  float s = 0.f;
+#pragma unroll
+  for (int kd = 0; kd < ND; ++kd) {
+    const u32x4 o = ld16(orow + kd * 16 + h * 8);
+    const u32x4 g = __builtin_bit_cast(u32x4, gf[kd]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s = fmaf(__uint_as_float(o[j] << 16), __uint_as_float(g[j] << 16), s);
+      s = fmaf(__uint_as_float(o[j] & 0xffff0000u), __uint_as_float(g[j] & 0xffff0000u), s);
+    }
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  dd = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  l2 = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+  if (h == 0 && qi < p.n_pad) {
+    const size_t row = (size_t)bh * p.n_pad + qi;
+    p.dvec[row] = qi < len ? dd : 0.f;
+    p.l2vec[row] = qi < len ? l2 : 0.f;
+  }
+}
+
 // Keys j >= kv_limit are hidden for batch entry b of length n (clamped to
 // [0, n]).
 __device__ __forceinline__ int kv_limit(const Params& p, int b, int n) {

@@ -351,10 +351,11 @@ fa_status fa_block_index_build(int64_t n, const uint8_t* block_mask,
 /*
  * fa_bwd_timed -- fa_bwd_gqa, additionally recording caller-owned HIP events on
  * `stream` between its kernels, for measurement harnesses that time each
- * kernel with events. events[0] is recorded before the D_i kernel,
- * events[1] before the dK/dV kernel (fp32: the single backward kernel),
- * events[2] after it and events[3] after the dQ kernel (bf16) -- i.e. at
- * the end. Any entry may
+ * kernel with events. events[0] is recorded at the start; bf16: events[1]
+ * after the dQ kernel (which also forms D_i and L_i log2 e), i.e. before the
+ * dK/dV kernel, and events[2] after it; fp32: events[1] after the D_i kernel,
+ * before the single backward kernel, events[2] after it; events[3] at the
+ * end (with events[2]). Any entry may
  * be NULL (not recorded); `events` itself may be NULL, which makes the call
  * identical to fa_bwd_gqa. The events must have been created on the device that
  * owns `stream` (hipEventCreate); the library records them and nothing else.

@@ -112,5 +112,31 @@ def test_launch_gaps_of_backward_calls(tmp_path):
     row = [l for l in lines if l.startswith("| `bwd_dkdv")]
     assert len(row) == 1, lines
     cells = [c.strip() for c in row[0].strip("|").split("|")]
-    assert cells[1] == "3"
-    assert [float(x) for x in cells[2:8]] == [6.0, 50.0, 30.0, 86.0, 89.0, 3.0]
+    assert cells[1] == "3" and cells[2] == "3"
+    assert [float(x) for x in cells[3:9]] == [6.0, 50.0, 30.0, 86.0, 89.0, 3.0]
+
+
+def test_launch_gaps_of_two_kernel_backward_calls(tmp_path):
+    """The bf16 backward is two launches, dQ (with the row terms) then dK/dV."""
+    db = tmp_path / "trace.db"
+    con = sqlite3.connect(str(db))
+    con.execute("create table kernels (name text, start integer, end integer)")
+    pre = "void fa::(anonymous namespace)::"
+    rows = []
+    t = 0
+    for _ in range(2):
+        rows.append((pre + "fwd_bf16_kernel<128, 64, true, false, 8>(fa::Params)", t, t + 30_000))
+        t += 31_000
+        rows.append((pre + "bwd_dq_kernel<128, 64, true, false, false>(fa::Params)", t, t + 40_000))
+        t += 42_500
+        rows.append((pre + "bwd_dkdv_kernel<128, 1, true, false>(fa::Params)", t, t + 60_000))
+        t += 70_000
+    con.executemany("insert into kernels values (?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    lines = bench.summarize_launch_gaps(str(db))
+    row = [l for l in lines if l.startswith("| `bwd_dkdv")]
+    assert len(row) == 1, lines
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    assert cells[1] == "2" and cells[2] == "2"
+    assert [float(x) for x in cells[3:9]] == [0.0, 60.0, 40.0, 100.0, 102.5, 2.5]
