@@ -71,6 +71,8 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth (published)
 KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
                   "exact_io_aware_fa_amd/csrc/kernels/fa_device.h")
 TRAFFIC_WORKLOAD = "long_causal_b1_h32_n16384_d128"
+# The dK/dV kernel each head dimension runs (bf16).
+DKDV_KERNEL = {64: "bwd_dkdv_d64_kernel", 128: "bwd_dkdv_kernel", 256: "bwd_dkdv_staged_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_%s_traffic.json" % TRAFFIC_WORKLOAD)
 
 
@@ -291,9 +293,10 @@ def load_traffic(src_hash: str, workload: str):
 
 
 def _short(name: str) -> str:
-    for key in ("fwd_bf16_kernel", "fwd_bf16_staged_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
-                "bwd_prep_kernel", "fwd_fp32_kernel", "bwd_fp32_kernel", "fwd_fp8_kernel",
-                "fp8_quant_kernel", "copyBuffer"):
+    for key in ("fwd_bf16_kernel", "fwd_bf16_staged_kernel", "fwd_bf16_d64_kernel",
+                "bwd_dkdv_kernel", "bwd_dkdv_d64_kernel", "bwd_dkdv_staged_kernel",
+                "bwd_dq_kernel", "bwd_dq_staged_kernel", "bwd_prep_kernel", "fwd_fp32_kernel",
+                "bwd_fp32_kernel", "fwd_fp8_kernel", "fp8_quant_kernel", "copyBuffer"):
         if key in name:
             if key == "copyBuffer":
                 return name
@@ -1055,7 +1058,7 @@ def main() -> int:
                 "dq_kernel_ms": round(avg(dq_ms), 4)},
         "sclk": sclk.result(),
         "roofline": {
-            "kernel": "bwd_dkdv_kernel (recompute backward, dK and dV, d=%d)" % d,
+            "kernel": "%s (recompute backward, dK and dV, d=%d)" % (DKDV_KERNEL[d], d),
             "bound": "mfma",
             "achieved": round(main_tf, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -35,6 +35,7 @@ GQA = [
     (6, 1, 257, 64, False, "bf16", True),      # multi-query
     (4, 2, 129, 256, True, "bf16", False),
     (8, 4, 1000, 64, True, "bf16", True),
+    (4, 2, 1300, 64, False, "bf16", True),
     (4, 1, 383, 256, False, "bf16", True),     # multi-query, d=256
     (6, 3, 200, 64, True, "fp32", True),
     (4, 1, 150, 128, False, "fp32", False),

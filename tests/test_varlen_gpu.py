@@ -48,6 +48,8 @@ def _run(w, inp):
 SMALL = [
     # (heads, heads_kv, lengths, d, causal, dtype)
     (4, 4, (5, 1, 0, 130, 64, 300), 64, True, "bf16"),
+    (4, 2, (129, 5, 700), 64, False, "bf16"),
+    (2, 1, (1500, 40), 64, True, "bf16"),
     (4, 2, (257, 3, 100), 128, False, "bf16"),
     (4, 1, (129, 383, 7), 256, True, "bf16"),
     (2, 2, (1000, 24), 128, True, "bf16"),

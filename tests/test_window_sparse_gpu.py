@@ -77,6 +77,9 @@ CASES = [
     (300, 128, True, "bf16", True, (100, -1), False, 4, 2),
     (520, 256, False, "bf16", False, (-1, 60), False, 2, 1),
     (700, 64, True, "bf16", False, (-1, -1), True, 2, 2),
+    (640, 64, True, "bf16", False, (200, -1), True, 4, 2),
+    (520, 64, False, "bf16", True, (90, 90), True, 2, 1),
+    (1500, 64, True, "bf16", True, (300, -1), True, 2, 1),
     (700, 128, False, "bf16", True, (150, 150), True, 2, 1),
     (640, 128, True, "bf16", False, (200, -1), True, 4, 4),
     (500, 256, True, "bf16", False, (-1, -1), True, 2, 2),
