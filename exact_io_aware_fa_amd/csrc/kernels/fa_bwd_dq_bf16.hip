@@ -163,24 +163,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
   }
 
   // Per-lane LDS element offsets (tile-invariant). Row reads of K and V: row
-  // c of a 32-row block, logical chunk kd*2 + h. Transposing reads of K:
-  // row h*4 + (c%16)/4 of a 16-row block, column mb*32 + 16*(c/16) +
-  // 4*(c%4); the second read of a fragment (rows +8) lands in block mb ^ HB.
-  int koff[ND], voff[ND], toff[NMB];
-#pragma unroll
-  for (int kd = 0; kd < ND; ++kd) {
-    koff[kd] = c * D + (((kd * 2 + h) ^ swz_both<D>(c)) << 3);
-    voff[kd] = c * D + (((kd * 2 + h) ^ swz_row<D>(c)) << 3);
-  }
+  // c of a 32-row block, logical chunk kd*2 + h, i.e. kbase ^ (kd << 4) and
+  // vbase ^ (kd << 4). Transposing reads of K: row h*4 + (c%16)/4 of a 16-row
+  // block, column mb*32 + 16*(c/16) + 4*(c%4), i.e. tbase ^ (mb << 5); the
+  // second read of a fragment (rows +8) lands in block mb ^ HB. (The
+  // swizzled chunk bits lie below the row's, so one base register and an
+  // XOR per read replace a table of offsets: the registers this saves are
+  // what keeps the sweep loops free of spills.)
+  const int kbase = c * D + ((h ^ swz_both<D>(c)) << 3);
+  const int vbase = c * D + ((h ^ swz_row<D>(c)) << 3);
+  int tbase;
   {
     const int trow = h * 4 + ((c & 15) >> 2);
     const int tcol = 16 * (c >> 4) + 4 * (c & 3);
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const int col = mb * 32 + tcol;
-      toff[mb] = trow * D + (((col >> 3) ^ swz_both<D>(trow)) << 3) + (col & 7);
-    }
+    tbase = trow * D + ((((tcol >> 3) ^ swz_both<D>(trow)) << 3) | (tcol & 7));
   }
+  auto koff = [&](int kd) FA_INLINE { return kbase ^ (kd << 4); };
+  auto voff = [&](int kd) FA_INLINE { return vbase ^ (kd << 4); };
+  auto toff = [&](int mb) FA_INLINE { return tbase ^ (mb << 5); };
 
   // One key tile: S^T = K Q^T and dP^T = V dO^T (keys x queries), then
   // P^T = exp2(S^T c - L log2 e), dS^T = P^T (dP^T - D) as bf16 B fragments
@@ -196,8 +196,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
       g[kb] = f32x16{};
 #pragma unroll
       for (int kd = 0; kd < ND; ++kd) {
-        s[kb] = mma32(as_bf16x8(ld16(sk + kb * 32 * D + koff[kd])), qf[kd], s[kb]);
-        g[kb] = mma32(as_bf16x8(ld16(sv + kb * 32 * D + voff[kd])), gf[kd], g[kb]);
+        s[kb] = mma32(as_bf16x8(ld16(sk + kb * 32 * D + koff(kd))), qf[kd], s[kb]);
+        g[kb] = mma32(as_bf16x8(ld16(sv + kb * 32 * D + voff(kd))), gf[kd], g[kb]);
       }
     }
     bf16x8 sf[NKB * 2];
@@ -236,8 +236,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Params p) {
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int kk = 0; kk < NKB * 2; ++kk) {
-        const u32x2 lo = ds_read_tr16(sk + kk * 16 * D + toff[mb]);
-        const u32x2 hi = ds_read_tr16(sk + (kk * 16 + 8) * D + toff[mb ^ HB]);
+        const u32x2 lo = ds_read_tr16(sk + kk * 16 * D + toff(mb));
+        const u32x2 hi = ds_read_tr16(sk + (kk * 16 + 8) * D + toff(mb ^ HB));
         acc[mb] = mma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sf[kk], acc[mb]);
       }
   };
