@@ -12,7 +12,7 @@
 // accumulated onto D) and P * G = -dS is accumulated, so dK is scaled by
 // -scale at the end.
 //
-// Mapping onto CDNA4. A workgroup is 8 wave64s (two per SIMD) and owns 128
+// Mapping onto CDNA4. A workgroup is 4 wave64s (one per SIMD) and owns 64
 // keys, 16 per wave, with their dK, dV accumulators (fp32) for the whole
 // query sweep (key/value-outer order: each written once, no atomics). The
 // products are v_mfma_f32_16x16x32_bf16 (16 x 16 results, reduction 32):
@@ -25,7 +25,7 @@
 //   packed to bf16; the A operand dO^T (Q^T) for those queries is two
 //   transposing LDS reads (ds_read_b64_tr_b16) of the row-major tile.
 // Compared with one wave per SIMD holding 32 keys (fa_bwd_bf16.hip), a wave
-// needs half the accumulator and K/V registers (126 VGPRs in all), so two
+// needs half the accumulator and K/V registers (128 VGPRs in all), so four
 // workgroups share a CU, four waves per SIMD, and each hides the others'
 // waits; in exchange each A operand read from LDS feeds 16 keys instead of
 // 32, twice the LDS reads per product. That trade wins where many short key
@@ -46,8 +46,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kBKV = 128;  // keys per workgroup (8 waves x 16)
+constexpr int kThreads = 256;
+constexpr int kBKV = 64;  // keys per workgroup (4 waves x 16)
 
 // acc[16x16] += A[16x32] B[32x16] on the bf16 matrix cores, fp32 accumulate.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, each with 8
@@ -77,7 +77,9 @@ __device__ __forceinline__ int swz16(int row) {
 }
 
 template <bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_d64_kernel(Params p) {
+// (Four workgroups per CU: the compiler keeps the kernel within 128
+// registers per lane.)
+__global__ __launch_bounds__(kThreads, 4) void bwd_dkdv_d64_kernel(Params p) {
   constexpr int D = 64;
   constexpr int BQ = 64;                  // queries per tile (one 1 KB load per wave per tensor)
   constexpr int NQ16 = BQ / 16;           // 16-query blocks of S and G
@@ -89,7 +91,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_d64_kernel(Params p) {
   constexpr int TILE = BQ * D;            // elements per Q (or dO) tile
   constexpr int NW = kThreads / 64;
   constexpr int RPL = 1024 / ROWB;        // rows per 1 KB load
-  static_assert(TILE * 2 == NW * 1024, "one 1 KB load per wave per tensor");
+  constexpr int LPW = TILE * 2 / 1024 / NW;  // 1 KB loads per wave per tensor
+  static_assert(LPW * NW * 1024 == TILE * 2, "tile split");
   static_assert(BQ * 4 <= 16 * 64, "L/D vector load");
 
   // Stage s: Q tile at sm<s>[0], dO tile at sm<s>[TILE]; L log2 e and D of
@@ -180,11 +183,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_d64_kernel(Params p) {
     const int wqlo = band.qlo(kw0);
     const int wqhi = band.qhi(min(kw0 + 15, kv_lim - 1));
 
-    // Tile loads: wave w fills rows [w*RPL, (w+1)*RPL) of the Q and dO
-    // tiles; lane l writes physical chunk l % CH of row l / CH, holding
-    // logical chunk (l % CH) ^ swz16(row).
-    const int ld_row = w * RPL + lane / CH;
-    const int ld_off = (ld_row * D + ((lane % CH) ^ swz16(ld_row)) * 8) * 2;
+    // Tile loads: wave w fills rows [w*LPW*RPL, (w+1)*LPW*RPL) of the Q and
+    // dO tiles, one 1 KB load per RPL rows; lane l writes physical chunk
+    // l % CH of row l / CH, holding logical chunk (l % CH) ^ swz16(row).
+    int ld_off[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int ld_row = (w * LPW + i) * RPL + lane / CH;
+      ld_off[i] = (ld_row * D + ((lane % CH) ^ swz16(ld_row)) * 8) * 2;
+    }
     // Operand offsets (elements, tile-invariant). Row reads (A of S, G): row
     // qb*16 + m, logical chunk kd*4 + g. Transposing reads (A of dV^T, dK^T):
     // lane addresses row 4g + (m >> 2) (+16 for the second read), column
@@ -219,8 +226,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_d64_kernel(Params p) {
         if (gq > 0) __syncthreads();
         auto issue = [&](int it, bf16* sm, float* sv) FA_INLINE {
           const int qb0 = it * BQ * ROWB;
-          bload_lds16(rq, qb0 + ld_off, sm + w * RPL * D);
-          bload_lds16(rg, qb0 + ld_off, sm + TILE + w * RPL * D);
+#pragma unroll
+          for (int i = 0; i < LPW; ++i) {
+            bload_lds16(rq, qb0 + ld_off[i], sm + (w * LPW + i) * RPL * D);
+            bload_lds16(rg, qb0 + ld_off[i], sm + TILE + (w * LPW + i) * RPL * D);
+          }
           if (w == 0 && lane < BQ / 4) {
             bload_lds16(rl, it * BQ * 4 + lane * 16, sv);
             bload_lds16_at(rd, it * BQ * 4 + lane * 16, sv, BQ * 4);
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_d64_kernel(Params p) {
       }  // query heads of the group
     };
     if constexpr (SPARSE) {
-      // The workgroup's 128 keys are one block column of the mask.
+      // The workgroup's 64 keys lie in one block column of the mask.
       const int nl = stage_blocks(col_blocks(p, k0 / kBlock), sblk, tid, kThreads, p.nb);
       sweep(sparse_tiles<kBlock / BQ>(sblk, nl, tb, te));
     } else {
