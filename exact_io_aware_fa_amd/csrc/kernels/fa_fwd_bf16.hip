@@ -166,6 +166,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
   bf16x8 pf[NKB * 2];   // P^T fragments of the tile between the two phases
 #pragma unroll
   for (int kk = 0; kk < NKB * 2; ++kk) pf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  // 4 waves: the hot steps alternate between pf and pf2 (one holds P of the
+  // previous tile for its P V product while the softmax fills the other).
+  bf16x8 pf2[NWAVES == 4 ? NKB * 2 : 1];
 
   // Loads of a key (or value) tile into LDS. Wave w fills rows
   // [w * LPW * RPL, (w + 1) * LPW * RPL); lane l of a 1 KB load writes
@@ -207,18 +210,38 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
   // K row c (rows kb*32 + c share the swizzle of c), logical chunk kd*2 + h;
   // V transposing reads at row h*4 + (c%16)/4 (+16 kk, +8), column
   // mb*32 + 16*(c/16) + 4*(c%4).
-  int koff[ND], voff[NMB];
+  // With 4 waves (d = 256: 16 + 8 offsets, and registers are scarce) each
+  // is a base register XOR a per-index constant instead: the swizzled chunk
+  // bits lie below the row's, so kd (mb) only flips bits 4.. (5..).
+  constexpr bool XOFF = NWAVES == 4;
+  int koff[XOFF ? 1 : ND], voff[XOFF ? 1 : NMB];
+  int kbase = 0, vbase = 0;
+  if constexpr (!XOFF) {
 #pragma unroll
-  for (int kd = 0; kd < ND; ++kd) koff[kd] = c * D + (((kd * 2 + h) ^ swz_row<D>(c)) << 3);
+    for (int kd = 0; kd < ND; ++kd) koff[kd] = c * D + (((kd * 2 + h) ^ swz_row<D>(c)) << 3);
+  }
   {
     const int trow = h * 4 + ((c & 15) >> 2);
     const int tcol = 16 * (c >> 4) + 4 * (c & 3);
+    if constexpr (XOFF) {
+      kbase = c * D + ((h ^ swz_row<D>(c)) << 3);
+      vbase = trow * D + ((((tcol >> 3) ^ swz_tr<D>(trow)) << 3) | (tcol & 7));
+    } else {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const int col = mb * 32 + tcol;
-      voff[mb] = trow * D + ((((col >> 3) ^ swz_tr<D>(trow))) << 3) + (col & 7);
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int col = mb * 32 + tcol;
+        voff[mb] = trow * D + ((((col >> 3) ^ swz_tr<D>(trow))) << 3) + (col & 7);
+      }
     }
   }
+  auto ko = [&](int kd) FA_INLINE {
+    if constexpr (XOFF) return kbase ^ (kd << 4);
+    else return koff[kd];
+  };
+  auto vo = [&](int mb) FA_INLINE {
+    if constexpr (XOFF) return vbase ^ (mb << 5);
+    else return voff[mb];
+  };
 
   // Matrix phase of step m: S^T of tile m (K in sk) into sc and
   // O^T += V^T P^T of tile m-1 (V in sv, P^T in pf), as a fixed sequence of
@@ -233,13 +256,13 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
   constexpr int NS = NKB * ND;        // S^T slots
   auto rd_pv = [&](const bf16* sv, int k) FA_INLINE {
     const int mb = k % NMB, kk = k / NMB;
-    const u32x2 lo = ds_read_tr16(sv + kk * 16 * D + voff[mb]);
-    const u32x2 hi = ds_read_tr16(sv + (kk * 16 + 8) * D + voff[mb]);
+    const u32x2 lo = ds_read_tr16(sv + kk * 16 * D + vo(mb));
+    const u32x2 hi = ds_read_tr16(sv + (kk * 16 + 8) * D + vo(mb));
     return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
   auto rd_s = [&](const bf16* sk, int k) FA_INLINE {
     const int kb = k % NKB, kd = k / NKB;
-    return as_bf16x8(ld16(sk + kb * 32 * D + koff[kd]));
+    return as_bf16x8(ld16(sk + kb * 32 * D + ko(kd)));
   };
   auto slots = [&](const bf16* sk, const bf16* sv, auto pv_tag, auto s_tag) FA_INLINE {
     constexpr bool PV = decltype(pv_tag)::value;
@@ -307,7 +330,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
   // the weight its product used. (With the exact max as reference that
   // weight is exactly 1 and needs no correction; with a lazy one it is
   // 2^delta, rounded.)
-  auto finish_tile = [&](float mt) FA_INLINE {
+  auto finish_tile = [&](float mt, bf16x8 (&pout)[NKB * 2]) FA_INLINE {
     // sc holds t = s * cs - fref; mt is the row's largest t (-inf if none).
     float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -331,14 +354,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           u[t] = pack_bf16x2(sc[kb][kc * 8 + 2 * t], sc[kb][kc * 8 + 2 * t + 1]);
-        pf[kb * 2 + kc] = as_bf16x8(u);
+        pout[kb * 2 + kc] = as_bf16x8(u);
       }
     // Pin the results here: otherwise the compiler sinks the exponentials
     // and the packing past the next barrier, next to their use in the
     // matrix phase, where they would no longer overlap the other group's
     // matrix work.
 #pragma unroll
-    for (int kk = 0; kk < NKB * 2; ++kk) asm volatile("" : "+v"(pf[kk]));
+    for (int kk = 0; kk < NKB * 2; ++kk) asm volatile("" : "+v"(pout[kk]));
     asm volatile("" : "+v"(lpart), "+v"(lcorr));
   };
   auto rescale = [&](float alpha) FA_INLINE {
@@ -376,7 +399,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
       fref += delta;
       mt -= delta;
     }
-    finish_tile(mt);
+    finish_tile(mt, pf);
   };
   // General tile (masked entries -inf, references possibly unset): the max
   // is taken over the raw scores first, the reference is set (or moved) to
@@ -403,7 +426,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[kb][r] = fmaf(sc[kb][r], cs, -ref);
-    finish_tile(fmaf(mraw, cs, -ref));
+    finish_tile(fmaf(mraw, cs, -ref), pf);
   };
   // General softmax phase of step j: tiles this wave does not need (before
   // the first step, outside its rows' keys or past the last) leave P^T zero,
@@ -440,10 +463,15 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
+  // With 4 waves there is no partner group to keep in phase, and every
+  // step must pass the same number of barriers in every wave (the hot step
+  // below has no mid-step barrier), so it is left out.
   auto mid_barrier = [&]() FA_INLINE {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NWAVES == 8) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto open_step = [&](int m, bf16* nk, bf16* nv) FA_INLINE {
     if (m > 0) wait_global_loads();
@@ -479,6 +507,86 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
     slots(sk, sv, std::true_type{}, std::true_type{});
   };
 
+  // 4 waves, hot step m: S^T of tile m (as in slots), then the softmax of
+  // tile m interleaved with O^T += V^T P^T of tile m-1 (pin, its P from the
+  // previous step), writing P of tile m to pout. The two do not depend on
+  // each other, and a wave alone on its SIMD has no partner whose matrix
+  // work could cover its vector work, so here one wave does both at once:
+  // each product slot (its V^T fragment read RA slots ahead, fenced like
+  // slots) carries a share of the softmax -- the score shift and row max
+  // beside the first half of the products, the exponentials, row sums and
+  // bf16 packing beside the second. The arithmetic and its order are those
+  // of softmax_hot (row-sum additions in the same order per accumulator; the
+  // max is exact in any order). A rescale of the row references reaches O~
+  // only after the last product of tile m-1, as in the sequential step.
+  auto hot4 = [&](int m, const bf16* sk, bf16* nk, bf16* nv, const bf16* sv,
+                  const bf16x8 (&pin)[NKB * 2], bf16x8 (&pout)[NKB * 2]) FA_INLINE {
+    static_assert(NWAVES == 8 || NPV == 16 * NKB, "two scores per product slot");
+    constexpr int NPVH = NPV / 2;  // slots in each half
+    constexpr int RA = 4;          // V^T fragments read this many slots ahead
+    open_step(m, nk, nv);
+    slots(sk, sv, std::false_type{}, std::true_type{});
+    bf16x8 fr[RA + 1];
+#pragma unroll
+    for (int k = 0; k < RA; ++k) fr[k] = rd_pv(sv, k);
+    auto pv = [&](int k) FA_INLINE {
+      if (k + RA < NPV) fr[(k + RA) % (RA + 1)] = rd_pv(sv, k + RA);
+      const int mb = k % NMB, kk = k / NMB;
+      acc[mb] = mma32(fr[k % (RA + 1)], pin[kk], acc[mb]);
+    };
+    // First half: shift two scores per slot, t = s * cs - fref, and fold
+    // them into one of two max chains.
+    float mx[2] = {kNegInf, kNegInf};
+#pragma unroll
+    for (int k = 0; k < NPVH; ++k) {
+      pv(k);
+      const float t0 = fmaf(sc[(2 * k) / 16][(2 * k) % 16], cs, -fref);
+      const float t1 = fmaf(sc[(2 * k + 1) / 16][(2 * k + 1) % 16], cs, -fref);
+      sc[(2 * k) / 16][(2 * k) % 16] = t0;
+      sc[(2 * k + 1) / 16][(2 * k + 1) % 16] = t1;
+      mx[k & 1] = fmaxf(fmaxf(mx[k & 1], t0), t1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float mt = halves_max(fmaxf(mx[0], mx[1]));
+    const bool move = __builtin_amdgcn_ballot_w64(mt > kLazy) != 0;
+    float alpha = 1.f;
+    if (move) {
+      // As in softmax_hot; O~ takes alpha below, after tile m-1's products.
+      const float delta = mt > kLazy ? mt : 0.f;
+#pragma unroll
+      for (int e = 0; e < 16 * NKB; ++e) sc[e / 16][e % 16] -= delta;
+      alpha = __builtin_amdgcn_exp2f(-delta);
+      lpart *= alpha;
+      lcorr *= alpha;
+      fref += delta;
+      mt -= delta;
+    }
+    // Second half: two probabilities per slot, their row-sum terms and
+    // their bf16 pair of the P^T fragment.
+    float rp[4] = {0.f, 0.f, 0.f, 0.f};
+    u32x4 pu[NKB * 2];
+#pragma unroll
+    for (int j = 0; j < NPVH; ++j) {
+      pv(NPVH + j);
+      const int e0 = 2 * j, r0 = e0 % 16;
+      const float x0 = __builtin_amdgcn_exp2f(sc[e0 / 16][e0 % 16]);
+      const float x1 = __builtin_amdgcn_exp2f(sc[(e0 + 1) / 16][(e0 + 1) % 16]);
+      rp[r0 & 3] += x0;
+      rp[(r0 + 1) & 3] += x1;
+      pu[(e0 / 16) * 2 + r0 / 8][(r0 % 8) / 2] = pack_bf16x2(x0, x1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lpart += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+    const float pm = __builtin_amdgcn_exp2f(mt);
+    lcorr += __uint_as_float(pack_bf16x2(pm, 0.f) << 16) - pm;
+#pragma unroll
+    for (int kk = 0; kk < NKB * 2; ++kk) pout[kk] = as_bf16x8(pu[kk]);
+    if (move) {
+#pragma unroll
+      for (int q = 0; q < NMB; ++q) acc[q] *= alpha;
+    }
+  };
+
   // Steps [hot_begin, hot_end) are hot for this wave: tile m exists and is
   // needed by the wave (S^T of tile m), and the softmax tile (m for group A,
   // m-1 for group B) is unmasked. Step 0 and the other steps take the
@@ -503,8 +611,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
       step_a(m + 1, sK0, sK1, sV0, sV1);
     }
     for (; m + 1 < hot_end; m += 2) {
-      hot_a(m, sK1, sK0, sV1, sV0);
-      hot_a(m + 1, sK0, sK1, sV0, sV1);
+      if constexpr (NWAVES == 4) {
+        // Step m (odd) reads P of m-1 from pf, writes pf2; step m+1 back.
+        hot4(m, sK1, sK0, sV1, sV0, pf, pf2);
+        hot4(m + 1, sK0, sK1, sV0, sV1, pf2, pf);
+      } else {
+        hot_a(m, sK1, sK0, sV1, sV0);
+        hot_a(m + 1, sK0, sK1, sV0, sV1);
+      }
     }
     for (; m <= ntiles; m += 2) {
       step_a(m, sK1, sK0, sV1, sV0);
