@@ -71,8 +71,11 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth (published)
 KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
                   "exact_io_aware_fa_amd/csrc/kernels/fa_device.h")
 TRAFFIC_WORKLOAD = "long_causal_b1_h32_n16384_d128"
-# The dK/dV kernel each head dimension runs (bf16).
-DKDV_KERNEL = {64: "bwd_dkdv_d64_kernel", 128: "bwd_dkdv_kernel", 256: "bwd_dkdv_staged_kernel"}
+def dkdv_kernel_name(d: int, n: int) -> str:
+    """The dK/dV kernel a bf16 backward of head dimension d and n rows runs."""
+    if d == 64:
+        return "bwd_dkdv_d64_kernel" if n <= 1024 else "bwd_dkdv_kernel"
+    return "bwd_dkdv_staged_kernel" if d == 256 else "bwd_dkdv_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_%s_traffic.json" % TRAFFIC_WORKLOAD)
 
 
@@ -1058,7 +1061,7 @@ def main() -> int:
                 "dq_kernel_ms": round(avg(dq_ms), 4)},
         "sclk": sclk.result(),
         "roofline": {
-            "kernel": "%s (recompute backward, dK and dV, d=%d)" % (DKDV_KERNEL[d], d),
+            "kernel": "%s (recompute backward, dK and dV, d=%d)" % (dkdv_kernel_name(d, n), d),
             "bound": "mfma",
             "achieved": round(main_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
