@@ -33,7 +33,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fa_bwd_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dkdv_d64.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dq_bf16.hip"),
-    os.path.join(CSRC, "kernels", "fa_bwd_dq_bf16_staged.hip"),
+    os.path.join(CSRC, "kernels", "fa_bwd_dq_d256.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_aux.hip"),
     os.path.join(CSRC, "kernels", "fa_fp32.hip"),
     os.path.join(CSRC, "kernels", "fa_block_index.hip"),

@@ -105,7 +105,7 @@ hipError_t launch_bwd_dkdv_bf16(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16_staged(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16_d64(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const Params& p, int d, hipStream_t s);
-hipError_t launch_bwd_dq_bf16_staged(const Params& p, int d, hipStream_t s);
+hipError_t launch_bwd_dq_bf16_d256(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_fp32(const Params& p, int d, hipStream_t s);
 hipError_t launch_block_index(const uint8_t* mask, int nb, int32_t* out, hipStream_t s);
 

@@ -1,5 +1,5 @@
 // Attention backward, dQ part: bf16 in/out, fp32 accumulate, for gfx950
-// (d = 64 and 128; d = 256 uses fa_bwd_dq_bf16_staged.hip).
+// (d = 64 and 128; d = 256 uses fa_bwd_dq_d256.hip).
 //
 // dQ = scale * dS K with dS = P * (dP - D), dP = dO V^T, and P rebuilt from
 // the saved row statistic, P_ij = exp(scale q_i.k_j - L_i) (page 1, "注意力
@@ -328,7 +328,7 @@ hipError_t launch_bwd_dq_bf16(const Params& p, int d, hipStream_t s) {
   switch (d) {
     case 64: return launch_d<64, 64>(p, s);
     case 128: return launch_d<128, 64>(p, s);
-    case 256: return launch_bwd_dq_bf16_staged(p, d, s);
+    case 256: return launch_bwd_dq_bf16_d256(p, d, s);
     default: return hipErrorInvalidValue;
   }
 }

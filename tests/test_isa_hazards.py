@@ -1,7 +1,8 @@
 """Static check of the matrix products that accumulate in VGPRs.
 
 The S and dP products of the backward's dK/dV kernels (d <= 128 and the
-register-staged d = 256 kernel) are inline assembly
+register-staged d = 256 kernel) and of the d = 256 dQ kernel are inline
+assembly
 (v_mfma_f32_32x32x16_bf16 with a VGPR accumulator), which the compiler's
 hazard tracking does not see. A kernel is only correct if no other
 instruction reads or writes a product's result registers until the product
@@ -13,7 +14,8 @@ product (an instruction counts one, s_nop N counts N + 1) nothing but the
 next product of the same accumulation chain (same registers as destination
 and accumulator) touches the result registers, nothing writes a separate C
 input, that no result overlaps the product's A, B or C operands, and that
-no vector instruction writes an operand just before a product reads it.
+a vector instruction that writes an operand is at least VALU_WAIT wait
+states ahead of the product that reads it.
 Runs on the CPU (hipcc cross-compiles).
 """
 
@@ -26,8 +28,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNELS = os.path.join(ROOT, "exact_io_aware_fa_amd", "csrc", "kernels")
-SOURCES = ("fa_bwd_bf16.hip", "fa_bwd_bf16_staged.hip")
+SOURCES = ("fa_bwd_bf16.hip", "fa_bwd_bf16_staged.hip", "fa_bwd_dq_d256.hip")
 WAIT_STATES = 20  # well above what an 8-pass product needs before its result is read
+VALU_WAIT = 2     # a vector write of a register before a matrix product reads it
 
 
 def _hipcc():
@@ -108,12 +111,16 @@ def test_no_access_to_vgpr_product_results_in_flight(assembly):
 
 
 def test_no_vector_write_of_vgpr_product_operands_just_before(assembly):
-    """A vector instruction that writes a register needs a few wait states
-    before a matrix product may read it as A, B or C; the compiler inserts
-    them for its own products only. For each operand register of an
-    assembly product, the nearest earlier instruction that writes it (within
-    WINDOW_BEFORE instructions) must not be a vector ALU instruction: the
-    operands come from LDS loads or from other products."""
+    """A vector instruction that writes a register needs VALU_WAIT wait
+    states before a matrix product may read it as A, B or C; the compiler
+    inserts them for its own products only (the register allocator may put a
+    v_accvgpr_read that brings an operand back from an AGPR right before an
+    assembly product). For each operand register of an assembly product,
+    the nearest earlier instruction that writes it (within WINDOW_BEFORE
+    instructions) must either not be a vector ALU instruction (LDS loads and
+    other products are waited for by counters and the hardware) or lie at
+    least VALU_WAIT wait states back (an instruction counts one, s_nop N
+    counts N + 1)."""
     WINDOW_BEFORE = 6
     bad = []
     for i, line in enumerate(assembly):
@@ -121,19 +128,33 @@ def test_no_vector_write_of_vgpr_product_operands_just_before(assembly):
             continue
         ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
         pending = _vgprs(ops[1]) | _vgprs(ops[2]) | (_vgprs(ops[3]) if ops[3] != ops[0] else set())
+        waited = 0
         for prev in reversed(assembly[max(i - WINDOW_BEFORE, 0):i]):
             if not pending:
                 break
             # Instructions whose first operand is a destination: vector ALU
             # and matrix instructions and loads (a store's first operand is
             # an address it reads).
-            if not prev.startswith(("v_", "ds_read", "buffer_load", "global_load", "scratch_load")) \
-                    or " " not in prev:
-                continue
-            written = _vgprs(prev.split(None, 1)[1].split(",")[0]) & pending
-            if written:
-                if prev.startswith("v_") and not prev.startswith("v_mfma"):
-                    bad.append((prev, line))
-                    break
-                pending -= written
+            if prev.startswith(("v_", "ds_read", "buffer_load", "global_load", "scratch_load")) \
+                    and " " in prev:
+                written = _vgprs(prev.split(None, 1)[1].split(",")[0]) & pending
+                if written:
+                    if prev.startswith("v_") and not prev.startswith("v_mfma") \
+                            and waited < VALU_WAIT:
+                        bad.append((prev, line))
+                        break
+                    pending -= written
+            waited += _wait_states(prev)
     assert not bad, bad[:5]
+
+
+def test_vector_write_check_catches_a_write_right_before_a_product():
+    """The check above on a hand-made sequence: an operand written by a
+    v_accvgpr_read one instruction before the product is flagged; with an
+    s_nop 1 in between it is not."""
+    seq = ["v_accvgpr_read_b32 v41, a133", "s_waitcnt lgkmcnt(4)",
+           "v_mfma_f32_32x32x16_bf16 v[16:31], v[160:163], v[38:41], 0"]
+    with pytest.raises(AssertionError):
+        test_no_vector_write_of_vgpr_product_operands_just_before(seq)
+    ok = seq[:2] + ["s_nop 1"] + seq[2:]
+    test_no_vector_write_of_vgpr_product_operands_just_before(ok)
