@@ -122,9 +122,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
     // else a dO unit; a unit is 4 rows x 8 dims. Rows past n are read
     // clamped to row n-1; every product involving them is masked (P = 0,
     // dS = 0) and their dQ rows are not written.
+    // L and D of the tile's queries travel with it (loaded here, one tile
+    // ahead, rather than when the tile is written to LDS, where the write
+    // would wait for them).
     u32x4 ureg[UPTH][4];
+    float lreg = 0.f, dreg = 0.f;
     auto gload = [&](int it) {
       const int q0 = it * BQ;
+      if (tid < BQ) {
+        const int q = min(q0 + tid, n - 1);
+        lreg = l2v[q];
+        dreg = dvec[q];
+      }
 #pragma unroll
       for (int i = 0; i < UPTH; ++i) {
         const int u0 = tid + i * kThreads;
@@ -156,9 +165,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_staged_kernel(Params p) 
           *reinterpret_cast<u32x2*>(&tr[(dg * 8 + e) * TSTR + qg * 4]) = column4(ureg[i], e);
       }
       if (tid < BQ) {
-        const int q = min(it * BQ + tid, n - 1);
-        sL[buf][tid] = l2v[q];
-        sDv[buf][tid] = dvec[q];
+        sL[buf][tid] = lreg;
+        sDv[buf][tid] = dreg;
       }
     };
 
