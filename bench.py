@@ -75,7 +75,7 @@ def dkdv_kernel_name(d: int, n: int) -> str:
     """The dK/dV kernel a bf16 backward of head dimension d and n rows runs."""
     if d == 64:
         return "bwd_dkdv_d64_kernel" if n <= 1024 else "bwd_dkdv_kernel"
-    return "bwd_dkdv_staged_kernel" if d == 256 else "bwd_dkdv_kernel"
+    return "bwd_dkdv_d256_kernel" if d == 256 else "bwd_dkdv_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_%s_traffic.json" % TRAFFIC_WORKLOAD)
 
 
@@ -297,7 +297,7 @@ def load_traffic(src_hash: str, workload: str):
 
 def _short(name: str) -> str:
     for key in ("fwd_bf16_kernel", "fwd_bf16_staged_kernel", "fwd_bf16_d64_kernel",
-                "bwd_dkdv_kernel", "bwd_dkdv_d64_kernel", "bwd_dkdv_staged_kernel",
+                "bwd_dkdv_kernel", "bwd_dkdv_d64_kernel", "bwd_dkdv_d256_kernel",
                 "bwd_dq_kernel", "bwd_dq_d256_kernel", "bwd_prep_kernel", "fwd_fp32_kernel",
                 "bwd_fp32_kernel", "fwd_fp8_kernel", "fp8_quant_kernel", "copyBuffer"):
         if key in name:

@@ -30,8 +30,8 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fa_fwd_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_fwd_bf16_d64.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_bf16.hip"),
-    os.path.join(CSRC, "kernels", "fa_bwd_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dkdv_d64.hip"),
+    os.path.join(CSRC, "kernels", "fa_bwd_dkdv_d256.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dq_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dq_d256.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_aux.hip"),

@@ -1,6 +1,6 @@
 // Attention backward, dK/dV part: bf16 in/out, fp32 accumulate, for gfx950
 // (d = 64 and 128; d = 64 with at most 1024 rows uses fa_bwd_dkdv_d64.hip,
-// d = 256 fa_bwd_bf16_staged.hip).
+// d = 256 fa_bwd_dkdv_d256.hip).
 //
 // Method: recomputation from the saved row statistic (page 1, "注意力为什么
 // 受限于显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 八; page 2,
@@ -506,7 +506,7 @@ hipError_t launch_bwd_dkdv_bf16(const Params& p, int d, hipStream_t s) {
     // sweep sets the time, and this kernel's pipelined waves run it faster.
     case 64: return p.n <= 1024 ? launch_bwd_dkdv_bf16_d64(p, d, s) : launch_d<64, 2>(p, s);
     case 128: return launch_d<128, 1>(p, s);
-    case 256: return launch_bwd_dkdv_bf16_staged(p, d, s);
+    case 256: return launch_bwd_dkdv_bf16_d256(p, d, s);
     default: return hipErrorInvalidValue;
   }
 }

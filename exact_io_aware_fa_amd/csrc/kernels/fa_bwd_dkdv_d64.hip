@@ -1,6 +1,6 @@
 // Attention backward, dK/dV part, for d = 64 and sequences of at most 1024
 // rows: bf16 in/out, fp32 accumulate, for gfx950 (the other shapes use
-// fa_bwd_bf16.hip and fa_bwd_bf16_staged.hip).
+// fa_bwd_bf16.hip and fa_bwd_dkdv_d256.hip).
 //
 // Method: recomputation from the saved row statistic (page 1, "注意力为什么
 // 受限于显存带宽：用算术强度与分块把 FlashAttention 推导清楚", section 八; page 2,

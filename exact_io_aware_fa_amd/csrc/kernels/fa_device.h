@@ -54,7 +54,7 @@ __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 acc) {
 // needs two wait states before a product reads it; the compiler inserts
 // them for its own products only, so a kernel using these forms must not
 // let one come closer (the ISA hazard test checks the generated code of
-// every kernel that uses them). The w forms (mma32_vw, mma32_v0w) open with
+// every kernel that uses them). The w forms (mma32_vw, mma32_v0w, mma32_vcw) open with
 // the two wait states themselves, for kernels where the register allocator
 // brings operands back from AGPRs right before the products.
 __device__ __forceinline__ f32x16 mma32_v(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -78,6 +78,12 @@ __device__ __forceinline__ f32x16 mma32_vw(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x16 mma32_v0w(bf16x8 a, bf16x8 b) {
   f32x16 d;
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ f32x16 mma32_vcw(bf16x8 a, bf16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
+               : "=&v"(d) : "v"(a), "v"(b), "v"(c));
   return d;
 }
 // An empty use of two values in VGPRs (keeps them, and their registers,

@@ -1,8 +1,7 @@
 """Static check of the matrix products that accumulate in VGPRs.
 
-The S and dP products of the backward's dK/dV kernels (d <= 128 and the
-register-staged d = 256 kernel) and of the d = 256 dQ kernel are inline
-assembly
+The S and dP products of the backward's dK/dV kernels (d <= 128 and
+d = 256) and of the d = 256 dQ kernel are inline assembly
 (v_mfma_f32_32x32x16_bf16 with a VGPR accumulator), which the compiler's
 hazard tracking does not see. A kernel is only correct if no other
 instruction reads or writes a product's result registers until the product
@@ -28,7 +27,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNELS = os.path.join(ROOT, "exact_io_aware_fa_amd", "csrc", "kernels")
-SOURCES = ("fa_bwd_bf16.hip", "fa_bwd_bf16_staged.hip", "fa_bwd_dq_d256.hip")
+SOURCES = ("fa_bwd_bf16.hip", "fa_bwd_dq_d256.hip", "fa_bwd_dkdv_d256.hip")
 WAIT_STATES = 20  # well above what an 8-pass product needs before its result is read
 VALU_WAIT = 2     # a vector write of a register before a matrix product reads it
 
