@@ -68,14 +68,18 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth (published)
-KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
+# The headline dK/dV kernel, the dispatch that picks it and their shared helpers.
+KERNEL_SOURCES = ("exact_io_aware_fa_amd/csrc/kernels/fa_bwd_dkdv_wide.hip",
+                  "exact_io_aware_fa_amd/csrc/kernels/fa_bwd_bf16.hip",
                   "exact_io_aware_fa_amd/csrc/kernels/fa_device.h")
 TRAFFIC_WORKLOAD = "long_causal_b1_h32_n16384_d128"
 def dkdv_kernel_name(d: int, n: int) -> str:
     """The dK/dV kernel a bf16 backward of head dimension d and n rows runs."""
     if d == 64:
         return "bwd_dkdv_d64_kernel" if n <= 1024 else "bwd_dkdv_kernel"
-    return "bwd_dkdv_d256_kernel" if d == 256 else "bwd_dkdv_kernel"
+    if d == 128:
+        return "bwd_dkdv_wide_kernel" if n >= 4096 else "bwd_dkdv_kernel"
+    return "bwd_dkdv_d256_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_%s_traffic.json" % TRAFFIC_WORKLOAD)
 
 
@@ -297,7 +301,7 @@ def load_traffic(src_hash: str, workload: str):
 
 def _short(name: str) -> str:
     for key in ("fwd_bf16_kernel", "fwd_bf16_staged_kernel", "fwd_bf16_d64_kernel",
-                "bwd_dkdv_kernel", "bwd_dkdv_d64_kernel", "bwd_dkdv_d256_kernel",
+                "bwd_dkdv_kernel", "bwd_dkdv_d64_kernel", "bwd_dkdv_d256_kernel", "bwd_dkdv_wide_kernel",
                 "bwd_dq_kernel", "bwd_dq_d256_kernel", "bwd_prep_kernel", "fwd_fp32_kernel",
                 "bwd_fp32_kernel", "fwd_fp8_kernel", "fp8_quant_kernel", "copyBuffer"):
         if key in name:
@@ -516,7 +520,7 @@ def summarize_rocprof(trace_db, fetch_db, write_db, copy_mib, command, out_md, o
     if tcc_db:
         lines += summarize_tcc(tcc_db)
     open(out_md, "w").write("\n".join(lines) + "\n")
-    bwd = [k for k in traffic if k.startswith("bwd_dkdv_kernel")]
+    bwd = [k for k in traffic if k.startswith(dkdv_kernel_name(128, 16384))]
     if bwd and out_json:
         t = traffic[bwd[0]]
         json.dump({"kernel": bwd[0], "kernel_source_hash": kernel_source_hash(),

@@ -32,6 +32,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "fa_bwd_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dkdv_d64.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dkdv_d256.hip"),
+    os.path.join(CSRC, "kernels", "fa_bwd_dkdv_wide.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dq_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dq_d256.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_aux.hip"),

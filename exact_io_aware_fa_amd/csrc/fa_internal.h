@@ -104,6 +104,7 @@ hipError_t launch_bwd_prep(const Params& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16_d64(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16_d256(const Params& p, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16_wide(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_dq_bf16_d256(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_fp32(const Params& p, int d, hipStream_t s);

@@ -140,3 +140,18 @@ def test_launch_gaps_of_two_kernel_backward_calls(tmp_path):
     cells = [c.strip() for c in row[0].strip("|").split("|")]
     assert cells[1] == "2" and cells[2] == "2"
     assert [float(x) for x in cells[3:9]] == [0.0, 60.0, 40.0, 100.0, 102.5, 2.5]
+
+
+def test_dkdv_kernel_names_follow_the_dispatch():
+    """The roofline line names the dK/dV kernel the library picks: the 64-key
+    wave kernel for d = 128 from 4096 rows, the per-dimension kernels else."""
+    assert bench.dkdv_kernel_name(128, 16384) == "bwd_dkdv_wide_kernel"
+    assert bench.dkdv_kernel_name(128, 4096) == "bwd_dkdv_wide_kernel"
+    assert bench.dkdv_kernel_name(128, 2048) == "bwd_dkdv_kernel"
+    assert bench.dkdv_kernel_name(64, 1024) == "bwd_dkdv_d64_kernel"
+    assert bench.dkdv_kernel_name(256, 8192) == "bwd_dkdv_d256_kernel"
+    pre = "void fa::(anonymous namespace)::"
+    assert bench._short(pre + "bwd_dkdv_wide_kernel<true>(fa::Params)") == \
+        "bwd_dkdv_wide_kernel<true>"
+    assert bench._short(pre + "bwd_dkdv_kernel<128, 1, true, false>(fa::Params)") == \
+        "bwd_dkdv_kernel<128, 1, true, false>"

@@ -27,7 +27,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNELS = os.path.join(ROOT, "exact_io_aware_fa_amd", "csrc", "kernels")
-SOURCES = ("fa_bwd_bf16.hip", "fa_bwd_dq_d256.hip", "fa_bwd_dkdv_d256.hip")
+SOURCES = ("fa_bwd_bf16.hip", "fa_bwd_dq_d256.hip", "fa_bwd_dkdv_d256.hip", "fa_bwd_dkdv_wide.hip")
 WAIT_STATES = 20  # well above what an 8-pass product needs before its result is read
 VALU_WAIT = 2     # a vector write of a register before a matrix product reads it
 

@@ -122,6 +122,9 @@ EDGE = [
     (300, 256, False, "bf16", False), (383, 256, True, "bf16", True),
     (1000, 64, False, "bf16", True), (65, 128, True, "fp32", False),
     (200, 256, False, "fp32", True), (31, 64, True, "fp32", True),
+    # d = 128 from 4096 rows runs the 64-keys-per-wave dK/dV kernel: ragged
+    # lengths and key padding there too
+    (4100, 128, True, "bf16", True), (4357, 128, False, "bf16", True),
 ]
 
 
