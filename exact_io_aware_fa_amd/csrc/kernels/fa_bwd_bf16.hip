@@ -506,11 +506,12 @@ hipError_t launch_bwd_dkdv_bf16(const Params& p, int d, hipStream_t s) {
     // sweep sets the time, and this kernel's pipelined waves run it faster.
     case 64: return p.n <= 1024 ? launch_bwd_dkdv_bf16_d64(p, d, s) : launch_d<64, 2>(p, s);
     // 64 keys per wave (fa_bwd_dkdv_wide.hip) from 4096 rows, without a
-    // block mask; shorter sequences leave too few of its 256-key workgroups
-    // to fill the GPU.
+    // block mask or a window; shorter sequences leave too few of its 256-key
+    // workgroups to fill the GPU.
     case 128:
-      return p.blk == nullptr && p.n >= 4096 ? launch_bwd_dkdv_bf16_wide(p, d, s)
-                                             : launch_d<128, 1>(p, s);
+      return p.blk == nullptr && p.win_left < 0 && p.win_right < 0 && p.n >= 4096
+                 ? launch_bwd_dkdv_bf16_wide(p, d, s)
+                 : launch_d<128, 1>(p, s);
     case 256: return launch_bwd_dkdv_bf16_d256(p, d, s);
     default: return hipErrorInvalidValue;
   }

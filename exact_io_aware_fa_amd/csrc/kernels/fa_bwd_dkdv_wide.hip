@@ -27,7 +27,9 @@
 // streaming in), row-major with the swizzle that serves both the row reads
 // and the transposing reads, one barrier per step. Block-sparse calls keep
 // the 128-key kernel: 256 keys span two block columns of the mask, whose
-// query-block lists would have to be merged.
+// query-block lists would have to be merged. So do windowed calls: at each
+// edge of the window a 256-key workgroup has twice the partly visible query
+// tiles of a 128-key one, and measured slower.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -454,7 +456,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_wide_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_bwd_dkdv_bf16_wide(const Params& p, int d, hipStream_t s) {
-  if (d != kD || p.blk != nullptr) return hipErrorInvalidValue;
+  if (d != kD || p.blk != nullptr || p.win_left >= 0 || p.win_right >= 0)
+    return hipErrorInvalidValue;
   const int t_c = (p.n + kBKV - 1) / kBKV;
   const long long total = (long long)t_c * p.batch * p.heads_kv;
   dim3 grid((unsigned)total), block(kThreads);
