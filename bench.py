@@ -300,7 +300,7 @@ def load_traffic(src_hash: str, workload: str):
 
 
 def _short(name: str) -> str:
-    for key in ("fwd_bf16_kernel", "fwd_bf16_staged_kernel", "fwd_bf16_d64_kernel",
+    for key in ("fwd_bf16_kernel", "fwd_bf16_d64_kernel",
                 "bwd_dkdv_kernel", "bwd_dkdv_d64_kernel", "bwd_dkdv_d256_kernel", "bwd_dkdv_wide_kernel",
                 "bwd_dq_kernel", "bwd_dq_d256_kernel", "bwd_prep_kernel", "fwd_fp32_kernel",
                 "bwd_fp32_kernel", "fwd_fp8_kernel", "fp8_quant_kernel", "copyBuffer"):

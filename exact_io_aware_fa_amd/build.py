@@ -27,7 +27,6 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [
     os.path.join(CSRC, "fa_api.hip"),
     os.path.join(CSRC, "kernels", "fa_fwd_bf16.hip"),
-    os.path.join(CSRC, "kernels", "fa_fwd_bf16_staged.hip"),
     os.path.join(CSRC, "kernels", "fa_fwd_bf16_d64.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_bf16.hip"),
     os.path.join(CSRC, "kernels", "fa_bwd_dkdv_d64.hip"),

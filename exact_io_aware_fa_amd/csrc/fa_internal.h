@@ -97,7 +97,6 @@ hipError_t launch_fp8_quantize(const Fp8QuantParams& p, int d, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s);
 
 hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s);
-hipError_t launch_fwd_bf16_staged(const Params& p, int d, hipStream_t s);
 hipError_t launch_fwd_bf16_d64(const Params& p, int d, hipStream_t s);
 hipError_t launch_fwd_fp32(const Params& p, int d, hipStream_t s);
 hipError_t launch_bwd_prep(const Params& p, int d, bool bf16, hipStream_t s);

@@ -1,6 +1,5 @@
 // Fused attention forward, bf16 in/out, fp32 accumulate, for gfx950
-// (d = 128 and 256; d = 64 uses fa_fwd_bf16_d64.hip, block-sparse d = 256
-// fa_fwd_bf16_staged.hip).
+// (d = 128 and 256; d = 64 and block-sparse d = 128 use fa_fwd_bf16_d64.hip).
 //
 // Method: the tiled forward of page 2 ("4. FlashAttention 深度剖析", 4.3.2)
 // with the per-block (m, l, O) update of page 1 ("注意力为什么受限于显存带宽：
@@ -67,13 +66,15 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BC, bool CAUSAL, bool WIN, int NWAVES>
+template <int D, int BC, bool CAUSAL, bool SPARSE, bool WIN, int NWAVES>
 __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
   // 8 waves: ping-pong between waves w and w + 4 (groups A and B); 4 waves:
   // every wave is in group A and runs both phases of each step.
   constexpr int kThreads = NWAVES * 64;
   constexpr int kBR = 32 * NWAVES;      // query rows per workgroup
   static_assert(NWAVES == 8 || NWAVES == 4, "workgroup shape");
+  // A block-sparse mask needs the workgroup's rows in one block row.
+  static_assert(!SPARSE || 32 * NWAVES == kBlock, "block-sparse workgroups are one block row");
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int ROWB = D * 2;           // bytes per row
   constexpr int TILEB = BC * ROWB;      // bytes per K or V tile
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) bf16 sK1[BC * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV0[BC * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV1[BC * D];
+  __shared__ int sblk[SPARSE ? kMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -136,19 +138,39 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
     }
   }
 
-  // Keys of this lane's row: [band.lo(qi), band.hi(qi)). Step m of the sweep handles key
-  // tile tb + m; the workgroup's rows need tiles [tb, tb + ntiles). This
-  // wave's rows need steps [s_first, s_last], and steps [su_lo, su_hi) hold
-  // only keys every row of the wave sees (the bounds are non-decreasing in
-  // the row); the other steps of the wave are masked.
+  // Keys of this lane's row: [band.lo(qi), band.hi(qi)). Step m of the
+  // sweep handles key tile tile_of(m): tb + m, or with a block mask the m-th
+  // tile of the listed blocks of the workgroup's block row inside
+  // [tb, te). This wave's rows need steps [s_first, s_last], and steps
+  // [su_lo, su_hi) hold only keys every row of the wave sees (the bounds are
+  // non-decreasing in the row, and so are the tiles of the steps); the
+  // other steps of the wave are masked.
   const Band<CAUSAL> band = make_band<CAUSAL>(p, n, kv_lim);
   const int tb = band.lo(q0) / BC;
-  const int ntiles = max((band.hi(min(q0 + kBR, n) - 1) + BC - 1) / BC - tb, 0);
+  const int te = (band.hi(min(q0 + kBR, n) - 1) + BC - 1) / BC;
   const int qw_last = min(qw0 + 31, n - 1);
-  const int s_first = band.lo(qw0) / BC - tb;
-  const int s_last = (band.hi(qw_last) - 1) / BC - tb;
-  const int su_lo = (band.lo(qw_last) + BC - 1) / BC - tb;
-  const int su_hi = band.hi(qw0) / BC - tb;
+  SparseTiles<kBlock / BC> st{};
+  if constexpr (SPARSE) {
+    const int nl = stage_blocks(row_blocks(p, q0 / kBlock), sblk, tid, kThreads, p.nb);
+    st = sparse_tiles<kBlock / BC>(sblk, nl, tb, te);
+  }
+  auto tile_of = [&](int m) FA_INLINE {
+    if constexpr (SPARSE) return st.tile(m);
+    else return tb + m;
+  };
+  const int ntiles = SPARSE ? st.count : max(te - tb, 0);
+  int s_first, s_last, su_lo, su_hi;
+  if constexpr (SPARSE) {
+    s_first = st.first_at_least(band.lo(qw0) / BC);
+    s_last = st.first_at_least((band.hi(qw_last) + BC - 1) / BC) - 1;
+    su_lo = st.first_at_least((band.lo(qw_last) + BC - 1) / BC);
+    su_hi = st.first_at_least(band.hi(qw0) / BC);
+  } else {
+    s_first = band.lo(qw0) / BC - tb;
+    s_last = (band.hi(qw_last) - 1) / BC - tb;
+    su_lo = (band.lo(qw_last) + BC - 1) / BC - tb;
+    su_hi = band.hi(qw0) / BC - tb;
+  }
 
   f32x16 acc[NMB];
 #pragma unroll
@@ -184,7 +206,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
     ld_voff[i] = (row * D + ((lane % CH) ^ swz_tr<D>(row)) * 8) * 2;
   }
   auto issue = [&](const bf16* src, const int (&off)[LPW], int j, bf16* dst) FA_INLINE {
-    const int kb0 = (tb + j) * BC;
+    const int kb0 = tile_of(j) * BC;
     const auto r = buffer_rsrc(src + (size_t)kb0 * D, max(min(kv_lim - kb0, BC), 0) * ROWB);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) bload_lds16(r, off[i], dst + (w * LPW + i) * RPL * D);
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(Params p) {
   // P^T as bf16 B fragments in pf (chunk kk holds keys kk*16 + {h*4 + 0..3,
   // 8 + h*4 + 0..3}).
   auto apply_mask = [&](int j) FA_INLINE {
-    const int kb0 = (tb + j) * BC;
+    const int kb0 = tile_of(j) * BC;
     // Row bounds, recomputed per masked tile from an opaque copy of the
     // row index (so they need no registers across the sweep).
     int qv = qi;
@@ -669,12 +691,16 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
   const int t_r = (p.n + 32 * NW - 1) / (32 * NW);
   const long long total = (long long)t_r * p.batch * p.heads;
   dim3 grid((unsigned)total), block(NW * 64);
-  // (Block-sparse masks never reach this kernel.)
-  return dispatch_mask_win(p, [&](auto causal, auto, auto win) {
-    hipLaunchKernelGGL(
-        (fwd_bf16_kernel<D, BC, decltype(causal)::value, decltype(win)::value, NW>), grid,
-        block, 0, s, p);
-    return hipGetLastError();
+  return dispatch_mask_win(p, [&](auto causal, auto sparse, auto win) {
+    // Block-sparse masks reach only the 4-wave form (d = 256).
+    if constexpr (decltype(sparse)::value && NW != 4) {
+      return hipErrorInvalidValue;
+    } else {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, decltype(causal)::value, decltype(sparse)::value,
+                                          decltype(win)::value, NW>),
+                         grid, block, 0, s, p);
+      return hipGetLastError();
+    }
   });
 }
 
@@ -686,9 +712,8 @@ hipError_t launch_fwd_bf16(const Params& p, int d, hipStream_t s) {
     // Block-sparse masks take the 4-wave kernel: its 128-row workgroups lie
     // in one block row of the mask.
     case 128: return p.blk != nullptr ? launch_fwd_bf16_d64(p, d, s) : launch_d<128, 64>(p, s);
-    // Block-sparse d = 256 takes the register-staged kernel (128-row
-    // workgroups lie in one block row of the mask; it supports the lists).
-    case 256: return p.blk != nullptr ? launch_fwd_bf16_staged(p, d, s) : launch_d<256, 64>(p, s);
+    // d = 256: 4-wave workgroups of 128 rows, one block row of a block mask.
+    case 256: return launch_d<256, 64>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
