@@ -83,6 +83,8 @@ CASES = [
     (700, 128, False, "bf16", True, (150, 150), True, 2, 1),
     (640, 128, True, "bf16", False, (200, -1), True, 4, 4),
     (500, 256, True, "bf16", False, (-1, -1), True, 2, 2),
+    (777, 256, False, "bf16", True, (200, 100), True, 2, 1),
+    (900, 256, True, "bf16", False, (300, -1), True, 4, 2),
     (300, 64, True, "fp32", True, (40, -1), False, 2, 2),
     (400, 128, False, "fp32", False, (-1, 90), True, 2, 1),
     (390, 256, True, "fp32", False, (64, -1), True, 2, 2),
