@@ -4,7 +4,8 @@
 Sequences are stored back to back per head ([heads, total, d]); each attends
 only to itself, causal positions counted from its first row. Small batches
 (an empty and a one-row sequence among them, grouped heads, d = 64/128/256,
-bf16 and fp32) are compared with the fp64 oracle per (head, sequence). At
+bf16 and fp32, and two d = 128 batches whose longest sequence passes 4096
+rows) are compared with the fp64 oracle per (head, sequence). At
 the measured size (32 heads, 16384 packed rows, lengths 256..4096, d = 128,
 causal) every output is compared bit for bit with the padded-layout call on
 each sequence on its own (the same kernels on the same rows), and seeded
@@ -53,6 +54,10 @@ SMALL = [
     (4, 2, (257, 3, 100), 128, False, "bf16"),
     (4, 1, (129, 383, 7), 256, True, "bf16"),
     (2, 2, (1000, 24), 128, True, "bf16"),
+    # Longest sequence from 4096 rows: the 64-keys-per-wave dK/dV kernel,
+    # whose 256-key workgroups past a shorter sequence's end exit at once.
+    (2, 1, (4500, 300, 0, 37), 128, True, "bf16"),
+    (2, 2, (129, 4200), 128, False, "bf16"),
     (4, 4, (300, 1, 65), 128, True, "fp32"),
     (2, 2, (31, 200), 256, False, "fp32"),
     (6, 3, (64, 64, 0, 64, 500), 64, False, "fp32"),
