@@ -761,3 +761,31 @@ def test_window_and_block_planted_mistakes_are_rejected():
     wrong_b = visible_mask(n, False, None, None, (-1, -1), bm.T)
     assert not np.array_equal(wrong_b, ref_b)
     assert np.array_equal(visible_mask(n, False, None, None, (-1, -1), bm), ref_b)
+
+
+@pytest.mark.parametrize("causal,window", [(True, (50, -1)), (False, (40, 30))])
+def test_window_locality_of_slices(causal, window):
+    """The property the maximum-size GPU test rests on: with a window, the
+    oracle on a slice [a, e) of the sequence gives the full problem's O, LSE
+    and dQ for rows whose window lies inside the slice, and its dK, dV for
+    keys whose queries do (the masks depend on i - j only)."""
+    from test_max_size_gpu import _segments, _valid
+    n, d = 900, 16
+    rng = np.random.default_rng(12)
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    full = head_backward(q, k, v, do, 0.3, causal, None, window)
+    left, right = window[0], 0 if causal else window[1]
+    for a, e in _segments(n, left, right):
+        (f_lo, f_hi), (k_lo, k_hi) = _valid(n, a, e, left, right)
+        assert f_hi - f_lo > 0 and k_hi - k_lo > 0
+        part = head_backward(q[a:e], k[a:e], v[a:e], do[a:e], 0.3, causal, None, window)
+        for name, lo, hi in (("o", f_lo, f_hi), ("lse", f_lo, f_hi), ("dq", f_lo, f_hi),
+                             ("dk", k_lo, k_hi), ("dv", k_lo, k_hi)):
+            np.testing.assert_allclose(part[name][lo - a:hi - a], full[name][lo:hi],
+                                       rtol=1e-10, atol=1e-12, err_msg=name)
+        # One row or key more on either side would reach outside the slice.
+        if a > 0:
+            lo = f_lo - 1 - a
+            assert not np.allclose(part["dq"][lo], full["dq"][f_lo - 1], rtol=1e-10, atol=1e-12)
+            lo = k_lo - 1 - a
+            assert not np.allclose(part["dk"][lo], full["dk"][k_lo - 1], rtol=1e-10, atol=1e-12)
