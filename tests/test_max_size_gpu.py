@@ -32,6 +32,7 @@ CASES = [
     # (n, d, causal, window, batch, heads, heads_kv)
     ((1 << 22) - 37, 256, True, (200, -1), 1, 2, 1),   # 2^31 - 18944 bytes per head
     ((1 << 22) - 5, 128, False, (150, 150), 1, 2, 2),
+    ((1 << 22) - 1, 64, True, (100, -1), 1, 4, 2),
 ]
 
 
