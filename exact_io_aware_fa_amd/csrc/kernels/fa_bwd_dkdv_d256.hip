@@ -323,8 +323,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_d256_kernel(Params p) {
       if (ns == 0) return;
       // Steps [su0, su1) hold only queries that see every key of the
       // workgroup.
-      const int su0 = tiles.first_at_least(iu0);
-      const int su1 = max(tiles.first_at_least(iu1), su0);
+      int su0, su1;
+      tiles.steps_of(iu0, iu1, su0, su1);
       for (int gq = 0; gq < p.group; ++gq) {
         // Query head gq of the group: its Q, dO and row vectors (work entry
         // of query head hk * group + gq).
@@ -439,12 +439,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_d256_kernel(Params p) {
         }
       }  // query heads of the group
     };
+    // Query tiles from the last down: in a causal sweep every workgroup of
+    // a head then starts at the same tile, so the workgroups running side by
+    // side read the same Q and dO tiles at about the same time (from the
+    // diagonal up they start 128 rows apart, and 32 of them on one L2 keep
+    // about 4 MB of d = 256 tiles in flight).
     if constexpr (SPARSE) {
       // The workgroup's 128 keys are one block column of the mask.
       const int nl = stage_blocks(col_blocks(p, k0 / kBlock), sblk, tid, kThreads, p.nb);
-      sweep(sparse_tiles<kBlock / BQ>(sblk, nl, tb, te));
+      sweep(reversed(sparse_tiles<kBlock / BQ>(sblk, nl, tb, te)));
     } else {
-      sweep(dense_tiles(tb, te));
+      sweep(reversed(dense_tiles(tb, te)));
     }
   }
 

@@ -43,24 +43,6 @@ constexpr int kBKV = 256;  // keys per workgroup (4 waves x 64)
 constexpr int kD = 128;
 constexpr int kBQ = 32;    // queries per tile
 
-// Query tiles [tb, te) from the last down. In a causal sweep every
-// workgroup of a head then starts at the same (last) tile and ends at its
-// own diagonal, so the workgroups running side by side read the same Q and
-// dO tiles at about the same time and the L2 serves all but the first. (From
-// the diagonal up, neighbouring workgroups start 256 rows apart, and 32 of
-// them on one L2 keep about 4 MB of tiles in flight.)
-struct DescTiles {
-  int te, count;
-  __device__ __forceinline__ int tile(int m) const {
-    return __builtin_amdgcn_readfirstlane(te - 1 - m);
-  }
-  // Steps [s0, s1) of the tiles in [lo, hi).
-  __device__ __forceinline__ void steps_of(int lo, int hi, int& s0, int& s1) const {
-    s0 = min(max(te - hi, 0), count);
-    s1 = min(max(te - lo, s0), count);
-  }
-};
-
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_wide_kernel(Params p) {
   constexpr int D = kD;
@@ -445,7 +427,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_wide_kernel(Params p) {
         }
       }  // query heads of the group
     };
-    sweep(DescTiles{te, max(te - tb, 0)});
+    // Query tiles from the last down. In a causal sweep every workgroup of a
+    // head then starts at the same (last) tile and ends at its own diagonal,
+    // so the workgroups running side by side read the same Q and dO tiles at
+    // about the same time and the L2 serves all but the first. (From the
+    // diagonal up, neighbouring workgroups start 256 rows apart, and 32 of
+    // them on one L2 keep about 4 MB of tiles in flight.)
+    sweep(reversed(dense_tiles(tb, te)));
   }
 
   // dK = scale * (dS^T Q), dV as accumulated.

@@ -390,6 +390,11 @@ struct DenseTiles {
   }
   // First step whose tile is >= x (count if none).
   __device__ __forceinline__ int first_at_least(int x) const { return min(max(x - t0, 0), count); }
+  // Steps [s0, s1) of the tiles in [lo, hi).
+  __device__ __forceinline__ void steps_of(int lo, int hi, int& s0, int& s1) const {
+    s0 = first_at_least(lo);
+    s1 = max(first_at_least(hi), s0);
+  }
 };
 __device__ __forceinline__ DenseTiles dense_tiles(int tb, int te) {
   return DenseTiles{tb, max(te - tb, 0)};
@@ -414,7 +419,42 @@ struct SparseTiles {
     const int m = a * TPB + max(x - lst[a] * TPB, 0) - s;
     return min(max(m, 0), count);
   }
+  __device__ __forceinline__ void steps_of(int lo, int hi, int& s0, int& s1) const {
+    s0 = first_at_least(lo);
+    s1 = max(first_at_least(hi), s0);
+  }
 };
+// The same tiles from the last one down (step m visits tile count-1-m).
+template <class T>
+struct ReversedTiles {
+  T up;
+  int count;
+  __device__ __forceinline__ int tile(int m) const { return up.tile(count - 1 - m); }
+  __device__ __forceinline__ void steps_of(int lo, int hi, int& s0, int& s1) const {
+    int a, e;
+    up.steps_of(lo, hi, a, e);
+    s0 = count - e;
+    s1 = count - a;
+  }
+};
+template <class T>
+__device__ __forceinline__ ReversedTiles<T> reversed(const T& t) {
+  return ReversedTiles<T>{t, t.count};
+}
+// Dense tiles from the last one down, [t0, te) visited te-1, te-2, ...
+struct DenseTilesDown {
+  int te, count;
+  __device__ __forceinline__ int tile(int m) const {
+    return __builtin_amdgcn_readfirstlane(te - 1 - m);
+  }
+  __device__ __forceinline__ void steps_of(int lo, int hi, int& s0, int& s1) const {
+    s0 = min(max(te - hi, 0), count);
+    s1 = min(max(te - lo, s0), count);
+  }
+};
+__device__ __forceinline__ DenseTilesDown reversed(const DenseTiles& t) {
+  return DenseTilesDown{t.t0 + t.count, t.count};
+}
 // The listed blocks (already in LDS, ascending, n entries) trimmed to the
 // tile range [tb, te).
 template <int TPB>
