@@ -154,7 +154,9 @@ class SclkSampler:
     """Samples the GPU's current shader clock from sysfs (pp_dpm_sclk, the
     level marked '*') in a background thread while the timed steps run; the
     main thread waits in a device synchronisation meanwhile. Reports the
-    median, minimum and maximum in MHz and the number of samples."""
+    median, minimum and maximum in MHz and the number of samples, and, where
+    the device's hwmon node exposes them, the board power read alongside
+    (power1_average or power1_input, microwatts) and its cap (power1_cap)."""
 
     def __init__(self, period_s: float = 0.004):
         import glob
@@ -166,6 +168,21 @@ class SclkSampler:
                      "no unique pp_dpm_sclk (%d found)" % len(cands))
         self.period = period_s
         self.samples = []
+        self.power = []
+        self.power_path = self.power_cap = None
+        if self.path:
+            dev = os.path.dirname(self.path)
+            for name in ("power1_average", "power1_input"):
+                found = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", name)))
+                if found:
+                    self.power_path = found[0]
+                    break
+            if self.power_path:
+                try:
+                    with open(os.path.join(os.path.dirname(self.power_path), "power1_cap")) as f:
+                        self.power_cap = float(f.read().strip()) / 1e6
+                except (OSError, ValueError):
+                    self.power_cap = None
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -184,6 +201,12 @@ class SclkSampler:
                 v = None
             if v is not None:
                 self.samples.append(v)
+            if self.power_path:
+                try:
+                    with open(self.power_path) as f:
+                        self.power.append(float(f.read().strip()) / 1e6)
+                except (OSError, ValueError):
+                    pass
             self._stop.wait(self.period)
 
     def __enter__(self):
@@ -201,9 +224,14 @@ class SclkSampler:
 
         if not self.samples:
             return {"source": self.note, "samples": 0}
-        return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
-                "max_mhz": max(self.samples), "samples": len(self.samples),
-                "source": self.note + ", sampled during the timed steps"}
+        out = {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
+               "max_mhz": max(self.samples), "samples": len(self.samples),
+               "source": self.note + ", sampled during the timed steps"}
+        if self.power:
+            out.update(power_median_w=round(statistics.median(self.power), 1),
+                       power_max_w=round(max(self.power), 1), power_cap_w=self.power_cap,
+                       power_source=os.path.basename(self.power_path))
+        return out
 
 
 def cpu_baseline(w, inp, budget_s: float = 10.0) -> dict:
@@ -745,6 +773,10 @@ def run_sweep(out_path: str | None, only=None) -> int:
                  "(%d samples)" % (sr["source"], sr["median_mhz"], sr["min_mhz"], sr["max_mhz"],
                                    sr["samples"]) if sr.get("samples") else
                  "Shader clock: not sampled (%s)" % sr["source"])
+    if sr.get("power_median_w") is not None:
+        sclk_line += "; board power (%s) median %.0f W, max %.0f W, cap %s W" % (
+            sr["power_source"], sr["power_median_w"], sr["power_max_w"],
+            "?" if sr["power_cap_w"] is None else "%.0f" % sr["power_cap_w"])
     lines = ["# Attention sweep on one MI355X", "",
              "Command: `python bench.py --sweep --out <this file>` (from the repository root).", "",
              "Clocks before the sweep (rocm-smi): " + clocks_before,
