@@ -57,6 +57,9 @@ CASES = [
                                                        False)],
     [("big", 1, 2, 2, 300, 64, "fp32", True, True), ("small", 1, 1, 1, 50, 64, "fp32", False,
                                                      False)],
+    # From 4096 rows, d = 128 runs the 64-keys-per-wave dK/dV kernel.
+    [("big", 1, 4, 2, 4200, 128, "bf16", True, True), ("small", 1, 2, 2, 4100, 128, "bf16",
+                                                        False, False)],
 ]
 
 
