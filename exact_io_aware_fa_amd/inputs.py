@@ -218,7 +218,9 @@ def make_inputs(w: Workload, with_grad_out: bool = True) -> dict:
     out = {"q": draw(qshape, w.qk_sigma), "k": draw(kvshape, w.qk_sigma),
            "v": draw(kvshape, 1.0)}
     out["do"] = draw(qshape, 1.0) if with_grad_out else None
-    out["kv_len"] = (torch.randint(w.n // 2, w.n + 1, (w.batch,), generator=g,
+    # Valid key lengths in [max(n/2, 1), n]: at least one key, as the torch
+    # wrappers require.
+    out["kv_len"] = (torch.randint(max(w.n // 2, 1), w.n + 1, (w.batch,), generator=g,
                                    dtype=torch.int32) if w.padded else None)
     return out
 
